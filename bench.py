@@ -1,0 +1,476 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-1 quantized decode path on one MI355X.
+
+Default workload: an 80-layer Llama-3.1-70B-shaped model (hidden 8192, 64/8 heads of 128,
+FFN 28672, vocabulary 128256) with synthetic weights in the Q4_K_M mix (Q4_K, with Q6_K
+for attn_v and ffn_down), all resident in HBM, greedy decode of one token per step after
+a 4096-slot synthetic fp16 KV cache.  A step is one whole token: embedding row, 80
+decode layers, final norm, LM head and argmax, every kernel in libnt.so.
+
+Prints one JSON line.  Other workloads (--config) print their own line for measurement
+runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B GEMV
+shapes in Q4_K and Q6_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
+host memory.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--layers", type=int, default=80, help="layers of the 70B model (measurement runs only)")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def host_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def timed_class(nt, torch, kclass, run, nbytes_per_launch):
+    """Average duration of one kernel class over the launches `run` makes, timed with HIP events
+    recorded around each launch on its stream."""
+    nt.nt_timing_begin(kclass, 1 << 20)
+    run()
+    torch.cuda.synchronize()
+    n, ms = nt.nt_timing_end()
+    avg_ms = ms / max(n, 1)
+    return {"launches": n, "avg_us": avg_ms * 1e3, "GBps": nbytes_per_launch / (avg_ms * 1e-3) / 1e9 if n else None}
+
+
+class Model70B:
+    """80 layer blobs + embedding + LM head + caches, generated layer by layer on the host
+    (pinned staging) and copied into HBM."""
+
+    def __init__(self, torch, nt, tg, mix, n_layers, resident_layers, n_prefill=4096, seed=0):
+        import synth
+        from synth import recipes
+        self.torch, self.nt, self.tg = torch, nt, tg
+        self.shape = recipes.LLAMA31_70B
+        self.mix = mix
+        self.n_layers = n_layers
+        self.vocab = recipes.VOCAB_70B
+        self.lay = recipes.blob_layout(self.shape, mix)
+        self.resident = set(resident_layers)
+        shp = self.shape
+        t0 = time.time()
+        stage = [torch.empty(self.lay.nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        done = [None, None]
+        copy_stream = torch.cuda.Stream()
+        self.dev_blobs, self.host_blobs = {}, {}
+        for l in range(n_layers):
+            if l in self.resident:
+                b = l % 2
+                hb = stage[b]
+                if done[b] is not None:
+                    done[b].synchronize()  # the copy that last read this staging buffer is done
+                recipes.fill_layer_blob(hb.data_ptr(), shp, mix, l, seed, self.lay)
+                d = torch.empty(self.lay.nbytes, dtype=torch.uint8, device="cuda")
+                copy_stream.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(copy_stream):
+                    d.copy_(hb, non_blocking=True)
+                    done[b] = torch.cuda.Event()
+                    done[b].record(copy_stream)
+                self.dev_blobs[l] = d
+            else:
+                hb = torch.empty(self.lay.nbytes, dtype=torch.uint8, pin_memory=True)
+                recipes.fill_layer_blob(hb.data_ptr(), shp, mix, l, seed, self.lay)
+                self.host_blobs[l] = hb
+            if l % 10 == 9:
+                log(f"  generated layer {l + 1}/{n_layers} ({time.time() - t0:.1f}s)")
+        copy_stream.synchronize()
+        del stage
+        # KV caches: [n_kv][max_ctx][128] fp16 per layer, slots < n_prefill ~ N(0,1)
+        cache_elems = shp.n_kv_heads * shp.max_ctx * shp.head_dim
+        self.kc, self.vc = [], []
+        kv_host = torch.empty(cache_elems, dtype=torch.int16, pin_memory=True)
+        for l in range(n_layers):
+            for which, lst in (("k", self.kc), ("v", self.vc)):
+                kv_host.zero_()
+                recipes.kv_cache_fill(kv_host.data_ptr(), shp, l, which, n_prefill, seed)
+                lst.append(kv_host.cuda())
+        # head
+        embd_fmt = out_fmt = synth.Q4_K if mix[ "q"] == synth.Q4_K else synth.Q6_K
+        self.embd_fmt, self.out_fmt = embd_fmt, out_fmt
+        eb = synth.matrix_bytes(embd_fmt, self.vocab, shp.dim)
+        hb = torch.empty(eb, dtype=torch.uint8, pin_memory=True)
+        synth.fill_blocks(hb.data_ptr(), embd_fmt, eb // synth.BLOCK_BYTES[embd_fmt], seed,
+                          recipes.stream_id(recipes.GLOBAL_LAYER, recipes.GID_TOKEN_EMBD))
+        self.embd = hb.cuda()
+        synth.fill_blocks(hb.data_ptr(), out_fmt, eb // synth.BLOCK_BYTES[out_fmt], seed,
+                          recipes.stream_id(recipes.GLOBAL_LAYER, recipes.GID_OUTPUT))
+        self.out = hb.cuda()
+        del hb
+        self.onorm = torch.from_numpy(synth.uniform_f32(shp.dim, seed, recipes.stream_id(recipes.GLOBAL_LAYER,
+                                                                                          recipes.GID_OUTPUT_NORM),
+                                                        0.9, 1.1)).cuda()
+        self.first_token = recipes.first_token(self.vocab, seed)
+        torch.cuda.synchronize()
+        log(f"  model ready in {time.time() - t0:.1f}s")
+
+    def plan(self):
+        tg, nt = self.tg, self.nt
+        shp = tg.layer_shape(self.shape)
+        lay = tg.layer_layout(self.lay.offset_list(), self.lay.fmt_list(), self.lay.nbytes)
+        ents = []
+        for l in range(self.n_layers):
+            if l in self.resident:
+                ents.append((self.dev_blobs[l].data_ptr(), True, self.kc[l].data_ptr(), self.vc[l].data_ptr()))
+            else:
+                ents.append((self.host_blobs[l].data_ptr(), False, self.kc[l].data_ptr(), self.vc[l].data_ptr()))
+        return tg.model_plan(shp, lay, ents)
+
+    def head(self):
+        return self.nt.ModelHead(self.embd_fmt, self.embd.data_ptr(), self.vocab, self.onorm.data_ptr(), self.out_fmt,
+                                 self.out.data_ptr())
+
+
+def token_bytes_70b(mix, n_layers, pos, vocab=128256):
+    """Algorithmic HBM bytes of one decode token at position pos: every weight once, the
+    embedding row, the KV slots read, the new K/V written, and the activations."""
+    import synth
+    from synth import recipes
+    shp = recipes.LLAMA31_70B
+    w = n_layers * recipes.layer_weight_bytes(shp, mix)
+    head_fmt = synth.Q4_K if mix["q"] == synth.Q4_K else synth.Q6_K
+    lm = synth.matrix_bytes(head_fmt, vocab, shp.dim)
+    embd_row = lm // vocab
+    kv_read = n_layers * 2 * shp.n_kv_heads * (pos + 1) * shp.head_dim * 2
+    kv_write = n_layers * 2 * shp.n_kv_heads * shp.head_dim * 2
+    gains = n_layers * 2 * shp.dim * 4 + shp.dim * 4
+    nq = shp.n_q_heads * shp.head_dim
+    # per layer: h read by 2 norm prologues + 2 residuals, q/o/a written and read, h written twice
+    acts = n_layers * 4 * (4 * shp.dim + 2 * nq + 2 * nq + 2 * shp.ffn_dim + 2 * shp.dim) + 4 * vocab
+    return w + lm + embd_row + kv_read + kv_write + gains + acts
+
+
+def ffn_up_bytes(mix, shape):
+    import synth
+    rows, cols = shape.ffn_dim, shape.dim
+    return 2 * synth.matrix_bytes(mix["gate"], rows, cols) + 4 * (2 * cols + rows)
+
+
+def cpu_baseline_70b(mix, target_s):
+    """The checker (fp64, OpenMP over the host threads) on a bounded sample of one decode
+    token: whole layers until target_s of CPU work, plus a slice of the LM head; scaled
+    to one 80-layer token."""
+    import oracle
+    import synth
+    from synth import recipes
+    shp = recipes.LLAMA31_70B
+    t_layers, n = 0.0, 0
+    h = recipes.hidden_input(shp.dim)
+    while n < 80 and t_layers < 0.8 * target_s:
+        w = recipes.layer_arrays(shp, mix, n)
+        kc = recipes.kv_cache_array(shp, n, "k", 4096)
+        vc = recipes.kv_cache_array(shp, n, "v", 4096)
+        t = time.time()
+        st = oracle.decode_layer(w, mix, shp, 4096, h, kc, vc)
+        t_layers += time.time() - t
+        h = st["h2"]
+        n += 1
+    rows = 8192
+    head_fmt = synth.Q4_K if mix["q"] == synth.Q4_K else synth.Q6_K
+    out = synth.quant_rows(head_fmt, shp.dim, range(rows), 0,
+                           recipes.stream_id(recipes.GLOBAL_LAYER, recipes.GID_OUTPUT))
+    t = time.time()
+    oracle.gemv(head_fmt, rows, shp.dim, out, oracle.rmsnorm(h, np.ones(shp.dim), shp.eps))
+    t_head = (time.time() - t) * (128256 / rows)
+    s_per_tok = 80 * (t_layers / n) + t_head
+    return {"value": 1.0 / s_per_tok, "unit": "tok/s", "cores": host_threads(), "kind": "oracle",
+            "sample": f"{n} of 80 decode layers (70B shape, pos 4096) and {rows} of 128256 LM-head rows, "
+                      f"fp64, scaled to one token ({t_layers + t_head * rows / 128256:.1f} s of CPU work)"}
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def bench_decode_70b(args, torch, nt, tg):
+    import synth
+    from synth import recipes
+    steps = args.steps if args.steps is not None else 128
+    warmup = args.warmup if args.warmup is not None else 4
+    mix = recipes.MIX_Q4_K_M
+    n_layers = args.layers
+    log(f"config 4: 70B Q4_K_M, {n_layers} layers resident, {steps} tokens after a 4096-slot cache")
+    m = Model70B(torch, nt, tg, mix, n_layers, range(n_layers))
+    plan, keep = m.plan()
+    head = m.head()
+    shp = tg.layer_shape(m.shape)
+    wsb = nt.nt_decode_token_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(m.shape.dim, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(m.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cs = torch.cuda.current_stream().cuda_stream
+
+    def run(n):
+        tok.fill_(m.first_token)
+        for i in range(n):
+            nt.nt_decode_token(None, plan, head, 4096 + i, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                               ws.data_ptr(), wsb, cs, cs, None)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tok_s = steps / dt
+    last_tok = int(tok.item())
+    # per-kernel-class durations (separate, instrumented passes over the same tokens)
+    kern = {}
+    fb = ffn_up_bytes(mix, m.shape)
+    for name, kc, nbytes in (("ffn_gate_up_swiglu", nt.K_FFN_UP, fb),
+                             ("ffn_down_resid", nt.K_FFN_DOWN,
+                              synth.matrix_bytes(mix["down"], 8192, 28672) + 4 * (28672 + 2 * 8192)),
+                             ("attn_in_qkv_rope", nt.K_ATTN_IN,
+                              sum(synth.matrix_bytes(mix[n], *m.shape.matrix_shape(n)) for n in ("q", "k", "v"))
+                              + 4 * (2 * 8192 + 8192) + 2 * 2 * 1024),
+                             ("attn_o_resid", nt.K_O, synth.matrix_bytes(mix["o"], 8192, 8192) + 4 * 3 * 8192),
+                             ("attention", nt.K_ATTN, 2 * 8 * 4160 * 128 * 2 + 4 * 2 * 8192),
+                             ("lm_head_argmax", nt.K_LM_HEAD,
+                              synth.matrix_bytes(synth.Q4_K, 128256, 8192) + 4 * (2 * 8192 + 128256))):
+        kern[name] = timed_class(nt, torch, kc, lambda: run(steps), nbytes)
+    tb = np.mean([token_bytes_70b(mix, n_layers, 4096 + i) for i in range(steps)])
+    ff = kern["ffn_gate_up_swiglu"]
+    res = {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4_k/q6_k weights, f32 math, f16 kv", "data": "synthetic (seeded, random weights of the named shape)",
+        "config": {"workload": "llama3.1-70b-shape Q4_K_M resident decode, 128256 vocab, 4096-slot fp16 KV prefill, "
+                               "greedy, batch 1", "layers": n_layers, "global_batch": 1, "seq_len": 4096 + steps,
+                   "parallelism": "none (1 GPU)"},
+        "step_hbm": {"algorithmic_bytes_per_token": int(tb), "GBps": tb * tok_s / 1e9,
+                     "frac_of_peak": tb * tok_s / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up_swiglu (fused Q4_K gate+up GEMV, SwiGLU epilogue)",
+                     "achieved": ff["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ff["GBps"] / HBM_PEAK_GBS if ff["GBps"] else None, "traffic": None,
+                     "bytes_per_launch": fb, "avg_launch_us": ff["avg_us"]},
+        "kernels": kern,
+        "last_token": last_tok,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (checker on a bounded sample)...")
+        del m
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline_70b(mix, args.cpu_seconds)
+    return res
+
+
+def rotating_gemv(torch, nt, fmt, rows, cols, copies, steps, warmup, seed=0):
+    """Time nt_gemv_q over `copies` distinct weight copies in rotation (past the 256 MB
+    last-level cache), HIP events around each launch."""
+    import synth
+    x = torch.from_numpy(synth.normal_f32(cols, seed, 999)).cuda()
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    nbytes = synth.matrix_bytes(fmt, rows, cols)
+    hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    ws = []
+    for c in range(copies):
+        synth.fill_blocks(hb.data_ptr(), fmt, nbytes // synth.BLOCK_BYTES[fmt], seed, 5000 + c)
+        ws.append(hb.cuda())
+    cs = torch.cuda.current_stream().cuda_stream
+
+    def run(n):
+        for i in range(n):
+            nt.nt_gemv_q(fmt, rows, cols, ws[i % copies].data_ptr(), x.data_ptr(), y.data_ptr(), cs)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    algo = nbytes + 4 * (rows + cols)
+    r = timed_class(nt, torch, nt.K_GEMV, lambda: run(steps), algo)
+    r.update({"rows": rows, "cols": cols, "format": synth.FORMAT_NAMES[fmt], "algorithmic_bytes": algo,
+              "frac_of_peak": r["GBps"] / HBM_PEAK_GBS, "copies": copies})
+    return r
+
+
+def bench_gemv_shapes(args, torch, nt, tg):
+    import synth
+    steps = args.steps or 200
+    warmup = args.warmup if args.warmup is not None else 10
+    out = []
+    if args.config == 1:
+        shapes = [(synth.Q8_0, 4096, 4096)]
+    else:
+        shapes = [(f, r, c) for f in (synth.Q4_K, synth.Q6_K)
+                  for (r, c) in ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672))]
+    for fmt, r, c in shapes:
+        nbytes = synth.matrix_bytes(fmt, r, c)
+        copies = max(2, int(np.ceil(600e6 / nbytes)))
+        res = rotating_gemv(torch, nt, fmt, r, c, copies, steps, warmup)
+        log(f"  {res['format']} {r}x{c}: {res['avg_us']:.2f} us, {res['GBps']:.0f} GB/s ({100 * res['frac_of_peak']:.1f}%)")
+        out.append(res)
+        torch.cuda.empty_cache()
+    best = max(out, key=lambda z: z["algorithmic_bytes"])
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": best["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": best["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "quantized weights, f32 math", "data": "synthetic",
+        "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K and Q6_K"},
+        "roofline": {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": best["frac_of_peak"], "traffic": None},
+        "gemv": out,
+    }
+
+
+def bench_layer_8b(args, torch, nt, tg):
+    import synth
+    from synth import recipes
+    steps = args.steps or 100
+    warmup = args.warmup if args.warmup is not None else 10
+    shape, mix = recipes.LLAMA3_8B, recipes.MIX_Q8_0
+    copies = 4  # 4 x 232 MB of distinct layers, past the 256 MB last-level cache
+    lays = [recipes.layer_arrays(shape, mix, l) for l in range(copies)]
+    dl = [{k: torch.from_numpy(v).cuda() for k, v in L.items()} for L in lays]
+    ws_list = [tg.layer_weights([mix[n] for n in recipes.TENSORS], [d[n] for n in recipes.TENSORS], d["attn_norm"],
+                                d["ffn_norm"]) for d in dl]
+    kc = torch.from_numpy(recipes.kv_cache_array(shape, 0, "k", 1024)).cuda()
+    vc = torch.from_numpy(recipes.kv_cache_array(shape, 0, "v", 1024)).cuda()
+    shp = tg.layer_shape(shape)
+    wsb = nt.nt_decode_layer_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.from_numpy(recipes.hidden_input(shape.dim)).cuda()
+    cs = torch.cuda.current_stream().cuda_stream
+
+    def run(n):
+        for i in range(n):
+            nt.nt_decode_layer(ws_list[i % copies], shp, 1023, h.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                               ws.data_ptr(), wsb, cs)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    t_layer = (time.perf_counter() - t0) / steps
+    lm = rotating_gemv(torch, nt, synth.Q8_0, 128256, 4096, 2, 50, 5)
+    tok_s = 1.0 / (32 * t_layer + lm["avg_us"] * 1e-6)
+    lb = recipes.layer_weight_bytes(shape, mix) + 2 * 8 * 1024 * 128 * 2
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": tok_s, "unit": "tok/s (derived: 32 layers + Q8_0 LM head)", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": t_layer * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "q8_0 weights, f32 math, f16 kv", "data": "synthetic",
+        "config": {"workload": "llama3-8b-shape Q8_0 decode layer, pos 1023, 1024-slot fp16 KV"},
+        "layer_us": t_layer * 1e6, "layer_GBps": lb / t_layer / 1e9, "layer_frac_of_peak": lb / t_layer / 1e9 / HBM_PEAK_GBS,
+        "lm_head": lm,
+    }
+
+
+def bench_stream_70b(args, torch, nt, tg):
+    from synth import recipes
+    steps = args.steps or 4
+    warmup = args.warmup if args.warmup is not None else 1
+    mix = recipes.MIX_Q6_K
+    n_layers = args.layers
+    n_res = min(26, n_layers)
+    log(f"config 5: 70B Q6_K, {n_res} resident, {n_layers - n_res} streamed from pinned host memory")
+    m = Model70B(torch, nt, tg, mix, n_layers, range(n_res))
+    plan, keep = m.plan()
+    head = m.head()
+    shp = tg.layer_shape(m.shape)
+    wsb = nt.nt_decode_token_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(m.shape.dim, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(m.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), m.lay.nbytes)
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    stats = nt.StreamStats()
+    # plain pinned copy ceiling
+    probe = m.host_blobs[min(m.host_blobs)] if m.host_blobs else None
+    ceil = None
+    if probe is not None:
+        for _ in range(2):
+            with torch.cuda.stream(copy):
+                staging[0].copy_(probe, non_blocking=True)
+        copy.synchronize()
+        t = time.perf_counter()
+        for _ in range(3):
+            with torch.cuda.stream(copy):
+                staging[0].copy_(probe, non_blocking=True)
+        copy.synchronize()
+        ceil = 3 * m.lay.nbytes / (time.perf_counter() - t) / 1e9
+
+    def run(n):
+        tok.fill_(m.first_token)
+        tot = 0
+        for i in range(n):
+            nt.nt_decode_token(st, plan, head, 4096 + i, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                               ws.data_ptr(), wsb, compute.cuda_stream, copy.cuda_stream, stats)
+            tot += stats.h2d_bytes
+        return tot
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    h2d = run(steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    nt.nt_stream_destroy(st)
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": steps / dt, "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q6_k weights, f32 math, f16 kv", "data": "synthetic",
+        "config": {"workload": "llama3.1-70b-shape Q6_K, 26 layers resident, 54 streamed from pinned host memory",
+                   "layers": n_layers},
+        "h2d_GBps": h2d / dt / 1e9, "pinned_copy_ceiling_GBps": ceil, "pcie_gen5_x16_GBps": 63.0,
+        "h2d_bytes_per_token": h2d / steps,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this decode path is single-GPU by design "
+              "(no sharding or collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_weight_streaming_dequant_amd as nt
+    from quantized_weight_streaming_dequant_amd import torch_glue as tg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    nt.load()
+    if args.config == 4:
+        res = bench_decode_70b(args, torch, nt, tg)
+    elif args.config in (1, 3):
+        res = bench_gemv_shapes(args, torch, nt, tg)
+    elif args.config == 2:
+        res = bench_layer_8b(args, torch, nt, tg)
+    else:
+        res = bench_stream_70b(args, torch, nt, tg)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+/*
+ * nt — batch-1 decode over block-quantized weights on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libnt.so.  Plain pointers and sizes only.  Unless a comment says
+ * otherwise, every pointer argument is DEVICE memory, every call only enqueues
+ * work on the given HIP stream (a hipStream_t passed as void*; NULL means the
+ * null stream) and returns, and device-side faults surface at the caller's
+ * next synchronisation.  The library never synchronises the device.
+ *
+ * Errors: every int-returning call returns NT_OK (0) or a negative nt_status;
+ * on error nothing has been enqueued and nt_last_error() (thread-local)
+ * describes the failure.
+ *
+ * Ownership: the caller owns every buffer (weights, activations, caches,
+ * workspaces).  The library allocates nothing on these paths and keeps no
+ * pointer after a call returns, except that an nt_streamer keeps its staging
+ * pointers and its events until nt_stream_destroy.
+ *
+ * Sources (the ntransformer pages): ntransformer overview, de.news.hada.io —
+ * "Überblick über NTransformer" (GGUF Q4_0, Q8_0, Q4_K_M, Q5_K, Q6_K, F16, F32
+ * weights), "Hauptfunktionen" (RoPE, GQA, SwiGLU, RMSNorm, KV cache; SLEP
+ * streaming overlapping transfer and compute with double buffering),
+ * "Architektur und Codestruktur" (GEMV, RMSNorm, RoPE, SwiGLU, softmax
+ * kernels), "Roadmap der Entwicklungsphasen" (F16 KV cache; a public C API is
+ * planned but not printed, so these signatures are this library's own);
+ * the 70B PCIe P2P article, blog.hotdry.top — §gpu-nvme-direct的实现架构
+ * (pinned staging memory, double buffering overlapped on streams),
+ * §传统数据路径的性能瓶颈分析 (each token reads every weight).
+ */
+#ifndef NT_H
+#define NT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block formats.  Matrices are rows x cols, stored row-major as rows runs of
+ * cols / block_elems consecutive blocks (cols is the contiguous dimension).
+ * Byte layouts (little-endian, fp16 = IEEE binary16), GGML's:
+ *   NT_Q8_0  34 B / 32 weights : d fp16 @0, q int8[32] @2                  w = d*q
+ *   NT_Q4_0  18 B / 32 weights : d fp16 @0, nibbles[16] @2                 w = d*(n-8)
+ *            (weight i<16: low nibble of byte i; i>=16: high nibble of byte i-16)
+ *   NT_Q4_K 144 B / 256 weights: d @0, dmin @2, 8 x (6-bit scale, 6-bit min) packed in 12 B @4,
+ *            nibbles[128] @16                                               w = d*sc*q - dmin*m
+ *   NT_Q6_K 210 B / 256 weights: low nibbles[128] @0, 2-bit highs[64] @128, int8 scales[16] @192,
+ *            d fp16 @208                                                    w = d*s*(q-32)
+ */
+typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3 } nt_format;
+
+typedef enum {
+  NT_OK = 0,
+  NT_EINVAL = -1,   /* null pointer, bad count, or inconsistent arguments */
+  NT_EFORMAT = -2,  /* unknown format id */
+  NT_ESHAPE = -3,   /* size not a multiple of the block, zero/negative, or over a stated limit */
+  NT_EALIGN = -4,   /* a pointer is not aligned as its argument requires */
+  NT_EHOSTMEM = -5, /* a host buffer that must be page-locked is not */
+  NT_EHIP = -6      /* a HIP runtime call failed (message has the HIP error) */
+} nt_status;
+
+const char* nt_last_error(void);
+const char* nt_version(void);
+
+int nt_block_elems(int fmt);                                /* weights per block, or NT_EFORMAT */
+int nt_block_bytes(int fmt);                                /* bytes per block, or NT_EFORMAT */
+int64_t nt_matrix_bytes(int fmt, int64_t rows, int64_t cols); /* bytes of a rows x cols matrix, or < 0 */
+
+/* Largest cols accepted by the GEMV entry points (x is held in LDS, padded). */
+#define NT_GEMV_MAX_COLS 32768
+
+/* Dequantize a whole matrix to fp32: w[r*cols + c].  Every value equals the
+ * block's exact weight rounded once (round-to-nearest-even) to fp32.
+ * A test hook for the bit-exactness of the decoders (format pages above).
+ * blocks: 4-byte aligned.  Returns NT_ESHAPE if cols % block_elems != 0. */
+int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, void* stream);
+
+/* y = W x for a block-quantized W (rows x cols), x and y fp32.
+ * The GEMV step of the decode path (ntransformer overview, "Architektur und
+ * Codestruktur").  blocks: 16-byte aligned; x: 16-byte aligned, cols floats;
+ * y: rows floats, overwritten, must not overlap x or blocks.
+ * cols must be a multiple of the block size and <= NT_GEMV_MAX_COLS;
+ * rows <= 2^31 - 1.  Accuracy: |y_r - sum_c w_rc x_c| <= 1e-3 * sum_c |w_rc x_c|
+ * (fp32 accumulation, scale factors applied per block). */
+int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream);
+
+/* RMSNorm: y_i = gain_i * x_i / sqrt(mean_j x_j^2 + eps)  (eps inside the root).
+ * ntransformer overview, "Hauptfunktionen" (RMSNorm).  y may equal x.  n <= 2^24. */
+int nt_rmsnorm(int64_t n, const float* x, const float* gain, float eps, float* y, void* stream);
+
+/* RoPE in place on n_heads consecutive heads of head_dim floats: the adjacent
+ * pair (2i, 2i+1) of each head turns by the angle pos * theta^(-2i/head_dim)
+ * (angles formed in fp64).  ntransformer overview, "Hauptfunktionen" (RoPE).
+ * head_dim even, <= 1024; pos >= 0. */
+int nt_rope(int n_heads, int head_dim, int pos, float theta, float* qk, void* stream);
+
+/* GQA decode attention for one token.  q: [n_q_heads][head_dim] fp32.
+ * k_cache, v_cache: [n_kv_heads][max_ctx][head_dim] fp16 bits.  Query head h
+ * reads KV head h / (n_q_heads / n_kv_heads) and attends over cache slots
+ * [0, n_ctx): s_t = q.k_t / sqrt(head_dim), p = softmax(s), out_h = sum_t p_t v_t.
+ * ntransformer overview, "Hauptfunktionen" (GQA, KV cache) and "Architektur
+ * und Codestruktur" (softmax).  out: [n_q_heads][head_dim] fp32.
+ * ws: workspace of nt_attn_decode_ws_bytes() bytes, 256-byte aligned; its
+ * counter region must be zero before the first call that uses it (e.g. a
+ * zero-filled allocation); every call leaves it zero again.
+ * head_dim == 128; n_q_heads % n_kv_heads == 0; n_q_heads / n_kv_heads <= 16;
+ * 1 <= n_ctx <= max_ctx. */
+int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int max_ctx, const float* q,
+                   const uint16_t* k_cache, const uint16_t* v_cache, float* out, void* ws, size_t ws_bytes,
+                   void* stream);
+size_t nt_attn_decode_ws_bytes(int n_q_heads, int n_kv_heads, int head_dim, int max_ctx);
+
+/* SwiGLU: out_i = gate_i / (1 + exp(-gate_i)) * up_i.
+ * ntransformer overview, "Hauptfunktionen" (SwiGLU).  out may equal gate or up. */
+int nt_swiglu(int64_t n, const float* gate, const float* up, float* out, void* stream);
+
+/* ------------------------------------------------------------------ layers */
+
+typedef struct {
+  int dim;        /* hidden size */
+  int n_q_heads;
+  int n_kv_heads;
+  int head_dim;   /* must be 128 */
+  int ffn_dim;
+  int max_ctx;    /* cache capacity in slots */
+  float eps;      /* RMSNorm epsilon */
+  float rope_theta;
+} nt_layer_shape;
+
+/* Matrix order in every per-layer array below. */
+enum { NT_W_Q = 0, NT_W_K, NT_W_V, NT_W_O, NT_W_GATE, NT_W_UP, NT_W_DOWN, NT_W_COUNT };
+
+typedef struct {
+  int fmt[NT_W_COUNT];        /* nt_format of q, k, v, o, gate, up, down */
+  const void* w[NT_W_COUNT];  /* device blocks, 16-byte aligned: q [nq*hd x dim], k, v [nkv*hd x dim],
+                                 o [dim x nq*hd], gate, up [ffn x dim], down [dim x ffn] */
+  const float* attn_norm;     /* [dim] */
+  const float* ffn_norm;      /* [dim] */
+} nt_layer_weights;
+
+/* One Llama decode layer for the token at position pos (ntransformer overview,
+ * "Hauptfunktionen"):
+ *   n1 = RMSNorm(h, attn_norm); q = Wq n1, k = Wk n1, v = Wv n1; RoPE(q, k, pos);
+ *   k, v -> fp16 (RNE) into cache slot pos; o = attention over slots [0, pos];
+ *   h1 = h + Wo o; n2 = RMSNorm(h1, ffn_norm); a = SwiGLU(Wg n2, Wu n2); h2 = h1 + Wd a.
+ * h: [dim] fp32, in/out (h2 on return).  k_cache, v_cache: [nkv][max_ctx][128] fp16 bits.
+ * ws: nt_decode_layer_ws_bytes() bytes, 256-byte aligned, zero-filled before its first use
+ * (its counter region is left zero by every call).  After the call ws holds, as fp32 arrays
+ * at these byte offsets (see nt_decode_layer_ws_offsets): the rotated query q [nq*hd],
+ * the attention output o [nq*hd], h1 [dim] and the SwiGLU output a [ffn].
+ * Constraints: head_dim 128; dim, nq*hd and ffn multiples of 256 and <= NT_GEMV_MAX_COLS;
+ * 0 <= pos < max_ctx; q/k/v share one format family launch (any of the four formats). */
+int nt_decode_layer(const nt_layer_weights* w, const nt_layer_shape* shp, int pos, float* h, uint16_t* k_cache,
+                    uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream);
+size_t nt_decode_layer_ws_bytes(const nt_layer_shape* shp);
+/* off[0..4] = byte offsets of q, o, h1, a and the attention partials inside the layer workspace */
+int nt_decode_layer_ws_offsets(const nt_layer_shape* shp, int64_t* off);
+
+/* ------------------------------------------------------------ token glue */
+
+/* h = dequantized row *token of an embedding table [n_vocab x dim] (token read on
+ * the device).  A token outside [0, n_vocab) writes zeros.  table: 4-byte aligned. */
+int nt_embed_row(int fmt, int64_t n_vocab, int64_t dim, const void* table, const int32_t* token, float* h,
+                 void* stream);
+
+/* *out_index = first index of the maximum of v[0..n) (greedy pick; ties -> lowest index). */
+int nt_argmax(int64_t n, const float* v, int32_t* out_index, void* stream);
+
+/* ------------------------------------------------------- models, streaming */
+
+/* Where each tensor of a layer sits in one contiguous layer blob (bytes). */
+typedef struct {
+  int64_t offset[NT_W_COUNT + 2]; /* q, k, v, o, gate, up, down, attn_norm, ffn_norm; 256-byte aligned */
+  int fmt[NT_W_COUNT];
+  int64_t blob_bytes;
+} nt_layer_layout;
+
+typedef struct {
+  const void* blob;     /* device pointer if resident, else page-locked HOST pointer */
+  int resident;         /* 1: run in place; 0: stream through a staging buffer */
+  uint16_t* k_cache;    /* device, [nkv][max_ctx][128] fp16 */
+  uint16_t* v_cache;
+} nt_layer_entry;
+
+typedef struct {
+  nt_layer_shape shape;
+  nt_layer_layout layout;
+  int n_layers;
+  const nt_layer_entry* layers; /* host array of n_layers entries */
+} nt_model_plan;
+
+typedef struct {
+  int64_t layers_streamed;  /* layers that ran from a staging buffer in this call */
+  int64_t h2d_bytes;        /* bytes copied host-to-device by this call (prefetches included) */
+} nt_stream_stats;
+
+typedef struct nt_streamer nt_streamer;
+
+/* A double-buffered layer streamer (ntransformer overview, "Hauptfunktionen":
+ * SLEP overlaps transfer and compute with double buffering; 70B PCIe P2P
+ * article, §gpu-nvme-direct的实现架构: pinned staging memory and two buffers on
+ * streams).  staging0/1: device buffers of staging_bytes each, 256-byte aligned,
+ * owned by the caller.  Creates four HIP events (on the current device). */
+int nt_stream_create(void* staging0, void* staging1, size_t staging_bytes, nt_streamer** out);
+void nt_stream_destroy(nt_streamer* st);
+
+/* Run all plan->n_layers layers for the token at pos over h (in/out, [dim]).
+ * Resident layers run in place on `compute`.  A streamed layer's blob is copied
+ * by hipMemcpyAsync on `copy` into a free staging buffer as soon as that buffer
+ * frees (the compute stream records "free" events, the copy stream "ready"
+ * events), so copies run ahead of compute and across calls: at the end of a
+ * call the first streamed layers of the next token are already in flight.
+ * Streamed blobs must be page-locked host memory (NT_EHOSTMEM otherwise) and
+ * fit staging_bytes.  ws as for nt_decode_layer.  compute != copy.  stats nullable.
+ * A streamer must be used with one plan at a time, from one host thread. */
+int nt_stream_layers(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, void* ws, size_t ws_bytes,
+                     void* compute, void* copy, nt_stream_stats* stats);
+
+typedef struct {
+  int embd_fmt;
+  const void* token_embd;   /* device [n_vocab x dim] blocks */
+  int64_t n_vocab;
+  const float* output_norm; /* device [dim] */
+  int out_fmt;
+  const void* output;       /* device [n_vocab x dim] blocks (LM head) */
+} nt_model_head;
+
+/* One greedy decode token: h = embed(*token); all layers (nt_stream_layers, or in
+ * place when st is NULL, which requires every layer resident); logits =
+ * W_out RMSNorm(h, output_norm); *token = argmax(logits) (ties -> lowest id).
+ * token: device int32, in/out.  logits: device [n_vocab] fp32.  h: device [dim].
+ * ws: nt_decode_token_ws_bytes() bytes (zero-filled before first use). */
+int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_head* head, int pos, int32_t* token,
+                    float* logits, float* h, void* ws, size_t ws_bytes, void* compute, void* copy,
+                    nt_stream_stats* stats);
+size_t nt_decode_token_ws_bytes(const nt_layer_shape* shp);
+
+/* ------------------------------------------------------- measurement hook */
+
+/* Kernel classes that can be timed with HIP events recorded around each launch
+ * on the launching stream (adds small gaps; for measurement runs only). */
+enum { NT_K_ATTN_IN = 0, NT_K_ATTN, NT_K_O, NT_K_FFN_UP, NT_K_FFN_DOWN, NT_K_LM_HEAD, NT_K_GEMV, NT_K_COUNT };
+/* Start timing launches of kernel class kclass (one class at a time); up to
+ * max_launches launches are recorded.  Creates events on the current device. */
+int nt_timing_begin(int kclass, int max_launches);
+/* Wait for the recorded launches, return their count and summed milliseconds, and stop timing. */
+int nt_timing_end(int* n_launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NT_H */

@@ -1,0 +1,608 @@
+// C ABI of libnt.so: argument checks, workspace layout, launch sequencing and the
+// double-buffered layer streamer.  Declarations and contracts: include/nt.h.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/nt.h"
+#include "attn.h"
+#include "common.h"
+#include "gemv.h"
+#include "small.h"
+
+using namespace nt;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(NT_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_Q6_K; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------ timing hook
+struct Timing {
+  std::mutex mu;
+  int kclass = -1;
+  int max_launches = 0;
+  std::vector<hipEvent_t> ev;  // begin/end pairs
+} g_timing;
+
+struct TimedLaunch {
+  hipStream_t s;
+  bool on = false;
+  TimedLaunch(int kclass, hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.kclass == kclass && (int)g_timing.ev.size() < 2 * g_timing.max_launches) {
+      hipEvent_t b, e;
+      if (hipEventCreate(&b) == hipSuccess && hipEventCreate(&e) == hipSuccess) {
+        (void)hipEventRecord(b, s);
+        g_timing.ev.push_back(b);
+        g_timing.ev.push_back(e);
+        on = true;
+      }
+    }
+  }
+  ~TimedLaunch() {
+    if (on) {
+      std::lock_guard<std::mutex> lk(g_timing.mu);
+      (void)hipEventRecord(g_timing.ev.back(), s);
+    }
+  }
+};
+
+// ------------------------------------------------------------ workspace layout
+struct LayerWs {
+  size_t q, o, h1, a, part, cnt, key, total;
+};
+
+LayerWs layer_ws(const nt_layer_shape& s) {
+  LayerWs w;
+  size_t off = 0;
+  const size_t nq = (size_t)s.n_q_heads * s.head_dim;
+  w.q = off; off = align256(off + 4 * nq);
+  w.o = off; off = align256(off + 4 * nq);
+  w.h1 = off; off = align256(off + 4 * (size_t)s.dim);
+  w.a = off; off = align256(off + 4 * (size_t)s.ffn_dim);
+  w.part = off; off = align256(off + 4 * attn_part_floats(s.n_q_heads, s.max_ctx));
+  w.cnt = off; off = align256(off + 4 * (size_t)s.n_kv_heads);
+  w.key = off; off = align256(off + 8);
+  w.total = off;
+  return w;
+}
+
+int check_shape(const nt_layer_shape* s) {
+  if (!s) return fail(NT_EINVAL, "shape is null");
+  if (s->head_dim != 128) return fail(NT_ESHAPE, "head_dim must be 128 (got %d)", s->head_dim);
+  if (s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->n_q_heads % s->n_kv_heads)
+    return fail(NT_ESHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", s->n_q_heads, s->n_kv_heads);
+  const int grp = s->n_q_heads / s->n_kv_heads;
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8 && grp != 16)
+    return fail(NT_ESHAPE, "query heads per KV head must be 1, 2, 4, 8 or 16 (got %d)", grp);
+  const int nq = s->n_q_heads * s->head_dim;
+  if (s->dim <= 0 || s->dim % 256 || s->dim > NT_GEMV_MAX_COLS)
+    return fail(NT_ESHAPE, "dim must be a positive multiple of 256 up to %d (got %d)", NT_GEMV_MAX_COLS, s->dim);
+  if (nq % 256 || nq > NT_GEMV_MAX_COLS) return fail(NT_ESHAPE, "n_q_heads*head_dim must be a multiple of 256 up to %d", NT_GEMV_MAX_COLS);
+  if (s->ffn_dim <= 0 || s->ffn_dim % 256 || s->ffn_dim > NT_GEMV_MAX_COLS)
+    return fail(NT_ESHAPE, "ffn_dim must be a positive multiple of 256 up to %d (got %d)", NT_GEMV_MAX_COLS, s->ffn_dim);
+  if (s->max_ctx <= 0) return fail(NT_ESHAPE, "max_ctx must be positive");
+  if (!(s->eps >= 0.f)) return fail(NT_EINVAL, "eps must be >= 0");
+  if (!(s->rope_theta > 0.f)) return fail(NT_EINVAL, "rope_theta must be > 0");
+  return NT_OK;
+}
+
+int check_weights(const nt_layer_weights* w) {
+  if (!w) return fail(NT_EINVAL, "weights are null");
+  for (int i = 0; i < NT_W_COUNT; ++i) {
+    if (!fmt_ok(w->fmt[i])) return fail(NT_EFORMAT, "unknown format %d for matrix %d", w->fmt[i], i);
+    if (!w->w[i]) return fail(NT_EINVAL, "matrix %d pointer is null", i);
+    if (!aligned(w->w[i], 16)) return fail(NT_EALIGN, "matrix %d must be 16-byte aligned", i);
+  }
+  if (w->fmt[NT_W_GATE] != w->fmt[NT_W_UP]) return fail(NT_EFORMAT, "gate and up must share a format");
+  if (!w->attn_norm || !w->ffn_norm) return fail(NT_EINVAL, "norm gains are null");
+  if (!aligned(w->attn_norm, 16) || !aligned(w->ffn_norm, 16)) return fail(NT_EALIGN, "norm gains must be 16-byte aligned");
+  return NT_OK;
+}
+
+GemvSeg make_seg(const void* w, int fmt, int rows, int cols, int tile0) {
+  GemvSeg g;
+  g.w = reinterpret_cast<const uint8_t*>(w);
+  g.fmt = fmt;
+  g.rows = rows;
+  g.row_bytes = (int64_t)(cols / block_elems(fmt)) * block_bytes(fmt);
+  g.tile0 = tile0;
+  return g;
+}
+
+GemvArgs blank_args() {
+  GemvArgs a;
+  memset(&a, 0, sizeof(a));
+  return a;
+}
+
+// Enqueue one decode layer (arguments already checked).
+int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float* h, uint16_t* kc, uint16_t* vc,
+              uint8_t* ws, hipStream_t st) {
+  const LayerWs L = layer_ws(s);
+  float* wq = reinterpret_cast<float*>(ws + L.q);
+  float* wo = reinterpret_cast<float*>(ws + L.o);
+  float* wh1 = reinterpret_cast<float*>(ws + L.h1);
+  float* wa = reinterpret_cast<float*>(ws + L.a);
+  const int nq = s.n_q_heads * s.head_dim, nkv = s.n_kv_heads * s.head_dim;
+  hipError_t e;
+
+  {  // a1-a3: RMSNorm prologue, q/k/v GEMV, RoPE + fp16 cache append epilogue
+    const GemvPlan p = gemv_plan(EPI_QKV, s.dim);
+    GemvArgs a = blank_args();
+    a.x = h; a.gain = w.attn_norm; a.eps = s.eps; a.cols = s.dim;
+    a.nseg = 3;
+    int t = 0;
+    a.seg[0] = make_seg(w.w[NT_W_Q], w.fmt[NT_W_Q], nq, s.dim, t); t += gemv_tiles(p, nq);
+    a.seg[1] = make_seg(w.w[NT_W_K], w.fmt[NT_W_K], nkv, s.dim, t); t += gemv_tiles(p, nkv);
+    a.seg[2] = make_seg(w.w[NT_W_V], w.fmt[NT_W_V], nkv, s.dim, t); t += gemv_tiles(p, nkv);
+    a.q_out = wq; a.k_cache = kc; a.v_cache = vc; a.pos = pos; a.max_ctx = s.max_ctx; a.rope_theta = s.rope_theta;
+    const int mask = (1 << w.fmt[NT_W_Q]) | (1 << w.fmt[NT_W_K]) | (1 << w.fmt[NT_W_V]);
+    TimedLaunch tl(NT_K_ATTN_IN, st);
+    if ((e = gemv_launch(mask, EPI_QKV, p, t, a, st)) != hipSuccess) return hip_fail(e, "attn_in launch");
+  }
+  {  // a4: GQA attention over slots [0, pos]
+    AttnArgs a;
+    a.q = wq; a.k_cache = kc; a.v_cache = vc; a.out = wo;
+    a.part = reinterpret_cast<float*>(ws + L.part);
+    a.counter = reinterpret_cast<int*>(ws + L.cnt);
+    a.n_kv = s.n_kv_heads; a.n_ctx = pos + 1; a.max_ctx = s.max_ctx;
+    a.slots_per_wave = attn_slots_per_wave(a.n_ctx, a.n_kv);
+    a.n_split = attn_n_split(a.n_ctx, a.slots_per_wave);
+    TimedLaunch tl(NT_K_ATTN, st);
+    if ((e = attn_launch(a, s.n_q_heads / s.n_kv_heads, st)) != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  {  // a5: O GEMV + residual (h1 also kept in the workspace)
+    const GemvPlan p = gemv_plan(EPI_RESID, nq);
+    GemvArgs a = blank_args();
+    a.x = wo; a.cols = nq; a.nseg = 1;
+    a.seg[0] = make_seg(w.w[NT_W_O], w.fmt[NT_W_O], s.dim, nq, 0);
+    a.y = h; a.resid = h; a.y2 = wh1;
+    TimedLaunch tl(NT_K_O, st);
+    if ((e = gemv_launch(1 << w.fmt[NT_W_O], EPI_RESID, p, gemv_tiles(p, s.dim), a, st)) != hipSuccess)
+      return hip_fail(e, "o launch");
+  }
+  {  // a6-a8: RMSNorm prologue, paired gate/up GEMV, SwiGLU epilogue
+    const GemvPlan p = gemv_plan(EPI_SWIGLU, s.dim);
+    GemvArgs a = blank_args();
+    a.x = h; a.gain = w.ffn_norm; a.eps = s.eps; a.cols = s.dim; a.nseg = 2;
+    a.seg[0] = make_seg(w.w[NT_W_GATE], w.fmt[NT_W_GATE], s.ffn_dim, s.dim, 0);
+    a.seg[1] = make_seg(w.w[NT_W_UP], w.fmt[NT_W_UP], s.ffn_dim, s.dim, 1 << 30);
+    a.y = wa;
+    TimedLaunch tl(NT_K_FFN_UP, st);
+    if ((e = gemv_launch(1 << w.fmt[NT_W_GATE], EPI_SWIGLU, p, gemv_tiles(p, s.ffn_dim), a, st)) != hipSuccess)
+      return hip_fail(e, "gate/up launch");
+  }
+  {  // a9: down GEMV + residual
+    const GemvPlan p = gemv_plan(EPI_RESID, s.ffn_dim);
+    GemvArgs a = blank_args();
+    a.x = wa; a.cols = s.ffn_dim; a.nseg = 1;
+    a.seg[0] = make_seg(w.w[NT_W_DOWN], w.fmt[NT_W_DOWN], s.dim, s.ffn_dim, 0);
+    a.y = h; a.resid = h;
+    TimedLaunch tl(NT_K_FFN_DOWN, st);
+    if ((e = gemv_launch(1 << w.fmt[NT_W_DOWN], EPI_RESID, p, gemv_tiles(p, s.dim), a, st)) != hipSuccess)
+      return hip_fail(e, "down launch");
+  }
+  return NT_OK;
+}
+
+nt_layer_weights weights_in_blob(const uint8_t* blob, const nt_layer_layout& lay) {
+  nt_layer_weights w;
+  for (int i = 0; i < NT_W_COUNT; ++i) {
+    w.fmt[i] = lay.fmt[i];
+    w.w[i] = blob + lay.offset[i];
+  }
+  w.attn_norm = reinterpret_cast<const float*>(blob + lay.offset[NT_W_COUNT]);
+  w.ffn_norm = reinterpret_cast<const float*>(blob + lay.offset[NT_W_COUNT + 1]);
+  return w;
+}
+
+int check_layout(const nt_layer_shape& s, const nt_layer_layout& lay) {
+  const int nq = s.n_q_heads * s.head_dim, nkv = s.n_kv_heads * s.head_dim;
+  const int64_t rows[NT_W_COUNT] = {nq, nkv, nkv, s.dim, s.ffn_dim, s.ffn_dim, s.dim};
+  const int64_t cols[NT_W_COUNT] = {s.dim, s.dim, s.dim, nq, s.dim, s.dim, s.ffn_dim};
+  for (int i = 0; i < NT_W_COUNT; ++i) {
+    if (!fmt_ok(lay.fmt[i])) return fail(NT_EFORMAT, "layout: unknown format %d for matrix %d", lay.fmt[i], i);
+    const int64_t nb = nt_matrix_bytes(lay.fmt[i], rows[i], cols[i]);
+    if (lay.offset[i] < 0 || lay.offset[i] % 256 || lay.offset[i] + nb > lay.blob_bytes)
+      return fail(NT_ESHAPE, "layout: matrix %d offset %lld (size %lld) is not 256-aligned inside the blob", i,
+                  (long long)lay.offset[i], (long long)nb);
+  }
+  for (int i = NT_W_COUNT; i < NT_W_COUNT + 2; ++i)
+    if (lay.offset[i] < 0 || lay.offset[i] % 256 || lay.offset[i] + 4 * (int64_t)s.dim > lay.blob_bytes)
+      return fail(NT_ESHAPE, "layout: gain %d offset is not 256-aligned inside the blob", i - NT_W_COUNT);
+  if (lay.fmt[NT_W_GATE] != lay.fmt[NT_W_UP]) return fail(NT_EFORMAT, "layout: gate and up must share a format");
+  return NT_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+struct nt_streamer {
+  uint8_t* staging[2];
+  size_t bytes;
+  hipEvent_t ready[2], freed[2];
+  bool freed_recorded[2];
+  const void* plan_layers;  // identity of the plan the sequence counters belong to
+  int n_streamed;
+  int64_t c_run;    // next streamed-layer sequence number to run
+  int64_t c_issue;  // next streamed-layer sequence number to copy
+};
+
+extern "C" {
+
+const char* nt_last_error(void) { return g_err.c_str(); }
+const char* nt_version(void) { return "nt 0.1 (gfx950)"; }
+
+int nt_block_elems(int fmt) { return fmt_ok(fmt) ? block_elems(fmt) : fail(NT_EFORMAT, "unknown format %d", fmt); }
+int nt_block_bytes(int fmt) { return fmt_ok(fmt) ? block_bytes(fmt) : fail(NT_EFORMAT, "unknown format %d", fmt); }
+
+int64_t nt_matrix_bytes(int fmt, int64_t rows, int64_t cols) {
+  if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
+  if (rows <= 0 || cols <= 0 || cols % block_elems(fmt)) return fail(NT_ESHAPE, "bad shape %lld x %lld", (long long)rows, (long long)cols);
+  return rows * (cols / block_elems(fmt)) * block_bytes(fmt);
+}
+
+int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, void* stream) {
+  if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
+  if (rows <= 0 || cols <= 0 || cols % block_elems(fmt)) return fail(NT_ESHAPE, "cols must be a positive multiple of %d", block_elems(fmt));
+  if (!blocks || !w) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(blocks, 4) || !aligned(w, 4)) return fail(NT_EALIGN, "blocks and w must be 4-byte aligned");
+  hipError_t e = dequant_launch(fmt, rows, cols, blocks, w, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "dequant launch");
+}
+
+int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream) {
+  if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
+  if (rows <= 0 || rows > 0x7FFFFFFF || cols <= 0 || cols % block_elems(fmt) || cols > NT_GEMV_MAX_COLS)
+    return fail(NT_ESHAPE, "need 0 < rows < 2^31 and cols a positive multiple of %d up to %d (got %lld x %lld)",
+                block_elems(fmt), NT_GEMV_MAX_COLS, (long long)rows, (long long)cols);
+  if (!blocks || !x || !y) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return fail(NT_EALIGN, "blocks and x must be 16-byte aligned, y 4-byte");
+  const GemvPlan p = gemv_plan(EPI_STORE, (int)cols);
+  GemvArgs a = blank_args();
+  a.x = x; a.cols = (int)cols; a.nseg = 1;
+  a.seg[0] = make_seg(blocks, fmt, (int)rows, (int)cols, 0);
+  a.y = y;
+  TimedLaunch tl(NT_K_GEMV, (hipStream_t)stream);
+  hipError_t e = gemv_launch(1 << fmt, EPI_STORE, p, gemv_tiles(p, (int)rows), a, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "gemv launch");
+}
+
+int nt_rmsnorm(int64_t n, const float* x, const float* gain, float eps, float* y, void* stream) {
+  if (n <= 0 || n > (1 << 24)) return fail(NT_ESHAPE, "n must be in [1, 2^24]");
+  if (!x || !gain || !y) return fail(NT_EINVAL, "null pointer");
+  if (!(eps >= 0.f)) return fail(NT_EINVAL, "eps must be >= 0");
+  hipError_t e = rmsnorm_launch(n, x, gain, eps, y, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "rmsnorm launch");
+}
+
+int nt_rope(int n_heads, int head_dim, int pos, float theta, float* qk, void* stream) {
+  if (n_heads <= 0 || head_dim <= 0 || head_dim % 2 || head_dim > 1024) return fail(NT_ESHAPE, "bad head shape");
+  if (pos < 0) return fail(NT_EINVAL, "pos must be >= 0");
+  if (!(theta > 0.f)) return fail(NT_EINVAL, "theta must be > 0");
+  if (!qk) return fail(NT_EINVAL, "null pointer");
+  hipError_t e = rope_launch(n_heads, head_dim, pos, theta, qk, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "rope launch");
+}
+
+size_t nt_attn_decode_ws_bytes(int n_q_heads, int n_kv_heads, int head_dim, int max_ctx) {
+  (void)head_dim;
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || max_ctx <= 0) return 0;
+  return align256(4 * attn_part_floats(n_q_heads, max_ctx)) + align256(4 * (size_t)n_kv_heads);
+}
+
+int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int max_ctx, const float* q,
+                   const uint16_t* k_cache, const uint16_t* v_cache, float* out, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (head_dim != 128) return fail(NT_ESHAPE, "head_dim must be 128");
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads) return fail(NT_ESHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  const int grp = n_q_heads / n_kv_heads;
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8 && grp != 16) return fail(NT_ESHAPE, "group size must be 1, 2, 4, 8 or 16");
+  if (n_ctx < 1 || n_ctx > max_ctx) return fail(NT_ESHAPE, "need 1 <= n_ctx <= max_ctx");
+  if (!q || !k_cache || !v_cache || !out || !ws) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(ws, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(q, 16))
+    return fail(NT_EALIGN, "ws must be 256-byte aligned; q and caches 16-byte aligned");
+  if (ws_bytes < nt_attn_decode_ws_bytes(n_q_heads, n_kv_heads, head_dim, max_ctx)) return fail(NT_EINVAL, "workspace too small");
+  AttnArgs a;
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.out = out;
+  a.part = reinterpret_cast<float*>(ws);
+  a.counter = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(ws) + align256(4 * attn_part_floats(n_q_heads, max_ctx)));
+  a.n_kv = n_kv_heads; a.n_ctx = n_ctx; a.max_ctx = max_ctx;
+  a.slots_per_wave = attn_slots_per_wave(n_ctx, n_kv_heads);
+  a.n_split = attn_n_split(n_ctx, a.slots_per_wave);
+  hipError_t e = attn_launch(a, grp, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "attention launch");
+}
+
+int nt_swiglu(int64_t n, const float* gate, const float* up, float* out, void* stream) {
+  if (n <= 0) return fail(NT_ESHAPE, "n must be positive");
+  if (!gate || !up || !out) return fail(NT_EINVAL, "null pointer");
+  hipError_t e = swiglu_launch(n, gate, up, out, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "swiglu launch");
+}
+
+size_t nt_decode_layer_ws_bytes(const nt_layer_shape* shp) {
+  if (!shp || shp->head_dim != 128 || shp->n_q_heads <= 0 || shp->n_kv_heads <= 0) return 0;
+  return layer_ws(*shp).total;
+}
+
+int nt_decode_layer_ws_offsets(const nt_layer_shape* shp, int64_t* off) {
+  int rc = check_shape(shp);
+  if (rc) return rc;
+  if (!off) return fail(NT_EINVAL, "null pointer");
+  const LayerWs L = layer_ws(*shp);
+  off[0] = (int64_t)L.q; off[1] = (int64_t)L.o; off[2] = (int64_t)L.h1; off[3] = (int64_t)L.a; off[4] = (int64_t)L.part;
+  return NT_OK;
+}
+
+int nt_decode_layer(const nt_layer_weights* w, const nt_layer_shape* shp, int pos, float* h, uint16_t* k_cache,
+                    uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shp);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (pos < 0 || pos >= shp->max_ctx) return fail(NT_ESHAPE, "pos %d outside [0, max_ctx)", pos);
+  if (!h || !k_cache || !v_cache || !ws) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(h, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(ws, 256))
+    return fail(NT_EALIGN, "h and caches must be 16-byte aligned, ws 256-byte");
+  if (ws_bytes < layer_ws(*shp).total) return fail(NT_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, layer_ws(*shp).total);
+  return run_layer(*w, *shp, pos, h, k_cache, v_cache, reinterpret_cast<uint8_t*>(ws), (hipStream_t)stream);
+}
+
+int nt_embed_row(int fmt, int64_t n_vocab, int64_t dim, const void* table, const int32_t* token, float* h,
+                 void* stream) {
+  if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
+  if (n_vocab <= 0 || dim <= 0 || dim % block_elems(fmt)) return fail(NT_ESHAPE, "bad embedding shape");
+  if (!table || !token || !h) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(table, 4)) return fail(NT_EALIGN, "table must be 4-byte aligned");
+  hipError_t e = embed_launch(fmt, n_vocab, dim, table, token, h, nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "embed launch");
+}
+
+int nt_argmax(int64_t n, const float* v, int32_t* out_index, void* stream) {
+  if (n <= 0 || n > 0x7FFFFFFF) return fail(NT_ESHAPE, "n must be in [1, 2^31)");
+  if (!v || !out_index) return fail(NT_EINVAL, "null pointer");
+  hipError_t e = argmax_launch(n, v, out_index, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "argmax launch");
+}
+
+int nt_stream_create(void* staging0, void* staging1, size_t staging_bytes, nt_streamer** out) {
+  if (!out) return fail(NT_EINVAL, "out is null");
+  *out = nullptr;
+  if (!staging0 || !staging1 || staging0 == staging1) return fail(NT_EINVAL, "need two distinct staging buffers");
+  if (!aligned(staging0, 256) || !aligned(staging1, 256)) return fail(NT_EALIGN, "staging buffers must be 256-byte aligned");
+  if (staging_bytes == 0) return fail(NT_EINVAL, "staging_bytes is 0");
+  nt_streamer* st = new nt_streamer();
+  st->staging[0] = reinterpret_cast<uint8_t*>(staging0);
+  st->staging[1] = reinterpret_cast<uint8_t*>(staging1);
+  st->bytes = staging_bytes;
+  for (int b = 0; b < 2; ++b) {
+    hipError_t e;
+    if ((e = hipEventCreateWithFlags(&st->ready[b], hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&st->freed[b], hipEventDisableTiming)) != hipSuccess) {
+      delete st;
+      return hip_fail(e, "hipEventCreate");
+    }
+    st->freed_recorded[b] = false;
+  }
+  st->plan_layers = nullptr;
+  st->n_streamed = 0;
+  st->c_run = st->c_issue = 0;
+  *out = st;
+  return NT_OK;
+}
+
+void nt_stream_destroy(nt_streamer* st) {
+  if (!st) return;
+  for (int b = 0; b < 2; ++b) {
+    (void)hipEventSynchronize(st->ready[b]);
+    (void)hipEventSynchronize(st->freed[b]);
+    (void)hipEventDestroy(st->ready[b]);
+    (void)hipEventDestroy(st->freed[b]);
+  }
+  delete st;
+}
+
+static int check_plan(const nt_model_plan* plan, bool need_resident) {
+  if (!plan || !plan->layers || plan->n_layers <= 0) return fail(NT_EINVAL, "empty plan");
+  int rc = check_shape(&plan->shape);
+  if (rc) return rc;
+  if ((rc = check_layout(plan->shape, plan->layout))) return rc;
+  for (int l = 0; l < plan->n_layers; ++l) {
+    const nt_layer_entry& e = plan->layers[l];
+    if (!e.blob || !e.k_cache || !e.v_cache) return fail(NT_EINVAL, "layer %d has a null pointer", l);
+    if (!aligned(e.blob, 256)) return fail(NT_EALIGN, "layer %d blob must be 256-byte aligned", l);
+    if (!e.resident) {
+      if (need_resident) return fail(NT_EINVAL, "layer %d is not resident and no streamer was given", l);
+      hipPointerAttribute_t attr;
+      memset(&attr, 0, sizeof(attr));
+      hipError_t he = hipPointerGetAttributes(&attr, e.blob);
+      if (he != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();  // clear a sticky error left by the query on pageable memory
+        return fail(NT_EHOSTMEM, "layer %d blob is not page-locked host memory", l);
+      }
+    }
+  }
+  return NT_OK;
+}
+
+static int stream_issue(nt_streamer* st, const nt_model_plan* plan, const std::vector<int>& streamed, hipStream_t copy,
+                        nt_stream_stats* stats) {
+  const int64_t q = st->c_issue;
+  const int b = (int)(q & 1);
+  const int layer = streamed[(size_t)(q % (int64_t)streamed.size())];
+  hipError_t e;
+  if (st->freed_recorded[b] && (e = hipStreamWaitEvent(copy, st->freed[b], 0)) != hipSuccess)
+    return hip_fail(e, "hipStreamWaitEvent(copy)");
+  const size_t nbytes = (size_t)plan->layout.blob_bytes;
+  if ((e = hipMemcpyAsync(st->staging[b], plan->layers[layer].blob, nbytes, hipMemcpyHostToDevice, copy)) != hipSuccess)
+    return hip_fail(e, "hipMemcpyAsync");
+  if ((e = hipEventRecord(st->ready[b], copy)) != hipSuccess) return hip_fail(e, "hipEventRecord(ready)");
+  if (stats) stats->h2d_bytes += (int64_t)nbytes;
+  st->c_issue = q + 1;
+  return NT_OK;
+}
+
+static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, uint8_t* ws,
+                              hipStream_t compute, hipStream_t copy, nt_stream_stats* stats) {
+  std::vector<int> streamed;
+  for (int l = 0; l < plan->n_layers; ++l)
+    if (!plan->layers[l].resident) streamed.push_back(l);
+  if (st && !streamed.empty()) {
+    if (st->plan_layers != (const void*)plan->layers || st->n_streamed != (int)streamed.size()) {
+      // a new plan: drain what the streamer had in flight, then restart its sequence
+      for (int b = 0; b < 2; ++b) {
+        (void)hipEventSynchronize(st->ready[b]);
+        (void)hipEventSynchronize(st->freed[b]);
+        st->freed_recorded[b] = false;
+      }
+      st->plan_layers = plan->layers;
+      st->n_streamed = (int)streamed.size();
+      st->c_run = st->c_issue = 0;
+    }
+  }
+  int rc;
+  if (st && !streamed.empty())
+    while (st->c_issue < st->c_run + 2)
+      if ((rc = stream_issue(st, plan, streamed, copy, stats))) return rc;
+  for (int l = 0; l < plan->n_layers; ++l) {
+    const nt_layer_entry& ent = plan->layers[l];
+    if (ent.resident) {
+      const nt_layer_weights w = weights_in_blob(reinterpret_cast<const uint8_t*>(ent.blob), plan->layout);
+      if ((rc = run_layer(w, plan->shape, pos, h, ent.k_cache, ent.v_cache, ws, compute))) return rc;
+      continue;
+    }
+    const int64_t q = st->c_run;
+    const int b = (int)(q & 1);
+    while (st->c_issue <= q)
+      if ((rc = stream_issue(st, plan, streamed, copy, stats))) return rc;
+    hipError_t e;
+    if ((e = hipStreamWaitEvent(compute, st->ready[b], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(compute)");
+    const nt_layer_weights w = weights_in_blob(st->staging[b], plan->layout);
+    if ((rc = run_layer(w, plan->shape, pos, h, ent.k_cache, ent.v_cache, ws, compute))) return rc;
+    if ((e = hipEventRecord(st->freed[b], compute)) != hipSuccess) return hip_fail(e, "hipEventRecord(freed)");
+    st->freed_recorded[b] = true;
+    st->c_run = q + 1;
+    if (stats) stats->layers_streamed += 1;
+    while (st->c_issue < st->c_run + 2)
+      if ((rc = stream_issue(st, plan, streamed, copy, stats))) return rc;
+  }
+  return NT_OK;
+}
+
+int nt_stream_layers(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, void* ws, size_t ws_bytes,
+                     void* compute, void* copy, nt_stream_stats* stats) {
+  if (stats) stats->layers_streamed = stats->h2d_bytes = 0;
+  int rc = check_plan(plan, st == nullptr);
+  if (rc) return rc;
+  if (pos < 0 || pos >= plan->shape.max_ctx) return fail(NT_ESHAPE, "pos %d outside [0, max_ctx)", pos);
+  if (!h || !ws) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(h, 16) || !aligned(ws, 256)) return fail(NT_EALIGN, "h must be 16-byte aligned, ws 256-byte");
+  if (ws_bytes < layer_ws(plan->shape).total) return fail(NT_EINVAL, "workspace too small");
+  if (st) {
+    if ((size_t)plan->layout.blob_bytes > st->bytes) return fail(NT_EINVAL, "layer blob larger than the staging buffers");
+    if (compute == copy) return fail(NT_EINVAL, "compute and copy streams must differ");
+  }
+  return stream_layers_impl(st, plan, pos, h, reinterpret_cast<uint8_t*>(ws), (hipStream_t)compute, (hipStream_t)copy,
+                            stats);
+}
+
+size_t nt_decode_token_ws_bytes(const nt_layer_shape* shp) { return nt_decode_layer_ws_bytes(shp); }
+
+int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_head* head, int pos, int32_t* token,
+                    float* logits, float* h, void* ws, size_t ws_bytes, void* compute, void* copy,
+                    nt_stream_stats* stats) {
+  if (stats) stats->layers_streamed = stats->h2d_bytes = 0;
+  int rc = check_plan(plan, st == nullptr);
+  if (rc) return rc;
+  if (!head || !head->token_embd || !head->output_norm || !head->output || !token || !logits || !h || !ws)
+    return fail(NT_EINVAL, "null pointer");
+  if (!fmt_ok(head->embd_fmt) || !fmt_ok(head->out_fmt)) return fail(NT_EFORMAT, "unknown head format");
+  if (head->n_vocab <= 0 || head->n_vocab > 0x7FFFFFFF) return fail(NT_ESHAPE, "bad vocabulary size");
+  if (!aligned(head->output, 16) || !aligned(head->token_embd, 4) || !aligned(head->output_norm, 16) || !aligned(h, 16) ||
+      !aligned(ws, 256))
+    return fail(NT_EALIGN, "misaligned head, h or ws pointer");
+  if (pos < 0 || pos >= plan->shape.max_ctx) return fail(NT_ESHAPE, "pos %d outside [0, max_ctx)", pos);
+  const LayerWs L = layer_ws(plan->shape);
+  if (ws_bytes < L.total) return fail(NT_EINVAL, "workspace too small");
+  if (st) {
+    if ((size_t)plan->layout.blob_bytes > st->bytes) return fail(NT_EINVAL, "layer blob larger than the staging buffers");
+    if (compute == copy) return fail(NT_EINVAL, "compute and copy streams must differ");
+  }
+  hipStream_t cs = (hipStream_t)compute;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  unsigned long long* key = reinterpret_cast<unsigned long long*>(wsb + L.key);
+  hipError_t e;
+  if ((e = embed_launch(head->embd_fmt, head->n_vocab, plan->shape.dim, head->token_embd, token, h, key, cs)) != hipSuccess)
+    return hip_fail(e, "embed launch");
+  if ((rc = stream_layers_impl(st, plan, pos, h, wsb, cs, (hipStream_t)copy, stats))) return rc;
+  {
+    const GemvPlan p = gemv_plan(EPI_LOGITS, plan->shape.dim);
+    GemvArgs a = blank_args();
+    a.x = h; a.gain = head->output_norm; a.eps = plan->shape.eps; a.cols = plan->shape.dim; a.nseg = 1;
+    a.seg[0] = make_seg(head->output, head->out_fmt, (int)head->n_vocab, plan->shape.dim, 0);
+    a.y = logits; a.amax = key;
+    TimedLaunch tl(NT_K_LM_HEAD, cs);
+    if ((e = gemv_launch(1 << head->out_fmt, EPI_LOGITS, p, gemv_tiles(p, (int)head->n_vocab), a, cs)) != hipSuccess)
+      return hip_fail(e, "lm head launch");
+  }
+  if ((e = token_from_key_launch(key, token, cs)) != hipSuccess) return hip_fail(e, "token launch");
+  return NT_OK;
+}
+
+int nt_timing_begin(int kclass, int max_launches) {
+  if (kclass < 0 || kclass >= NT_K_COUNT || max_launches <= 0) return fail(NT_EINVAL, "bad timing request");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (hipEvent_t ev : g_timing.ev) (void)hipEventDestroy(ev);
+  g_timing.ev.clear();
+  g_timing.kclass = kclass;
+  g_timing.max_launches = max_launches;
+  return NT_OK;
+}
+
+int nt_timing_end(int* n_launches, double* total_ms) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  double tot = 0.0;
+  int n = 0;
+  int rc = NT_OK;
+  for (size_t i = 0; i + 1 < g_timing.ev.size(); i += 2) {
+    if (hipEventSynchronize(g_timing.ev[i + 1]) != hipSuccess) { rc = fail(NT_EHIP, "event sync failed"); break; }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_timing.ev[i], g_timing.ev[i + 1]) != hipSuccess) { rc = fail(NT_EHIP, "elapsed time failed"); break; }
+    tot += ms;
+    ++n;
+  }
+  for (hipEvent_t ev : g_timing.ev) (void)hipEventDestroy(ev);
+  g_timing.ev.clear();
+  g_timing.kclass = -1;
+  if (n_launches) *n_launches = n;
+  if (total_ms) *total_ms = tot;
+  return rc;
+}
+
+}  // extern "C"

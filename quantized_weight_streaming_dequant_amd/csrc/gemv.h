@@ -1,0 +1,57 @@
+// Fused dequantize-and-GEMV: launch interface shared by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nt {
+
+enum GemvEpi {
+  EPI_STORE = 0,   // y[r] = (W x)[r]
+  EPI_RESID = 1,   // y[r] = resid[r] + (W x)[r]; y2[r] (if set) = the same value
+  EPI_SWIGLU = 2,  // seg0 = gate, seg1 = up: y[r] = silu(gate r) * (up r)
+  EPI_QKV = 3,     // seg0 = q, seg1 = k, seg2 = v: RoPE on q and k, q -> q_out, k/v -> fp16 cache slot pos
+  EPI_LOGITS = 4   // y[r] = (W x)[r] and a packed (value, index) max folded into *amax
+};
+
+struct GemvSeg {
+  const uint8_t* w;   // blocks of this matrix
+  int64_t row_bytes;
+  int rows;
+  int fmt;
+  int tile0;          // first workgroup index of this matrix
+};
+
+struct GemvArgs {
+  const float* x;     // [cols]
+  const float* gain;  // RMSNorm gain [cols] applied to x first, or null
+  float eps;
+  int cols;
+  int nseg;
+  GemvSeg seg[3];
+  float* y;
+  const float* resid;
+  float* y2;
+  float* q_out;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int pos;
+  int max_ctx;
+  double rope_theta;
+  unsigned long long* amax;
+};
+
+struct GemvPlan {
+  int rows_per_wave;
+  int waves;
+  size_t lds_bytes;
+};
+
+// Launch geometry for a format mix and shape.
+GemvPlan gemv_plan(int epi, int cols);
+// Number of workgroups a segment of `rows` rows needs under `plan`.
+int gemv_tiles(const GemvPlan& p, int rows);
+// Enqueue.  fmt_mask: bit f set for every format present in the segments.
+hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_tiles, const GemvArgs& a, hipStream_t s);
+
+}  // namespace nt

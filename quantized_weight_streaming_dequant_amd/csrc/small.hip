@@ -1,0 +1,218 @@
+// Stand-alone decode-path kernels: dequantize (test hook), RMSNorm, RoPE, SwiGLU,
+// embedding row, argmax.  In the fused layer these steps run inside the GEMV
+// prologues/epilogues (gemv.hip); the stand-alone forms serve the per-op C ABI.
+// Ops from the ntransformer overview (de.news.hada.io), "Hauptfunktionen" and
+// "Architektur und Codestruktur"; block formats from "Überblick über NTransformer".
+#include "common.h"
+#include "small.h"
+
+namespace nt {
+
+// ------------------------------------------------------------ dequantize
+// One thread per 32 weights.  Every product below is exact in fp32 (at most 24
+// significant bits), so the single rounding happens at the Q4_K subtraction and the
+// result is the exact weight rounded once to fp32.
+
+__device__ __forceinline__ uint32_t byte_at(const uint8_t* p, int i) { return p[i]; }
+__device__ __forceinline__ float f16_at(const uint8_t* p) { return h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8)); }
+
+__device__ void dequant_group(int fmt, const uint8_t* blk, int grp, float* out) {
+  if (fmt == FMT_Q8_0) {
+    const float d = f16_at(blk);
+    for (int i = 0; i < 32; ++i) out[i] = d * (float)(int8_t)blk[2 + i];
+  } else if (fmt == FMT_Q4_0) {
+    const float d = f16_at(blk);
+    for (int i = 0; i < 32; ++i) {
+      const int n = i < 16 ? (blk[2 + i] & 15) : (blk[2 + i - 16] >> 4);
+      out[i] = d * (float)(n - 8);
+    }
+  } else if (fmt == FMT_Q4_K) {
+    // grp = sub-block j (32 weights)
+    const int j = grp;
+    const float d = f16_at(blk), dmin = f16_at(blk + 2);
+    const uint8_t* S = blk + 4;
+    int sc, m;
+    if (j < 4) {
+      sc = S[j] & 63;
+      m = S[j + 4] & 63;
+    } else {
+      sc = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
+      m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
+    }
+    const float dsc = d * (float)sc, dm = dmin * (float)m;
+    const uint8_t* Q = blk + 16 + 32 * (j >> 1);
+    const int shift = 4 * (j & 1);
+    for (int l = 0; l < 32; ++l) out[l] = dsc * (float)((Q[l] >> shift) & 15) - dm;
+  } else {
+    // Q6_K, grp = 32-weight run: h = grp/4, t = grp%4
+    const int h = grp >> 2, t = grp & 3;
+    const uint8_t* QL = blk + 64 * h + 32 * (t & 1);
+    const uint8_t* QH = blk + 128 + 32 * h;
+    const int8_t* sc = reinterpret_cast<const int8_t*>(blk + 192);
+    const float d = f16_at(blk + 208);
+    for (int l = 0; l < 32; ++l) {
+      const int q = ((QL[l] >> (4 * (t >> 1))) & 15) | (((QH[l] >> (2 * t)) & 3) << 4);
+      const float ds = d * (float)sc[8 * h + 2 * t + (l >> 4)];
+      out[l] = ds * (float)(q - 32);
+    }
+  }
+}
+
+__global__ void dequant_kernel(int fmt, int64_t rows, int64_t cols, const uint8_t* __restrict__ blocks,
+                               float* __restrict__ w) {
+  const int be = block_elems(fmt), bb = block_bytes(fmt);
+  const int64_t groups_per_row = cols / 32;
+  const int64_t total = rows * groups_per_row;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < total; gi += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = gi / groups_per_row, cg = gi % groups_per_row;
+    const int64_t c0 = cg * 32;
+    const int64_t b = c0 / be;
+    const int grp = (int)((c0 % be) / 32);
+    const uint8_t* blk = blocks + (r * (cols / be) + b) * bb;
+    float tmp[32];
+    dequant_group(fmt, blk, grp, tmp);
+    float* o = w + r * cols + c0;
+    for (int i = 0; i < 32; ++i) o[i] = tmp[i];
+  }
+}
+
+hipError_t dequant_launch(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, hipStream_t s) {
+  const int64_t total = rows * (cols / 32);
+  const int64_t nb = (total + 255) / 256;
+  const int grid = (int)(nb < 65536 ? nb : 65536);
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(256), 0, s, fmt, rows, cols,
+                     reinterpret_cast<const uint8_t*>(blocks), w);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ embedding row
+__global__ void embed_kernel(int fmt, int64_t n_vocab, int64_t dim, const uint8_t* __restrict__ table,
+                             const int32_t* __restrict__ token, float* __restrict__ h,
+                             unsigned long long* __restrict__ amax_reset) {
+  const int tok = *token;
+  if (amax_reset && blockIdx.x == 0 && threadIdx.x == 0) *amax_reset = 0ull;
+  const int be = block_elems(fmt), bb = block_bytes(fmt);
+  const int64_t ngroups = dim / 32;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < ngroups; gi += (int64_t)gridDim.x * blockDim.x) {
+    float tmp[32];
+    if (tok >= 0 && tok < n_vocab) {
+      const int64_t c0 = gi * 32;
+      const uint8_t* blk = table + ((int64_t)tok * (dim / be) + c0 / be) * bb;
+      dequant_group(fmt, blk, (int)((c0 % be) / 32), tmp);
+    } else {
+      for (int i = 0; i < 32; ++i) tmp[i] = 0.f;
+    }
+    for (int i = 0; i < 32; ++i) h[gi * 32 + i] = tmp[i];
+  }
+}
+
+hipError_t embed_launch(int fmt, int64_t n_vocab, int64_t dim, const void* table, const int32_t* token, float* h,
+                        unsigned long long* amax_reset, hipStream_t s) {
+  const int64_t ng = dim / 32;
+  const int grid = (int)((ng + 63) / 64);
+  hipLaunchKernelGGL(embed_kernel, dim3(grid), dim3(64), 0, s, fmt, n_vocab, dim,
+                     reinterpret_cast<const uint8_t*>(table), token, h, amax_reset);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ RMSNorm
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(int64_t n, const float* __restrict__ x,
+                                                       const float* __restrict__ g, float eps, float* y) {
+  __shared__ float red[16];
+  float ss = 0.f;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) ss += x[i] * x[i];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
+  const float scale = 1.0f / sqrtf(t / (float)n + eps);
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) y[i] = x[i] * scale * g[i];
+}
+
+hipError_t rmsnorm_launch(int64_t n, const float* x, const float* g, float eps, float* y, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, s, n, x, g, eps, y);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ RoPE
+__global__ void rope_kernel(int n_heads, int head_dim, int pos, double theta, float* qk) {
+  const int npairs = n_heads * (head_dim / 2);
+  for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < npairs; p += gridDim.x * blockDim.x) {
+    const int head = p / (head_dim / 2), i = p % (head_dim / 2);
+    const double f = pow(theta, -2.0 * (double)i / (double)head_dim);
+    double ang = (double)pos * f;
+    ang -= 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
+    float sn, cs;
+    sincosf((float)ang, &sn, &cs);
+    float* v = qk + (int64_t)head * head_dim + 2 * i;
+    const float x0 = v[0], x1 = v[1];
+    v[0] = x0 * cs - x1 * sn;
+    v[1] = x0 * sn + x1 * cs;
+  }
+}
+
+hipError_t rope_launch(int n_heads, int head_dim, int pos, double theta, float* qk, hipStream_t s) {
+  const int npairs = n_heads * (head_dim / 2);
+  hipLaunchKernelGGL(rope_kernel, dim3((npairs + 255) / 256), dim3(256), 0, s, n_heads, head_dim, pos, theta, qk);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ SwiGLU
+__global__ void swiglu_kernel(int64_t n, const float* gate, const float* up, float* out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float g = gate[i], u = up[i];
+    out[i] = g / (1.0f + __expf(-g)) * u;
+  }
+}
+
+hipError_t swiglu_launch(int64_t n, const float* gate, const float* up, float* out, hipStream_t s) {
+  const int64_t nb = (n + 255) / 256;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)(nb < 65536 ? nb : 65536)), dim3(256), 0, s, n, gate, up, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ argmax
+__device__ __forceinline__ uint32_t okey(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__global__ __launch_bounds__(1024) void argmax_kernel(int64_t n, const float* __restrict__ v, int32_t* out) {
+  __shared__ unsigned long long red[16];
+  unsigned long long best = 0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const float x = v[i] != v[i] ? -INFINITY : v[i];
+    const unsigned long long key = ((unsigned long long)okey(x) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
+    best = key > best ? key : best;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(best, off, 64);
+    best = o > best ? o : best;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long b = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) b = red[i] > b ? red[i] : b;
+    *out = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+  }
+}
+
+hipError_t argmax_launch(int64_t n, const float* v, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(1), dim3(1024), 0, s, n, v, out);
+  return hipGetLastError();
+}
+
+__global__ void token_from_key_kernel(const unsigned long long* key, int32_t* token) {
+  *token = (int32_t)(0xFFFFFFFFu - (uint32_t)(*key & 0xFFFFFFFFull));
+}
+
+hipError_t token_from_key_launch(const unsigned long long* key, int32_t* token, hipStream_t s) {
+  hipLaunchKernelGGL(token_from_key_kernel, dim3(1), dim3(1), 0, s, key, token);
+  return hipGetLastError();
+}
+
+}  // namespace nt

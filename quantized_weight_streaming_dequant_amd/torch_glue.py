@@ -1,0 +1,57 @@
+"""Marshalling between torch tensors and the C ABI structs (pointers and shapes only)."""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+
+
+def ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def stream_handle(s: torch.cuda.Stream | None = None) -> int:
+    s = s if s is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def layer_shape(shp) -> _abi.LayerShape:
+    """From any object with dim, n_q_heads, n_kv_heads, head_dim, ffn_dim, max_ctx, eps, rope_theta."""
+    return _abi.LayerShape(shp.dim, shp.n_q_heads, shp.n_kv_heads, shp.head_dim, shp.ffn_dim, shp.max_ctx,
+                           shp.eps, shp.rope_theta)
+
+
+def layer_weights(fmts: list[int], mats: list[torch.Tensor], attn_norm: torch.Tensor,
+                  ffn_norm: torch.Tensor) -> _abi.LayerWeights:
+    w = _abi.LayerWeights()
+    for i in range(_abi.W_COUNT):
+        w.fmt[i] = fmts[i]
+        w.w[i] = mats[i].data_ptr()
+    w.attn_norm = attn_norm.data_ptr()
+    w.ffn_norm = ffn_norm.data_ptr()
+    return w
+
+
+def layer_layout(offsets: list[int], fmts: list[int], blob_bytes: int) -> _abi.LayerLayout:
+    lay = _abi.LayerLayout()
+    for i, o in enumerate(offsets):
+        lay.offset[i] = o
+    for i, f in enumerate(fmts):
+        lay.fmt[i] = f
+    lay.blob_bytes = blob_bytes
+    return lay
+
+
+def model_plan(shape: _abi.LayerShape, layout: _abi.LayerLayout, entries: list[tuple[int, bool, int, int]]):
+    """entries: (blob address, resident, k_cache address, v_cache address) per layer.
+    Returns (plan, keepalive); keep the second value alive while the plan is used."""
+    arr = (_abi.LayerEntry * len(entries))()
+    for i, (blob, resident, kc, vc) in enumerate(entries):
+        arr[i].blob = blob
+        arr[i].resident = 1 if resident else 0
+        arr[i].k_cache = kc
+        arr[i].v_cache = vc
+    plan = _abi.ModelPlan(shape, layout, len(entries), ctypes.cast(arr, ctypes.POINTER(_abi.LayerEntry)))
+    return plan, arr

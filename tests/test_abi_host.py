@@ -1,0 +1,136 @@
+"""The C ABI library loads, exports every symbol include/nt.h declares, and rejects
+bad arguments on the host before anything is enqueued (CPU only: none of these
+calls reaches the GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_weight_streaming_dequant_amd as nt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nt.h")
+
+
+def declared_functions() -> list[str]:
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nt_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_path_calls():
+    names = declared_functions()
+    for need in ("nt_gemv_q", "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_swiglu", "nt_decode_layer",
+                 "nt_stream_layers", "nt_dequant"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(nt.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(nt.EXPORTS) == declared_functions()
+
+
+def test_block_geometry():
+    assert [nt.nt_block_elems(f) for f in range(4)] == [32, 32, 256, 256]
+    assert [nt.nt_block_bytes(f) for f in range(4)] == [34, 18, 144, 210]
+    assert nt.nt_matrix_bytes(nt.Q6_K, 8192, 28672) == 192_675_840
+    assert nt.nt_matrix_bytes(nt.Q4_K, 28672, 8192) == 132_120_576
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: nt.nt_gemv_q(9, 16, 256, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemv_q(nt.Q4_K, 16, 100, 16, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_gemv_q(nt.Q4_K, 0, 256, 16, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_gemv_q(nt.Q4_K, 16, 65536, 16, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_gemv_q(nt.Q8_0, 16, 256, None, 16, 16), nt.NT_EINVAL),
+    (lambda: nt.nt_gemv_q(nt.Q8_0, 16, 256, 18, 16, 16), nt.NT_EALIGN),
+    (lambda: nt.nt_dequant(nt.Q6_K, 4, 255, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_rope(8, 127, 0, 5e5, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_rope(8, 128, -1, 5e5, 16), nt.NT_EINVAL),
+    (lambda: nt.nt_attn_decode(64, 8, 64, 10, 16, 16, 16, 16, 16, 256, 1 << 20), nt.NT_ESHAPE),
+    (lambda: nt.nt_attn_decode(64, 8, 128, 17, 16, 16, 16, 16, 16, 256, 1 << 20), nt.NT_ESHAPE),
+    (lambda: nt.nt_attn_decode(64, 8, 128, 16, 16, 16, 16, 16, 16, 128, 1 << 20), nt.NT_EALIGN),
+    (lambda: nt.nt_attn_decode(60, 8, 128, 16, 16, 16, 16, 16, 16, 256, 1 << 20), nt.NT_ESHAPE),
+    (lambda: nt.nt_attn_decode(64, 8, 128, 16, 16, 16, 16, 16, 16, 256, 8), nt.NT_EINVAL),
+    (lambda: nt.nt_swiglu(0, 16, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_rmsnorm(100, None, 16, 1e-5, 16), nt.NT_EINVAL),
+    (lambda: nt.nt_argmax(0, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_embed_row(nt.Q4_K, 10, 100, 16, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_stream_create(None, 256, 1024), nt.NT_EINVAL),
+    (lambda: nt.nt_stream_create(256, 256, 1024), nt.NT_EINVAL),
+    (lambda: nt.nt_stream_create(256, 512 + 16, 1024), nt.NT_EALIGN),
+])
+def test_bad_arguments_are_rejected(call, code):
+    with pytest.raises(nt.NtError) as ei:
+        call()
+    assert ei.value.code == code
+    assert nt.last_error()
+
+
+def _shape(**kw):
+    base = dict(dim=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn_dim=14336, max_ctx=1024, eps=1e-5,
+                rope_theta=5e5)
+    base.update(kw)
+    return nt.LayerShape(*[base[k] for k in ("dim", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "max_ctx",
+                                              "eps", "rope_theta")])
+
+
+def _weights(fmt=nt.Q8_0, ptr=4096):
+    w = nt.LayerWeights()
+    for i in range(nt.W_COUNT):
+        w.fmt[i] = fmt
+        w.w[i] = ptr
+    w.attn_norm = ptr
+    w.ffn_norm = ptr
+    return w
+
+
+@pytest.mark.parametrize("shape_kw,wfix,pos,code", [
+    (dict(head_dim=64), None, 0, nt.NT_ESHAPE),
+    (dict(n_q_heads=30), None, 0, nt.NT_ESHAPE),
+    (dict(n_q_heads=96, n_kv_heads=8), None, 0, nt.NT_ESHAPE),  # group of 12
+    (dict(dim=4000), None, 0, nt.NT_ESHAPE),
+    (dict(ffn_dim=40960), None, 0, nt.NT_ESHAPE),
+    ({}, None, 1024, nt.NT_ESHAPE),
+    ({}, None, -1, nt.NT_ESHAPE),
+    ({}, "badfmt", 0, nt.NT_EFORMAT),
+    ({}, "mixed_ffn", 0, nt.NT_EFORMAT),
+    ({}, "misaligned", 0, nt.NT_EALIGN),
+    ({}, "null", 0, nt.NT_EINVAL),
+])
+def test_decode_layer_checks(shape_kw, wfix, pos, code):
+    shp = _shape(**shape_kw)
+    w = _weights()
+    if wfix == "badfmt":
+        w.fmt[3] = 11
+    elif wfix == "mixed_ffn":
+        w.fmt[nt.W_GATE] = nt.Q4_K
+    elif wfix == "misaligned":
+        w.w[2] = 4096 + 8
+    elif wfix == "null":
+        w.w[5] = None
+    with pytest.raises(nt.NtError) as ei:
+        nt.nt_decode_layer(w, shp, pos, 4096, 4096, 4096, 4096, 1 << 30)
+    assert ei.value.code == code
+
+
+def test_workspace_sizes_and_offsets():
+    shp = _shape()
+    ws = nt.nt_decode_layer_ws_bytes(shp)
+    off = nt.nt_decode_layer_ws_offsets(shp)
+    assert all(v % 256 == 0 for v in off.values())
+    assert off["q"] < off["o"] < off["h1"] < off["a"] < off["part"] < ws
+    assert ws >= 4 * (2 * 4096 + 4096 + 14336)
+    assert nt.nt_attn_decode_ws_bytes(64, 8, 128, 4224) > 4 * 64 * 130
+    assert nt.nt_decode_token_ws_bytes(shp) >= ws
+
+
+def test_layer_workspace_too_small():
+    with pytest.raises(nt.NtError) as ei:
+        nt.nt_decode_layer(_weights(), _shape(), 5, 4096, 4096, 4096, 4096, 1024)
+    assert ei.value.code == nt.NT_EINVAL

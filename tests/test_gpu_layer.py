@@ -1,0 +1,278 @@
+"""GPU parity of the fused decode layer, the greedy token step and layer streaming
+(MI355X only), through the C ABI.
+
+Stage-wise, teacher-forced acceptance (each stage judged on the GPU's own input
+to it): the fp16 K/V written at slot pos within one binary16 step of the
+checker's rounding; the rotated query, attention output, h1, SwiGLU output and
+h2 each within 1e-3 of their normalisers.  Streaming must be bit-identical to
+running the same layers resident.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_weight_streaming_dequant_amd as nt
+import synth
+from quantized_weight_streaming_dequant_amd import torch_glue as tg
+from synth import recipes
+from tests.gpu_util import check_rel, dev, host, same_value, say, stream
+
+pytestmark = pytest.mark.gpu
+
+
+class DeviceLayer:
+    """One layer's tensors on the device, generated from the seed streams."""
+
+    def __init__(self, shape, mix, layer, n_slots, seed=0):
+        self.shape, self.mix, self.layer = shape, mix, layer
+        self.host = recipes.layer_arrays(shape, mix, layer, seed)
+        self.dev = {k: dev(v) for k, v in self.host.items()}
+        self.kc_host = recipes.kv_cache_array(shape, layer, "k", n_slots, seed)
+        self.vc_host = recipes.kv_cache_array(shape, layer, "v", n_slots, seed)
+        self.kc = dev(self.kc_host)
+        self.vc = dev(self.vc_host)
+
+    def weights(self):
+        return tg.layer_weights([self.mix[n] for n in recipes.TENSORS], [self.dev[n] for n in recipes.TENSORS],
+                                self.dev["attn_norm"], self.dev["ffn_norm"])
+
+
+def run_layer_and_check(shape, mix, pos, n_slots, layer=0, sample_rows=None):
+    say(f"decode layer dim={shape.dim} nq={shape.n_q_heads} nkv={shape.n_kv_heads} ffn={shape.ffn_dim} pos={pos}")
+    L = DeviceLayer(shape, mix, layer, n_slots)
+    shp = tg.layer_shape(shape)
+    wsb = nt.nt_decode_layer_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    off = nt.nt_decode_layer_ws_offsets(shp)
+    h0 = recipes.hidden_input(shape.dim)
+    h = dev(h0)
+    nt.nt_decode_layer(L.weights(), shp, pos, h.data_ptr(), L.kc.data_ptr(), L.vc.data_ptr(), ws.data_ptr(), wsb,
+                       stream())
+    torch.cuda.synchronize()
+    nq = shape.n_q_heads * shape.head_dim
+
+    def wsf(name, n):
+        return ws[off[name]:off[name] + 4 * n].view(torch.float32).cpu().numpy()
+
+    g_q, g_o, g_h1, g_a = wsf("q", nq), wsf("o", nq), wsf("h1", shape.dim), wsf("a", shape.ffn_dim)
+    g_h2 = host(h)
+    kc, vc = host(L.kc), host(L.vc)
+    g_k16, g_v16 = kc[:, pos, :].ravel(), vc[:, pos, :].ravel()
+    # untouched cache slots stay as they were
+    keep = np.ones(shape.max_ctx, bool)
+    keep[pos] = False
+    assert same_value(kc[:, keep], L.kc_host[:, keep]) and same_value(vc[:, keep], L.vc_host[:, keep])
+
+    st = oracle.decode_layer(L.host, mix, shape, pos, h0, L.kc_host, L.vc_host,
+                             forced={"k16": g_k16, "v16": g_v16, "q": g_q, "o": g_o, "h1": g_h1, "a": g_a})
+    assert st["k16_ulp"] <= 1 and st["v16_ulp"] <= 1, (st["k16_ulp"], st["v16_ulp"])
+    # RoPE mixes rows 2i and 2i+1: the pair's GEMV normalisers bound the rotated error
+    qn = np.repeat(st["q_nrm"][0::2] + st["q_nrm"][1::2], 2)
+    res = {}
+    res["q"] = check_rel(g_q, st["q"], qn, what="q")
+    res["o"] = check_rel(g_o, st["o"], st["o_nrm"], what="attention")
+    res["h1"] = check_rel(g_h1, st["h1"], st["h1_nrm"], what="h1")
+    # a = silu(g) u: with |dg| <= e N_g and |du| <= e N_u, |da| <= e (1.1 N_g |u| + |g| N_u) + O(e^2)
+    na = 1.1 * st["gate_nrm"] * np.abs(st["up"]) + (np.abs(st["gate"]) + 1e-3 * st["gate_nrm"]) * st["up_nrm"]
+    res["a"] = check_rel(g_a, st["a"], na, what="swiglu")
+    res["h2"] = check_rel(g_h2, st["h2"], st["h2_nrm"], what="h2")
+    # free-running (no forcing) end-to-end error, reported only
+    free = oracle.decode_layer(L.host, mix, shape, pos, h0, L.kc_host, L.vc_host)
+    rel = np.max(np.abs(g_h2 - free["h2"]) / (free["h2_nrm"]))
+    say("  stage worst rel errors " + ", ".join(f"{k} {v:.1e}" for k, v in res.items()) + f"; free-running h2 {rel:.1e}")
+    return res
+
+
+def test_layer_8b_q8_0_full_size():
+    """Llama-3-8B-shaped layer, Q8_0, pos 1023 over a 1024-slot fp16 cache."""
+    run_layer_and_check(recipes.LLAMA3_8B, recipes.MIX_Q8_0, pos=1023, n_slots=1024)
+
+
+def test_layer_70b_q4_k_m_full_size():
+    """Llama-3.1-70B-shaped layer in the Q4_K_M mix at pos 4096 over a 4096-slot prefill."""
+    run_layer_and_check(recipes.LLAMA31_70B, recipes.MIX_Q4_K_M, pos=4096, n_slots=4096)
+
+
+def test_layer_70b_q6_k_full_size():
+    run_layer_and_check(recipes.LLAMA31_70B, recipes.MIX_Q6_K, pos=4200, n_slots=4096, layer=3)
+
+
+SMALL = recipes.LayerShape(dim=1024, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn_dim=2816, max_ctx=96)
+
+
+@pytest.mark.parametrize("mix,pos", [(recipes.MIX_Q4_K_M, 0), (recipes.MIX_Q8_0, 50), (recipes.MIX_Q6_K, 95),
+                                     ({n: synth.Q4_0 for n in recipes.TENSORS}, 17)])
+def test_layer_small_shapes(mix, pos):
+    run_layer_and_check(SMALL, mix, pos=pos, n_slots=96)
+
+
+# ------------------------------------------------------------------ model, token, streaming
+
+class Model:
+    """A small model in one contiguous blob per layer; some layers in pinned host memory."""
+
+    def __init__(self, shape, mix, n_layers, vocab, streamed=(), n_slots=None, seed=0):
+        self.shape, self.mix, self.n_layers, self.vocab = shape, mix, n_layers, vocab
+        self.lay = recipes.blob_layout(shape, mix)
+        self.blobs_dev = []
+        self.blobs_host = []
+        for l in range(n_layers):
+            hb = torch.empty(self.lay.nbytes, dtype=torch.uint8, pin_memory=True)
+            recipes.fill_layer_blob(hb.data_ptr(), shape, mix, l, seed, self.lay)
+            self.blobs_host.append(hb)
+            self.blobs_dev.append(hb.cuda())
+        self.streamed = set(streamed)
+        n_slots = n_slots if n_slots is not None else shape.max_ctx
+        self.kc0 = [recipes.kv_cache_array(shape, l, "k", n_slots, seed) for l in range(n_layers)]
+        self.vc0 = [recipes.kv_cache_array(shape, l, "v", n_slots, seed) for l in range(n_layers)]
+        self.embd = synth.quant_matrix(synth.Q4_K, vocab, shape.dim, seed, recipes.stream_id(recipes.GLOBAL_LAYER, 0))
+        self.out = synth.quant_matrix(synth.Q4_K, vocab, shape.dim, seed, recipes.stream_id(recipes.GLOBAL_LAYER, 1))
+        self.onorm = synth.uniform_f32(shape.dim, seed, recipes.stream_id(recipes.GLOBAL_LAYER, 2), 0.9, 1.1)
+        self.embd_d, self.out_d, self.onorm_d = dev(self.embd), dev(self.out), dev(self.onorm)
+
+    def caches(self):
+        return [dev(k) for k in self.kc0], [dev(v) for v in self.vc0]
+
+    def plan(self, kcs, vcs, streamed=None):
+        streamed = self.streamed if streamed is None else streamed
+        shp = tg.layer_shape(self.shape)
+        lay = tg.layer_layout(self.lay.offset_list(), self.lay.fmt_list(), self.lay.nbytes)
+        ents = []
+        for l in range(self.n_layers):
+            if l in streamed:
+                ents.append((self.blobs_host[l].data_ptr(), False, kcs[l].data_ptr(), vcs[l].data_ptr()))
+            else:
+                ents.append((self.blobs_dev[l].data_ptr(), True, kcs[l].data_ptr(), vcs[l].data_ptr()))
+        return tg.model_plan(shp, lay, ents)
+
+    def head(self):
+        return nt.ModelHead(synth.Q4_K, self.embd_d.data_ptr(), self.vocab, self.onorm_d.data_ptr(), synth.Q4_K,
+                            self.out_d.data_ptr())
+
+
+def decode_tokens(model, streamed, tok0, pos0, n_tokens, staging=None):
+    kcs, vcs = model.caches()
+    plan, keep = model.plan(kcs, vcs, streamed)
+    shp = tg.layer_shape(model.shape)
+    wsb = nt.nt_decode_token_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(model.shape.dim, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(model.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.tensor([tok0], dtype=torch.int32, device="cuda")
+    compute = torch.cuda.Stream()
+    copy = torch.cuda.Stream()
+    st = None
+    if streamed:
+        st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), staging[0].numel())
+    toks, hs, lgs = [], [], []
+    stats = nt.StreamStats()
+    try:
+        for i in range(n_tokens):
+            torch.cuda.synchronize()
+            nt.nt_decode_token(st, plan, model.head(), pos0 + i, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                               ws.data_ptr(), wsb, compute.cuda_stream, copy.cuda_stream, stats)
+            torch.cuda.synchronize()
+            toks.append(int(tok.cpu()[0]))
+            hs.append(h.cpu().numpy().copy())
+            lgs.append(logits.cpu().numpy().copy())
+    finally:
+        if st is not None:
+            torch.cuda.synchronize()
+            nt.nt_stream_destroy(st)
+    return toks, hs, lgs, [host(k) for k in kcs], [host(v) for v in vcs], stats
+
+
+TINY = recipes.LayerShape(dim=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn_dim=2048, max_ctx=64)
+
+
+def test_token_step_and_streaming_bit_identical():
+    say("token step: resident vs streamed (layers 1 and 3 of 4)")
+    m = Model(TINY, recipes.MIX_Q4_K_M, 4, vocab=1000, n_slots=32)
+    tok0 = synth.uniform_index(1000, 0, 77)
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    a = decode_tokens(m, set(), tok0, 32, 3)
+    b = decode_tokens(m, {1, 3}, tok0, 32, 3, staging)
+    assert a[0] == b[0]
+    for x, y in zip(a[1], b[1]):
+        assert same_value(x, y)
+    for x, y in zip(a[2], b[2]):
+        assert same_value(x, y)
+    for x, y in zip(a[3] + a[4], b[3] + b[4]):
+        assert same_value(x, y)
+    assert b[5].layers_streamed == 2
+    say(f"  tokens {a[0]}")
+    # the checker: logits of the last token from the GPU's final hidden state, and the greedy pick
+    h_last = a[1][-1]
+    n = oracle.rmsnorm(h_last, m.onorm, TINY.eps)
+    ref, nrm = oracle.gemv(synth.Q4_K, 1000, TINY.dim, m.out, n)
+    check_rel(a[2][-1], ref, nrm, what="logits")
+    best = ref.max()
+    assert ref[a[0][-1]] >= best - 1e-3 * nrm[a[0][-1]]
+
+
+def test_token_step_matches_layer_calls():
+    """nt_decode_token = embedding row, then the layers, then the head, with the same kernels."""
+    say("token step vs per-layer calls")
+    m = Model(TINY, recipes.MIX_Q4_K_M, 3, vocab=500, n_slots=20)
+    tok0 = 123
+    toks, hs, lgs, kcs, vcs, _ = decode_tokens(m, set(), tok0, 20, 1)
+    # replay by hand through nt_embed_row + nt_decode_layer
+    kd, vd = m.caches()
+    shp = tg.layer_shape(TINY)
+    wsb = nt.nt_decode_layer_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(TINY.dim, dtype=torch.float32, device="cuda")
+    t = torch.tensor([tok0], dtype=torch.int32, device="cuda")
+    nt.nt_embed_row(synth.Q4_K, 500, TINY.dim, m.embd_d.data_ptr(), t.data_ptr(), h.data_ptr(), stream())
+    assert same_value(host(h), oracle.dequant_f32(synth.Q4_K, 500, TINY.dim, m.embd)[tok0])
+    for l in range(3):
+        blob = m.blobs_dev[l]
+        mats = [blob[m.lay.offsets[n]:] for n in recipes.TENSORS]
+        w = tg.layer_weights(m.lay.fmt_list(), mats, blob[m.lay.offsets["attn_norm"]:].view(torch.float32),
+                             blob[m.lay.offsets["ffn_norm"]:].view(torch.float32))
+        nt.nt_decode_layer(w, shp, 20, h.data_ptr(), kd[l].data_ptr(), vd[l].data_ptr(), ws.data_ptr(), wsb, stream())
+    assert same_value(host(h), hs[0])
+    for l in range(3):
+        assert same_value(host(kd[l]), kcs[l]) and same_value(host(vd[l]), vcs[l])
+
+
+def test_streaming_70b_q6_k_layer_bit_identical():
+    """A real-size Q6_K 70B layer (701.9 MB) run from pinned host memory through a staging
+    buffer gives bit-identical results to the same blob run resident."""
+    say("streaming a 70B Q6_K layer")
+    shape = recipes.LLAMA31_70B
+    m = Model(shape, recipes.MIX_Q6_K, 2, vocab=256, n_slots=4096)
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    a = decode_tokens(m, set(), 7, 4096, 2)
+    b = decode_tokens(m, {1}, 7, 4096, 2, staging)
+    assert a[0] == b[0]
+    for x, y in zip(a[1] + a[2], b[1] + b[2]):
+        assert same_value(x, y)
+    assert b[5].h2d_bytes >= m.lay.nbytes
+
+
+def test_stream_rejects_pageable_host_memory():
+    m = Model(TINY, recipes.MIX_Q4_K_M, 2, vocab=100, n_slots=8)
+    kcs, vcs = m.caches()
+    pageable = np.zeros(m.lay.nbytes + 256, np.uint8)
+    addr = (pageable.ctypes.data + 255) // 256 * 256
+    shp = tg.layer_shape(TINY)
+    lay = tg.layer_layout(m.lay.offset_list(), m.lay.fmt_list(), m.lay.nbytes)
+    plan, keep = tg.model_plan(shp, lay, [(m.blobs_dev[0].data_ptr(), True, kcs[0].data_ptr(), vcs[0].data_ptr()),
+                                          (addr, False, kcs[1].data_ptr(), vcs[1].data_ptr())])
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), m.lay.nbytes)
+    ws = torch.zeros(nt.nt_decode_layer_ws_bytes(shp), dtype=torch.uint8, device="cuda")
+    h = torch.zeros(TINY.dim, dtype=torch.float32, device="cuda")
+    c1, c2 = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        with pytest.raises(nt.NtError) as ei:
+            nt.nt_stream_layers(st, plan, 8, h.data_ptr(), ws.data_ptr(), ws.numel(), c1.cuda_stream, c2.cuda_stream)
+        assert ei.value.code == nt.NT_EHOSTMEM
+    finally:
+        nt.nt_stream_destroy(st)

@@ -1,0 +1,222 @@
+"""GPU parity of the per-op C ABI against the fp64 checker (MI355X only).
+
+Every call goes through libnt.so's C ABI.  Acceptance: dequantization bit-exact
+(by value); GEMV |y - y_ref| <= 1e-3 * sum_c |w_rc x_c| per row (and exactly 0
+where that sum is 0); the small ops within 1e-3 of their own normalisers.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_weight_streaming_dequant_amd as nt
+import synth
+from synth import recipes
+from tests.blockpack import pack_q4_0, pack_q4_k, pack_q6_k, pack_q8_0
+from tests.gpu_util import check_rel, dev, host, same_value, say, stream
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K]
+NAMES = {synth.Q8_0: "Q8_0", synth.Q4_0: "Q4_0", synth.Q4_K: "Q4_K", synth.Q6_K: "Q6_K"}
+
+
+def gpu_gemv(fmt, rows, cols, blocks, x):
+    wb = dev(blocks)
+    xd = dev(x.astype(np.float32))
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    nt.nt_gemv_q(fmt, rows, cols, wb.data_ptr(), xd.data_ptr(), y.data_ptr(), stream())
+    return host(y)
+
+
+def gpu_dequant(fmt, rows, cols, blocks):
+    wb = dev(blocks)
+    w = torch.empty(rows * cols, dtype=torch.float32, device="cuda")
+    nt.nt_dequant(fmt, rows, cols, wb.data_ptr(), w.data_ptr(), stream())
+    return host(w).reshape(rows, cols)
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows,cols", [(1, 256), (7, 768), (33, 4096), (5, 28672)])
+def test_dequant_bit_exact(fmt, rows, cols):
+    say(f"dequant {NAMES[fmt]} {rows}x{cols}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=1, stream=100 + fmt)
+    got = gpu_dequant(fmt, rows, cols, blocks)
+    ref = oracle.dequant_f32(fmt, rows, cols, blocks)
+    assert same_value(got, ref)
+
+
+def test_dequant_hand_blocks_bit_exact():
+    say("dequant hand blocks")
+    cases = [
+        (synth.Q8_0, pack_q8_0(-3.0, [-128, 127] * 16) + pack_q8_0(2.0 ** -24, list(range(-16, 16)))),
+        (synth.Q4_0, pack_q4_0(65504.0, list(range(16)) * 2) + pack_q4_0(-0.5, [15 - (i % 16) for i in range(32)])),
+        (synth.Q4_K, pack_q4_k(0.001, 0.01, [63] * 8, [63] * 8, [i % 16 for i in range(256)]) +
+         pack_q4_k(-2.0, 6.1e-5, list(range(56, 64)), list(range(8)), [(i * 7) % 16 for i in range(256)])),
+        (synth.Q6_K, pack_q6_k(0.01, [-128, 127] * 8, [i % 64 for i in range(256)]) +
+         pack_q6_k(-6.0e-8, [-64 + 8 * k for k in range(16)], [(i * 5 + 3) % 64 for i in range(256)])),
+    ]
+    for fmt, raw in cases:
+        blocks = np.frombuffer(raw, np.uint8)
+        cols = synth.BLOCK_ELEMS[fmt] * 2
+        got = gpu_dequant(fmt, 1, cols, blocks)
+        ref = oracle.dequant_f32(fmt, 1, cols, blocks)
+        assert same_value(got, ref), NAMES[fmt]
+
+
+# ------------------------------------------------------------------ GEMV
+
+GEMV_SHAPES = {
+    # rows x cols: single block, ragged block counts (odd row byte counts put rows at
+    # alternating 4-byte phases), rows past a workgroup tile, and the workload shapes
+    synth.Q8_0: [(1, 32), (3, 32), (37, 2144), (301, 1056), (4096, 4096), (14336, 4096), (4096, 14336)],
+    synth.Q4_0: [(1, 32), (5, 96), (29, 1440), (257, 4096), (4096, 4096)],
+    synth.Q4_K: [(1, 256), (23, 1280), (130, 4352), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
+    synth.Q6_K: [(1, 256), (19, 768), (77, 2304), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
+}
+GEMV_CASES = [(f, r, c) for f in FMTS for (r, c) in GEMV_SHAPES[f]]
+
+
+@pytest.mark.parametrize("fmt,rows,cols", GEMV_CASES)
+def test_gemv_matches_oracle(fmt, rows, cols):
+    say(f"gemv {NAMES[fmt]} {rows}x{cols}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=0, stream=200 + fmt)
+    x = synth.normal_f32(cols, seed=0, stream=300 + fmt)
+    y = gpu_gemv(fmt, rows, cols, blocks, x)
+    ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+    worst = check_rel(y, ref, nrm, what=f"{NAMES[fmt]} {rows}x{cols}")
+    say(f"  worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_one_hot_and_zero(fmt):
+    """One-hot x picks a dequantized column exactly; all-zero blocks give exact zeros."""
+    rows, cols = 64, 1024
+    say(f"gemv one-hot {NAMES[fmt]}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=2, stream=400 + fmt)
+    w32 = oracle.dequant_f32(fmt, rows, cols, blocks)
+    for j in (0, 31, 32, 255, 256, 777, 1023):
+        x = np.zeros(cols, np.float32)
+        x[j] = 1.0
+        y = gpu_gemv(fmt, rows, cols, blocks, x)
+        ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+        check_rel(y, ref, nrm, what=f"one-hot {j}")
+        # one nonzero product per row: every partial term is exact, so the only
+        # rounding is the one that also makes the dequantized weight
+        assert same_value(y, w32[:, j])
+    zb = np.zeros_like(blocks)
+    y = gpu_gemv(fmt, rows, cols, zb, synth.normal_f32(cols, 0, 5))
+    assert np.all(y == 0)
+
+
+def test_gemv_misaligned_base_rejected():
+    blocks = dev(synth.quant_matrix(synth.Q4_K, 4, 256, 0, 1))
+    x = torch.zeros(256, dtype=torch.float32, device="cuda")
+    y = torch.zeros(4, dtype=torch.float32, device="cuda")
+    with pytest.raises(nt.NtError) as ei:
+        nt.nt_gemv_q(synth.Q4_K, 3, 256, blocks.data_ptr() + 4, x.data_ptr(), y.data_ptr(), stream())
+    assert ei.value.code == nt.NT_EALIGN
+
+
+# ------------------------------------------------------------------ small ops
+
+def test_rmsnorm():
+    for n in (1, 100, 4096, 8192, 28672):
+        say(f"rmsnorm n={n}")
+        x = synth.normal_f32(n, 0, 11) * 3.0
+        g = synth.uniform_f32(n, 0, 12, 0.9, 1.1)
+        xd, gd = dev(x), dev(g)
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        nt.nt_rmsnorm(n, xd.data_ptr(), gd.data_ptr(), 1e-5, y.data_ptr(), stream())
+        ref = oracle.rmsnorm(x, g, 1e-5)
+        check_rel(host(y), ref, np.abs(ref) + 1e-30, what=f"rmsnorm {n}")
+
+
+def test_rmsnorm_in_place():
+    n = 8192
+    x = synth.normal_f32(n, 0, 13)
+    g = synth.uniform_f32(n, 0, 14, 0.9, 1.1)
+    xd, gd = dev(x), dev(g)
+    nt.nt_rmsnorm(n, xd.data_ptr(), gd.data_ptr(), 1e-5, xd.data_ptr(), stream())
+    ref = oracle.rmsnorm(x, g, 1e-5)
+    check_rel(host(xd), ref, np.abs(ref) + 1e-30)
+
+
+@pytest.mark.parametrize("pos", [0, 1, 1023, 4096, 4223])
+def test_rope(pos):
+    say(f"rope pos={pos}")
+    n_heads, hd = 72, 128
+    x = synth.normal_f32(n_heads * hd, 0, 15) * 20
+    xd = dev(x)
+    nt.nt_rope(n_heads, hd, pos, 500000.0, xd.data_ptr(), stream())
+    ref = oracle.rope(x, n_heads, hd, pos, 500000.0)
+    pair = np.repeat(np.hypot(x[0::2].astype(np.float64), x[1::2]), 2)
+    check_rel(host(xd), ref, pair, what=f"rope {pos}")
+
+
+def test_swiglu():
+    n = 28672
+    g = synth.normal_f32(n, 0, 16) * 6
+    g[:4] = [0.0, 100.0, -100.0, -1000.0]
+    u = synth.normal_f32(n, 0, 17)
+    gd, ud = dev(g), dev(u)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    nt.nt_swiglu(n, gd.data_ptr(), ud.data_ptr(), out.data_ptr(), stream())
+    ref, nrm = oracle.swiglu(g, u)
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    check_rel(got, ref, nrm, what="swiglu")
+
+
+ATTN_CASES = [  # n_q, n_kv, n_ctx, max_ctx, q scale
+    (32, 8, 1024, 1024, 1.0), (32, 8, 1024, 1024, 8.0), (64, 8, 4097, 4224, 1.0), (64, 8, 4224, 4224, 6.0),
+    (64, 8, 1, 4224, 1.0), (64, 8, 65, 128, 1.0), (8, 8, 300, 512, 1.0), (16, 8, 77, 96, 2.0), (16, 1, 333, 400, 1.0),
+]
+
+
+@pytest.mark.parametrize("n_q,n_kv,n_ctx,max_ctx,qs", ATTN_CASES)
+def test_attention(n_q, n_kv, n_ctx, max_ctx, qs):
+    say(f"attention nq={n_q} nkv={n_kv} n_ctx={n_ctx} max_ctx={max_ctx} qscale={qs}")
+    hd = 128
+    q = synth.normal_f32(n_q * hd, 0, 18) * qs
+    kc = synth.normal_f16_bits(n_kv * max_ctx * hd, 0, 19)
+    vc = synth.normal_f16_bits(n_kv * max_ctx * hd, 0, 20)
+    qd, kd, vd = dev(q), dev(kc), dev(vc)
+    out = torch.empty(n_q * hd, dtype=torch.float32, device="cuda")
+    wsb = nt.nt_attn_decode_ws_bytes(n_q, n_kv, hd, max_ctx)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    for rep in range(2):  # the second call checks that the counters were left at zero
+        nt.nt_attn_decode(n_q, n_kv, hd, n_ctx, max_ctx, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(),
+                          ws.data_ptr(), wsb, stream())
+        ref, nrm = oracle.attn(q, kc, vc, n_q, n_kv, hd, n_ctx, max_ctx)
+        check_rel(host(out), ref, nrm, what=f"attention rep {rep}")
+
+
+# ------------------------------------------------------------------ token glue
+
+def test_embed_row_and_argmax():
+    fmt, vocab, dim = synth.Q4_K, 1000, 1024
+    say("embed row + argmax")
+    table = synth.quant_matrix(fmt, vocab, dim, 0, 21)
+    td = dev(table)
+    h = torch.empty(dim, dtype=torch.float32, device="cuda")
+    for tok in (0, 1, 517, 999, -1, 1000):
+        t = torch.tensor([tok], dtype=torch.int32, device="cuda")
+        nt.nt_embed_row(fmt, vocab, dim, td.data_ptr(), t.data_ptr(), h.data_ptr(), stream())
+        got = host(h)
+        if 0 <= tok < vocab:
+            assert same_value(got, oracle.dequant_f32(fmt, vocab, dim, table)[tok])
+        else:
+            assert np.all(got == 0)
+    for n in (1, 7, 128256):
+        v = synth.normal_f32(n, 0, 22)
+        if n > 7:
+            v[5000] = v[90000] = v.max() + 1  # a tie: the lower index wins
+        vd = dev(v)
+        o = torch.zeros(1, dtype=torch.int32, device="cuda")
+        nt.nt_argmax(n, vd.data_ptr(), o.data_ptr(), stream())
+        assert int(host(o)[0]) == oracle.argmax(v)
