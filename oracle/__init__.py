@@ -198,8 +198,8 @@ def decode_layer(w: dict, fmts: dict, shape, pos: int, h, k_cache, v_cache, forc
     w: name -> uint8 blocks for q, k, v, o, gate, up, down; fp32 gains under
     attn_norm and ffn_norm.  k_cache / v_cache: uint16 [n_kv][max_ctx][hd]
     (copied, not modified).  forced (nullable) may hold the GPU's captured
-    values: 'k16'/'v16' (fp16 bits written at slot pos, accepted within one
-    binary16 step of the oracle's own rounding), 'q' (post-RoPE query),
+    values: 'k16'/'v16' (fp16 bits written at slot pos; their distance in
+    binary16 steps from the oracle's own rounding is reported), 'q' (post-RoPE query),
     'o' (attention output), 'h1' (hidden state after the attention residual),
     'a' (SwiGLU output).  A forced stage replaces the oracle's own value as the
     next stage's input; the oracle's own value is still reported.

@@ -2,9 +2,9 @@
 (MI355X only), through the C ABI.
 
 Stage-wise, teacher-forced acceptance (each stage judged on the GPU's own input
-to it): the fp16 K/V written at slot pos within one binary16 step of the
-checker's rounding; the rotated query, attention output, h1, SwiGLU output and
-h2 each within 1e-3 of their normalisers.  Streaming must be bit-identical to
+to it): the fp16 K/V written at slot pos within the GEMV tolerance of the exact
+value plus half a binary16 step; the rotated query, attention output, h1,
+SwiGLU output and h2 each within 1e-3 of their normalisers.  Streaming must be bit-identical to
 running the same layers resident.
 """
 from __future__ import annotations
@@ -70,10 +70,18 @@ def run_layer_and_check(shape, mix, pos, n_slots, layer=0, sample_rows=None):
 
     st = oracle.decode_layer(L.host, mix, shape, pos, h0, L.kc_host, L.vc_host,
                              forced={"k16": g_k16, "v16": g_v16, "q": g_q, "o": g_o, "h1": g_h1, "a": g_a})
-    assert st["k16_ulp"] <= 1 and st["v16_ulp"] <= 1, (st["k16_ulp"], st["v16_ulp"])
     # RoPE mixes rows 2i and 2i+1: the pair's GEMV normalisers bound the rotated error
     qn = np.repeat(st["q_nrm"][0::2] + st["q_nrm"][1::2], 2)
+    kn = np.repeat(st["k_nrm"][0::2] + st["k_nrm"][1::2], 2)
     res = {}
+    # the cache holds RNE_fp16(v') for some v' within the GEMV tolerance of the exact value:
+    # |fp16 - exact| <= 1e-3 N + half a binary16 step at that value
+    for name, bits, exact, nrm in (("k16", g_k16, st["k"], kn), ("v16", g_v16, st["v"], st["v_nrm"])):
+        val = bits.view(np.float16).astype(np.float64)
+        half_step = np.spacing(np.abs(bits.view(np.float16))).astype(np.float64) / 2
+        err = np.abs(val - exact)
+        assert np.all(err <= 1e-3 * nrm + half_step), f"{name}: worst {np.max(err / (1e-3 * nrm + half_step)):.3f}"
+        res[name] = float(np.max(np.maximum(err - half_step, 0) / nrm))
     res["q"] = check_rel(g_q, st["q"], qn, what="q")
     res["o"] = check_rel(g_o, st["o"], st["o_nrm"], what="attention")
     res["h1"] = check_rel(g_h1, st["h1"], st["h1_nrm"], what="h1")
