@@ -101,9 +101,9 @@ int nt_rope(int n_heads, int head_dim, int pos, float theta, float* qk, void* st
  * [0, n_ctx): s_t = q.k_t / sqrt(head_dim), p = softmax(s), out_h = sum_t p_t v_t.
  * ntransformer overview, "Hauptfunktionen" (GQA, KV cache) and "Architektur
  * und Codestruktur" (softmax).  out: [n_q_heads][head_dim] fp32.
- * ws: workspace of nt_attn_decode_ws_bytes() bytes, 256-byte aligned; its
- * counter region must be zero before the first call that uses it (e.g. a
- * zero-filled allocation); every call leaves it zero again.
+ * ws: scratch of nt_attn_decode_ws_bytes() bytes, 256-byte aligned, for the
+ * per-split partials (two kernels: split partials, then their merge); no initial
+ * contents are required.
  * head_dim == 128; n_q_heads % n_kv_heads == 0; n_q_heads / n_kv_heads <= 16;
  * 1 <= n_ctx <= max_ctx. */
 int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int max_ctx, const float* q,
@@ -145,8 +145,8 @@ typedef struct {
  *   k, v -> fp16 (RNE) into cache slot pos; o = attention over slots [0, pos];
  *   h1 = h + Wo o; n2 = RMSNorm(h1, ffn_norm); a = SwiGLU(Wg n2, Wu n2); h2 = h1 + Wd a.
  * h: [dim] fp32, in/out (h2 on return).  k_cache, v_cache: [nkv][max_ctx][128] fp16 bits.
- * ws: nt_decode_layer_ws_bytes() bytes, 256-byte aligned, zero-filled before its first use
- * (its counter region is left zero by every call).  After the call ws holds, as fp32 arrays
+ * ws: nt_decode_layer_ws_bytes() bytes, 256-byte aligned; no initial contents are required.
+ * After the call ws holds, as fp32 arrays
  * at these byte offsets (see nt_decode_layer_ws_offsets): the rotated query q [nq*hd],
  * the attention output o [nq*hd], h1 [dim] and the SwiGLU output a [ffn].
  * Constraints: head_dim 128; dim, nq*hd and ffn multiples of 256 and <= NT_GEMV_MAX_COLS;
@@ -230,7 +230,7 @@ typedef struct {
  * place when st is NULL, which requires every layer resident); logits =
  * W_out RMSNorm(h, output_norm); *token = argmax(logits) (ties -> lowest id).
  * token: device int32, in/out.  logits: device [n_vocab] fp32.  h: device [dim].
- * ws: nt_decode_token_ws_bytes() bytes (zero-filled before first use). */
+ * ws: nt_decode_token_ws_bytes() bytes, 256-byte aligned; no initial contents are required. */
 int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_head* head, int pos, int32_t* token,
                     float* logits, float* h, void* ws, size_t ws_bytes, void* compute, void* copy,
                     nt_stream_stats* stats);

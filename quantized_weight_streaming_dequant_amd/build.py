@@ -29,33 +29,35 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines: tuple = (), build_dir: str = BUILD) -> str:
+    """Compile every source and link libnt.so at `out` (defines: extra -D flags)."""
+    os.makedirs(build_dir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(build_dir, src + ".o")
+        dflags = [f"-D{d}" for d in defines]
+        cmd = [HIPCC, *FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
-            cmd = [HIPCC, *[f for f in FLAGS if f != "--offload-arch=gfx950"], "-x", "hip", "--offload-arch=gfx950",
-                   "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *[f for f in FLAGS if f != "--offload-arch=gfx950"], *dflags, "-x", "hip",
+                   "--offload-arch=gfx950", "-c", os.path.join(CSRC, src), "-o", obj]
         objs.append(obj)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
     failed = False
     for src, p in procs:
-        out, _ = p.communicate()
-        out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l and "ignoring feature" not in l)
+        log, _ = p.communicate()
+        log = "\n".join(l for l in log.splitlines() if "packed-fp32-ops" not in l and "ignoring feature" not in l)
         if p.returncode != 0:
             failed = True
-            print(f"--- hipcc failed on {src}:\n{out}", file=sys.stderr)
-        elif verbose and out.strip():
-            print(out, file=sys.stderr)
+            print(f"--- hipcc failed on {src}:\n{log}", file=sys.stderr)
+        elif verbose and log.strip():
+            print(log, file=sys.stderr)
     if failed:
         raise RuntimeError("HIP build failed")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

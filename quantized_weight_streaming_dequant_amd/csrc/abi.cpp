@@ -73,7 +73,7 @@ struct TimedLaunch {
 
 // ------------------------------------------------------------ workspace layout
 struct LayerWs {
-  size_t q, o, h1, a, part, cnt, key, total;
+  size_t q, o, h1, a, part, key, total;
 };
 
 LayerWs layer_ws(const nt_layer_shape& s) {
@@ -85,7 +85,6 @@ LayerWs layer_ws(const nt_layer_shape& s) {
   w.h1 = off; off = align256(off + 4 * (size_t)s.dim);
   w.a = off; off = align256(off + 4 * (size_t)s.ffn_dim);
   w.part = off; off = align256(off + 4 * attn_part_floats(s.n_q_heads, s.max_ctx));
-  w.cnt = off; off = align256(off + 4 * (size_t)s.n_kv_heads);
   w.key = off; off = align256(off + 8);
   w.total = off;
   return w;
@@ -124,13 +123,13 @@ int check_weights(const nt_layer_weights* w) {
   return NT_OK;
 }
 
-GemvSeg make_seg(const void* w, int fmt, int rows, int cols, int tile0) {
+GemvSeg make_seg(const void* w, int fmt, int rows, int cols, int grp0) {
   GemvSeg g;
   g.w = reinterpret_cast<const uint8_t*>(w);
   g.fmt = fmt;
   g.rows = rows;
   g.row_bytes = (int64_t)(cols / block_elems(fmt)) * block_bytes(fmt);
-  g.tile0 = tile0;
+  g.grp0 = grp0;
   return g;
 }
 
@@ -157,9 +156,9 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     a.x = h; a.gain = w.attn_norm; a.eps = s.eps; a.cols = s.dim;
     a.nseg = 3;
     int t = 0;
-    a.seg[0] = make_seg(w.w[NT_W_Q], w.fmt[NT_W_Q], nq, s.dim, t); t += gemv_tiles(p, nq);
-    a.seg[1] = make_seg(w.w[NT_W_K], w.fmt[NT_W_K], nkv, s.dim, t); t += gemv_tiles(p, nkv);
-    a.seg[2] = make_seg(w.w[NT_W_V], w.fmt[NT_W_V], nkv, s.dim, t); t += gemv_tiles(p, nkv);
+    a.seg[0] = make_seg(w.w[NT_W_Q], w.fmt[NT_W_Q], nq, s.dim, t); t += gemv_groups(p, nq);
+    a.seg[1] = make_seg(w.w[NT_W_K], w.fmt[NT_W_K], nkv, s.dim, t); t += gemv_groups(p, nkv);
+    a.seg[2] = make_seg(w.w[NT_W_V], w.fmt[NT_W_V], nkv, s.dim, t); t += gemv_groups(p, nkv);
     a.q_out = wq; a.k_cache = kc; a.v_cache = vc; a.pos = pos; a.max_ctx = s.max_ctx; a.rope_theta = s.rope_theta;
     const int mask = (1 << w.fmt[NT_W_Q]) | (1 << w.fmt[NT_W_K]) | (1 << w.fmt[NT_W_V]);
     TimedLaunch tl(NT_K_ATTN_IN, st);
@@ -169,7 +168,6 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     AttnArgs a;
     a.q = wq; a.k_cache = kc; a.v_cache = vc; a.out = wo;
     a.part = reinterpret_cast<float*>(ws + L.part);
-    a.counter = reinterpret_cast<int*>(ws + L.cnt);
     a.n_kv = s.n_kv_heads; a.n_ctx = pos + 1; a.max_ctx = s.max_ctx;
     a.slots_per_wave = attn_slots_per_wave(a.n_ctx, a.n_kv);
     a.n_split = attn_n_split(a.n_ctx, a.slots_per_wave);
@@ -183,7 +181,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     a.seg[0] = make_seg(w.w[NT_W_O], w.fmt[NT_W_O], s.dim, nq, 0);
     a.y = h; a.resid = h; a.y2 = wh1;
     TimedLaunch tl(NT_K_O, st);
-    if ((e = gemv_launch(1 << w.fmt[NT_W_O], EPI_RESID, p, gemv_tiles(p, s.dim), a, st)) != hipSuccess)
+    if ((e = gemv_launch(1 << w.fmt[NT_W_O], EPI_RESID, p, gemv_groups(p, s.dim), a, st)) != hipSuccess)
       return hip_fail(e, "o launch");
   }
   {  // a6-a8: RMSNorm prologue, paired gate/up GEMV, SwiGLU epilogue
@@ -194,7 +192,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     a.seg[1] = make_seg(w.w[NT_W_UP], w.fmt[NT_W_UP], s.ffn_dim, s.dim, 1 << 30);
     a.y = wa;
     TimedLaunch tl(NT_K_FFN_UP, st);
-    if ((e = gemv_launch(1 << w.fmt[NT_W_GATE], EPI_SWIGLU, p, gemv_tiles(p, s.ffn_dim), a, st)) != hipSuccess)
+    if ((e = gemv_launch(1 << w.fmt[NT_W_GATE], EPI_SWIGLU, p, gemv_groups(p, s.ffn_dim), a, st)) != hipSuccess)
       return hip_fail(e, "gate/up launch");
   }
   {  // a9: down GEMV + residual
@@ -204,7 +202,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     a.seg[0] = make_seg(w.w[NT_W_DOWN], w.fmt[NT_W_DOWN], s.dim, s.ffn_dim, 0);
     a.y = h; a.resid = h;
     TimedLaunch tl(NT_K_FFN_DOWN, st);
-    if ((e = gemv_launch(1 << w.fmt[NT_W_DOWN], EPI_RESID, p, gemv_tiles(p, s.dim), a, st)) != hipSuccess)
+    if ((e = gemv_launch(1 << w.fmt[NT_W_DOWN], EPI_RESID, p, gemv_groups(p, s.dim), a, st)) != hipSuccess)
       return hip_fail(e, "down launch");
   }
   return NT_OK;
@@ -290,7 +288,7 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
   a.seg[0] = make_seg(blocks, fmt, (int)rows, (int)cols, 0);
   a.y = y;
   TimedLaunch tl(NT_K_GEMV, (hipStream_t)stream);
-  hipError_t e = gemv_launch(1 << fmt, EPI_STORE, p, gemv_tiles(p, (int)rows), a, (hipStream_t)stream);
+  hipError_t e = gemv_launch(1 << fmt, EPI_STORE, p, gemv_groups(p, (int)rows), a, (hipStream_t)stream);
   return e == hipSuccess ? NT_OK : hip_fail(e, "gemv launch");
 }
 
@@ -314,7 +312,7 @@ int nt_rope(int n_heads, int head_dim, int pos, float theta, float* qk, void* st
 size_t nt_attn_decode_ws_bytes(int n_q_heads, int n_kv_heads, int head_dim, int max_ctx) {
   (void)head_dim;
   if (n_q_heads <= 0 || n_kv_heads <= 0 || max_ctx <= 0) return 0;
-  return align256(4 * attn_part_floats(n_q_heads, max_ctx)) + align256(4 * (size_t)n_kv_heads);
+  return align256(4 * attn_part_floats(n_q_heads, max_ctx));
 }
 
 int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int max_ctx, const float* q,
@@ -332,7 +330,6 @@ int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int m
   AttnArgs a;
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.out = out;
   a.part = reinterpret_cast<float*>(ws);
-  a.counter = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(ws) + align256(4 * attn_part_floats(n_q_heads, max_ctx)));
   a.n_kv = n_kv_heads; a.n_ctx = n_ctx; a.max_ctx = max_ctx;
   a.slots_per_wave = attn_slots_per_wave(n_ctx, n_kv_heads);
   a.n_split = attn_n_split(n_ctx, a.slots_per_wave);
@@ -568,7 +565,7 @@ int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_h
     a.seg[0] = make_seg(head->output, head->out_fmt, (int)head->n_vocab, plan->shape.dim, 0);
     a.y = logits; a.amax = key;
     TimedLaunch tl(NT_K_LM_HEAD, cs);
-    if ((e = gemv_launch(1 << head->out_fmt, EPI_LOGITS, p, gemv_tiles(p, (int)head->n_vocab), a, cs)) != hipSuccess)
+    if ((e = gemv_launch(1 << head->out_fmt, EPI_LOGITS, p, gemv_groups(p, (int)head->n_vocab), a, cs)) != hipSuccess)
       return hip_fail(e, "lm head launch");
   }
   if ((e = token_from_key_launch(key, token, cs)) != hipSuccess) return hip_fail(e, "token launch");

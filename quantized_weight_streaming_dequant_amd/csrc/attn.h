@@ -13,7 +13,6 @@ struct AttnArgs {
   const uint16_t* v_cache;
   float* out;              // [n_q][128]
   float* part;             // [n_kv][n_split][G][130] partials (workspace)
-  int* counter;            // [n_kv] zero on entry, zero on exit (workspace)
   int n_kv;
   int n_ctx;
   int max_ctx;

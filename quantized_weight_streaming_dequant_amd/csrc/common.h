@@ -65,20 +65,38 @@ __device__ __forceinline__ float sb1(uint32_t v) { return (float)(int8_t)((v >> 
 __device__ __forceinline__ float sb2(uint32_t v) { return (float)(int8_t)((v >> 16) & 0xFFu); }
 __device__ __forceinline__ float sb3(uint32_t v) { return (float)(int8_t)(v >> 24); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Cross-lane moves inside rows of 16 lanes (DPP): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.  After the four steps every lane of a row holds the row's
+// reduction; the four row results are then read as scalars and combined.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
+__device__ __forceinline__ float row_lane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Sum over the 64 lanes, returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
+}
+// Maximum over the 64 lanes, returned to every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
 }
 
-// Activation vector layout in LDS: 4 pad floats after every 64 columns, so that lanes
-// reading consecutive 32- or 64-column runs with 128-bit reads spread over the banks.
-__host__ __device__ __forceinline__ int xpad(int c) { return c + ((c >> 6) << 2); }
-__host__ __device__ __forceinline__ int xpad_len(int cols) { return cols + (((cols + 63) >> 6) << 2); }
+// Activation vector layout in LDS: 4 pad floats after every 64 columns and 4 more after
+// every 512, so that lanes reading runs 64 columns apart (Q8_0, Q4_0, Q4_K slices) and
+// runs 512 columns apart (Q6_K slices of alternate superblocks) with 128-bit reads
+// spread over the banks.  Runs of 16 aligned columns stay contiguous.
+__host__ __device__ __forceinline__ int xpad(int c) { return c + ((c >> 6) << 2) + ((c >> 9) << 2); }
+__host__ __device__ __forceinline__ int xpad_len(int cols) { return xpad(cols + 511); }
 
 }  // namespace nt

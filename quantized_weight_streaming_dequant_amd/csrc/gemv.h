@@ -19,7 +19,7 @@ struct GemvSeg {
   int64_t row_bytes;
   int rows;
   int fmt;
-  int tile0;          // first workgroup index of this matrix
+  int grp0;           // index of this matrix's first row group in the launch
 };
 
 struct GemvArgs {
@@ -49,9 +49,10 @@ struct GemvPlan {
 
 // Launch geometry for a format mix and shape.
 GemvPlan gemv_plan(int epi, int cols);
-// Number of workgroups a segment of `rows` rows needs under `plan`.
-int gemv_tiles(const GemvPlan& p, int rows);
-// Enqueue.  fmt_mask: bit f set for every format present in the segments.
-hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_tiles, const GemvArgs& a, hipStream_t s);
+// Row groups (of rows_per_wave rows) a segment of `rows` rows makes under `plan`.
+int gemv_groups(const GemvPlan& p, int rows);
+// Enqueue.  fmt_mask: bit f set for every format present in the segments; n_groups: the
+// launch's row groups over all segments.
+hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s);
 
 }  // namespace nt
