@@ -25,6 +25,11 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 
 
+
+def v_to_device_layout(torch, v, n_kv, max_ctx, hd=128):
+    """[n_kv][max_ctx][hd] fp16 V cache -> the library's [n_kv][max_ctx/8][hd][8] (device copy)."""
+    return v.view(n_kv, max_ctx // 8, 8, hd).transpose(2, 3).contiguous().view(-1)
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -103,7 +108,8 @@ class Model70B:
                 log(f"  generated layer {l + 1}/{n_layers} ({time.time() - t0:.1f}s)")
         copy_stream.synchronize()
         del stage
-        # KV caches: [n_kv][max_ctx][128] fp16 per layer, slots < n_prefill ~ N(0,1)
+        # KV caches per layer, slots < n_prefill ~ N(0,1): K as [n_kv][max_ctx][128] fp16,
+        # V regrouped on the device into the library's [n_kv][max_ctx/8][128][8]
         cache_elems = shp.n_kv_heads * shp.max_ctx * shp.head_dim
         self.kc, self.vc = [], []
         kv_host = torch.empty(cache_elems, dtype=torch.int16, pin_memory=True)
@@ -111,7 +117,10 @@ class Model70B:
             for which, lst in (("k", self.kc), ("v", self.vc)):
                 kv_host.zero_()
                 recipes.kv_cache_fill(kv_host.data_ptr(), shp, l, which, n_prefill, seed)
-                lst.append(kv_host.cuda())
+                d = kv_host.cuda()
+                if which == "v":
+                    d = v_to_device_layout(torch, d, shp.n_kv_heads, shp.max_ctx)
+                lst.append(d)
         # head
         embd_fmt = out_fmt = synth.Q4_K if mix[ "q"] == synth.Q4_K else synth.Q6_K
         self.embd_fmt, self.out_fmt = embd_fmt, out_fmt
@@ -350,7 +359,8 @@ def bench_layer_8b(args, torch, nt, tg):
     ws_list = [tg.layer_weights([mix[n] for n in recipes.TENSORS], [d[n] for n in recipes.TENSORS], d["attn_norm"],
                                 d["ffn_norm"]) for d in dl]
     kc = torch.from_numpy(recipes.kv_cache_array(shape, 0, "k", 1024)).cuda()
-    vc = torch.from_numpy(recipes.kv_cache_array(shape, 0, "v", 1024)).cuda()
+    vc = v_to_device_layout(torch, torch.from_numpy(recipes.kv_cache_array(shape, 0, "v", 1024)).cuda(),
+                            shape.n_kv_heads, shape.max_ctx)
     shp = tg.layer_shape(shape)
     wsb = nt.nt_decode_layer_ws_bytes(shp)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")

@@ -95,8 +95,16 @@ int nt_rmsnorm(int64_t n, const float* x, const float* gain, float eps, float* y
  * head_dim even, <= 1024; pos >= 0. */
 int nt_rope(int n_heads, int head_dim, int pos, float theta, float* qk, void* stream);
 
+/* KV cache layout (per layer, head_dim 128, fp16 bits, capacity max_ctx slots):
+ *   K: [n_kv_heads][max_ctx][128]: element (g, t, d) at (g * max_ctx + t) * 128 + d;
+ *   V: groups of 8 slots, [n_kv_heads][max_ctx / 8][128][8]: element (g, t, d) at
+ *      g * max_ctx * 128 + ((t / 8) * 128 + d) * 8 + t % 8,
+ * so that the 8 consecutive slots of one dimension are one 16-byte piece (the operand
+ * shape of the attention's p V product). */
+#define NT_MAX_CTX 524288
+
 /* GQA decode attention for one token.  q: [n_q_heads][head_dim] fp32.
- * k_cache, v_cache: [n_kv_heads][max_ctx][head_dim] fp16 bits.  Query head h
+ * k_cache, v_cache: fp16 bits in the KV cache layout below.  Query head h
  * reads KV head h / (n_q_heads / n_kv_heads) and attends over cache slots
  * [0, n_ctx): s_t = q.k_t / sqrt(head_dim), p = softmax(s), out_h = sum_t p_t v_t.
  * ntransformer overview, "Hauptfunktionen" (GQA, KV cache) and "Architektur
@@ -104,8 +112,9 @@ int nt_rope(int n_heads, int head_dim, int pos, float theta, float* qk, void* st
  * ws: scratch of nt_attn_decode_ws_bytes() bytes, 256-byte aligned, for the
  * per-split partials (two kernels: split partials, then their merge); no initial
  * contents are required.
- * head_dim == 128; n_q_heads % n_kv_heads == 0; n_q_heads / n_kv_heads <= 16;
- * 1 <= n_ctx <= max_ctx. */
+ * head_dim == 128; n_q_heads % n_kv_heads == 0; n_q_heads / n_kv_heads in
+ * {1, 2, 4, 8, 16}; max_ctx a multiple of 8 up to NT_MAX_CTX; 1 <= n_ctx <= max_ctx.
+ * Slots at or past n_ctx may hold any bits; they are not used. */
 int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int max_ctx, const float* q,
                    const uint16_t* k_cache, const uint16_t* v_cache, float* out, void* ws, size_t ws_bytes,
                    void* stream);
@@ -123,7 +132,7 @@ typedef struct {
   int n_kv_heads;
   int head_dim;   /* must be 128 */
   int ffn_dim;
-  int max_ctx;    /* cache capacity in slots */
+  int max_ctx;    /* cache capacity in slots: a multiple of 8, <= NT_MAX_CTX */
   float eps;      /* RMSNorm epsilon */
   float rope_theta;
 } nt_layer_shape;
@@ -144,7 +153,7 @@ typedef struct {
  *   n1 = RMSNorm(h, attn_norm); q = Wq n1, k = Wk n1, v = Wv n1; RoPE(q, k, pos);
  *   k, v -> fp16 (RNE) into cache slot pos; o = attention over slots [0, pos];
  *   h1 = h + Wo o; n2 = RMSNorm(h1, ffn_norm); a = SwiGLU(Wg n2, Wu n2); h2 = h1 + Wd a.
- * h: [dim] fp32, in/out (h2 on return).  k_cache, v_cache: [nkv][max_ctx][128] fp16 bits.
+ * h: [dim] fp32, in/out (h2 on return).  k_cache, v_cache: the KV cache layout above.
  * ws: nt_decode_layer_ws_bytes() bytes, 256-byte aligned; no initial contents are required.
  * After the call ws holds, as fp32 arrays
  * at these byte offsets (see nt_decode_layer_ws_offsets): the rotated query q [nq*hd],
@@ -179,7 +188,7 @@ typedef struct {
 typedef struct {
   const void* blob;     /* device pointer if resident, else page-locked HOST pointer */
   int resident;         /* 1: run in place; 0: stream through a staging buffer */
-  uint16_t* k_cache;    /* device, [nkv][max_ctx][128] fp16 */
+  uint16_t* k_cache;    /* device, fp16, the KV cache layout above */
   uint16_t* v_cache;
 } nt_layer_entry;
 
@@ -239,7 +248,10 @@ size_t nt_decode_token_ws_bytes(const nt_layer_shape* shp);
 /* ------------------------------------------------------- measurement hook */
 
 /* Kernel classes that can be timed with HIP events recorded around each launch
- * on the launching stream (adds small gaps; for measurement runs only). */
+ * on the launching stream (adds small gaps; for measurement runs only).  The first
+ * five are the launches of a decode layer, NT_K_LM_HEAD the LM head of
+ * nt_decode_token / nt_model_head; NT_K_ATTN also covers nt_attn_decode and
+ * NT_K_GEMV covers nt_gemv_q. */
 enum { NT_K_ATTN_IN = 0, NT_K_ATTN, NT_K_O, NT_K_FFN_UP, NT_K_FFN_DOWN, NT_K_LM_HEAD, NT_K_GEMV, NT_K_COUNT };
 /* Start timing launches of kernel class kclass (one class at a time); up to
  * max_launches launches are recorded.  Creates events on the current device. */

@@ -17,7 +17,8 @@ Q8_0, Q4_0, Q4_K, Q6_K = 0, 1, 2, 3
 NT_OK, NT_EINVAL, NT_EFORMAT, NT_ESHAPE, NT_EALIGN, NT_EHOSTMEM, NT_EHIP = 0, -1, -2, -3, -4, -5, -6
 W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN, W_COUNT = range(8)
 K_ATTN_IN, K_ATTN, K_O, K_FFN_UP, K_FFN_DOWN, K_LM_HEAD, K_GEMV = range(7)
-GEMV_MAX_COLS = 32768
+GEMV_MAX_COLS = NT_GEMV_MAX_COLS = 32768
+NT_MAX_CTX = 524288  # cache capacity limit (slots); KV cache max_ctx must also be a multiple of 8
 
 
 class NtError(RuntimeError):

@@ -104,7 +104,8 @@ int check_shape(const nt_layer_shape* s) {
   if (nq % 256 || nq > NT_GEMV_MAX_COLS) return fail(NT_ESHAPE, "n_q_heads*head_dim must be a multiple of 256 up to %d", NT_GEMV_MAX_COLS);
   if (s->ffn_dim <= 0 || s->ffn_dim % 256 || s->ffn_dim > NT_GEMV_MAX_COLS)
     return fail(NT_ESHAPE, "ffn_dim must be a positive multiple of 256 up to %d (got %d)", NT_GEMV_MAX_COLS, s->ffn_dim);
-  if (s->max_ctx <= 0) return fail(NT_ESHAPE, "max_ctx must be positive");
+  if (s->max_ctx <= 0 || s->max_ctx % 8 || s->max_ctx > ATTN_MAX_CTX)
+    return fail(NT_ESHAPE, "max_ctx must be a positive multiple of 8 up to %d (got %d)", ATTN_MAX_CTX, s->max_ctx);
   if (!(s->eps >= 0.f)) return fail(NT_EINVAL, "eps must be >= 0");
   if (!(s->rope_theta > 0.f)) return fail(NT_EINVAL, "rope_theta must be > 0");
   return NT_OK;
@@ -169,8 +170,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     a.q = wq; a.k_cache = kc; a.v_cache = vc; a.out = wo;
     a.part = reinterpret_cast<float*>(ws + L.part);
     a.n_kv = s.n_kv_heads; a.n_ctx = pos + 1; a.max_ctx = s.max_ctx;
-    a.slots_per_wave = attn_slots_per_wave(a.n_ctx, a.n_kv);
-    a.n_split = attn_n_split(a.n_ctx, a.slots_per_wave);
+    a.n_split = attn_n_split(a.n_ctx);
     TimedLaunch tl(NT_K_ATTN, st);
     if ((e = attn_launch(a, s.n_q_heads / s.n_kv_heads, st)) != hipSuccess) return hip_fail(e, "attention launch");
   }
@@ -322,6 +322,8 @@ int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int m
   if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads) return fail(NT_ESHAPE, "n_q_heads must be a multiple of n_kv_heads");
   const int grp = n_q_heads / n_kv_heads;
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8 && grp != 16) return fail(NT_ESHAPE, "group size must be 1, 2, 4, 8 or 16");
+  if (max_ctx <= 0 || max_ctx % 8 || max_ctx > ATTN_MAX_CTX)
+    return fail(NT_ESHAPE, "max_ctx must be a positive multiple of 8 up to %d (got %d)", ATTN_MAX_CTX, max_ctx);
   if (n_ctx < 1 || n_ctx > max_ctx) return fail(NT_ESHAPE, "need 1 <= n_ctx <= max_ctx");
   if (!q || !k_cache || !v_cache || !out || !ws) return fail(NT_EINVAL, "null pointer");
   if (!aligned(ws, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(q, 16))
@@ -331,9 +333,12 @@ int nt_attn_decode(int n_q_heads, int n_kv_heads, int head_dim, int n_ctx, int m
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.out = out;
   a.part = reinterpret_cast<float*>(ws);
   a.n_kv = n_kv_heads; a.n_ctx = n_ctx; a.max_ctx = max_ctx;
-  a.slots_per_wave = attn_slots_per_wave(n_ctx, n_kv_heads);
-  a.n_split = attn_n_split(n_ctx, a.slots_per_wave);
-  hipError_t e = attn_launch(a, grp, (hipStream_t)stream);
+  a.n_split = attn_n_split(n_ctx);
+  hipError_t e;
+  {
+    TimedLaunch tl(NT_K_ATTN, (hipStream_t)stream);
+    e = attn_launch(a, grp, (hipStream_t)stream);
+  }
   return e == hipSuccess ? NT_OK : hip_fail(e, "attention launch");
 }
 

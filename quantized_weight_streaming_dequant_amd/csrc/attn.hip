@@ -1,236 +1,328 @@
-// GQA decode attention over an fp16 KV cache, one new token, gfx950.
+// GQA decode attention over an fp16 KV cache, one new token, gfx950 (MFMA).
 //
 // The pages' layer has GQA attention over a KV cache kept in fp16 (ntransformer
 // overview, de.news.hada.io, "Hauptfunktionen" and "Roadmap der
 // Entwicklungsphasen"), with a softmax kernel ("Architektur und Codestruktur").
-// With only 8 KV heads, one workgroup per head would leave most of the chip idle, so
-// the cache is split along the sequence: workgroup (split, kv head) handles a run of
-// 4*cw slots for all query heads of the group (each K and V row is read once per
-// group), each of its four waves cw of them.  The kernel is bound by load latency, so
-// every lane issues all of its K and V loads before it computes anything:
-//  * scores: 64/cw lanes per slot, each over its share of the 128 dimensions (K rows
-//    read as contiguous 16-byte pieces), combined with lane shuffles;
-//  * max-subtracted exponentials in exp2 units (q is pre-scaled by log2(e)/sqrt(128));
-//  * p V: lane = two of the 128 output dimensions, one 4-byte V load per slot;
-//  * the four waves merge through LDS into one (max, sum, unnormalised output) partial
-//    per head, written to the workspace;
-//  * a second kernel, one workgroup per query head, merges the splits' partials.
+//
+// Both products of one KV head's group are small dense contractions, so they run on
+// the matrix cores (v_mfma_f32_16x16x32_f16) while keeping fp32-level accuracy:
+//  * scores S = K Q^T: K rows are exact fp16.  Each query head's row, pre-scaled by
+//    log2(e)/sqrt(128) and by a power of two that brings its largest entry to
+//    [2^13, 2^14), is split into hi = fp16(x) and lo = fp16(x - hi) (|x - hi - lo| is
+//    about 2^-22 |x|); hi parts fill columns 0-7 of the 16-column operand, lo parts
+//    columns 8-15, and the two columns of a head are summed after the MFMA.
+//  * p V: p (in exp2 units, max-subtracted) is scaled by 2^12 and split the same way
+//    into two fp16 rows per head; V is exact fp16; the rows are summed afterwards.
+// Products of fp16 values are exact in fp32, so the error is the fp32 accumulation
+// plus the ~2^-22 split residue, far inside the 1e-3 budget.
+//
+// Layout: K cache [n_kv][max_ctx][128] (row per slot); V cache in groups of 8 slots,
+// [n_kv][max_ctx/8][128][8], so that one 16-byte load gives a lane the 8 consecutive
+// slots of one dimension that the B operand of p V wants.
+//
+// Work split: workgroup (split, kv head) covers 128 slots, each of its four waves 32.
+// A wave's two 16-slot score tiles map MFMA row r to slot 8(r/4) + 4 tile + r%4, so
+// that the output layout (lane l: rows 4(l/16)..+3, column l%16) leaves each lane
+// the eight consecutive slots 8(l/16)..+7 of its column: exactly its A operand for
+// p V, with no data movement.  The four waves merge through LDS into one (max, sum,
+// unnormalised output) partial per head; a second kernel merges the splits.  With a
+// single split the first kernel writes the normalised output itself.
 #include "attn.h"
 #include "common.h"
 
 namespace nt {
 
-constexpr int HD = 128;
-constexpr int AW = 4;          // waves per workgroup
-constexpr int MAX_SPLIT_FAST = 32;  // splits merged with one round of loads
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int G, int CW>
-__global__ __launch_bounds__(AW * 64) void attn_decode_kernel(const AttnArgs a) {
-  constexpr int LPS = 64 / CW;    // lanes per slot in the score phase
-  constexpr int DPL = HD / LPS;   // dimensions per lane in the score phase
-  __shared__ float4 qs4[G * HD / 4];
-  __shared__ float pe[AW][G][CW];
-  __shared__ float wpart[AW][G][HD + 2];
-  float* qs = reinterpret_cast<float*>(qs4);
+constexpr int HD = 128;
+constexpr int AW = 4;              // waves per workgroup
+constexpr int SW = 32;             // cache slots per wave
+constexpr int SWG = AW * SW;       // cache slots per workgroup (one split)
+constexpr int QPAD = HD + 8;       // halves per staged query row
+constexpr int OPAD = HD + 4;       // floats per staged output row
+constexpr float PSCALE = 4096.f;   // p is split at 2^12 p
+constexpr int CWV = 4;             // waves of the merge kernel
+constexpr int CK = 16;             // splits per merge wave per round of loads
+
+__device__ __forceinline__ h8 as_h8(u32x4 v) { return __builtin_bit_cast(h8, v); }
+
+template <int G>
+__global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a) {
+  constexpr int NB = (G + 7) / 8;  // column blocks of 8 heads (hi and lo columns each)
+  constexpr int HPW = (G + AW - 1) / AW;  // query heads staged per wave
+  __shared__ __attribute__((aligned(16))) _Float16 qx[NB][16][QPAD];
+  __shared__ float qsig[NB * 8];
+  __shared__ float ol[AW][NB][16][OPAD];
+  __shared__ float wml[AW][NB * 8][2];
 
   const int split = blockIdx.x, g = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t0 = split * (AW * CW) + wave * CW;  // first slot of this wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, qd = lane >> 4;
+  const int n_ctx = a.n_ctx;
+  const int t0 = split * SWG + wave * SW;  // first slot of this wave
+  const bool active = t0 < n_ctx;          // wave-uniform
 
-  // ---- issue every global load of this wave first
-  const int slot = lane / LPS, part = lane % LPS;
-  const int t = t0 + slot;
-  const bool live = t < a.n_ctx;
-  u32x4 kv[DPL / 8];
+  // ---- 1. loads: this wave's query heads first (needed first), then its K and V tiles
+  float2 qv[HPW];
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) {  // unconditional (a wave past the group rereads its last head)
+    const int hh = min(wave + AW * k, G - 1);
+    qv[k] = *reinterpret_cast<const float2*>(a.q + (size_t)(g * G + hh) * HD + 2 * lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the cache loads
+  // Unconditional, with slots clamped into [0, n_ctx): a branch here would make the
+  // compiler wait for every load before the query staging below.
+  u32x4 kt[2][4], vt[8];
   {
-    const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.k_cache + ((size_t)g * a.max_ctx + (live ? t : 0)) * HD +
-                                                         part * DPL);
+    const uint16_t* kb = a.k_cache + (size_t)g * a.max_ctx * HD;
 #pragma unroll
-    for (int c = 0; c < DPL / 8; ++c) kv[c] = live ? ld16(kr + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-  }
-  uint32_t vv[CW];
-  {
-    const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v_cache + ((size_t)g * a.max_ctx) * HD + 2 * lane);
+    for (int ta = 0; ta < 2; ++ta) {
+      const int t = min(t0 + 8 * (r >> 2) + 4 * ta + (r & 3), n_ctx - 1);
+      const uint8_t* p = reinterpret_cast<const uint8_t*>(kb + (size_t)t * HD + 8 * qd);
 #pragma unroll
-    for (int j = 0; j < CW; ++j) vv[j] = (t0 + j < a.n_ctx) ? ld4(vb + (size_t)(t0 + j) * HD * 2) : 0u;
-  }
-  // q of the group's heads, scaled so that scores come out in exp2 units
-  const float qscale = 1.4426950408889634f * 0.08838834764831845f;
-  for (int i = threadIdx.x; i < G * HD; i += AW * 64) qs[i] = a.q[(size_t)(g * G) * HD + i] * qscale;
-  __syncthreads();
-
-  // ---- scores over this lane's dimensions, combined across the slot's lanes
-  float s[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) s[h] = 0.f;
-#pragma unroll
-  for (int c = 0; c < DPL / 8; ++c) {
-    const uint32_t w4[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
-    float kf[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kf[2 * j] = h2f(w4[j]);
-      kf[2 * j + 1] = h2f(w4[j] >> 16);
+      for (int j = 0; j < 4; ++j) kt[ta][j] = ld16(p + 64 * j);  // dims 32 j + 8 qd .. +7
     }
+    const int grp = min((t0 >> 3) + qd, (n_ctx - 1) >> 3);
+    const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v_cache + (size_t)g * a.max_ctx * HD +
+                                                         ((size_t)grp * HD + r) * 8);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float4 qa = qs4[(h * HD + part * DPL + 8 * c) / 4];
-      const float4 qb = qs4[(h * HD + part * DPL + 8 * c) / 4 + 1];
-      s[h] += qa.x * kf[0];
-      s[h] += qa.y * kf[1];
-      s[h] += qa.z * kf[2];
-      s[h] += qa.w * kf[3];
-      s[h] += qb.x * kf[4];
-      s[h] += qb.y * kf[5];
-      s[h] += qb.z * kf[6];
-      s[h] += qb.w * kf[7];
-    }
+    for (int j = 0; j < 8; ++j) vt[j] = ld16(vp + 256 * j);  // dimension 16 j + r, slots 8 grp .. +7
   }
-#pragma unroll
-  for (int off = 1; off < LPS; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) s[h] += __shfl_xor(s[h], off, 64);
-  }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- softmax pieces of this wave
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = wave_max(live ? s[h] : -INFINITY);
-    const float e = live ? exp2f(s[h] - m[h]) : 0.f;  // m is -inf only if no slot is live
-    l[h] = wave_sum(part == 0 ? e : 0.f);
-    if (part == 0) pe[wave][h][slot] = e;
+  // ---- 2. stage hi/lo fp16 parts of the scaled queries (columns of absent heads are zero)
+  if (G < 8) {
+    for (int i = threadIdx.x; i < 16 * QPAD; i += AW * 64)
+      if (((i / QPAD) & 7) >= G) qx[0][i / QPAD][i % QPAD] = (_Float16)0.f;
   }
-  __syncthreads();
-
-  // ---- p V: lane = dimensions 2 lane, 2 lane + 1
-  float o0[G], o1[G];
+  if (threadIdx.x < NB * 8 && (int)threadIdx.x >= G) qsig[threadIdx.x] = 1.f;
+  const float qscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
 #pragma unroll
-  for (int h = 0; h < G; ++h) o0[h] = o1[h] = 0.f;
-#pragma unroll
-  for (int j = 0; j < CW; ++j) {
-    const float v0 = h2f(vv[j]), v1 = h2f(vv[j] >> 16);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = pe[wave][h][j];
-      o0[h] += p * v0;
-      o1[h] += p * v1;
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    wpart[wave][h][2 * lane] = o0[h];
-    wpart[wave][h][2 * lane + 1] = o1[h];
-    if (lane == 0) {
-      wpart[wave][h][HD] = m[h];
-      wpart[wave][h][HD + 1] = l[h];
+  for (int k = 0; k < HPW; ++k) {
+    const int hh = wave + AW * k;
+    if (hh < G) {
+      float x0 = qv[k].x * qscale, x1 = qv[k].y * qscale;
+      const float am = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      float sig = 1.f;
+      if (am > 0.f) {
+        int e;
+        (void)frexpf(am, &e);
+        sig = ldexpf(1.f, e - 14);  // am / sig in [2^13, 2^14)
+      }
+      const float inv = 1.f / sig;  // a power of two: exact
+      x0 *= inv;
+      x1 *= inv;
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const int cb = hh >> 3, c = hh & 7;
+      qx[cb][c][2 * lane] = h0;
+      qx[cb][c][2 * lane + 1] = h1;
+      qx[cb][c + 8][2 * lane] = (_Float16)(x0 - (float)h0);
+      qx[cb][c + 8][2 * lane + 1] = (_Float16)(x1 - (float)h1);
+      if (lane == 0) qsig[hh] = sig;
     }
   }
   __syncthreads();
 
-  // ---- merge the four waves: this split's partial, written to the workspace
-  float* part_out = a.part + (((size_t)g * a.n_split + split) * G) * (HD + 2);
-  for (int i = threadIdx.x; i < G * (HD + 2); i += AW * 64) {
-    const int h = i / (HD + 2), d = i % (HD + 2);
+  if (active) {
+    // ---- 3. scores: B operand of lane (column r, quarter qd) for MFMA j = dims 32 j + 8 qd .. +7
+    float s[NB][8];  // s[cb][k]: slot t0 + 8 qd + k, head 8 cb + (r & 7)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      h8 bq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bq[j] = *reinterpret_cast<const h8*>(&qx[cb][r][32 * j + 8 * qd]);
+      const float sig = qsig[cb * 8 + (r & 7)];
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kt[ta][j]), bq[j], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = acc[i];
+          v += dpp_mov<0x128>(v);  // row_ror:8 -> the head's other column (hi + lo)
+          const int t = t0 + 8 * qd + 4 * ta + i;
+          s[cb][4 * ta + i] = (t < n_ctx) ? v * sig : -INFINITY;
+        }
+      }
+    }
+
+    // V entries of slots past n_ctx may hold anything: zero them (0 * NaN would poison)
+    if (t0 + SW > n_ctx) {
+      const int nl = n_ctx - (t0 + 8 * qd);  // live slots of this lane's group of 8
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t w4[4] = {vt[j].x, vt[j].y, vt[j].z, vt[j].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t keep = (2 * c + 1 < nl) ? 0xFFFFFFFFu : (2 * c < nl) ? 0x0000FFFFu : 0u;
+          w4[c] &= keep;
+        }
+        vt[j] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
+
+    // ---- 4. softmax pieces over the wave's 32 slots, then P V
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      float m = s[cb][0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) m = fmaxf(m, s[cb][k]);
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));  // slot 0 of the wave is live: m is finite
+      float l = 0.f;
+      h8 pa;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float p = (s[cb][k] == -INFINITY) ? 0.f : exp2f(s[cb][k] - m);
+        l += p;
+        const float pp = p * PSCALE;
+        const _Float16 hi = (_Float16)pp;
+        pa[k] = (r < 8) ? hi : (_Float16)(pp - (float)hi);
+      }
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      if (qd == 0 && r < 8) {
+        wml[wave][cb * 8 + r][0] = m;
+        wml[wave][cb * 8 + r][1] = l;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f4 o = {0.f, 0.f, 0.f, 0.f};
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, as_h8(vt[j]), o, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ol[wave][cb][4 * qd + i][16 * j + r] = o[i];
+      }
+    }
+  } else if (lane < NB * 8) {
+    wml[wave][lane][0] = -INFINITY;
+    wml[wave][lane][1] = 0.f;
+  }
+  __syncthreads();
+
+  // ---- 5. merge the four waves (rows h and h + 8 of a column block are one head's hi and lo)
+  for (int idx = threadIdx.x; idx < G * HD; idx += AW * 64) {
+    const int h = idx >> 7, d = idx & (HD - 1);
+    const int cb = h >> 3, hr = h & 7;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < AW; ++w) M = fmaxf(M, wpart[w][h][HD]);
-    float v;
-    if (d == HD) {
-      v = M;
-    } else if (M == -INFINITY) {
-      v = 0.f;
+    for (int w = 0; w < AW; ++w) M = fmaxf(M, wml[w][h][0]);
+    float v = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < AW; ++w) {
+      const float mw = wml[w][h][0];
+      if (mw != -INFINITY) {
+        const float f = exp2f(mw - M);
+        v += (ol[w][cb][hr][d] + ol[w][cb][hr + 8][d]) * f;
+        L += wml[w][h][1] * f;
+      }
+    }
+    v *= 1.f / PSCALE;
+    if (a.n_split == 1) {
+      a.out[(size_t)(g * G + h) * HD + d] = v / L;
     } else {
-      v = 0.f;
-#pragma unroll
-      for (int w = 0; w < AW; ++w) {
-        const float mwv = wpart[w][h][HD];
-        if (mwv != -INFINITY) v += wpart[w][h][d] * exp2f(mwv - M);
+      float* po = a.part + (((size_t)g * a.n_split + split) * G + h) * (HD + 2);
+      po[d] = v;
+      if (d == 0) {
+        po[HD] = M;
+        po[HD + 1] = L;
       }
     }
-    part_out[i] = v;
   }
 }
 
-// Merge of the splits' partials: one workgroup per query head, lane = two output
-// dimensions; every partial of the head is loaded in one round per 32 splits.
+// Merge of the splits' partials: one workgroup per query head.  Wave w takes splits
+// w, w + 4, ...; lane = output dimensions 2 lane, 2 lane + 1.  Every split's maximum
+// and sum go through LDS; the output loads of the first 64 splits are issued together
+// with them.
 template <int G>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs a) {
-  __shared__ float ms[MAX_SPLIT_FAST], ls[MAX_SPLIT_FAST];
-  const int hq = blockIdx.x;  // query head
+__global__ __launch_bounds__(CWV * 64) void attn_combine_kernel(const AttnArgs a) {
+  extern __shared__ float cm[];  // [n_split] maxima, then [n_split] sums
+  __shared__ float red[CWV][HD];
+  __shared__ float wred[CWV][2];
+  const int hq = blockIdx.x;
   const int g = hq / G, hg = hq % G;
-  const int lane = threadIdx.x;
-  const int d = 2 * lane;
-  const float* gp = a.part + ((size_t)g * a.n_split * G + hg) * (HD + 2);  // split sp at gp + sp*G*(HD+2)
-  const size_t sstride = (size_t)G * (HD + 2);
-  float runM = -INFINITY, runL = 0.f, r0 = 0.f, r1 = 0.f;
-  for (int base = 0; base < a.n_split; base += MAX_SPLIT_FAST) {
-    const int nb = min(MAX_SPLIT_FAST, a.n_split - base);
-    if (lane < nb) {
-      ms[lane] = gp[(size_t)(base + lane) * sstride + HD];
-      ls[lane] = gp[(size_t)(base + lane) * sstride + HD + 1];
-    }
-    float2 ov[MAX_SPLIT_FAST];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ns = a.n_split;
+  const float* gp = a.part + ((size_t)g * ns * G + hg) * (HD + 2);
+  const size_t ss = (size_t)G * (HD + 2);
+
+  float2 ov[CK];
 #pragma unroll
-    for (int k = 0; k < MAX_SPLIT_FAST; ++k)
-      if (k < nb) ov[k] = *reinterpret_cast<const float2*>(gp + (size_t)(base + k) * sstride + d);
-    __syncthreads();
-    float M = runM;
+  for (int k = 0; k < CK; ++k) {
+    const int sp = wave + CWV * k;
+    if (sp < ns) ov[k] = *reinterpret_cast<const float2*>(gp + sp * ss + 2 * lane);
+  }
+  float mloc = -INFINITY;
+  for (int sp = threadIdx.x; sp < ns; sp += CWV * 64) {
+    const float m = gp[sp * ss + HD];
+    cm[sp] = m;
+    cm[ns + sp] = gp[sp * ss + HD + 1];
+    mloc = fmaxf(mloc, m);
+  }
+  mloc = wave_max(mloc);
+  if (lane == 0) wred[wave][0] = mloc;
+  __syncthreads();
+  float M = wred[0][0];
 #pragma unroll
-    for (int k = 0; k < MAX_SPLIT_FAST; ++k)
-      if (k < nb) M = fmaxf(M, ms[k]);
-    const float f0 = (runM == -INFINITY) ? 0.f : exp2f(runM - M);
-    runL *= f0;
-    r0 *= f0;
-    r1 *= f0;
+  for (int w = 1; w < CWV; ++w) M = fmaxf(M, wred[w][0]);
+  float lloc = 0.f;
+  for (int sp = threadIdx.x; sp < ns; sp += CWV * 64) lloc += cm[ns + sp] * exp2f(cm[sp] - M);
+  lloc = wave_sum(lloc);
+  if (lane == 0) wred[wave][1] = lloc;
+
+  float o0 = 0.f, o1 = 0.f;
+  for (int base = 0;; base += CWV * CK) {
 #pragma unroll
-    for (int k = 0; k < MAX_SPLIT_FAST; ++k) {
-      if (k < nb && ms[k] != -INFINITY) {
-        const float f = exp2f(ms[k] - M);
-        runL += ls[k] * f;
-        r0 += ov[k].x * f;
-        r1 += ov[k].y * f;
+    for (int k = 0; k < CK; ++k) {
+      const int sp = base + wave + CWV * k;
+      if (sp < ns) {
+        const float f = exp2f(cm[sp] - M);
+        o0 += ov[k].x * f;
+        o1 += ov[k].y * f;
       }
     }
-    runM = M;
-    __syncthreads();  // ms/ls are rewritten by the next chunk
+    if (base + CWV * CK >= ns) break;
+#pragma unroll
+    for (int k = 0; k < CK; ++k) {
+      const int sp = base + CWV * CK + wave + CWV * k;
+      if (sp < ns) ov[k] = *reinterpret_cast<const float2*>(gp + sp * ss + 2 * lane);
+    }
   }
-  const float inv = 1.0f / runL;
-  *reinterpret_cast<float2*>(a.out + (size_t)hq * HD + d) = make_float2(r0 * inv, r1 * inv);
+  red[wave][2 * lane] = o0;
+  red[wave][2 * lane + 1] = o1;
+  __syncthreads();
+  if (threadIdx.x < HD) {
+    float L = 0.f, v = 0.f;
+#pragma unroll
+    for (int w = 0; w < CWV; ++w) {
+      L += wred[w][1];
+      v += red[w][threadIdx.x];
+    }
+    a.out[(size_t)hq * HD + threadIdx.x] = v / L;
+  }
 }
 
-int attn_slots_per_wave(int n_ctx, int n_kv) {
-  (void)n_kv;
-  // the smallest run per wave that keeps the merge within two rounds of loads
-  for (int cw = 16; cw < 64; cw *= 2)
-    if ((n_ctx + AW * cw - 1) / (AW * cw) <= 2 * MAX_SPLIT_FAST) return cw;
-  return 64;
-}
+int attn_n_split(int n_ctx) { return (n_ctx + SWG - 1) / SWG; }
 
-int attn_n_split(int n_ctx, int slots_per_wave) { return (n_ctx + AW * slots_per_wave - 1) / (AW * slots_per_wave); }
+static int attn_max_split() { return ATTN_MAX_CTX / SWG; }
 
 size_t attn_part_floats(int n_q, int max_ctx) {
-  const int max_split = (max_ctx + AW * 16 - 1) / (AW * 16);
-  return (size_t)max_split * (size_t)n_q * (HD + 2);
+  return (size_t)attn_n_split(max_ctx) * (size_t)n_q * (HD + 2);
 }
 
 template <int G>
 static hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_split, a.n_kv), block(AW * 64);
-  switch (a.slots_per_wave) {
-    case 16: hipLaunchKernelGGL((attn_decode_kernel<G, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attn_decode_kernel<G, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attn_decode_kernel<G, 64>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(attn_partial_kernel<G>, dim3(a.n_split, a.n_kv), dim3(AW * 64), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3(a.n_kv * G), dim3(64), 0, s, a);
+  if (e != hipSuccess || a.n_split == 1) return e;
+  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3(a.n_kv * G), dim3(CWV * 64), 2 * sizeof(float) * a.n_split, s, a);
   return hipGetLastError();
 }
 
 hipError_t attn_launch(const AttnArgs& a, int group, hipStream_t s) {
+  if (a.n_split != attn_n_split(a.n_ctx) || a.n_split > attn_max_split() || a.max_ctx % 8) return hipErrorInvalidValue;
   switch (group) {
     case 1: return launch_g<1>(a, s);
     case 2: return launch_g<2>(a, s);

@@ -42,14 +42,15 @@ __device__ __forceinline__ float hi_h(uint32_t v) { return __half2float(__ushort
 
 // Weight loads.  Nontemporal loads were measured slower on every GEMV shape here (by
 // 10-30%), so plain cached loads are the default.
-template <typename T>
-__device__ __forceinline__ T wload(const T* p) {
-  if constexpr (NT_GEMV_NONTEMPORAL) return __builtin_nontemporal_load(p);
-  else return *p;
-}
-__device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return wload(reinterpret_cast<const u32x4*>(p)); }
-__device__ __forceinline__ uint32_t wld4(const uint8_t* p) { return wload(reinterpret_cast<const uint32_t*>(p)); }
-__device__ __forceinline__ uint32_t wld2(const uint8_t* p) { return (uint32_t)wload(reinterpret_cast<const uint16_t*>(p)); }
+#if NT_GEMV_NONTEMPORAL
+__device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+__device__ __forceinline__ uint32_t wld4(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
+__device__ __forceinline__ uint32_t wld2(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)); }
+#else
+__device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return ld16(p); }
+__device__ __forceinline__ uint32_t wld4(const uint8_t* p) { return ld4(p); }
+__device__ __forceinline__ uint32_t wld2(const uint8_t* p) { return ld2(p); }
+#endif
 
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -580,9 +581,10 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int s, const GemvSeg
             kp[1] = f2h_rne(r1);
           }
         } else {
-          uint16_t* vp = a.v_cache + ((size_t)head * a.max_ctx + a.pos) * HD + dd;
+          // V cache groups of 8 slots: [head][slot / 8][dim][slot % 8]
+          uint16_t* vp = a.v_cache + (size_t)head * a.max_ctx * HD + ((size_t)(a.pos >> 3) * HD + dd) * 8 + (a.pos & 7);
           vp[0] = f2h_rne(y0);
-          vp[1] = f2h_rne(y1);
+          vp[8] = f2h_rne(y1);
         }
       }
     }

@@ -50,3 +50,16 @@ def same_value(a, b) -> bool:
     a = np.asarray(a)
     b = np.asarray(b)
     return a.shape == b.shape and bool(np.all(a == b))
+
+
+def v_to_device(vc, n_kv: int, max_ctx: int, hd: int = 128) -> np.ndarray:
+    """[n_kv][max_ctx][hd] V cache -> the library's layout [n_kv][max_ctx/8][hd][8]
+    (groups of 8 slots, slot-minor)."""
+    a = np.asarray(vc).reshape(n_kv, max_ctx // 8, 8, hd)
+    return np.ascontiguousarray(a.transpose(0, 1, 3, 2))
+
+
+def v_from_device(vt, n_kv: int, max_ctx: int, hd: int = 128) -> np.ndarray:
+    """Inverse of v_to_device."""
+    a = np.asarray(vt).reshape(n_kv, max_ctx // 8, hd, 8)
+    return np.ascontiguousarray(a.transpose(0, 1, 3, 2)).reshape(n_kv, max_ctx, hd)

@@ -57,6 +57,8 @@ def test_block_geometry():
     (lambda: nt.nt_attn_decode(64, 8, 128, 16, 16, 16, 16, 16, 16, 128, 1 << 20), nt.NT_EALIGN),
     (lambda: nt.nt_attn_decode(60, 8, 128, 16, 16, 16, 16, 16, 16, 256, 1 << 20), nt.NT_ESHAPE),
     (lambda: nt.nt_attn_decode(64, 8, 128, 16, 16, 16, 16, 16, 16, 256, 8), nt.NT_EINVAL),
+    (lambda: nt.nt_attn_decode(64, 8, 128, 16, 20, 16, 16, 16, 16, 256, 1 << 20), nt.NT_ESHAPE),  # max_ctx % 8
+    (lambda: nt.nt_attn_decode(64, 8, 128, 16, 2 * nt.NT_MAX_CTX, 16, 16, 16, 16, 256, 1 << 30), nt.NT_ESHAPE),
     (lambda: nt.nt_swiglu(0, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_rmsnorm(100, None, 16, 1e-5, 16), nt.NT_EINVAL),
     (lambda: nt.nt_argmax(0, 16, 16), nt.NT_ESHAPE),
@@ -97,6 +99,8 @@ def _weights(fmt=nt.Q8_0, ptr=4096):
     (dict(dim=4000), None, 0, nt.NT_ESHAPE),
     (dict(ffn_dim=40960), None, 0, nt.NT_ESHAPE),
     ({}, None, 1024, nt.NT_ESHAPE),
+    (dict(max_ctx=1020), None, 0, nt.NT_ESHAPE),
+    (dict(max_ctx=2 * nt.NT_MAX_CTX), None, 0, nt.NT_ESHAPE),
     ({}, None, -1, nt.NT_ESHAPE),
     ({}, "badfmt", 0, nt.NT_EFORMAT),
     ({}, "mixed_ffn", 0, nt.NT_EFORMAT),
@@ -134,3 +138,11 @@ def test_layer_workspace_too_small():
     with pytest.raises(nt.NtError) as ei:
         nt.nt_decode_layer(_weights(), _shape(), 5, 4096, 4096, 4096, 4096, 1024)
     assert ei.value.code == nt.NT_EINVAL
+
+
+def test_header_constants_match_binding():
+    import re
+    text = open(HEADER).read()
+    for name in ("NT_MAX_CTX", "NT_GEMV_MAX_COLS"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(nt, name), name

@@ -20,7 +20,7 @@ import quantized_weight_streaming_dequant_amd as nt
 import synth
 from quantized_weight_streaming_dequant_amd import torch_glue as tg
 from synth import recipes
-from tests.gpu_util import check_rel, dev, host, same_value, say, stream
+from tests.gpu_util import check_rel, dev, host, same_value, say, stream, v_from_device, v_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ class DeviceLayer:
         self.kc_host = recipes.kv_cache_array(shape, layer, "k", n_slots, seed)
         self.vc_host = recipes.kv_cache_array(shape, layer, "v", n_slots, seed)
         self.kc = dev(self.kc_host)
-        self.vc = dev(self.vc_host)
+        self.vc = dev(v_to_device(self.vc_host, shape.n_kv_heads, shape.max_ctx))
 
     def weights(self):
         return tg.layer_weights([self.mix[n] for n in recipes.TENSORS], [self.dev[n] for n in recipes.TENSORS],
@@ -61,7 +61,7 @@ def run_layer_and_check(shape, mix, pos, n_slots, layer=0, sample_rows=None):
 
     g_q, g_o, g_h1, g_a = wsf("q", nq), wsf("o", nq), wsf("h1", shape.dim), wsf("a", shape.ffn_dim)
     g_h2 = host(h)
-    kc, vc = host(L.kc), host(L.vc)
+    kc, vc = host(L.kc), v_from_device(host(L.vc), shape.n_kv_heads, shape.max_ctx)
     g_k16, g_v16 = kc[:, pos, :].ravel(), vc[:, pos, :].ravel()
     # untouched cache slots stay as they were
     keep = np.ones(shape.max_ctx, bool)
@@ -144,7 +144,8 @@ class Model:
         self.embd_d, self.out_d, self.onorm_d = dev(self.embd), dev(self.out), dev(self.onorm)
 
     def caches(self):
-        return [dev(k) for k in self.kc0], [dev(v) for v in self.vc0]
+        return ([dev(k) for k in self.kc0],
+                [dev(v_to_device(v, self.shape.n_kv_heads, self.shape.max_ctx)) for v in self.vc0])
 
     def plan(self, kcs, vcs, streamed=None):
         streamed = self.streamed if streamed is None else streamed

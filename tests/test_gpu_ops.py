@@ -15,7 +15,7 @@ import quantized_weight_streaming_dequant_amd as nt
 import synth
 from synth import recipes
 from tests.blockpack import pack_q4_0, pack_q4_k, pack_q6_k, pack_q8_0
-from tests.gpu_util import check_rel, dev, host, same_value, say, stream
+from tests.gpu_util import v_to_device, check_rel, dev, host, same_value, say, stream
 
 pytestmark = pytest.mark.gpu
 
@@ -174,8 +174,25 @@ def test_swiglu():
 
 ATTN_CASES = [  # n_q, n_kv, n_ctx, max_ctx, q scale
     (32, 8, 1024, 1024, 1.0), (32, 8, 1024, 1024, 8.0), (64, 8, 4097, 4224, 1.0), (64, 8, 4224, 4224, 6.0),
-    (64, 8, 1, 4224, 1.0), (64, 8, 65, 128, 1.0), (8, 8, 300, 512, 1.0), (16, 8, 77, 96, 2.0), (16, 1, 333, 400, 1.0),
+    (64, 8, 1, 4224, 1.0), (64, 8, 65, 128, 1.0), (64, 8, 128, 128, 1.0), (64, 8, 129, 136, 1.0),
+    (8, 8, 300, 512, 1.0), (16, 8, 77, 96, 2.0), (16, 1, 333, 400, 1.0), (128, 8, 1000, 1024, 1.0),
+    (64, 8, 16384, 16384, 1.0), (64, 8, 9001, 16384, 1e-6), (64, 8, 2049, 2560, 30.0),
 ]
+
+
+def run_attention(n_q, n_kv, n_ctx, max_ctx, q, kc, vc, reps=2):
+    hd = 128
+    qd, kd = dev(q), dev(kc)
+    vd = dev(v_to_device(vc, n_kv, max_ctx))
+    out = torch.empty(n_q * hd, dtype=torch.float32, device="cuda")
+    wsb = nt.nt_attn_decode_ws_bytes(n_q, n_kv, hd, max_ctx)
+    ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device="cuda")  # no initial contents are needed
+    res = []
+    for rep in range(reps):
+        nt.nt_attn_decode(n_q, n_kv, hd, n_ctx, max_ctx, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(),
+                          ws.data_ptr(), wsb, stream())
+        res.append(host(out).copy())
+    return res
 
 
 @pytest.mark.parametrize("n_q,n_kv,n_ctx,max_ctx,qs", ATTN_CASES)
@@ -185,15 +202,51 @@ def test_attention(n_q, n_kv, n_ctx, max_ctx, qs):
     q = synth.normal_f32(n_q * hd, 0, 18) * qs
     kc = synth.normal_f16_bits(n_kv * max_ctx * hd, 0, 19)
     vc = synth.normal_f16_bits(n_kv * max_ctx * hd, 0, 20)
-    qd, kd, vd = dev(q), dev(kc), dev(vc)
-    out = torch.empty(n_q * hd, dtype=torch.float32, device="cuda")
-    wsb = nt.nt_attn_decode_ws_bytes(n_q, n_kv, hd, max_ctx)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
-    for rep in range(2):  # the second call checks that the counters were left at zero
-        nt.nt_attn_decode(n_q, n_kv, hd, n_ctx, max_ctx, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(),
-                          ws.data_ptr(), wsb, stream())
-        ref, nrm = oracle.attn(q, kc, vc, n_q, n_kv, hd, n_ctx, max_ctx)
-        check_rel(host(out), ref, nrm, what=f"attention rep {rep}")
+    ref, nrm = oracle.attn(q, kc, vc, n_q, n_kv, hd, n_ctx, max_ctx)
+    outs = run_attention(n_q, n_kv, n_ctx, max_ctx, q, kc, vc)
+    for rep, got in enumerate(outs):
+        check_rel(got, ref, nrm, what=f"attention rep {rep}")
+    assert same_value(outs[0], outs[1])  # no state carried between calls
+
+
+@pytest.mark.parametrize("n_ctx", [1, 37, 131, 1000])
+def test_attention_ignores_slots_past_n_ctx(n_ctx):
+    """Slots at or past n_ctx may hold any bits (here NaN and inf) without affecting the result."""
+    n_q, n_kv, max_ctx, hd = 64, 8, 1024, 128
+    say(f"attention with NaN/inf past n_ctx={n_ctx}")
+    q = synth.normal_f32(n_q * hd, 0, 22)
+    kc = synth.normal_f16_bits(n_kv * max_ctx * hd, 0, 23).reshape(n_kv, max_ctx, hd)
+    vc = synth.normal_f16_bits(n_kv * max_ctx * hd, 0, 24).reshape(n_kv, max_ctx, hd)
+    kc[:, n_ctx:, 0::2] = 0x7E00  # NaN
+    kc[:, n_ctx:, 1::2] = 0x7C00  # +inf
+    vc[:, n_ctx:, 0::2] = 0xFC00  # -inf
+    vc[:, n_ctx:, 1::2] = 0x7E00
+    ref, nrm = oracle.attn(q, kc.ravel(), vc.ravel(), n_q, n_kv, hd, n_ctx, max_ctx)
+    (got,) = run_attention(n_q, n_kv, n_ctx, max_ctx, q, kc.ravel(), vc.ravel(), reps=1)
+    check_rel(got, ref, nrm, what="attention")
+
+
+def test_attention_one_hot_is_exact_value_row():
+    """A query that selects one slot by a huge margin returns that slot's V row (fp16 values,
+    exactly representable): the split merge and the hi/lo products must not disturb it."""
+    n_q, n_kv, max_ctx, n_ctx, hd = 16, 2, 1024, 700, 128
+    say("attention one-hot")
+    kc = np.zeros((n_kv, max_ctx, hd), np.uint16)
+    vc = synth.normal_f16_bits(n_kv * max_ctx * hd, 0, 25).reshape(n_kv, max_ctx, hd)
+    pick = [5, 311, 698, 0, 130, 129, 127, 640]  # slot per query head of group 0; group 1 mirrors it
+    kc[:, :, :] = np.float16(0.0).view(np.uint16)
+    q = np.zeros((n_q, hd), np.float32)
+    for h in range(n_q):
+        g = h // (n_q // n_kv)
+        t = pick[h % 8]
+        kc[g, t, h % 8] = np.float16(1.0).view(np.uint16)
+        q[h, h % 8] = 4000.0  # score 4000/sqrt(128) ~ 354 above every other slot
+    outs = run_attention(n_q, n_kv, n_ctx, max_ctx, q.ravel(), kc.ravel(), vc.ravel(), reps=1)
+    got = outs[0].reshape(n_q, hd)
+    vf = vc.view(np.float16).astype(np.float32)
+    for h in range(n_q):
+        g = h // (n_q // n_kv)
+        assert np.array_equal(got[h], vf[g, pick[h % 8]]), h
 
 
 # ------------------------------------------------------------------ token glue
