@@ -39,6 +39,9 @@ __device__ __forceinline__ float hi_h(uint32_t v) { return __half2float(__ushort
 #ifndef NT_GEMV_NONTEMPORAL
 #define NT_GEMV_NONTEMPORAL 0
 #endif
+#ifndef NT_GEMV_STREAM
+#define NT_GEMV_STREAM 1  // the streamed (global->LDS) path wherever the shape allows it
+#endif
 
 // Weight loads.  Nontemporal loads were measured slower on every GEMV shape here (by
 // 10-30%), so plain cached loads are the default.
@@ -716,6 +719,467 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   }
 }
 
+
+// ================================================================== streamed GEMV
+//
+// Column-stationary layout for shapes whose rows are 16-byte aligned.  A workgroup owns a
+// contiguous range of row tasks; its waves split the columns into slices (4096 columns
+// for the 256-weight superblock formats, 2048 for the 32-weight block formats) and, when
+// a slice leaves waves over, split the tasks among them.  Each wave
+//  * holds its slice of x in registers (64 or 32 floats per lane, loaded once), so x is
+//    neither staged in LDS nor re-read per weight;
+//  * streams the slice bytes of its rows from HBM into its own LDS ring with 16-byte
+//    global->LDS transfers (global_load_lds_dwordx4): every transfer instruction reads
+//    1 KiB of consecutive bytes, and D rows are in flight without costing registers;
+//  * reads each row's pieces from LDS in the lane layout its format wants (unaligned
+//    fields realigned with v_alignbyte), forms the lane's partial dot product and
+//    reduces it over the wave; the slices of a row meet in LDS at the end.
+// Lane layouts: superblock formats, lane = quarter g of superblock s (s = lane / 4):
+// columns 256 s + 64 g .. + 63 of the slice; block formats, lane = block: 32 columns.
+
+constexpr int ST_SLICE_COLS_K = 4096;
+constexpr int ST_SLICE_COLS_B = 2048;
+constexpr int ST_MAX_WAVES = 16;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+typedef uint32_t u32x4a16 __attribute__((ext_vector_type(4), aligned(16)));
+__device__ __forceinline__ u32x4 lds16a(const uint8_t* p) {
+  const u32x4a16 v = *reinterpret_cast<const u32x4a16*>(p);
+  return u32x4{v.x, v.y, v.z, v.w};
+}
+// o[k] = the 4 bytes at p + 4k, where p sits `phase` (0 or 2) bytes past a 4-byte boundary
+template <int N>
+__device__ __forceinline__ void lds_run(const uint8_t* p, uint32_t phase, uint32_t (&o)[N]) {
+  const uint8_t* a = p - phase;
+  uint32_t w[N + 1];
+#pragma unroll
+  for (int k = 0; k <= N; ++k) w[k] = lds4(a + 4 * k);
+#pragma unroll
+  for (int k = 0; k < N; ++k) o[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], phase);
+}
+
+// Q4_K lane part: quarter g of superblock s: nibble bytes 32g..32g+31 at 16 + 32g; low
+// nibbles are sub-block 2g (x[0..31]), high nibbles sub-block 2g+1 (x[32..63]).
+struct Q4K_S {
+  static constexpr int FMT = FMT_Q4_K, BB = 144, K = 1;
+  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[64], const float (&xs)[4]) {
+    const int s = lane >> 2, g = lane & 3;
+    const uint8_t* p = slot + s * 144;
+    const u32x4 hd = lds16a(p);
+    const u32x4 qa = lds16a(p + 16 + 32 * g), qb = lds16a(p + 32 + 32 * g);
+    const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    const uint32_t mlo = vreg(NIB_LO), mhi = vreg(NIB_HI), m1024 = vreg(F16_1024);
+    float slo0 = 0.f, slo1 = 0.f, shi0 = 0.f, shi1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v = q[i], u = v >> 8;
+      const uint32_t p0 = and_or(v, mlo, m1024), p1 = and_or(v, mhi, m1024);
+      const uint32_t p2 = and_or(u, mlo, m1024), p3 = and_or(u, mhi, m1024);
+      slo0 += lo_h(p0) * x[4 * i];
+      slo1 += lo_h(p2) * x[4 * i + 1];
+      slo0 += hi_h(p0) * x[4 * i + 2];
+      slo1 += hi_h(p2) * x[4 * i + 3];
+      shi0 += lo_h(p1) * x[32 + 4 * i];
+      shi1 += lo_h(p3) * x[33 + 4 * i];
+      shi0 += hi_h(p1) * x[34 + 4 * i];
+      shi1 += hi_h(p3) * x[35 + 4 * i];
+    }
+    // scale and min of sub-blocks 2g, 2g+1 (field positions as in the register path)
+    const bool upper = g >= 2;
+    const uint32_t o = 16u * (uint32_t)(g & 1);
+    const uint32_t wl = upper ? 4u : 6u, wh = upper ? 2u : 0u, om = upper ? o + 4u : o;
+    const uint32_t Y = hd.y, Z = hd.z, W = hd.w;
+    const uint32_t srcS = upper ? W : Y, srcM = upper ? W : Z;
+    const uint32_t sca = __builtin_amdgcn_ubfe(srcS, o, wl) | (__builtin_amdgcn_ubfe(Y, o + 6u, wh) << 4);
+    const uint32_t scb = __builtin_amdgcn_ubfe(srcS, o + 8u, wl) | (__builtin_amdgcn_ubfe(Y, o + 14u, wh) << 4);
+    const uint32_t ma = __builtin_amdgcn_ubfe(srcM, om, wl) | (__builtin_amdgcn_ubfe(Z, o + 6u, wh) << 4);
+    const uint32_t mb = __builtin_amdgcn_ubfe(srcM, om + 8u, wl) | (__builtin_amdgcn_ubfe(Z, o + 14u, wh) << 4);
+    const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
+    const float xa = xs[0] + xs[1], xb = xs[2] + xs[3];
+    const float A = (slo0 + slo1) - 1024.f * xa;  // sum q x over sub-block 2g
+    const float B = (shi0 + shi1) - 1024.f * xb;  // 16 sum q x over sub-block 2g+1
+    float r = (d * (float)sca) * A;
+    r += (d * 0.0625f * (float)scb) * B;
+    r -= dmin * ((float)ma * xa + (float)mb * xb);
+    return r;
+  }
+};
+
+// Q6_K lane part: quarter g = 2n + hi of superblock s: columns 128n + 64hi + l (l < 64).
+// Column 128n + 64hi + l for l < 32 takes the low (hi = 0) or high (hi = 1) nibble of
+// low-bit byte 64n + l and bits 4hi..4hi+1 of high-bit byte 32n + l; for l >= 32 the
+// nibble of byte 64n + l and bits 4hi+2..4hi+3 of high-bit byte 32n + l - 32.  Scale of
+// columns 16j.. of the quarter: int8 at 192 + 8n + 4hi + j (j = 0..3); w = d s (q - 32).
+// The 6-bit code goes into an fp16 1024 + m q, m = 1 (hi = 0: nibble at bits 0..3, top
+// bits at 4..5) or m = 16 (hi = 1: nibble left at bits 4..7, top bits moved to 8..9), so
+// neither half needs a nibble shift.  A superblock at an odd index sits 2 bytes past a
+// 4-byte boundary in the ring; its fields are realigned per lane.
+struct Q6K_S {
+  static constexpr int FMT = FMT_Q6_K, BB = 210, K = 1;
+  static __device__ __forceinline__ uint32_t keep(uint32_t v) {  // stop the and-or pairs from being refactored
+    asm("" : "+v"(v));
+    return v;
+  }
+  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[64], const float (&xs)[4]) {
+    const int s = lane >> 2, g = lane & 3, n = g >> 1, hi = g & 1;
+    const uint8_t* p = slot + s * 210;
+    const uint32_t ph = (uint32_t)(s & 1) * 2u;
+    uint32_t H[8], S[1], D[1];
+    lds_run<8>(p + 128 + 32 * n, ph, H);
+    lds_run<1>(p + 192 + 8 * n + 4 * hi, ph, S);
+    lds_run<1>(p + 208, ph, D);
+    const uint32_t mnib = vreg(hi ? 0x00F000F0u : 0x000F000Fu);
+    const uint32_t mh = vreg(hi ? 0x03000300u : 0x00300030u);
+    const uint32_t m1024 = vreg(F16_1024);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // per 16 columns: sum (1024 + m q) x
+    // two halves of 32 columns: low-bit bytes 64n + 32 half + l, top bits of high-bit byte
+    // 32n + l at 4hi + 2 half
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t L[8];
+      lds_run<8>(p + 64 * n + 32 * half, ph, L);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t la = L[k], h = H[k];
+        const uint32_t a02 = and_or(half ? h << 2 : h << 4, mh, keep(and_or(la, mnib, m1024)));
+        const uint32_t a13 = and_or(half ? h >> 6 : h >> 4, mh, keep(and_or(la >> 8, mnib, m1024)));
+        float& ca = acc[2 * half + (k >> 2)];
+        ca += lo_h(a02) * x[32 * half + 4 * k];
+        ca += lo_h(a13) * x[32 * half + 4 * k + 1];
+        ca += hi_h(a02) * x[32 * half + 4 * k + 2];
+        ca += hi_h(a13) * x[32 * half + 4 * k + 3];
+      }
+    }
+    // sum (q - 32) x over group j = (acc_j - 1024 X_j) / m - 32 X_j
+    const float im = hi ? 0.0625f : 1.f;
+    const float d = h2f(D[0]);
+    float r = 0.f;
+    r += (float)(int8_t)(S[0] & 0xFFu) * ((acc[0] - 1024.f * xs[0]) * im - 32.f * xs[0]);
+    r += (float)(int8_t)((S[0] >> 8) & 0xFFu) * ((acc[1] - 1024.f * xs[1]) * im - 32.f * xs[1]);
+    r += (float)(int8_t)((S[0] >> 16) & 0xFFu) * ((acc[2] - 1024.f * xs[2]) * im - 32.f * xs[2]);
+    r += (float)(int8_t)(S[0] >> 24) * ((acc[3] - 1024.f * xs[3]) * im - 32.f * xs[3]);
+    return d * r;
+  }
+};
+
+// Q8_0 lane part: block l: fp16 d, then 32 int8 q; w = d q.
+struct Q80_S {
+  static constexpr int FMT = FMT_Q8_0, BB = 34, K = 0;
+  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[32], const float (&xs)[2]) {
+    (void)xs;
+    const uint8_t* p = slot + lane * 34;
+    const uint32_t pd = (uint32_t)(lane & 1) * 2u;  // 34 lane mod 4
+    uint32_t Q[8], D[1];
+    lds_run<8>(p + 2, 2u - pd, Q);
+    lds_run<1>(p, pd, D);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t v = Q[k];
+      a0 += sb0(v) * x[4 * k];
+      a1 += sb1(v) * x[4 * k + 1];
+      a0 += sb2(v) * x[4 * k + 2];
+      a1 += sb3(v) * x[4 * k + 3];
+    }
+    return h2f(D[0]) * (a0 + a1);
+  }
+};
+
+// Q4_0 lane part: block l: fp16 d, then 16 bytes; column i < 16 is the low nibble of
+// byte i, column 16 + i the high nibble; w = d (n - 8).
+struct Q40_S {
+  static constexpr int FMT = FMT_Q4_0, BB = 18, K = 0;
+  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[32], const float (&xs)[2]) {
+    const uint8_t* p = slot + lane * 18;
+    const uint32_t pd = (uint32_t)(lane & 1) * 2u;  // 18 lane mod 4
+    uint32_t Q[4], D[1];
+    lds_run<4>(p + 2, 2u - pd, Q);
+    lds_run<1>(p, pd, D);
+    const uint32_t mlo = vreg(NIB_LO), mhi = vreg(NIB_HI), m1024 = vreg(F16_1024);
+    float slo = 0.f, shi = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t v = Q[k], u = v >> 8;
+      const uint32_t p0 = and_or(v, mlo, m1024), p1 = and_or(v, mhi, m1024);
+      const uint32_t p2 = and_or(u, mlo, m1024), p3 = and_or(u, mhi, m1024);
+      slo += lo_h(p0) * x[4 * k];
+      slo += lo_h(p2) * x[4 * k + 1];
+      slo += hi_h(p0) * x[4 * k + 2];
+      slo += hi_h(p2) * x[4 * k + 3];
+      shi += lo_h(p1) * x[16 + 4 * k];
+      shi += lo_h(p3) * x[17 + 4 * k];
+      shi += hi_h(p1) * x[18 + 4 * k];
+      shi += hi_h(p3) * x[19 + 4 * k];
+    }
+    // sum (n - 8) x = (slo - 1024 X0) + (shi - 1024 X1) / 16 - 8 (X0 + X1)
+    const float r = (slo - 1032.f * xs[0]) + (shi - 1024.f * xs[1]) * 0.0625f - 8.f * xs[1];
+    return h2f(D[0]) * r;
+  }
+};
+
+struct StreamArgs {
+  GemvArgs a;
+  int tstart[3];   // first task of each segment
+  int tasks;       // tasks of the launch (SWIGLU: 2 per row, gate then up)
+  int tpw;         // tasks per workgroup (even)
+  int ns;          // column slices
+  int rsub;        // waves per slice
+};
+
+// Per-wave constants of the launch's segments (one for STORE / RESID / LOGITS, gate and
+// up for SWIGLU, q / k / v for QKV), kept in registers across the task loop.
+template <int EPI>
+struct SegCache {
+  static constexpr int NS = (EPI == EPI_SWIGLU) ? 2 : (EPI == EPI_QKV) ? 3 : 1;
+  const uint8_t* base[NS];  // this wave's slice of row 0
+  int64_t rb[NS];           // row bytes
+  int last[NS];             // index of the slice's last 16-byte piece
+  int fmt[NS];
+  int ts1, ts2;             // first task of segments 1 and 2 (QKV)
+};
+
+template <int KF, int EPI>
+__device__ __forceinline__ SegCache<EPI> seg_cache(const StreamArgs& sa, int sl) {
+  SegCache<EPI> c;
+  constexpr int per_slice = KF ? (ST_SLICE_COLS_K / 256) : (ST_SLICE_COLS_B / 32);
+  const int b0 = sl * per_slice;
+  const int nb = min(per_slice, sa.a.cols / (KF ? 256 : 32) - b0);
+#pragma unroll
+  for (int i = 0; i < SegCache<EPI>::NS; ++i) {
+    const GemvSeg& sg = sa.a.seg[i];
+    const int bb = block_bytes(sg.fmt);
+    c.base[i] = sg.w + (size_t)b0 * bb;
+    c.rb[i] = sg.row_bytes;
+    c.last[i] = ((nb * bb) >> 4) - 1;
+    c.fmt[i] = sg.fmt;
+  }
+  c.ts1 = sa.tstart[1];
+  c.ts2 = sa.tstart[2];
+  return c;
+}
+
+// Segment and row of task t.
+template <int EPI>
+__device__ __forceinline__ void st_task(const SegCache<EPI>& c, int t, int& seg, int& row) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    seg = t & 1;
+    row = t >> 1;
+  } else if constexpr (EPI == EPI_QKV) {
+    seg = t >= c.ts2 ? 2 : t >= c.ts1 ? 1 : 0;
+    row = t - (seg == 2 ? c.ts2 : seg == 1 ? c.ts1 : 0);
+  } else {
+    seg = 0;
+    row = t;
+  }
+}
+
+template <int EPI, typename T>
+__device__ __forceinline__ T seg_pick(const T (&v)[SegCache<EPI>::NS], int seg) {
+  if constexpr (SegCache<EPI>::NS == 1) return v[0];
+  else if constexpr (SegCache<EPI>::NS == 2) return seg ? v[1] : v[0];
+  else return seg == 2 ? v[2] : seg == 1 ? v[1] : v[0];
+}
+
+// Issue the NI transfers of task t's slice bytes into a ring slot.  Lanes past the slice's
+// last 16-byte piece re-read that piece, so every task issues exactly NI instructions.
+template <int EPI, int NI>
+__device__ __forceinline__ void st_issue(const SegCache<EPI>& c, int t, int lane, uint8_t* slot) {
+  int seg, row;
+  st_task<EPI>(c, t, seg, row);
+  const uint8_t* src = seg_pick<EPI>(c.base, seg) + (size_t)row * seg_pick<EPI>(c.rb, seg);
+  const int last = seg_pick<EPI>(c.last, seg);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) dma16(src + 16 * min(64 * i + lane, last), slot + 1024 * i);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+template <int KF, int EPI, int D, int NI>
+__global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const StreamArgs sa) {
+  constexpr int XN = KF ? 64 : 32;   // x values per lane
+  constexpr int XG = KF ? 4 : 2;     // 16-column sums per lane
+  constexpr int SLOT = 1024 * NI;
+  extern __shared__ float4 smem4[];
+  const GemvArgs& a = sa.a;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nw = (int)(blockDim.x >> 6);
+  const int sl = wave % sa.ns, sub = wave / sa.ns;
+  const SegCache<EPI> sc = seg_cache<KF, EPI>(sa, sl);
+  uint8_t* ring = reinterpret_cast<uint8_t*>(smem4) + (size_t)wave * D * SLOT;
+  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem4) + (size_t)nw * D * SLOT);
+  __shared__ float ssq[ST_MAX_WAVES];
+  __shared__ float2 rope[64];
+  __shared__ unsigned long long wbest[ST_MAX_WAVES];
+  if constexpr (EPI == EPI_QKV) {
+    if (threadIdx.x < 64) rope[threadIdx.x] = rope_cs(a.rope_theta, a.pos, threadIdx.x);
+  }
+  const int t0 = (int)blockIdx.x * sa.tpw, t1 = min(sa.tasks, t0 + sa.tpw);
+
+  // ---- x slice into registers, issued first so that it arrives first
+  const int c0 = KF ? sl * ST_SLICE_COLS_K + 64 * lane : sl * ST_SLICE_COLS_B + 32 * lane;
+  const bool xvalid = c0 < a.cols;
+  float x[XN];
+  {
+    const float4* xp = reinterpret_cast<const float4*>(a.x + (xvalid ? c0 : 0));
+#pragma unroll
+    for (int i = 0; i < XN / 4; ++i) {
+      const float4 v = xp[i];
+      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- the first D tasks of this wave in flight (every wave has a slice and a share of tasks)
+#pragma unroll
+  for (int d = 0; d < D; ++d) st_issue<EPI, NI>(sc, min(t0 + sub + d * sa.rsub, t1 - 1), lane, ring + d * SLOT);
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- RMSNorm prologue: scale from the sum of squares over all slices
+  if (a.gain) {
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < XN; ++i) q += x[i] * x[i];
+    q = wave_sum(xvalid ? q : 0.f);
+    if (sub == 0 && lane == 0) ssq[sl] = q;
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < sa.ns; ++i) tot += ssq[i];
+    const float scale = 1.0f / sqrtf(tot / (float)a.cols + a.eps);
+    const float4* gp = reinterpret_cast<const float4*>(a.gain + (xvalid ? c0 : 0));
+#pragma unroll
+    for (int i = 0; i < XN / 4; ++i) {
+      const float4 gg = gp[i];
+      x[4 * i] = x[4 * i] * scale * gg.x;
+      x[4 * i + 1] = x[4 * i + 1] * scale * gg.y;
+      x[4 * i + 2] = x[4 * i + 2] * scale * gg.z;
+      x[4 * i + 3] = x[4 * i + 3] * scale * gg.w;
+    }
+  }
+  float xs[XG];
+#pragma unroll
+  for (int j = 0; j < XG; ++j) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += x[16 * j + i];
+    xs[j] = t;
+  }
+
+  // ---- the wave's tasks: t0 + sub, t0 + sub + rsub, ...
+  {
+    int d = 0;
+    for (int t = t0 + sub; t < t1; t += sa.rsub) {
+      uint8_t* slot = ring + d * SLOT;
+      wait_vm<NI * (D - 1)>();
+      int seg, row;
+      st_task<EPI>(sc, t, seg, row);
+      float v = 0.f;
+      if (xvalid) {
+        const int fmt = seg_pick<EPI>(sc.fmt, seg);
+        if constexpr (KF) {
+          v = Q6K_S::dot(slot, lane, x, xs);  // the launcher sends Q4_K to the register path
+        } else {
+          if (fmt == FMT_Q8_0) v = Q80_S::dot(slot, lane, x, xs);
+          else v = Q40_S::dot(slot, lane, x, xs);
+        }
+      }
+      // the slot has been read: refill it with the task D steps ahead
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      st_issue<EPI, NI>(sc, min(t + D * sa.rsub, t1 - 1), lane, slot);
+      v = row16_sum(v);
+      if ((lane & 15) == 0) part[(((t - t0) * sa.ns + sl) << 2) + (lane >> 4)] = v;
+      d = (d + 1 == D) ? 0 : d + 1;
+    }
+    wait_vm<0>();
+  }
+  __syncthreads();
+
+  // ---- epilogue: one thread per task (per pair for SWIGLU and QKV)
+  unsigned long long best = 0;
+  const int nt = t1 - t0;
+  auto total = [&](int i) {
+    const float4* q = reinterpret_cast<const float4*>(part) + i * sa.ns;
+    float v = 0.f;
+    for (int j = 0; j < sa.ns; ++j) {
+      const float4 f = q[j];
+      v += (f.x + f.y) + (f.z + f.w);
+    }
+    return v;
+  };
+  if constexpr (EPI == EPI_STORE || EPI == EPI_LOGITS || EPI == EPI_RESID) {
+    for (int i = threadIdx.x; i < nt; i += blockDim.x) {
+      const int r = t0 + i;
+      const float v = total(i);
+      if constexpr (EPI == EPI_RESID) {
+        const float o = a.resid[r] + v;
+        a.y[r] = o;
+        if (a.y2) a.y2[r] = o;
+      } else {
+        a.y[r] = v;
+      }
+      if constexpr (EPI == EPI_LOGITS) {
+        const unsigned long long key = logit_key(v, r);
+        best = key > best ? key : best;
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    for (int i = 2 * threadIdx.x; i < nt; i += 2 * blockDim.x) a.y[(t0 + i) >> 1] = silu_mul(total(i), total(i + 1));
+  } else if constexpr (EPI == EPI_QKV) {
+    constexpr int HD = 128;
+    for (int i = 2 * threadIdx.x; i < nt; i += 2 * blockDim.x) {
+      int seg, r;
+      st_task<EPI>(sc, t0 + i, seg, r);
+      const float y0 = total(i), y1 = total(i + 1);
+      const int head = r / HD, dd = r % HD;
+      if (seg < 2) {
+        const float2 c = rope[dd >> 1];
+        const float r0 = y0 * c.x - y1 * c.y;
+        const float r1 = y0 * c.y + y1 * c.x;
+        if (seg == 0) {
+          a.q_out[r] = r0;
+          a.q_out[r + 1] = r1;
+        } else {
+          uint16_t* kp = a.k_cache + ((size_t)head * a.max_ctx + a.pos) * HD + dd;
+          kp[0] = f2h_rne(r0);
+          kp[1] = f2h_rne(r1);
+        }
+      } else {
+        // V cache groups of 8 slots: [head][slot / 8][dim][slot % 8]
+        uint16_t* vp = a.v_cache + (size_t)head * a.max_ctx * HD + ((size_t)(a.pos >> 3) * HD + dd) * 8 + (a.pos & 7);
+        vp[0] = f2h_rne(y0);
+        vp[8] = f2h_rne(y1);
+      }
+    }
+  }
+  if constexpr (EPI == EPI_LOGITS) {
+    // one atomic per workgroup
+    for (int off = 32; off >= 1; off >>= 1) {
+      const unsigned long long o = __shfl_xor(best, off, 64);
+      best = o > best ? o : best;
+    }
+    if (lane == 0) wbest[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long b = 0;
+      for (int w = 0; w < nw; ++w) b = wbest[w] > b ? wbest[w] : b;
+      if (b) atomicMax(a.amax, b);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 static int num_cu() {
@@ -790,7 +1254,119 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
   }
 }
 
+// ---- streamed path
+static bool st_family(int fmt) { return fmt == FMT_Q4_K || fmt == FMT_Q6_K; }
+
+constexpr size_t ST_LDS_MAX = 160 * 1024 - 2048;  // dynamic LDS budget (static LDS on top)
+
+template <int KF, int EPI, int D, int NI>
+static hipError_t st_launch(const StreamArgs& sa, int grid, int nw, size_t lds, hipStream_t s) {
+  auto kern = gemv_stream_kernel<KF, EPI, D, NI>;
+  static bool raised = false;  // the dynamic LDS limit of this instantiation
+  if (!raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)ST_LDS_MAX);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(nw * 64), lds, s, sa);
+  return hipGetLastError();
+}
+
+// Ring configurations: transfers per task NI (slot = NI KiB) and ring depth D.
+template <int EPI>
+static hipError_t st_dispatch(bool kf, int ni, int d, const StreamArgs& sa, int grid, int nw, size_t lds, hipStream_t s) {
+  if (kf) {
+    if (ni == 3) return d == 3 ? st_launch<1, EPI, 3, 3>(sa, grid, nw, lds, s) : st_launch<1, EPI, 2, 3>(sa, grid, nw, lds, s);
+    return st_launch<1, EPI, 2, 4>(sa, grid, nw, lds, s);
+  }
+  if (ni == 2) return d == 3 ? st_launch<0, EPI, 3, 2>(sa, grid, nw, lds, s) : st_launch<0, EPI, 2, 2>(sa, grid, nw, lds, s);
+  return d == 3 ? st_launch<0, EPI, 3, 3>(sa, grid, nw, lds, s) : st_launch<0, EPI, 2, 3>(sa, grid, nw, lds, s);
+}
+
+// Launch the streamed path if the shape allows it (rows and x 16-byte aligned, one format
+// family).  Returns hipErrorNotSupported, with nothing launched, if it does not.
+static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) {
+  const int nseg = (epi == EPI_SWIGLU) ? 2 : a.nseg;
+  // the kernel's segment layout: one matrix, gate + up, or q + k + v
+  if (nseg != (epi == EPI_SWIGLU ? 2 : epi == EPI_QKV ? 3 : 1)) return hipErrorNotSupported;
+  const bool kf = st_family(a.seg[0].fmt);
+  for (int i = 0; i < nseg; ++i) {
+    const GemvSeg& g = a.seg[i];
+    if (st_family(g.fmt) != kf) return hipErrorNotSupported;
+    // Q4_K measured faster on the register path (its x traffic: each wave here holds its
+    // own copy of its slice of x, versus one copy per workgroup there)
+    if (g.fmt == FMT_Q4_K) return hipErrorNotSupported;
+    if ((reinterpret_cast<uintptr_t>(g.w) & 15) || (g.row_bytes & 15) || g.rows <= 0) return hipErrorNotSupported;
+  }
+  if ((reinterpret_cast<uintptr_t>(a.x) & 15) || (a.gain && (reinterpret_cast<uintptr_t>(a.gain) & 15)))
+    return hipErrorNotSupported;
+  const int slice_cols = kf ? ST_SLICE_COLS_K : ST_SLICE_COLS_B;
+  if (a.cols % (kf ? 256 : 32)) return hipErrorNotSupported;
+  StreamArgs sa;
+  sa.a = a;
+  sa.ns = (a.cols + slice_cols - 1) / slice_cols;
+  if (sa.ns > ST_MAX_WAVES) return hipErrorNotSupported;
+  int slot = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const int per_slice = kf ? slice_cols / 256 : slice_cols / 32;
+    const int nblk = a.cols / (kf ? 256 : 32);
+    // + 16: the realigning LDS reads of the last block may run up to 6 bytes past it
+    const int bytes = min(per_slice, nblk) * block_bytes(a.seg[i].fmt) + 16;
+    slot = max(slot, (bytes + 1023) / 1024 * 1024);
+  }
+  // the instantiated slot sizes: 3 or 4 KiB (superblock formats), 2 or 3 KiB (block formats)
+  int ni = slot / 1024;
+  if (kf) ni = ni <= 3 ? 3 : ni;
+  else ni = ni <= 2 ? 2 : ni;
+  if (ni > (kf ? 4 : 3)) return hipErrorNotSupported;
+  int tasks = 0;
+  if (epi == EPI_SWIGLU) {
+    if (a.seg[1].rows != a.seg[0].rows) return hipErrorNotSupported;
+    tasks = 2 * a.seg[0].rows;
+    sa.tstart[0] = 0; sa.tstart[1] = 0; sa.tstart[2] = 0;
+  } else {
+    for (int i = 0; i < nseg; ++i) {
+      sa.tstart[i] = tasks;
+      if ((epi == EPI_QKV) && (a.seg[i].rows & 1)) return hipErrorNotSupported;
+      tasks += a.seg[i].rows;
+    }
+    for (int i = nseg; i < 3; ++i) sa.tstart[i] = tasks;
+  }
+  sa.tasks = tasks;
+  const int ncu = num_cu();
+  int tpw = (tasks + ncu - 1) / ncu;
+  tpw = max(2, (tpw + 1) & ~1);
+  sa.tpw = tpw;
+  const int grid = (tasks + tpw - 1) / tpw;
+  const size_t part = (size_t)tpw * sa.ns * 4 * sizeof(float);
+  const size_t slot_bytes = (size_t)ni * 1024;
+  int rsub = max(1, ST_MAX_WAVES / sa.ns);
+  int d = 3;
+  for (;;) {
+    const size_t nw = (size_t)sa.ns * rsub;
+    if (ni < 4 && nw * 3 * slot_bytes + part <= ST_LDS_MAX) { d = 3; break; }
+    if (nw * 2 * slot_bytes + part <= ST_LDS_MAX) { d = 2; break; }
+    if (rsub == 1) return hipErrorNotSupported;
+    --rsub;
+  }
+  sa.rsub = rsub;
+  const int nw = sa.ns * rsub;
+  const size_t lds = (size_t)nw * d * slot_bytes + part;
+  switch (epi) {
+    case EPI_STORE: return st_dispatch<EPI_STORE>(kf, ni, d, sa, grid, nw, lds, s);
+    case EPI_RESID: return st_dispatch<EPI_RESID>(kf, ni, d, sa, grid, nw, lds, s);
+    case EPI_SWIGLU: return st_dispatch<EPI_SWIGLU>(kf, ni, d, sa, grid, nw, lds, s);
+    case EPI_QKV: return st_dispatch<EPI_QKV>(kf, ni, d, sa, grid, nw, lds, s);
+    default: return st_dispatch<EPI_LOGITS>(kf, ni, d, sa, grid, nw, lds, s);
+  }
+}
+
 hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s) {
+  if (NT_GEMV_STREAM) {
+    const hipError_t e = gemv_stream_launch(epi, a, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   switch (epi) {
     case EPI_STORE: return launch_mask<EPI_STORE>(fmt_mask, plan, n_groups, a, s);
     case EPI_RESID: return launch_mask<EPI_RESID>(fmt_mask, plan, n_groups, a, s);

@@ -72,11 +72,16 @@ def test_dequant_hand_blocks_bit_exact():
 
 GEMV_SHAPES = {
     # rows x cols: single block, ragged block counts (odd row byte counts put rows at
-    # alternating 4-byte phases), rows past a workgroup tile, and the workload shapes
-    synth.Q8_0: [(1, 32), (3, 32), (37, 2144), (301, 1056), (4096, 4096), (14336, 4096), (4096, 14336)],
-    synth.Q4_0: [(1, 32), (5, 96), (29, 1440), (257, 4096), (4096, 4096)],
-    synth.Q4_K: [(1, 256), (23, 1280), (130, 4352), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
-    synth.Q6_K: [(1, 256), (19, 768), (77, 2304), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
+    # alternating 4-byte phases: the register path), rows past a workgroup's task range,
+    # 16-byte-aligned rows with a partial last column slice (the streamed path), and the
+    # workload shapes
+    synth.Q8_0: [(1, 32), (3, 32), (37, 2144), (301, 1056), (37, 2304), (3, 256), (4096, 4096), (14336, 4096),
+                 (4096, 14336)],
+    synth.Q4_0: [(1, 32), (5, 96), (29, 1440), (29, 2304), (257, 4096), (4096, 4096)],
+    synth.Q4_K: [(1, 256), (23, 1280), (130, 4352), (3, 12288), (8192, 8192), (1024, 8192), (28672, 8192),
+                 (8192, 28672)],
+    synth.Q6_K: [(1, 256), (19, 768), (77, 2304), (77, 6144), (5, 2048), (8192, 8192), (1024, 8192), (28672, 8192),
+                 (8192, 28672)],
 }
 GEMV_CASES = [(f, r, c) for f in FMTS for (r, c) in GEMV_SHAPES[f]]
 
