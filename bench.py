@@ -43,10 +43,55 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--layers", type=int, default=80, help="layers of the 70B model (measurement runs only)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (the reference for HBM byte counters)")
     return p.parse_args()
 
 
 # ----------------------------------------------------------------------------- helpers
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up_q4k_70b_traffic.txt")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "quantized_weight_streaming_dequant_amd", "csrc", f)
+                   for f in ("gemv.hip", "gemv.h", "common.h")]
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a plain copy of
+    known size), or None when there is none or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                if line.startswith("TRAFFIC_JSON "):
+                    d = json.loads(line[len("TRAFFIC_JSON "):])
+                    if d.get("sources_sha256") == sources_digest():
+                        return d["hbm_bytes_per_launch"]
+    except OSError:
+        pass
+    return None
+
+
+def copy_calibration(torch):
+    """A plain device copy of 1 GiB, ten times: the kernel whose byte counters are known."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes": n, "copies": 10}
+
 
 def host_threads() -> int:
     env = os.environ.get("OMP_NUM_THREADS")
@@ -152,6 +197,16 @@ class Model70B:
                 ents.append((self.host_blobs[l].data_ptr(), False, self.kc[l].data_ptr(), self.vc[l].data_ptr()))
         return tg.model_plan(shp, lay, ents)
 
+    def layer_weights(self, l):
+        """nt_layer_weights of resident layer l (pointers into its blob)."""
+        from synth import recipes
+        blob = self.dev_blobs[l]
+        off = self.lay.offsets
+        mats = [blob[off[n]:] for n in recipes.TENSORS]
+        return self.tg.layer_weights([self.mix[n] for n in recipes.TENSORS], mats,
+                                     blob[off["attn_norm"]:].view(self.torch.float32),
+                                     blob[off["ffn_norm"]:].view(self.torch.float32))
+
     def head(self):
         return self.nt.ModelHead(self.embd_fmt, self.embd.data_ptr(), self.vocab, self.onorm.data_ptr(), self.out_fmt,
                                  self.out.data_ptr())
@@ -249,9 +304,29 @@ def bench_decode_70b(args, torch, nt, tg):
     dt = time.perf_counter() - t0
     tok_s = steps / dt
     last_tok = int(tok.item())
-    # per-kernel-class durations (separate, instrumented passes over the same tokens)
-    kern = {}
+    # the roofline kernel on its own: the fused gate/up launch of every layer back to back
+    # (each layer's weights once per round), HIP events around the batch on the launching stream
     fb = ffn_up_bytes(mix, m.shape)
+    lw = [m.layer_weights(l) for l in range(n_layers)]
+    h_in = torch.from_numpy(recipes.hidden_input(m.shape.dim)).cuda()
+    a_out = torch.empty(m.shape.ffn_dim, dtype=torch.float32, device="cuda")
+
+    def ffn(n):
+        for i in range(n):
+            nt.nt_ffn_up(lw[i % n_layers], shp, h_in.data_ptr(), a_out.data_ptr(), cs)
+
+    ffn(n_layers)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_ffn = 3 * n_layers
+    torch.cuda.synchronize()
+    ev0.record()
+    ffn(n_ffn)
+    ev1.record()
+    ev1.synchronize()
+    ffn_us = ev0.elapsed_time(ev1) * 1e3 / n_ffn
+    # per-kernel-class durations inside the decode (separate, instrumented passes over the same
+    # tokens; an event pair around every launch adds a few microseconds to each)
+    kern = {}
     for name, kc, nbytes in (("ffn_gate_up_swiglu", nt.K_FFN_UP, fb),
                              ("ffn_down_resid", nt.K_FFN_DOWN,
                               synth.matrix_bytes(mix["down"], 8192, 28672) + 4 * (28672 + 2 * 8192)),
@@ -275,10 +350,11 @@ def bench_decode_70b(args, torch, nt, tg):
                    "parallelism": "none (1 GPU)"},
         "step_hbm": {"algorithmic_bytes_per_token": int(tb), "GBps": tb * tok_s / 1e9,
                      "frac_of_peak": tb * tok_s / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up_swiglu (fused Q4_K gate+up GEMV, SwiGLU epilogue)",
-                     "achieved": ff["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ff["GBps"] / HBM_PEAK_GBS if ff["GBps"] else None, "traffic": None,
-                     "bytes_per_launch": fb, "avg_launch_us": ff["avg_us"]},
+        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up_swiglu (fused RMSNorm + Q4_K gate/up GEMV + SwiGLU)",
+                     "achieved": fb / (ffn_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": fb / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "bytes_per_launch": fb, "avg_launch_us": ffn_us, "launches": n_ffn,
+                     "timing": "HIP events around back-to-back launches over all layers' weights"},
         "kernels": kern,
         "last_token": last_tok,
     }
@@ -470,6 +546,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(torch)), flush=True)
+        return
     nt.load()
     if args.config == 4:
         res = bench_decode_70b(args, torch, nt, tg)

@@ -163,6 +163,13 @@ typedef struct {
 int nt_decode_layer(const nt_layer_weights* w, const nt_layer_shape* shp, int pos, float* h, uint16_t* k_cache,
                     uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream);
 size_t nt_decode_layer_ws_bytes(const nt_layer_shape* shp);
+
+/* The FFN input half of a decode layer on its own, the same launch nt_decode_layer makes:
+ * a = SwiGLU(Wg n, Wu n) with n = RMSNorm(h, ffn_norm) (ntransformer overview,
+ * "Hauptfunktionen": RMSNorm, SwiGLU).  h: device [dim] fp32, 16-byte aligned, read only;
+ * a: device [ffn] fp32.  Same shape and weight constraints as nt_decode_layer (the other
+ * matrices of w must be valid pointers but are not read). */
+int nt_ffn_up(const nt_layer_weights* w, const nt_layer_shape* shp, const float* h, float* a, void* stream);
 /* off[0..4] = byte offsets of q, o, h1, a and the attention partials inside the layer workspace */
 int nt_decode_layer_ws_offsets(const nt_layer_shape* shp, int64_t* off);
 

@@ -67,7 +67,7 @@ _lib = None
 EXPORTS = [
     "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
-    "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_embed_row", "nt_argmax", "nt_stream_create",
+    "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
     "nt_stream_destroy", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_timing_begin",
     "nt_timing_end",
 ]
@@ -98,6 +98,7 @@ def load(path: str = LIB_PATH):
         "nt_swiglu": ([i64, vp, vp, vp, vp], i),
         "nt_decode_layer": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerShape), i, vp, vp, vp, vp, sz, vp], i),
         "nt_decode_layer_ws_bytes": ([ctypes.POINTER(LayerShape)], sz),
+        "nt_ffn_up": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerShape), vp, vp, vp], i),
         "nt_decode_layer_ws_offsets": ([ctypes.POINTER(LayerShape), ctypes.POINTER(ctypes.c_int64)], i),
         "nt_embed_row": ([i, i64, i64, vp, vp, vp, vp], i),
         "nt_argmax": ([i64, vp, vp, vp], i),
@@ -177,6 +178,10 @@ def nt_swiglu(n, gate, up, out, stream=None):
 def nt_decode_layer(weights: LayerWeights, shape: LayerShape, pos, h, k_cache, v_cache, ws, ws_bytes, stream=None):
     return _check(load().nt_decode_layer(ctypes.byref(weights), ctypes.byref(shape), pos, h, k_cache, v_cache, ws,
                                          ws_bytes, stream))
+
+
+def nt_ffn_up(weights: LayerWeights, shape: LayerShape, h, a, stream=None):
+    return _check(load().nt_ffn_up(ctypes.byref(weights), ctypes.byref(shape), h, a, stream))
 
 
 def nt_decode_layer_ws_bytes(shape: LayerShape) -> int:

@@ -140,6 +140,19 @@ GemvArgs blank_args() {
   return a;
 }
 
+// Enqueue the FFN input half of a layer: a = SwiGLU(Wg n, Wu n), n = RMSNorm(h, ffn_norm).
+static hipError_t ffn_up_launch(const nt_layer_weights& w, const nt_layer_shape& s, const float* h, float* out,
+                                hipStream_t st) {
+  const GemvPlan p = gemv_plan(EPI_SWIGLU, s.dim);
+  GemvArgs a = blank_args();
+  a.x = h; a.gain = w.ffn_norm; a.eps = s.eps; a.cols = s.dim; a.nseg = 2;
+  a.seg[0] = make_seg(w.w[NT_W_GATE], w.fmt[NT_W_GATE], s.ffn_dim, s.dim, 0);
+  a.seg[1] = make_seg(w.w[NT_W_UP], w.fmt[NT_W_UP], s.ffn_dim, s.dim, 1 << 30);
+  a.y = out;
+  TimedLaunch tl(NT_K_FFN_UP, st);
+  return gemv_launch(1 << w.fmt[NT_W_GATE], EPI_SWIGLU, p, gemv_groups(p, s.ffn_dim), a, st);
+}
+
 // Enqueue one decode layer (arguments already checked).
 int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float* h, uint16_t* kc, uint16_t* vc,
               uint8_t* ws, hipStream_t st) {
@@ -184,17 +197,8 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     if ((e = gemv_launch(1 << w.fmt[NT_W_O], EPI_RESID, p, gemv_groups(p, s.dim), a, st)) != hipSuccess)
       return hip_fail(e, "o launch");
   }
-  {  // a6-a8: RMSNorm prologue, paired gate/up GEMV, SwiGLU epilogue
-    const GemvPlan p = gemv_plan(EPI_SWIGLU, s.dim);
-    GemvArgs a = blank_args();
-    a.x = h; a.gain = w.ffn_norm; a.eps = s.eps; a.cols = s.dim; a.nseg = 2;
-    a.seg[0] = make_seg(w.w[NT_W_GATE], w.fmt[NT_W_GATE], s.ffn_dim, s.dim, 0);
-    a.seg[1] = make_seg(w.w[NT_W_UP], w.fmt[NT_W_UP], s.ffn_dim, s.dim, 1 << 30);
-    a.y = wa;
-    TimedLaunch tl(NT_K_FFN_UP, st);
-    if ((e = gemv_launch(1 << w.fmt[NT_W_GATE], EPI_SWIGLU, p, gemv_groups(p, s.ffn_dim), a, st)) != hipSuccess)
-      return hip_fail(e, "gate/up launch");
-  }
+  // a6-a8: RMSNorm prologue, paired gate/up GEMV, SwiGLU epilogue
+  if ((e = ffn_up_launch(w, s, h, wa, st)) != hipSuccess) return hip_fail(e, "gate/up launch");
   {  // a9: down GEMV + residual
     const GemvPlan p = gemv_plan(EPI_RESID, s.ffn_dim);
     GemvArgs a = blank_args();
@@ -374,6 +378,16 @@ int nt_decode_layer(const nt_layer_weights* w, const nt_layer_shape* shp, int po
     return fail(NT_EALIGN, "h and caches must be 16-byte aligned, ws 256-byte");
   if (ws_bytes < layer_ws(*shp).total) return fail(NT_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, layer_ws(*shp).total);
   return run_layer(*w, *shp, pos, h, k_cache, v_cache, reinterpret_cast<uint8_t*>(ws), (hipStream_t)stream);
+}
+
+int nt_ffn_up(const nt_layer_weights* w, const nt_layer_shape* shp, const float* h, float* a, void* stream) {
+  int rc;
+  if ((rc = check_shape(shp))) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (!h || !a) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(h, 16) || !aligned(a, 4)) return fail(NT_EALIGN, "h must be 16-byte aligned, a 4-byte");
+  const hipError_t e = ffn_up_launch(*w, *shp, h, a, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "gate/up launch");
 }
 
 int nt_embed_row(int fmt, int64_t n_vocab, int64_t dim, const void* table, const int32_t* token, float* h,

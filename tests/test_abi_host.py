@@ -123,6 +123,28 @@ def test_decode_layer_checks(shape_kw, wfix, pos, code):
     assert ei.value.code == code
 
 
+@pytest.mark.parametrize("shape_kw,wfix,code", [
+    (dict(head_dim=64), None, nt.NT_ESHAPE),
+    (dict(ffn_dim=40960), None, nt.NT_ESHAPE),
+    ({}, "mixed_ffn", nt.NT_EFORMAT),
+    ({}, "null_h", nt.NT_EINVAL),
+    ({}, "misaligned_h", nt.NT_EALIGN),
+])
+def test_ffn_up_checks(shape_kw, wfix, code):
+    shp = _shape(**shape_kw)
+    w = _weights()
+    h = 4096
+    if wfix == "mixed_ffn":
+        w.fmt[nt.W_GATE] = nt.Q4_K
+    elif wfix == "null_h":
+        h = None
+    elif wfix == "misaligned_h":
+        h = 4096 + 4
+    with pytest.raises(nt.NtError) as ei:
+        nt.nt_ffn_up(w, shp, h, 4096)
+    assert ei.value.code == code
+
+
 def test_workspace_sizes_and_offsets():
     shp = _shape()
     ws = nt.nt_decode_layer_ws_bytes(shp)

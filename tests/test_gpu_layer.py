@@ -119,6 +119,26 @@ def test_layer_small_shapes(mix, pos):
     run_layer_and_check(SMALL, mix, pos=pos, n_slots=96)
 
 
+@pytest.mark.parametrize("shape,mix", [(SMALL, recipes.MIX_Q4_K_M), (recipes.LLAMA31_70B, recipes.MIX_Q4_K_M),
+                                       (recipes.LLAMA3_8B, recipes.MIX_Q8_0)])
+def test_ffn_up_entry_matches_layer(shape, mix):
+    """nt_ffn_up on the layer's own h1 reproduces the SwiGLU output nt_decode_layer leaves in
+    its workspace, bit for bit (the same launch)."""
+    say(f"ffn_up entry dim={shape.dim} ffn={shape.ffn_dim}")
+    L = DeviceLayer(shape, mix, 0, 8)
+    shp = tg.layer_shape(shape)
+    wsb = nt.nt_decode_layer_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    off = nt.nt_decode_layer_ws_offsets(shp)
+    h = dev(recipes.hidden_input(shape.dim))
+    nt.nt_decode_layer(L.weights(), shp, 7, h.data_ptr(), L.kc.data_ptr(), L.vc.data_ptr(), ws.data_ptr(), wsb, stream())
+    h1 = ws[off["h1"]:off["h1"] + 4 * shape.dim].view(torch.float32).clone()
+    a_layer = host(ws[off["a"]:off["a"] + 4 * shape.ffn_dim].view(torch.float32))
+    a = torch.full((shape.ffn_dim,), float("nan"), dtype=torch.float32, device="cuda")
+    nt.nt_ffn_up(L.weights(), shp, h1.data_ptr(), a.data_ptr(), stream())
+    assert same_value(host(a), a_layer)
+
+
 # ------------------------------------------------------------------ model, token, streaming
 
 class Model:
