@@ -39,21 +39,36 @@ __device__ __forceinline__ float hi_h(uint32_t v) { return __half2float(__ushort
 #ifndef NT_GEMV_NONTEMPORAL
 #define NT_GEMV_NONTEMPORAL 0
 #endif
+#ifndef NT_GEMV_ROWS
+#define NT_GEMV_ROWS 2  // rows per work item of the register path (the gate/up pair always takes 1 of each)
+#endif
+#ifndef NT_GEMV_DEPTH
+#define NT_GEMV_DEPTH 2  // work items in flight per wave on the register path (gate/up pair: 2)
+#endif
+#ifndef NT_GEMV_DEPTH_PAIR
+#define NT_GEMV_DEPTH_PAIR 2  // the same for the gate/up pair
+#endif
 #ifndef NT_GEMV_STREAM
 #define NT_GEMV_STREAM 1  // the streamed (global->LDS) path wherever the shape allows it
 #endif
 
-// Weight loads.  Nontemporal loads were measured slower on every GEMV shape here (by
-// 10-30%), so plain cached loads are the default.
+// Weight loads, through global-address-space pointers: a load the compiler can only prove
+// to be generic becomes a flat load, which also counts against the LDS wait counter, so every
+// wait for an LDS read would wait for the prefetched weights too.  Nontemporal loads were
+// measured slower on every GEMV shape here (by 10-30%), so plain cached loads are the default.
+#define NT_GPTR(T, p) ((const __attribute__((address_space(1))) T*)(p))
 #if NT_GEMV_NONTEMPORAL
-__device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
-__device__ __forceinline__ uint32_t wld4(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
-__device__ __forceinline__ uint32_t wld2(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)); }
+__device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return __builtin_nontemporal_load(NT_GPTR(u32x4, p)); }
+__device__ __forceinline__ uint32_t wld4(const uint8_t* p) { return __builtin_nontemporal_load(NT_GPTR(uint32_t, p)); }
+__device__ __forceinline__ uint32_t wld2(const uint8_t* p) { return __builtin_nontemporal_load(NT_GPTR(uint16_t, p)); }
 #else
-__device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return ld16(p); }
-__device__ __forceinline__ uint32_t wld4(const uint8_t* p) { return ld4(p); }
-__device__ __forceinline__ uint32_t wld2(const uint8_t* p) { return ld2(p); }
+__device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return *NT_GPTR(u32x4, p); }
+__device__ __forceinline__ uint32_t wld4(const uint8_t* p) { return *NT_GPTR(uint32_t, p); }
+__device__ __forceinline__ uint32_t wld2(const uint8_t* p) { return *NT_GPTR(uint16_t, p); }
 #endif
+__device__ __forceinline__ u32x2 wld8(const uint8_t* p) { return *NT_GPTR(u32x2, p); }
+
+typedef uint32_t u32x4a16 __attribute__((ext_vector_type(4), aligned(16)));
 
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -73,6 +88,98 @@ constexpr uint32_t NIB_LO = 0x000F000Fu, NIB_HI = 0x00F000F0u;
 // src1); selector values 0-3 pick src1 bytes, 4-7 src0 bytes
 constexpr uint32_t PERM_B02 = 0x07020500u, PERM_B13 = 0x07030501u;
 
+// ------------------------------------------------------------------ activations as limbs
+//
+// The register path keeps x in LDS as XL signed 8-bit limbs per column.  Each block of 32
+// columns has a power-of-two scale s, the smallest with max |x| / s <= 127, and the
+// fixed-point value X = rint(x / s 256^(XL-1)) is split into balanced base-256 digits:
+//   X = 256^(XL-1) x1 + ... + x_XL,   x1 in [-127, 127], the others in [-128, 127],
+// so x is represented to within s 2^-(8 XL - 7) (two limbs: max |x of the block| / 32512).
+// Every step is exact in fp32 (scaling by a power of two, rounding to an integer below
+// 2^24).  The weight codes are small integers, so over a run of columns
+// sum q x = s (D1 + D2 / 256 + D3 / 65536) where Dk = sum q xk is formed exactly by
+// v_dot4_i32_i8 (four 8-bit products and the accumulation in one instruction), in place of
+// a convert and an fp32 FMA per weight.  The offset and min terms of the formats use exact
+// fp32 sums of x per 16 columns.
+// A limb plane holds byte c at xq_off(c): 16 pad bytes after every 64 columns, so lanes that
+// read 16-column runs 64 columns apart with 128-bit reads spread over the banks.
+#ifndef NT_GEMV_XLIMBS
+#define NT_GEMV_XLIMBS 2
+#endif
+constexpr int XL = NT_GEMV_XLIMBS;
+static_assert(XL == 2 || XL == 3, "two or three limbs");
+
+__host__ __device__ __forceinline__ int xq_off(int c) { return c + ((c >> 6) << 4); }
+__host__ __device__ __forceinline__ int xq_plane(int cols) { return (xq_off(cols) + 15) & ~15; }
+
+// The staged activation vector, as the register-path kernels see it in LDS.
+struct XLimbs {
+  uint8_t* q;   // XL planes of xq_plane(cols) bytes
+  int plane;
+  float* sc;    // scale s / 256^(XL-1) per 32 columns
+  float* s16;   // sum of x per 16 columns (fp32)
+};
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+// 256^(XL-1) (D1 + D2 / 256 (+ D3 / 65536)): the staged scale per 32 columns is stored as
+// s / 256^(XL-1), so that the product of the two is s (D1 + ...).  |Dk| < 2^20 here (at most
+// 32 codes of magnitude <= 128 times digits of magnitude <= 128), so 256 D1 + D2 fits an int.
+__device__ __forceinline__ float limb_sum(const int (&d)[XL]) {
+  if constexpr (XL == 3)
+    return (float)d[0] * 65536.f + (float)((d[1] << 8) + d[2]);
+  else
+    return (float)((d[0] << 8) + d[1]);
+}
+// The limbs of 16 columns starting at c (a multiple of 16): 4 dwords per plane.
+struct XRun {
+  u32x4 p[XL];
+};
+__device__ __forceinline__ XRun x_run(const XLimbs& xs, int c) {
+  XRun r;
+  const uint8_t* b = xs.q + xq_off(c);
+#pragma unroll
+  for (int k = 0; k < XL; ++k) {
+    const u32x4a16 v = *reinterpret_cast<const u32x4a16*>(b + k * xs.plane);
+    r.p[k] = u32x4{v.x, v.y, v.z, v.w};
+  }
+  return r;
+}
+// d[l] += sum over the four bytes of q and of dword i of limb plane l
+__device__ __forceinline__ void dot_limbs(uint32_t q, const XRun& x, int i, int (&d)[XL]) {
+#pragma unroll
+  for (int l = 0; l < XL; ++l) d[l] = sdot4(q, x.p[l][i], d[l]);
+}
+template <int NR>
+__device__ __forceinline__ void zero_limbs(int (&d)[NR][XL]) {
+#pragma unroll
+  for (int k = 0; k < NR; ++k)
+#pragma unroll
+    for (int l = 0; l < XL; ++l) d[k][l] = 0;
+}
+
+// t[k] = (sum over 16 columns at c of code k times x~) / s, for NR rows of 16 codes (4 dwords)
+// each: the limb planes are read one at a time, each feeding every row
+template <int NR>
+__device__ __forceinline__ void run_dot(const XLimbs& xs, int c, const uint32_t (&q)[NR][4], float (&t)[NR]) {
+  int d[NR][XL];
+  const uint8_t* b = xs.q + xq_off(c);
+#pragma unroll
+  for (int l = 0; l < XL; ++l) {
+    const u32x4a16 x = *reinterpret_cast<const u32x4a16*>(b + l * xs.plane);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      d[k][l] = sdot4(q[k][0], x.x, 0);
+      d[k][l] = sdot4(q[k][1], x.y, d[k][l]);
+      d[k][l] = sdot4(q[k][2], x.z, d[k][l]);
+      d[k][l] = sdot4(q[k][3], x.w, d[k][l]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) t[k] = limb_sum(d[k]);
+}
+
 // ------------------------------------------------------------------ formats
 //
 // Each format provides:
@@ -83,8 +190,12 @@ constexpr uint32_t PERM_B02 = 0x07020500u, PERM_B13 = 0x07030501u;
 
 // Q8_0: lane = one 34-byte block; steps visit the even blocks, then the odd ones.
 struct Q8_0F {
+  // the block's 34 bytes from the dword boundary B at or before it: phase 0 (block at B):
+  // w = bytes 0..31, e = bytes 32..33; phase 2 (block at B + 2): e = the scale (bytes 2..3),
+  // w = bytes 4..35.  The same three loads either way, so the count in flight is static.
   struct Raw {
-    uint32_t w[9];
+    uint32_t w[8];
+    uint32_t e;
     uint32_t ph;
   };
   static __device__ __forceinline__ int steps(int cols) {
@@ -106,65 +217,59 @@ struct Q8_0F {
     Raw r;
     const uint8_t* A = rowp + (size_t)(ok ? blk : (blk & 1)) * 34;
     r.ph = uni((uint32_t)((uintptr_t)A & 3u));  // the same for every lane of the step
-    if (r.ph == 0) {
-      const u32x4 a = wld16(A), b = wld16(A + 16);
-      r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-      r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
-      r.w[8] = wld2(A + 32);
-    } else {
-      r.w[0] = wld4(A - 2);
-      const u32x4 a = wld16(A + 2), b = wld16(A + 18);
-      r.w[1] = a.x; r.w[2] = a.y; r.w[3] = a.z; r.w[4] = a.w;
-      r.w[5] = b.x; r.w[6] = b.y; r.w[7] = b.z; r.w[8] = b.w;
-    }
+    const uint8_t* B = A - r.ph;
+    const int o = r.ph ? 4 : 0;
+    const u32x4 a = wld16(B + o), b = wld16(B + o + 16);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+    r.e = wld2(r.ph ? A : B + 32);
     return r;
   }
   template <int NR>
-  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane,
-                                             const float* __restrict__ xl, const float* __restrict__ xs16,
+  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane, const XLimbs& xs,
                                              float (&acc)[NR]) {
-    (void)xs16;
     bool ok;
     const int blk = block_of(cols, step, lane, ok);
     if (!ok) return;
-    const float4* xp = reinterpret_cast<const float4*>(xl + xpad(blk << 5));
-    float s[NR];
     uint32_t q[NR][8];
     float d[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      s[k] = 0.f;
       if (raw[k].ph == 0) {
         d[k] = h2f(raw[k].w[0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[k][i] = __builtin_amdgcn_alignbyte(raw[k].w[i + 1], raw[k].w[i], 2);
+        for (int i = 0; i < 8; ++i) q[k][i] = __builtin_amdgcn_alignbyte(i < 7 ? raw[k].w[i + 1] : raw[k].e, raw[k].w[i], 2);
       } else {
-        d[k] = h2f(raw[k].w[0] >> 16);
+        d[k] = h2f(raw[k].e);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[k][i] = raw[k].w[i + 1];
+        for (int i = 0; i < 8; ++i) q[k][i] = raw[k].w[i];
       }
     }
+    int D[NR][XL];
+    zero_limbs(D);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 xv = xp[i];
+    for (int h = 0; h < 2; ++h) {
+      const XRun x = x_run(xs, (blk << 5) + 16 * h);
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        s[k] += sb0(q[k][i]) * xv.x;
-        s[k] += sb1(q[k][i]) * xv.y;
-        s[k] += sb2(q[k][i]) * xv.z;
-        s[k] += sb3(q[k][i]) * xv.w;
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < NR; ++k) dot_limbs(q[k][4 * h + i], x, i, D[k]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    const float s = xs.sc[blk];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) acc[k] += d[k] * s[k];
+    for (int k = 0; k < NR; ++k) acc[k] += (d[k] * s) * limb_sum(D[k]);
   }
 };
 
 // Q4_0: lane = one 18-byte block; weights 0..15 are the low nibbles, 16..31 the high ones.
+// w = d (q - 8): summed as d (s sum q x~ - 8 sum x).
 struct Q4_0F {
+  // phase 0 (block at the dword boundary B): w = bytes 0..15, e = bytes 16..17; phase 2:
+  // e = the scale (bytes 2..3), w = bytes 4..19 (as for Q8_0: two loads either way)
   struct Raw {
-    uint32_t w[5];
+    uint32_t w[4];
+    uint32_t e;
     uint32_t ph;
   };
   static __device__ __forceinline__ int steps(int cols) { return Q8_0F::steps(cols); }
@@ -174,73 +279,56 @@ struct Q4_0F {
     Raw r;
     const uint8_t* A = rowp + (size_t)(ok ? blk : (blk & 1)) * 18;
     r.ph = uni((uint32_t)((uintptr_t)A & 3u));
-    if (r.ph == 0) {
-      const u32x4 a = wld16(A);
-      r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-      r.w[4] = wld2(A + 16);
-    } else {
-      r.w[0] = wld4(A - 2);
-      const u32x4 a = wld16(A + 2);
-      r.w[1] = a.x; r.w[2] = a.y; r.w[3] = a.z; r.w[4] = a.w;
-    }
+    const uint8_t* B = A - r.ph;
+    const u32x4 a = wld16(B + (r.ph ? 4 : 0));
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.e = wld2(r.ph ? A : B + 16);
     return r;
   }
   template <int NR>
-  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane,
-                                             const float* __restrict__ xl, const float* __restrict__ xs16,
+  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane, const XLimbs& xs,
                                              float (&acc)[NR]) {
     bool ok;
     const int blk = Q8_0F::block_of(cols, step, lane, ok);
     if (!ok) return;
-    const float4* xp = reinterpret_cast<const float4*>(xl + xpad(blk << 5));
-    const float xlo = xs16[2 * blk], xhi = xs16[2 * blk + 1];
-    float slo[NR], shi[NR], d[NR];
     uint32_t q[NR][4];
+    float d[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      slo[k] = shi[k] = 0.f;
       if (raw[k].ph == 0) {
         d[k] = h2f(raw[k].w[0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[k][i] = __builtin_amdgcn_alignbyte(raw[k].w[i + 1], raw[k].w[i], 2);
+        for (int i = 0; i < 4; ++i) q[k][i] = __builtin_amdgcn_alignbyte(i < 3 ? raw[k].w[i + 1] : raw[k].e, raw[k].w[i], 2);
       } else {
-        d[k] = h2f(raw[k].w[0] >> 16);
+        d[k] = h2f(raw[k].e);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[k][i] = raw[k].w[i + 1];
+        for (int i = 0; i < 4; ++i) q[k][i] = raw[k].w[i];
       }
     }
-    const uint32_t mlo = vreg(NIB_LO), mhi = vreg(NIB_HI), m1024 = vreg(F16_1024);
+    const uint32_t m0f = vreg(0x0F0F0F0Fu);
+    int D[NR][XL];
+    zero_limbs(D);
+    // h = 0: low nibbles, columns 0..15 of the block; h = 1: high nibbles, columns 16..31
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 xa = xp[i], xb = xp[4 + i];  // columns 4i.. (low nibbles), 16+4i.. (high nibbles)
+    for (int h = 0; h < 2; ++h) {
+      const XRun x = x_run(xs, (blk << 5) + 16 * h);
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const uint32_t v = q[k][i], u = v >> 8;
-        const uint32_t p0 = and_or(v, mlo, m1024), p1 = and_or(v, mhi, m1024);
-        const uint32_t p2 = and_or(u, mlo, m1024), p3 = and_or(u, mhi, m1024);
-        slo[k] += lo_h(p0) * xa.x;
-        slo[k] += lo_h(p2) * xa.y;
-        slo[k] += hi_h(p0) * xa.z;
-        slo[k] += hi_h(p2) * xa.w;
-        shi[k] += lo_h(p1) * xb.x;
-        shi[k] += lo_h(p3) * xb.y;
-        shi[k] += hi_h(p1) * xb.z;
-        shi[k] += hi_h(p3) * xb.w;
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < NR; ++k) dot_limbs(h == 0 ? (q[k][i] & m0f) : ((q[k][i] >> 4) & m0f), x, i, D[k]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slo = sum (1024 + n) x, shi = sum (1024 + 16 n) x;  w = d (n - 8)
+    const float s = xs.sc[blk];
+    const float xsum = xs.s16[2 * blk] + xs.s16[2 * blk + 1];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const float sn = (slo[k] - 1024.f * xlo) + 0.0625f * (shi[k] - 1024.f * xhi);
-      acc[k] += d[k] * (sn - 8.f * (xlo + xhi));
-    }
+    for (int k = 0; k < NR; ++k) acc[k] += d[k] * (s * limb_sum(D[k]) - 8.f * xsum);
   }
 };
 
 // Q4_K: lane = quarter g of a 144-byte superblock: the 32 nibble bytes at 16 + 32 g, whose
 // low nibbles are sub-block 2g and high nibbles sub-block 2g+1 (64 weights); 16 superblocks
-// per step.  w = d sc q - dmin m, summed per sub-block as d sc (sum q x) - dmin m (sum x).
+// per step.  w = d sc q - dmin m, summed per sub-block as d sc s (sum q x~) - dmin m (sum x);
+// a sub-block is one 32-column scale block of x.
 struct Q4_KF {
   struct Raw {
     u32x4 hd, qa, qb;
@@ -259,66 +347,57 @@ struct Q4_KF {
     return r;
   }
   template <int NR>
-  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane,
-                                             const float* __restrict__ xl, const float* __restrict__ xs16,
+  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane, const XLimbs& xs,
                                              float (&acc)[NR]) {
     const int nsb = cols >> 8;
     const int sb = step * 16 + (lane >> 2);
     if (sb >= nsb) return;
     const int g = lane & 3;
     const int c0 = (sb << 8) + (g << 6);
-    const float4* xp = reinterpret_cast<const float4*>(xl + xpad(c0));
-    const float xa = xs16[c0 >> 4] + xs16[(c0 >> 4) + 1];
-    const float xb = xs16[(c0 >> 4) + 2] + xs16[(c0 >> 4) + 3];
-    float slo[NR], shi[NR];
+    const uint32_t m0f = vreg(0x0F0F0F0Fu);
+    int da[NR][XL], db[NR][XL];
+    zero_limbs(da);
+    zero_limbs(db);
+    // run h of 16 columns at c0 + 16 h: low nibbles of qa (h = 0) and qb (h = 1) belong to
+    // sub-block 2g, high nibbles of qa (h = 2) and qb (h = 3) to sub-block 2g + 1
 #pragma unroll
-    for (int k = 0; k < NR; ++k) slo[k] = shi[k] = 0.f;
-    const uint32_t mlo = vreg(NIB_LO), mhi = vreg(NIB_HI), m1024 = vreg(F16_1024);
+    for (int h = 0; h < 4; ++h) {
+      const XRun x = x_run(xs, c0 + 16 * h);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // nibble bytes 4i..4i+3: low nibbles -> columns c0+4i.., high nibbles -> c0+32+4i..
-      const float4 xv = xp[i], xw = xp[8 + i];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const uint32_t v = (i < 4) ? raw[k].qa[i & 3] : raw[k].qb[i & 3];
-        const uint32_t u = v >> 8;
-        const uint32_t p0 = and_or(v, mlo, m1024), p1 = and_or(v, mhi, m1024);
-        const uint32_t p2 = and_or(u, mlo, m1024), p3 = and_or(u, mhi, m1024);
-        slo[k] += lo_h(p0) * xv.x;
-        slo[k] += lo_h(p2) * xv.y;
-        slo[k] += hi_h(p0) * xv.z;
-        slo[k] += hi_h(p2) * xv.w;
-        shi[k] += lo_h(p1) * xw.x;
-        shi[k] += lo_h(p3) * xw.y;
-        shi[k] += hi_h(p1) * xw.z;
-        shi[k] += hi_h(p3) * xw.w;
-      }
-      // keep each chunk's LDS reads next to their use: hoisting all of them costs 64 VGPRs
+        for (int k = 0; k < NR; ++k) {
+          const uint32_t v = (h & 1) ? raw[k].qb[i] : raw[k].qa[i];
+          if (h < 2)
+            dot_limbs(v & m0f, x, i, da[k]);
+          else
+            dot_limbs((v >> 4) & m0f, x, i, db[k]);
+        }
+      // keep each run's LDS reads next to their use
       __builtin_amdgcn_sched_barrier(0);
     }
-    // 6-bit scale/min of sub-blocks 2g and 2g+1 from the scale words Y (bytes 4..7), Z (8..11),
-    // W (12..15).  Sub-blocks 0..3: scale = bits of Y, min = bits of Z, at byte 2(g&1) (and +1).
-    // Sub-blocks 4..7: low four bits in W (scale: low nibble, min: high nibble), top two bits
-    // in bits 6..7 of the same bytes of Y (scale) and Z (min).  All lane-constant field
-    // positions, so each field is one or two bit-field extracts (width 0 extracts 0).
+    const float sA = xs.sc[c0 >> 5], sB = xs.sc[(c0 >> 5) + 1];
+    const float xa = xs.s16[c0 >> 4] + xs.s16[(c0 >> 4) + 1];
+    const float xb = xs.s16[(c0 >> 4) + 2] + xs.s16[(c0 >> 4) + 3];
+    // 6-bit scales and mins of sub-blocks 2g, 2g+1 gathered as the bytes [sc_a, sc_b, m_a, m_b]
+    // from the scale words Y (bytes 4..7), Z (8..11), W (12..15), p = 2 (g & 1):
+    //  sub-blocks 0..3: scale = bits 0..5 of Y byte p (+1), min = bits 0..5 of Z byte p (+1);
+    //  sub-blocks 4..7: low four bits from W byte p (+1) (scale: low nibble, min: high
+    //  nibble), top two bits from bits 6..7 of Y (scale) and Z (min) byte p (+1).
+    const uint32_t p = 2u * (uint32_t)(g & 1);
+    const uint32_t sel = p | ((p + 1) << 8) | ((p + 4) << 16) | ((p + 5) << 24);  // [Y p, Y p+1, Z p, Z p+1]
     const bool upper = g >= 2;
-    const uint32_t o = 16u * (uint32_t)(g & 1);
-    const uint32_t wl = upper ? 4u : 6u, wh = upper ? 2u : 0u, om = upper ? o + 4u : o;
+    const uint32_t mlow = vreg(upper ? 0x0F0F0F0Fu : 0x3F3F3F3Fu), mtop = vreg(upper ? 0x30303030u : 0u);
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const uint32_t Y = raw[k].hd.y, Z = raw[k].hd.z, W = raw[k].hd.w;
-      const uint32_t srcS = upper ? W : Y, srcM = upper ? W : Z;
-      const uint32_t sca = __builtin_amdgcn_ubfe(srcS, o, wl) | (__builtin_amdgcn_ubfe(Y, o + 6u, wh) << 4);
-      const uint32_t scb = __builtin_amdgcn_ubfe(srcS, o + 8u, wl) | (__builtin_amdgcn_ubfe(Y, o + 14u, wh) << 4);
-      const uint32_t ma = __builtin_amdgcn_ubfe(srcM, om, wl) | (__builtin_amdgcn_ubfe(Z, o + 6u, wh) << 4);
-      const uint32_t mb = __builtin_amdgcn_ubfe(srcM, om + 8u, wl) | (__builtin_amdgcn_ubfe(Z, o + 14u, wh) << 4);
+      const uint32_t yz = __builtin_amdgcn_perm(Z, Y, sel);
+      const uint32_t lo = upper ? __builtin_amdgcn_perm(W >> 4, W, sel) : yz;  // [W p, W p+1, W p>>4, W p+1>>4]
+      const uint32_t sm = and_or(yz >> 2, mtop, lo & mlow);
       const float d = h2f(raw[k].hd.x), dmin = h2f(raw[k].hd.x >> 16);
-      // slo = sum (1024 + q) x over sub-block 2g, shi = sum (1024 + 16 q) x over 2g+1
-      const float A = slo[k] - 1024.f * xa;
-      const float B = shi[k] - 1024.f * xb;
-      acc[k] += (d * (float)sca) * A;
-      acc[k] += (d * 0.0625f * (float)scb) * B;
-      acc[k] -= dmin * ((float)ma * xa + (float)mb * xb);
+      acc[k] += (d * sA * ub0(sm)) * limb_sum(da[k]);
+      acc[k] += (d * sB * ub1(sm)) * limb_sum(db[k]);
+      acc[k] -= dmin * (ub2(sm) * xa + ub3(sm) * xb);
     }
   }
 };
@@ -328,8 +407,8 @@ struct Q4_KF {
 // bytes), the 16 high-bit bytes at 128 + 32h + 16half, and the scale group at 192 + 8h.
 // Its 32 weights are runs t = tp and t = tp + 2 of 16: column 256sb + 128h + 32t + 16half + l,
 // low nibble (t < 2) or high nibble (t >= 2) of low-nibble byte l, top bits 2t..2t+1 of
-// high-bit byte l, scale byte 2t + half of the group.  w = d s (q - 32), summed per run as
-// d s (sum q x - 32 sum x).  Even and odd superblocks go in separate steps (210 = 2 mod 4).
+// high-bit byte l, scale byte 2t + half of the group.  w = d sc (q - 32), summed per run as
+// d sc (s sum q x~ - 32 sum x).  Even and odd superblocks go in separate steps (210 = 2 mod 4).
 struct Q6_KF {
   struct Raw {
     uint32_t l[5], h[5], s[3];
@@ -361,42 +440,34 @@ struct Q6_KF {
     const u32x4 a = wld16(B + oL), c = wld16(B + oH);
     r.l[0] = a.x; r.l[1] = a.y; r.l[2] = a.z; r.l[3] = a.w;
     r.h[0] = c.x; r.h[1] = c.y; r.h[2] = c.z; r.h[3] = c.w;
-    const u32x2 sv = ld8(B + oS);
+    const u32x2 sv = wld8(B + oS);
     r.s[0] = sv.x; r.s[1] = sv.y;
-    if (r.ph != 0) {
-      // the 2-byte phase needs one more dword past each piece (still inside the superblock)
-      r.l[4] = wld4(B + oL + 16);
-      r.h[4] = wld4(B + oH + 16);
-      r.s[2] = wld4(B + oS + 8);
-    } else {
-      r.l[4] = r.h[4] = r.s[2] = 0;
-    }
+    // the 2-byte phase needs one more dword past each piece (inside the superblock); the
+    // loads are issued at either phase so that the count in flight is static (at phase 0
+    // the scale dword re-reads an earlier one: bytes 208..211 would run past the block)
+    r.l[4] = wld4(B + oL + 16);
+    r.h[4] = wld4(B + oH + 16);
+    r.s[2] = wld4(B + oS + (r.ph ? 8 : 4));
     r.d = wld2(A + 208);
     return r;
   }
   template <int NR>
-  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane,
-                                             const float* __restrict__ xl, const float* __restrict__ xs16,
+  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane, const XLimbs& xs,
                                              float (&acc)[NR]) {
     bool ok;
     const int sb = sb_of(cols, step, lane, ok);
     if (!ok) return;
     const int e = lane & 7, hh = e >> 2, tp = (e >> 1) & 1, half = e & 1;
     const int c1 = (sb << 8) + 128 * hh + 32 * tp + 16 * half;  // run t = tp; run tp + 2 is 64 columns on
-    const float4* xp0 = reinterpret_cast<const float4*>(xl + xpad(c1));
-    const float4* xp1 = reinterpret_cast<const float4*>(xl + xpad(c1 + 64));
-    const float xs0 = xs16[c1 >> 4], xs1 = xs16[(c1 >> 4) + 4];
     const uint32_t m0f = vreg(0x0F0F0F0Fu), m30 = vreg(0x30303030u);
     const uint32_t sh0 = 4u - 2u * (uint32_t)tp;  // top bits of run tp   -> bits 4..5 (left shift)
     const uint32_t sh1 = 2u * (uint32_t)tp;       // top bits of run tp+2 -> bits 4..5 (right shift)
-    float s0[NR], s1[NR];
+    // four 6-bit codes per dword, one per byte: cA of run tp, cB of run tp + 2
+    uint32_t cA[NR][4], cB[NR][4];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) s0[k] = s1[k] = 0.f;
+    for (int k = 0; k < NR; ++k)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 xv = xp0[i], xw = xp1[i];
-#pragma unroll
-      for (int k = 0; k < NR; ++k) {
+      for (int i = 0; i < 4; ++i) {
         uint32_t L, H;
         if (raw[k].ph == 0) {
           L = raw[k].l[i];
@@ -405,24 +476,14 @@ struct Q6_KF {
           L = __builtin_amdgcn_alignbyte(raw[k].l[i + 1], raw[k].l[i], 2);
           H = __builtin_amdgcn_alignbyte(raw[k].h[i + 1], raw[k].h[i], 2);
         }
-        // four 6-bit codes of each run, one per byte, then fp16 pairs 1024 + code
-        const uint32_t c0 = and_or(H << sh0, m30, L & m0f);
-        const uint32_t c1v = and_or(H >> sh1, m30, (L >> 4) & m0f);
-        const uint32_t p0 = __builtin_amdgcn_perm(F16_1024, c0, PERM_B02);
-        const uint32_t p1 = __builtin_amdgcn_perm(F16_1024, c0, PERM_B13);
-        const uint32_t p2 = __builtin_amdgcn_perm(F16_1024, c1v, PERM_B02);
-        const uint32_t p3 = __builtin_amdgcn_perm(F16_1024, c1v, PERM_B13);
-        s0[k] += lo_h(p0) * xv.x;
-        s0[k] += lo_h(p1) * xv.y;
-        s0[k] += hi_h(p0) * xv.z;
-        s0[k] += hi_h(p1) * xv.w;
-        s1[k] += lo_h(p2) * xw.x;
-        s1[k] += lo_h(p3) * xw.y;
-        s1[k] += hi_h(p2) * xw.z;
-        s1[k] += hi_h(p3) * xw.w;
+        cA[k][i] = and_or(H << sh0, m30, L & m0f);
+        cB[k][i] = and_or(H >> sh1, m30, (L >> 4) & m0f);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    float tA[NR], tB[NR];
+    run_dot(xs, c1, cA, tA);
+    run_dot(xs, c1 + 64, cB, tB);
+    const float s0 = xs.sc[c1 >> 5], s1 = xs.sc[(c1 + 64) >> 5];
+    const float xs0 = xs.s16[c1 >> 4], xs1 = xs.s16[(c1 >> 4) + 4];
     const uint32_t sb8 = 8u * (uint32_t)(2 * tp + half);  // byte of the scale in each scale dword
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
@@ -436,14 +497,20 @@ struct Q6_KF {
       }
       const float sc0 = (float)(int8_t)((S0 >> sb8) & 0xFFu);  // run tp
       const float sc1 = (float)(int8_t)((S1 >> sb8) & 0xFFu);  // run tp + 2
-      // s = sum (1024 + q) x = sum (q - 32) x + 1056 sum x
-      const float tot = sc0 * (s0[k] - 1056.f * xs0) + sc1 * (s1[k] - 1056.f * xs1);
+      const float tot = sc0 * (s0 * tA[k] - 32.f * xs0) + sc1 * (s1 * tB[k] - 32.f * xs1);
       acc[k] += h2f(raw[k].d) * tot;
     }
   }
 };
 
 // ------------------------------------------------------------------ kernel
+
+// Rows per work item and items in flight per wave on the register path: the gate/up pair
+// carries two rows already; the q/k/v launch needs RoPE pairs (2 rows) in one item.
+template <int EPI>
+constexpr int GEMV_DEPTH = EPI == EPI_QKV ? 2 : EPI == EPI_SWIGLU ? NT_GEMV_DEPTH_PAIR : NT_GEMV_DEPTH;
+template <int EPI>
+constexpr int GEMV_ROWS = (EPI == EPI_SWIGLU) ? 1 : (EPI == EPI_QKV) ? 2 : NT_GEMV_ROWS;
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -455,9 +522,34 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// Stage x (optionally RMS-normalised) into LDS and the sums of every 16 columns.
-// Every thread of the workgroup calls this exactly once.
-__device__ __forceinline__ void stage_x(const GemvArgs& a, float* xl, float* xs16, float* red) {
+// Power-of-two staging scale of a 32-column block whose largest |x| has the bit pattern mb
+// (of a non-negative float, NaN included): the smallest s = 2^e with max |x| / s <= 127.
+// Returns su = s / 256^(XL-1) (the stored scale) and k = 1 / su, which maps x to its
+// fixed-point value X.  e is kept >= -100, so both stay normal numbers.  A block holding a
+// NaN or an infinity gets scale NaN, so the rows it meets come out NaN.
+__device__ __forceinline__ void limb_scale(uint32_t mb, float& su, float& k) {
+  int E = (int)(mb >> 23) - 127;  // exponent of max |x| (-127 for 0 and subnormals)
+  E = E < -100 ? -100 : E;
+  int e = E - 6;                  // max |x| / 2^(E-6) lies in [64, 128)
+  if (__uint_as_float(mb) * __uint_as_float((uint32_t)(127 - e) << 23) > 127.f) ++e;
+  constexpr int FB = 8 * (XL - 1);
+  su = mb >= 0x7F800000u ? __uint_as_float(0x7FC00000u) : __uint_as_float((uint32_t)(127 + e - FB) << 23);
+  k = __uint_as_float((uint32_t)(127 + FB - e) << 23);
+}
+
+// bytes 0 of a, b, c, d -> one dword, a in the lowest byte
+__device__ __forceinline__ uint32_t pack_b0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u), hi = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Stage x (optionally RMS-normalised) into LDS: XL limb planes, the scale of every 32
+// columns and the fp32 sum of every 16.  Every thread of the workgroup calls this exactly
+// once.  A thread takes 16 columns; threads 2t and 2t+1 (one DPP quad pair) share a scale.
+// Digits of X: the last limb is the low byte of X, the middle one (three limbs) the low
+// byte of (X + 128) >> 8, the first (X + 128 (+ 32768)) >> 8 (XL - 1): each digit is the
+// signed byte that leaves the rest divisible by 256.
+__device__ __forceinline__ void stage_x(const GemvArgs& a, const XLimbs& xs, float* red) {
   const int cols = a.cols;
   float scale = 1.f;
   if (a.gain) {
@@ -469,26 +561,58 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, float* xl, float* xs1
     ss = block_sum(ss, red);
     scale = 1.0f / sqrtf(ss / (float)cols + a.eps);
   }
+  // cols / 16 is even and the block size a multiple of 64, so both threads of a pair run
+  // the same iterations
   for (int gi = threadIdx.x; gi < (cols >> 4); gi += blockDim.x) {
     const float4* src = reinterpret_cast<const float4*>(a.x + gi * 16);
-    float4 v[4] = {src[0], src[1], src[2], src[3]};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 t = src[i];
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
     if (a.gain) {
       const float4* gp = reinterpret_cast<const float4*>(a.gain + gi * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 gg = gp[i];
-        v[i].x = v[i].x * scale * gg.x; v[i].y = v[i].y * scale * gg.y;
-        v[i].z = v[i].z * scale * gg.z; v[i].w = v[i].w * scale * gg.w;
+        v[4 * i] = v[4 * i] * scale * gg.x; v[4 * i + 1] = v[4 * i + 1] * scale * gg.y;
+        v[4 * i + 2] = v[4 * i + 2] * scale * gg.z; v[4 * i + 3] = v[4 * i + 3] * scale * gg.w;
       }
     }
-    float4* dst = reinterpret_cast<float4*>(xl + xpad(gi * 16));
-    float s = 0.f;
+    float sum = 0.f;
+    uint32_t mb = 0;  // max of |x| as bit patterns: a NaN orders above every number
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      sum += v[i] + v[i + 1];
+      mb = max(mb, max(__float_as_uint(v[i]) & 0x7FFFFFFFu, __float_as_uint(v[i + 1]) & 0x7FFFFFFFu));
+    }
+    xs.s16[gi] = sum;
+    mb = max(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, true));  // the pair's 32 columns
+    float s, k;
+    limb_scale(mb, s, k);
+    if ((gi & 1) == 0) xs.sc[gi >> 1] = s;
+    uint32_t w[XL][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dst[i] = v[i];
-      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+      uint32_t b[XL][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int X = (int)rintf(v[4 * i + j] * k);
+        b[XL - 1][j] = (uint32_t)X;
+        if constexpr (XL == 3) {
+          b[1][j] = (uint32_t)((X + 128) >> 8);
+          b[0][j] = (uint32_t)((X + 32896) >> 16);
+        } else {
+          b[0][j] = (uint32_t)((X + 128) >> 8);
+        }
+      }
+#pragma unroll
+      for (int l = 0; l < XL; ++l) w[l][i] = pack_b0(b[l][0], b[l][1], b[l][2], b[l][3]);
     }
-    xs16[gi] = s;
+#pragma unroll
+    for (int l = 0; l < XL; ++l)
+      *reinterpret_cast<u32x4a16*>(xs.q + l * xs.plane + xq_off(gi * 16)) = u32x4a16{w[l][0], w[l][1], w[l][2], w[l][3]};
   }
   __syncthreads();
 }
@@ -599,75 +723,77 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int s, const GemvSeg
 // step) are in flight while the current step computes.  For the first segment the wave
 // issues its first loads before the workgroup stages x, so that both latencies overlap;
 // every wave takes part in the staging.
-template <typename F, int R, int EPI>
-__device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, int wid, int W, float* xl,
-                                            float* xs16, float* red, unsigned long long& best, const float2* rope) {
+// DEPTH - 1 items in flight ahead of the one computed, in a ring of DEPTH register buffers
+// (unrolled over the ring, so that no buffer is copied).
+template <typename F, int R, int EPI, int DEPTH>
+__device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, int wid, int W, const XLimbs& xs,
+                                            float* red, unsigned long long& best, const float2* rope) {
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * R : R;
+  typedef typename F::Raw Raw;
   const GemvSeg sg = a.seg[s];
   const int n_groups = (sg.rows + R - 1) / R;
-  int k = (wid - sg.grp0) % W;
-  if (k < 0) k += W;
-  const bool any = k < n_groups;
+  int k0 = (wid - sg.grp0) % W;
+  if (k0 < 0) k0 += W;
   const int nsteps = F::steps(a.cols);
+  // this wave's work items, in order: (group k0 + i W, step t) for i = 0, 1, ... and t = 0..nsteps-1
+  const int n_items = (k0 < n_groups) ? ((n_groups - 1 - k0) / W + 1) * nsteps : 0;
 
-  const uint8_t* rp[NR];
-  int row0 = k * R;
+  // load cursor: the item whose blocks are loaded next (DEPTH - 1 items ahead of the one computed)
+  int lk = k0, lt = 0;
+  auto issue = [&](Raw (&buf)[NR]) {
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int r = min(row0 + j, sg.rows - 1);  // past-the-end rows re-read the last row; results dropped
-    rp[j] = sg.w + (size_t)r * sg.row_bytes;
-    if constexpr (EPI == EPI_SWIGLU) rp[R + j] = a.seg[1].w + (size_t)r * sg.row_bytes;
+    for (int j = 0; j < R; ++j) {
+      const int r = min(lk * R + j, sg.rows - 1);  // past-the-end rows re-read the last row; results dropped
+      buf[j] = F::load(sg.w + (size_t)r * sg.row_bytes, a.cols, lt, lane);
+      if constexpr (EPI == EPI_SWIGLU) buf[R + j] = F::load(a.seg[1].w + (size_t)r * sg.row_bytes, a.cols, lt, lane);
+    }
+    if (++lt == nsteps) {
+      lt = 0;
+      lk += W;
+    }
+  };
+  Raw b0[NR], b1[NR], b2[NR];
+  if (n_items > 0) {
+    issue(b0);
+    if (DEPTH == 3) issue(b1);
   }
-  typename F::Raw cur[NR], nxt[NR];
-  if (any) {
-#pragma unroll
-    for (int j = 0; j < NR; ++j) cur[j] = F::load(rp[j], a.cols, 0, lane);
-  }
-  if (s == 0) stage_x(a, xl, xs16, red);
-  if (!any) return;
+  if (s == 0) stage_x(a, xs, red);
+  if (n_items == 0) return;
   float acc[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = 0.f;
-  int step = 0;
-  for (;;) {
-    // the next work item: the next step of these rows, or step 0 of the next group
-    int nstep = step + 1, nk = k, nrow0 = row0;
-    const uint8_t* nrp[NR];
-#pragma unroll
-    for (int j = 0; j < NR; ++j) nrp[j] = rp[j];
-    if (nstep == nsteps) {
-      nstep = 0;
-      nk = k + W;
-      nrow0 = nk * R;
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        const int r = min(nrow0 + j, sg.rows - 1);
-        nrp[j] = sg.w + (size_t)r * sg.row_bytes;
-        if constexpr (EPI == EPI_SWIGLU) nrp[R + j] = a.seg[1].w + (size_t)r * sg.row_bytes;
-      }
-    }
-    const bool more = nk < n_groups;
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < NR; ++j) nxt[j] = F::load(nrp[j], a.cols, nstep, lane);
-    }
-    F::template fma<NR>(cur, a.cols, step, lane, xl, xs16, acc);
-    if (step == nsteps - 1) {
+  int ck = k0, ct = 0, item = 0;  // compute cursor
+  // compute the item in `cur` while the DEPTH - 1 after it are in flight; refill the buffer
+  // that the previous item used
+  auto step = [&](const Raw (&cur)[NR], Raw (&refill)[NR]) -> bool {
+    // unconditional (past the last item the loads re-read clamped rows), so that the count
+    // of loads in flight is static and the wait for this item leaves the later ones in flight
+    issue(refill);
+    F::template fma<NR>(cur, a.cols, ct, lane, xs, acc);
+    if (ct == nsteps - 1) {
 #pragma unroll
       for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
-      epilogue<R, EPI>(a, s, sg, row0, lane, acc, best, rope);
+      epilogue<R, EPI>(a, s, sg, ck * R, lane, acc, best, rope);
 #pragma unroll
       for (int j = 0; j < NR; ++j) acc[j] = 0.f;
     }
-    if (!more) break;
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      cur[j] = nxt[j];
-      rp[j] = nrp[j];
+    if (++ct == nsteps) {
+      ct = 0;
+      ck += W;
     }
-    row0 = nrow0;
-    k = nk;
-    step = nstep;
+    return ++item < n_items;
+  };
+  if constexpr (DEPTH == 3) {
+    for (;;) {
+      if (!step(b0, b2)) break;
+      if (!step(b1, b0)) break;
+      if (!step(b2, b1)) break;
+    }
+  } else {
+    for (;;) {
+      if (!step(b0, b1)) break;
+      if (!step(b1, b0)) break;
+    }
   }
 }
 
@@ -675,9 +801,12 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
 template <int FMTMASK, int R, int NW, int EPI>
 __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   extern __shared__ float4 smem4[];
-  float* xl = reinterpret_cast<float*>(smem4);
-  float* xs16 = xl + xpad_len(a.cols);
-  float* red = xs16 + (a.cols >> 4);
+  XLimbs xs;
+  xs.q = reinterpret_cast<uint8_t*>(smem4);
+  xs.plane = xq_plane(a.cols);
+  xs.sc = reinterpret_cast<float*>(xs.q + XL * xs.plane);
+  xs.s16 = xs.sc + (a.cols >> 5);
+  float* red = xs.s16 + (a.cols >> 4);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wid = (int)blockIdx.x * NW + wave;
@@ -692,16 +821,16 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   for (int s = 0; s < nseg; ++s) {
     switch (a.seg[s].fmt) {
       case FMT_Q8_0:
-        if constexpr ((FMTMASK >> FMT_Q8_0) & 1) run_segment<Q8_0F, R, EPI>(a, s, lane, wid, W, xl, xs16, red, best, rope);
+        if constexpr ((FMTMASK >> FMT_Q8_0) & 1) run_segment<Q8_0F, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
         break;
       case FMT_Q4_0:
-        if constexpr ((FMTMASK >> FMT_Q4_0) & 1) run_segment<Q4_0F, R, EPI>(a, s, lane, wid, W, xl, xs16, red, best, rope);
+        if constexpr ((FMTMASK >> FMT_Q4_0) & 1) run_segment<Q4_0F, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
         break;
       case FMT_Q4_K:
-        if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI>(a, s, lane, wid, W, xl, xs16, red, best, rope);
+        if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
         break;
       default:
-        if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI>(a, s, lane, wid, W, xl, xs16, red, best, rope);
+        if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
         break;
     }
   }
@@ -745,7 +874,6 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 __device__ __forceinline__ uint32_t lds4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
-typedef uint32_t u32x4a16 __attribute__((ext_vector_type(4), aligned(16)));
 __device__ __forceinline__ u32x4 lds16a(const uint8_t* p) {
   const u32x4a16 v = *reinterpret_cast<const u32x4a16*>(p);
   return u32x4{v.x, v.y, v.z, v.w};
@@ -1195,11 +1323,14 @@ static int num_cu() {
   return n_cu;
 }
 
-static size_t lds_for(int cols) { return sizeof(float) * (size_t)(xpad_len(cols) + (cols >> 4) + 16); }
+// limb planes, scales per 32 columns, sums per 16 columns, 16 floats of reduction space
+static size_t lds_for(int cols) {
+  return (size_t)XL * xq_plane(cols) + sizeof(float) * (size_t)((cols >> 5) + (cols >> 4) + 16);
+}
 
 GemvPlan gemv_plan(int epi, int cols) {
   GemvPlan p;
-  p.rows_per_wave = (epi == EPI_SWIGLU) ? 1 : 2;  // the paired gate/up launch already carries two rows
+  p.rows_per_wave = (epi == EPI_SWIGLU) ? 1 : (epi == EPI_QKV) ? 2 : NT_GEMV_ROWS;
   p.lds_bytes = lds_for(cols);
   // one copy of x per workgroup: when only one fits in a CU's LDS, make it 16 waves
   p.waves = p.lds_bytes > 80 * 1024 ? 16 : 8;
@@ -1210,7 +1341,7 @@ int gemv_groups(const GemvPlan& p, int rows) { return (rows + p.rows_per_wave - 
 
 template <int FMTMASK, int NW, int EPI>
 static hipError_t launch_one(const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s) {
-  constexpr int R = (EPI == EPI_SWIGLU) ? 1 : 2;
+  constexpr int R = GEMV_ROWS<EPI>;
   auto kern = gemv_kernel<FMTMASK, R, NW, EPI>;
   // resident workgroups per CU at this LDS size, cached per instantiation
   static int per_cu = 0;
