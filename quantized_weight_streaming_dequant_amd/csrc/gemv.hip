@@ -27,10 +27,7 @@ namespace nt {
 
 // ------------------------------------------------------------------ helpers
 
-constexpr uint32_t F16_1024 = 0x64006400u;  // two fp16 1024.0: OR a small integer into the mantissa
 
-__device__ __forceinline__ float lo_h(uint32_t v) { return __half2float(__ushort_as_half((unsigned short)(v & 0xFFFFu))); }
-__device__ __forceinline__ float hi_h(uint32_t v) { return __half2float(__ushort_as_half((unsigned short)(v >> 16))); }
 
 // Launch-geometry and load-policy defaults (overridable at build time).
 #ifndef NT_GEMV_WG_PER_CU_MAX
@@ -81,12 +78,6 @@ __device__ __forceinline__ uint32_t vreg(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
 }
-
-// Nibble-to-fp16 masks: low nibbles of bytes 0 and 2, high nibbles of bytes 0 and 2.
-constexpr uint32_t NIB_LO = 0x000F000Fu, NIB_HI = 0x00F000F0u;
-// v_perm_b32 selectors: result bytes {src1.b0, src0.b1, src1.b2, src0.b3} (resp. b1, b3 of
-// src1); selector values 0-3 pick src1 bytes, 4-7 src0 bytes
-constexpr uint32_t PERM_B02 = 0x07020500u, PERM_B13 = 0x07030501u;
 
 // ------------------------------------------------------------------ activations as limbs
 //
@@ -543,12 +534,31 @@ __device__ __forceinline__ uint32_t pack_b0(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
+// The limb digits of four consecutive columns v[0..3] (k from limb_scale): dword i of each
+// limb plane l of w.  The last limb is the low byte of X, the middle one (three limbs) the
+// low byte of (X + 128) >> 8, the first (X + 128 (+ 32768)) >> 8 (XL - 1): each digit is
+// the signed byte that leaves the rest divisible by 256.
+template <int N>
+__device__ __forceinline__ void limb_digits(const float* v, float k, uint32_t (&w)[XL][N], int i) {
+  uint32_t b[XL][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int X = (int)rintf(v[j] * k);
+    b[XL - 1][j] = (uint32_t)X;
+    if constexpr (XL == 3) {
+      b[1][j] = (uint32_t)((X + 128) >> 8);
+      b[0][j] = (uint32_t)((X + 32896) >> 16);
+    } else {
+      b[0][j] = (uint32_t)((X + 128) >> 8);
+    }
+  }
+#pragma unroll
+  for (int l = 0; l < XL; ++l) w[l][i] = pack_b0(b[l][0], b[l][1], b[l][2], b[l][3]);
+}
+
 // Stage x (optionally RMS-normalised) into LDS: XL limb planes, the scale of every 32
 // columns and the fp32 sum of every 16.  Every thread of the workgroup calls this exactly
 // once.  A thread takes 16 columns; threads 2t and 2t+1 (one DPP quad pair) share a scale.
-// Digits of X: the last limb is the low byte of X, the middle one (three limbs) the low
-// byte of (X + 128) >> 8, the first (X + 128 (+ 32768)) >> 8 (XL - 1): each digit is the
-// signed byte that leaves the rest divisible by 256.
 __device__ __forceinline__ void stage_x(const GemvArgs& a, const XLimbs& xs, float* red) {
   const int cols = a.cols;
   float scale = 1.f;
@@ -594,22 +604,7 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, const XLimbs& xs, flo
     if ((gi & 1) == 0) xs.sc[gi >> 1] = s;
     uint32_t w[XL][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t b[XL][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int X = (int)rintf(v[4 * i + j] * k);
-        b[XL - 1][j] = (uint32_t)X;
-        if constexpr (XL == 3) {
-          b[1][j] = (uint32_t)((X + 128) >> 8);
-          b[0][j] = (uint32_t)((X + 32896) >> 16);
-        } else {
-          b[0][j] = (uint32_t)((X + 128) >> 8);
-        }
-      }
-#pragma unroll
-      for (int l = 0; l < XL; ++l) w[l][i] = pack_b0(b[l][0], b[l][1], b[l][2], b[l][3]);
-    }
+    for (int i = 0; i < 4; ++i) limb_digits(&v[4 * i], k, w, i);
 #pragma unroll
     for (int l = 0; l < XL; ++l)
       *reinterpret_cast<u32x4a16*>(xs.q + l * xs.plane + xq_off(gi * 16)) = u32x4a16{w[l][0], w[l][1], w[l][2], w[l][3]};
@@ -889,69 +884,23 @@ __device__ __forceinline__ void lds_run(const uint8_t* p, uint32_t phase, uint32
   for (int k = 0; k < N; ++k) o[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], phase);
 }
 
-// Q4_K lane part: quarter g of superblock s: nibble bytes 32g..32g+31 at 16 + 32g; low
-// nibbles are sub-block 2g (x[0..31]), high nibbles sub-block 2g+1 (x[32..63]).
-struct Q4K_S {
-  static constexpr int FMT = FMT_Q4_K, BB = 144, K = 1;
-  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[64], const float (&xs)[4]) {
-    const int s = lane >> 2, g = lane & 3;
-    const uint8_t* p = slot + s * 144;
-    const u32x4 hd = lds16a(p);
-    const u32x4 qa = lds16a(p + 16 + 32 * g), qb = lds16a(p + 32 + 32 * g);
-    const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-    const uint32_t mlo = vreg(NIB_LO), mhi = vreg(NIB_HI), m1024 = vreg(F16_1024);
-    float slo0 = 0.f, slo1 = 0.f, shi0 = 0.f, shi1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t v = q[i], u = v >> 8;
-      const uint32_t p0 = and_or(v, mlo, m1024), p1 = and_or(v, mhi, m1024);
-      const uint32_t p2 = and_or(u, mlo, m1024), p3 = and_or(u, mhi, m1024);
-      slo0 += lo_h(p0) * x[4 * i];
-      slo1 += lo_h(p2) * x[4 * i + 1];
-      slo0 += hi_h(p0) * x[4 * i + 2];
-      slo1 += hi_h(p2) * x[4 * i + 3];
-      shi0 += lo_h(p1) * x[32 + 4 * i];
-      shi1 += lo_h(p3) * x[33 + 4 * i];
-      shi0 += hi_h(p1) * x[34 + 4 * i];
-      shi1 += hi_h(p3) * x[35 + 4 * i];
-    }
-    // scale and min of sub-blocks 2g, 2g+1 (field positions as in the register path)
-    const bool upper = g >= 2;
-    const uint32_t o = 16u * (uint32_t)(g & 1);
-    const uint32_t wl = upper ? 4u : 6u, wh = upper ? 2u : 0u, om = upper ? o + 4u : o;
-    const uint32_t Y = hd.y, Z = hd.z, W = hd.w;
-    const uint32_t srcS = upper ? W : Y, srcM = upper ? W : Z;
-    const uint32_t sca = __builtin_amdgcn_ubfe(srcS, o, wl) | (__builtin_amdgcn_ubfe(Y, o + 6u, wh) << 4);
-    const uint32_t scb = __builtin_amdgcn_ubfe(srcS, o + 8u, wl) | (__builtin_amdgcn_ubfe(Y, o + 14u, wh) << 4);
-    const uint32_t ma = __builtin_amdgcn_ubfe(srcM, om, wl) | (__builtin_amdgcn_ubfe(Z, o + 6u, wh) << 4);
-    const uint32_t mb = __builtin_amdgcn_ubfe(srcM, om + 8u, wl) | (__builtin_amdgcn_ubfe(Z, o + 14u, wh) << 4);
-    const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
-    const float xa = xs[0] + xs[1], xb = xs[2] + xs[3];
-    const float A = (slo0 + slo1) - 1024.f * xa;  // sum q x over sub-block 2g
-    const float B = (shi0 + shi1) - 1024.f * xb;  // 16 sum q x over sub-block 2g+1
-    float r = (d * (float)sca) * A;
-    r += (d * 0.0625f * (float)scb) * B;
-    r -= dmin * ((float)ma * xa + (float)mb * xb);
-    return r;
-  }
-};
+// The streamed lane parts take the lane's x as XL limb planes of XN / 4 dwords (xq), the
+// stored scale of each of its 32-column blocks (xsc) and the fp32 sums of each 16 columns
+// (xs), as staged by limb_digits / limb_scale.
 
 // Q6_K lane part: quarter g = 2n + hi of superblock s: columns 128n + 64hi + l (l < 64).
 // Column 128n + 64hi + l for l < 32 takes the low (hi = 0) or high (hi = 1) nibble of
 // low-bit byte 64n + l and bits 4hi..4hi+1 of high-bit byte 32n + l; for l >= 32 the
 // nibble of byte 64n + l and bits 4hi+2..4hi+3 of high-bit byte 32n + l - 32.  Scale of
-// columns 16j.. of the quarter: int8 at 192 + 8n + 4hi + j (j = 0..3); w = d s (q - 32).
-// The 6-bit code goes into an fp16 1024 + m q, m = 1 (hi = 0: nibble at bits 0..3, top
-// bits at 4..5) or m = 16 (hi = 1: nibble left at bits 4..7, top bits moved to 8..9), so
-// neither half needs a nibble shift.  A superblock at an odd index sits 2 bytes past a
-// 4-byte boundary in the ring; its fields are realigned per lane.
+// columns 16j.. of the quarter: int8 at 192 + 8n + 4hi + j (j = 0..3); w = d sc (q - 32),
+// summed per 16 columns as d sc (s sum q x~ - 32 sum x).  The four codes of a dword are
+// the nibbles (shifted down by 4hi) with the top bits rotated into bits 4..5 of each byte.
+// A superblock at an odd index sits 2 bytes past a 4-byte boundary in the ring; its fields
+// are realigned per lane.
 struct Q6K_S {
   static constexpr int FMT = FMT_Q6_K, BB = 210, K = 1;
-  static __device__ __forceinline__ uint32_t keep(uint32_t v) {  // stop the and-or pairs from being refactored
-    asm("" : "+v"(v));
-    return v;
-  }
-  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[64], const float (&xs)[4]) {
+  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const uint32_t (&xq)[XL][16],
+                                              const float (&xsc)[2], const float (&xs)[4]) {
     const int s = lane >> 2, g = lane & 3, n = g >> 1, hi = g & 1;
     const uint8_t* p = slot + s * 210;
     const uint32_t ph = (uint32_t)(s & 1) * 2u;
@@ -959,92 +908,83 @@ struct Q6K_S {
     lds_run<8>(p + 128 + 32 * n, ph, H);
     lds_run<1>(p + 192 + 8 * n + 4 * hi, ph, S);
     lds_run<1>(p + 208, ph, D);
-    const uint32_t mnib = vreg(hi ? 0x00F000F0u : 0x000F000Fu);
-    const uint32_t mh = vreg(hi ? 0x03000300u : 0x00300030u);
-    const uint32_t m1024 = vreg(F16_1024);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // per 16 columns: sum (1024 + m q) x
-    // two halves of 32 columns: low-bit bytes 64n + 32 half + l, top bits of high-bit byte
-    // 32n + l at 4hi + 2 half
+    const uint32_t m0f = vreg(0x0F0F0F0Fu), m30 = vreg(0x30303030u);
+    const uint32_t sl = 4u * (uint32_t)hi;
+    int dg[4][XL];  // per 16 columns
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int l = 0; l < XL; ++l) dg[j][l] = 0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t L[8];
       lds_run<8>(p + 64 * n + 32 * half, ph, L);
+      const uint32_t rot = (sl + 2u * (uint32_t)half + 28u) & 31u;  // top bits 4hi + 2half -> bit 4
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const uint32_t la = L[k], h = H[k];
-        const uint32_t a02 = and_or(half ? h << 2 : h << 4, mh, keep(and_or(la, mnib, m1024)));
-        const uint32_t a13 = and_or(half ? h >> 6 : h >> 4, mh, keep(and_or(la >> 8, mnib, m1024)));
-        float& ca = acc[2 * half + (k >> 2)];
-        ca += lo_h(a02) * x[32 * half + 4 * k];
-        ca += lo_h(a13) * x[32 * half + 4 * k + 1];
-        ca += hi_h(a02) * x[32 * half + 4 * k + 2];
-        ca += hi_h(a13) * x[32 * half + 4 * k + 3];
+        const uint32_t code = and_or(__builtin_amdgcn_alignbit(H[k], H[k], rot), m30, (L[k] >> sl) & m0f);
+        int(&d)[XL] = dg[2 * half + (k >> 2)];
+#pragma unroll
+        for (int l = 0; l < XL; ++l) d[l] = sdot4(code, xq[l][8 * half + k], d[l]);
       }
     }
-    // sum (q - 32) x over group j = (acc_j - 1024 X_j) / m - 32 X_j
-    const float im = hi ? 0.0625f : 1.f;
-    const float d = h2f(D[0]);
     float r = 0.f;
-    r += (float)(int8_t)(S[0] & 0xFFu) * ((acc[0] - 1024.f * xs[0]) * im - 32.f * xs[0]);
-    r += (float)(int8_t)((S[0] >> 8) & 0xFFu) * ((acc[1] - 1024.f * xs[1]) * im - 32.f * xs[1]);
-    r += (float)(int8_t)((S[0] >> 16) & 0xFFu) * ((acc[2] - 1024.f * xs[2]) * im - 32.f * xs[2]);
-    r += (float)(int8_t)(S[0] >> 24) * ((acc[3] - 1024.f * xs[3]) * im - 32.f * xs[3]);
-    return d * r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sc = (float)(int8_t)((S[0] >> (8 * j)) & 0xFFu);
+      r += sc * (xsc[j >> 1] * limb_sum(dg[j]) - 32.f * xs[j]);
+    }
+    return h2f(D[0]) * r;
   }
 };
 
 // Q8_0 lane part: block l: fp16 d, then 32 int8 q; w = d q.
 struct Q80_S {
   static constexpr int FMT = FMT_Q8_0, BB = 34, K = 0;
-  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[32], const float (&xs)[2]) {
+  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const uint32_t (&xq)[XL][8],
+                                              const float (&xsc)[1], const float (&xs)[2]) {
     (void)xs;
     const uint8_t* p = slot + lane * 34;
     const uint32_t pd = (uint32_t)(lane & 1) * 2u;  // 34 lane mod 4
     uint32_t Q[8], D[1];
     lds_run<8>(p + 2, 2u - pd, Q);
     lds_run<1>(p, pd, D);
-    float a0 = 0.f, a1 = 0.f;
+    int d[XL];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t v = Q[k];
-      a0 += sb0(v) * x[4 * k];
-      a1 += sb1(v) * x[4 * k + 1];
-      a0 += sb2(v) * x[4 * k + 2];
-      a1 += sb3(v) * x[4 * k + 3];
-    }
-    return h2f(D[0]) * (a0 + a1);
+    for (int l = 0; l < XL; ++l) d[l] = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int l = 0; l < XL; ++l) d[l] = sdot4(Q[k], xq[l][k], d[l]);
+    return h2f(D[0]) * (xsc[0] * limb_sum(d));
   }
 };
 
 // Q4_0 lane part: block l: fp16 d, then 16 bytes; column i < 16 is the low nibble of
-// byte i, column 16 + i the high nibble; w = d (n - 8).
+// byte i, column 16 + i the high nibble; w = d (q - 8).
 struct Q40_S {
   static constexpr int FMT = FMT_Q4_0, BB = 18, K = 0;
-  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const float (&x)[32], const float (&xs)[2]) {
+  static __device__ __forceinline__ float dot(const uint8_t* slot, int lane, const uint32_t (&xq)[XL][8],
+                                              const float (&xsc)[1], const float (&xs)[2]) {
     const uint8_t* p = slot + lane * 18;
     const uint32_t pd = (uint32_t)(lane & 1) * 2u;  // 18 lane mod 4
     uint32_t Q[4], D[1];
     lds_run<4>(p + 2, 2u - pd, Q);
     lds_run<1>(p, pd, D);
-    const uint32_t mlo = vreg(NIB_LO), mhi = vreg(NIB_HI), m1024 = vreg(F16_1024);
-    float slo = 0.f, shi = 0.f;
+    const uint32_t m0f = vreg(0x0F0F0F0Fu);
+    int d[XL];
+#pragma unroll
+    for (int l = 0; l < XL; ++l) d[l] = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t v = Q[k], u = v >> 8;
-      const uint32_t p0 = and_or(v, mlo, m1024), p1 = and_or(v, mhi, m1024);
-      const uint32_t p2 = and_or(u, mlo, m1024), p3 = and_or(u, mhi, m1024);
-      slo += lo_h(p0) * x[4 * k];
-      slo += lo_h(p2) * x[4 * k + 1];
-      slo += hi_h(p0) * x[4 * k + 2];
-      slo += hi_h(p2) * x[4 * k + 3];
-      shi += lo_h(p1) * x[16 + 4 * k];
-      shi += lo_h(p3) * x[17 + 4 * k];
-      shi += hi_h(p1) * x[18 + 4 * k];
-      shi += hi_h(p3) * x[19 + 4 * k];
+      const uint32_t lo = Q[k] & m0f, hi = (Q[k] >> 4) & m0f;
+#pragma unroll
+      for (int l = 0; l < XL; ++l) {
+        d[l] = sdot4(lo, xq[l][k], d[l]);
+        d[l] = sdot4(hi, xq[l][4 + k], d[l]);
+      }
     }
-    // sum (n - 8) x = (slo - 1024 X0) + (shi - 1024 X1) / 16 - 8 (X0 + X1)
-    const float r = (slo - 1032.f * xs[0]) + (shi - 1024.f * xs[1]) * 0.0625f - 8.f * xs[1];
-    return h2f(D[0]) * r;
+    return h2f(D[0]) * (xsc[0] * limb_sum(d) - 8.f * (xs[0] + xs[1]));
   }
 };
 
@@ -1202,8 +1142,22 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
   for (int j = 0; j < XG; ++j) {
     float t = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t += x[16 * j + i];
+    for (int i = 0; i < 16; i += 2) t += x[16 * j + i] + x[16 * j + i + 1];
     xs[j] = t;
+  }
+  // the lane's columns are whole 32-column blocks: their limbs and scales, as staged for
+  // the register path
+  uint32_t xq[XL][XN / 4];
+  float xsc[XN / 32];
+#pragma unroll
+  for (int b = 0; b < XN / 32; ++b) {
+    uint32_t mb = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mb = max(mb, __float_as_uint(x[32 * b + i]) & 0x7FFFFFFFu);
+    float k;
+    limb_scale(mb, xsc[b], k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) limb_digits(&x[32 * b + 4 * i], k, xq, 8 * b + i);
   }
 
   // ---- the wave's tasks: t0 + sub, t0 + sub + rsub, ...
@@ -1218,10 +1172,10 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
       if (xvalid) {
         const int fmt = seg_pick<EPI>(sc.fmt, seg);
         if constexpr (KF) {
-          v = Q6K_S::dot(slot, lane, x, xs);  // the launcher sends Q4_K to the register path
+          v = Q6K_S::dot(slot, lane, xq, xsc, xs);  // the launcher sends Q4_K to the register path
         } else {
-          if (fmt == FMT_Q8_0) v = Q80_S::dot(slot, lane, x, xs);
-          else v = Q40_S::dot(slot, lane, x, xs);
+          if (fmt == FMT_Q8_0) v = Q80_S::dot(slot, lane, xq, xsc, xs);
+          else v = Q40_S::dot(slot, lane, xq, xsc, xs);
         }
       }
       // the slot has been read: refill it with the task D steps ahead
