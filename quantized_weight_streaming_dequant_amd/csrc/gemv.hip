@@ -85,9 +85,11 @@ __device__ __forceinline__ uint32_t vreg(uint32_t v) {
 // columns has a power-of-two scale s, the smallest with max |x| / s <= 127, and the
 // fixed-point value X = rint(x / s 256^(XL-1)) is split into balanced base-256 digits:
 //   X = 256^(XL-1) x1 + ... + x_XL,   x1 in [-127, 127], the others in [-128, 127],
-// so x is represented to within s 2^-(8 XL - 7) (two limbs: max |x of the block| / 32512).
-// Every step is exact in fp32 (scaling by a power of two, rounding to an integer below
-// 2^24).  The weight codes are small integers, so over a run of columns
+// so x is represented to within s 2^-(8 XL - 7) < max |x of the block| 2 / (127 2^(8 XL - 7)):
+// / 8.3e6 with three limbs, / 32512 with two.  Every step is exact in fp32 (scaling by a
+// power of two, rounding to an integer below 2^24).  Three limbs are the default: with two,
+// a block holding one activation 10^4 times its neighbours (as large outlier channels do)
+// leaves some rows within a few times of a 1e-3 sum |w x| error; with three, within 1e-6.  The weight codes are small integers, so over a run of columns
 // sum q x = s (D1 + D2 / 256 + D3 / 65536) where Dk = sum q xk is formed exactly by
 // v_dot4_i32_i8 (four 8-bit products and the accumulation in one instruction), in place of
 // a convert and an fp32 FMA per weight.  The offset and min terms of the formats use exact
@@ -95,7 +97,7 @@ __device__ __forceinline__ uint32_t vreg(uint32_t v) {
 // A limb plane holds byte c at xq_off(c): 16 pad bytes after every 64 columns, so lanes that
 // read 16-column runs 64 columns apart with 128-bit reads spread over the banks.
 #ifndef NT_GEMV_XLIMBS
-#define NT_GEMV_XLIMBS 2
+#define NT_GEMV_XLIMBS 3
 #endif
 constexpr int XL = NT_GEMV_XLIMBS;
 static_assert(XL == 2 || XL == 3, "two or three limbs");

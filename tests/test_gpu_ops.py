@@ -97,6 +97,32 @@ def test_gemv_matches_oracle(fmt, rows, cols):
     say(f"  worst rel err {worst:.2e}")
 
 
+OUTLIER_KINDS = {
+    # multiplier per column on top of N(0, 1): one channel per 32 columns at 100x, a single
+    # channel at 10^4x, three channels at 2000x (the shapes of large outlier activations)
+    "every_block_100x": lambda c: np.where(np.arange(c) % 32 == 7, 100.0, 1.0),
+    "one_channel_1e4x": lambda c: np.where(np.arange(c) == 100, 1e4, 1.0),
+    "three_channels_2000x": lambda c: np.where(np.isin(np.arange(c), [100, 2000, 5000]), 2000.0, 1.0),
+}
+
+
+@pytest.mark.parametrize("kind", list(OUTLIER_KINDS))
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_outlier_activations(fmt, kind):
+    """x with large outlier channels: each 32-column block of x is staged on the scale of its
+    largest entry, so the other entries of an outlier's block lose the most; they stay far
+    inside the tolerance (worst seen ~2e-6 of sum |w x|, checked against 1e-5)."""
+    rows, cols = 512, 8192
+    say(f"gemv outliers {kind} {NAMES[fmt]}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=3, stream=500 + fmt)
+    x = (synth.normal_f32(cols, seed=3, stream=600 + fmt) * OUTLIER_KINDS[kind](cols)).astype(np.float32)
+    y = gpu_gemv(fmt, rows, cols, blocks, x)
+    ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+    check_rel(y, ref, nrm, what=f"{NAMES[fmt]} {kind}")
+    worst = check_rel(y, ref, nrm, tol=1e-5, what=f"{NAMES[fmt]} {kind} (limb precision)")
+    say(f"  worst rel err {worst:.2e}")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_one_hot_and_zero(fmt):
     """One-hot x picks a dequantized column exactly; all-zero blocks give exact zeros."""
