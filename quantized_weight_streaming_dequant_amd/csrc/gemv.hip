@@ -558,58 +558,103 @@ __device__ __forceinline__ void limb_digits(const float* v, float k, uint32_t (&
   for (int l = 0; l < XL; ++l) w[l][i] = pack_b0(b[l][0], b[l][1], b[l][2], b[l][3]);
 }
 
+// x and gain of this thread's first 16 columns, loaded before a wave issues its first weight
+// loads: loads complete in issue order, so staging from loads issued after the weights would
+// wait for the weights.  Threads past the last group load the last group (unused).
+struct XPre {
+  float4 v[4], g[4];
+};
+__device__ __forceinline__ XPre stage_x_load(const GemvArgs& a) {
+  XPre p;
+  const int gi = min((int)threadIdx.x, (a.cols >> 4) - 1);
+  const float4* src = reinterpret_cast<const float4*>(a.x + gi * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p.v[i] = src[i];
+  // loaded even without a gain (then from x, unused), so that the loads in flight do not
+  // depend on the branch and the staging can wait for x alone
+  const float4* gp = reinterpret_cast<const float4*>((a.gain ? a.gain : a.x) + gi * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p.g[i] = gp[i];
+  return p;
+}
+
+// One group of 16 columns (already normalised) into the limb planes, its sum and, from the
+// even thread of each pair, the pair's scale.
+__device__ __forceinline__ void stage_group(const XLimbs& xs, int gi, const float (&v)[16]) {
+  float sum = 0.f;
+  uint32_t mb = 0;  // max of |x| as bit patterns: a NaN orders above every number
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    sum += v[i] + v[i + 1];
+    mb = max(mb, max(__float_as_uint(v[i]) & 0x7FFFFFFFu, __float_as_uint(v[i + 1]) & 0x7FFFFFFFu));
+  }
+  xs.s16[gi] = sum;
+  mb = max(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, true));  // the pair's 32 columns
+  float s, k;
+  limb_scale(mb, s, k);
+  if ((gi & 1) == 0) xs.sc[gi >> 1] = s;
+  uint32_t w[XL][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) limb_digits(&v[4 * i], k, w, i);
+#pragma unroll
+  for (int l = 0; l < XL; ++l)
+    *reinterpret_cast<u32x4a16*>(xs.q + l * xs.plane + xq_off(gi * 16)) = u32x4a16{w[l][0], w[l][1], w[l][2], w[l][3]};
+}
+
 // Stage x (optionally RMS-normalised) into LDS: XL limb planes, the scale of every 32
 // columns and the fp32 sum of every 16.  Every thread of the workgroup calls this exactly
-// once.  A thread takes 16 columns; threads 2t and 2t+1 (one DPP quad pair) share a scale.
-__device__ __forceinline__ void stage_x(const GemvArgs& a, const XLimbs& xs, float* red) {
-  const int cols = a.cols;
+// once, with what stage_x_load returned.  A thread takes 16 columns per round, the first
+// round from the preloaded registers; threads 2t and 2t+1 (one DPP quad pair) share a scale.
+// cols / 16 is even and the block size a multiple of 64, so both threads of a pair run the
+// same rounds.
+__device__ __forceinline__ void stage_x(const GemvArgs& a, const XPre& pre, const XLimbs& xs, float* red) {
+  const int cols = a.cols, ng = cols >> 4;
+  const int g0 = (int)threadIdx.x;
   float scale = 1.f;
   if (a.gain) {
     float ss = 0.f;
-    for (int c = threadIdx.x * 4; c < cols; c += blockDim.x * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(a.x + c);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    if (g0 < ng) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ss += pre.v[i].x * pre.v[i].x + pre.v[i].y * pre.v[i].y + pre.v[i].z * pre.v[i].z + pre.v[i].w * pre.v[i].w;
+    }
+    for (int c = (g0 + (int)blockDim.x) * 16; c < cols; c += blockDim.x * 16) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 t = src[i];
+        ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+      }
     }
     ss = block_sum(ss, red);
     scale = 1.0f / sqrtf(ss / (float)cols + a.eps);
   }
-  // cols / 16 is even and the block size a multiple of 64, so both threads of a pair run
-  // the same iterations
-  for (int gi = threadIdx.x; gi < (cols >> 4); gi += blockDim.x) {
+  if (g0 < ng) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 t = pre.v[i];
+      if (a.gain) {
+        t.x = t.x * scale * pre.g[i].x; t.y = t.y * scale * pre.g[i].y;
+        t.z = t.z * scale * pre.g[i].z; t.w = t.w * scale * pre.g[i].w;
+      }
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+    stage_group(xs, g0, v);
+  }
+  for (int gi = g0 + (int)blockDim.x; gi < ng; gi += blockDim.x) {
     const float4* src = reinterpret_cast<const float4*>(a.x + gi * 16);
     float v[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 t = src[i];
+      float4 t = src[i];
+      if (a.gain) {
+        const float4 g = reinterpret_cast<const float4*>(a.gain + gi * 16)[i];
+        t.x = t.x * scale * g.x; t.y = t.y * scale * g.y; t.z = t.z * scale * g.z; t.w = t.w * scale * g.w;
+      }
       v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
     }
-    if (a.gain) {
-      const float4* gp = reinterpret_cast<const float4*>(a.gain + gi * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 gg = gp[i];
-        v[4 * i] = v[4 * i] * scale * gg.x; v[4 * i + 1] = v[4 * i + 1] * scale * gg.y;
-        v[4 * i + 2] = v[4 * i + 2] * scale * gg.z; v[4 * i + 3] = v[4 * i + 3] * scale * gg.w;
-      }
-    }
-    float sum = 0.f;
-    uint32_t mb = 0;  // max of |x| as bit patterns: a NaN orders above every number
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      sum += v[i] + v[i + 1];
-      mb = max(mb, max(__float_as_uint(v[i]) & 0x7FFFFFFFu, __float_as_uint(v[i + 1]) & 0x7FFFFFFFu));
-    }
-    xs.s16[gi] = sum;
-    mb = max(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, true));  // the pair's 32 columns
-    float s, k;
-    limb_scale(mb, s, k);
-    if ((gi & 1) == 0) xs.sc[gi >> 1] = s;
-    uint32_t w[XL][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) limb_digits(&v[4 * i], k, w, i);
-#pragma unroll
-    for (int l = 0; l < XL; ++l)
-      *reinterpret_cast<u32x4a16*>(xs.q + l * xs.plane + xq_off(gi * 16)) = u32x4a16{w[l][0], w[l][1], w[l][2], w[l][3]};
+    stage_group(xs, gi, v);
   }
   __syncthreads();
 }
@@ -722,9 +767,10 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int s, const GemvSeg
 // every wave takes part in the staging.
 // DEPTH - 1 items in flight ahead of the one computed, in a ring of DEPTH register buffers
 // (unrolled over the ring, so that no buffer is copied).
-template <typename F, int R, int EPI, int DEPTH>
+template <typename F, int R, int EPI, int DEPTH, bool STAGE>
 __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, int wid, int W, const XLimbs& xs,
-                                            float* red, unsigned long long& best, const float2* rope) {
+                                            float* red, unsigned long long& best, const float2* rope,
+                                            const XPre xpre) {
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * R : R;
   typedef typename F::Raw Raw;
   const GemvSeg sg = a.seg[s];
@@ -750,11 +796,11 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
     }
   };
   Raw b0[NR], b1[NR], b2[NR];
-  if (n_items > 0) {
-    issue(b0);
-    if (DEPTH == 3) issue(b1);
-  }
-  if (s == 0) stage_x(a, xs, red);
+  // issued even by a wave without items (clamped rows; segments have at least one row), so
+  // that the count in flight is static and the staging's waits leave these loads in flight
+  issue(b0);
+  if (DEPTH == 3) issue(b1);
+  if constexpr (STAGE) stage_x(a, xpre, xs, red);
   if (n_items == 0) return;
   float acc[NR];
 #pragma unroll
@@ -794,6 +840,27 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
   }
 }
 
+// Segment s with its format's work loop (STAGE: the first segment, which stages x).
+template <int FMTMASK, int R, int EPI, bool STAGE>
+__device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int wid, int W, const XLimbs& xs,
+                                        float* red, unsigned long long& best, const float2* rope, const XPre xpre) {
+  constexpr int D = GEMV_DEPTH<EPI>;
+  switch (a.seg[s].fmt) {
+    case FMT_Q8_0:
+      if constexpr ((FMTMASK >> FMT_Q8_0) & 1) run_segment<Q8_0F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      break;
+    case FMT_Q4_0:
+      if constexpr ((FMTMASK >> FMT_Q4_0) & 1) run_segment<Q4_0F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      break;
+    case FMT_Q4_K:
+      if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      break;
+    default:
+      if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      break;
+  }
+}
+
 // At least four waves per SIMD (at most 128 VGPRs): the stream needs many waves in flight.
 template <int FMTMASK, int R, int NW, int EPI>
 __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
@@ -814,23 +881,12 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   if constexpr (EPI == EPI_QKV) {
     if (threadIdx.x < 64) rope[threadIdx.x] = rope_cs(a.rope_theta, a.pos, threadIdx.x);
   }
+  // x is loaded first (its loads then complete before the weights'); the first segment
+  // stages it after issuing its first weight loads
+  const XPre xpre = stage_x_load(a);
+  run_any<FMTMASK, R, EPI, true>(a, 0, lane, wid, W, xs, red, best, rope, xpre);
   const int nseg = (EPI == EPI_SWIGLU) ? 1 : a.nseg;
-  for (int s = 0; s < nseg; ++s) {
-    switch (a.seg[s].fmt) {
-      case FMT_Q8_0:
-        if constexpr ((FMTMASK >> FMT_Q8_0) & 1) run_segment<Q8_0F, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
-        break;
-      case FMT_Q4_0:
-        if constexpr ((FMTMASK >> FMT_Q4_0) & 1) run_segment<Q4_0F, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
-        break;
-      case FMT_Q4_K:
-        if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
-        break;
-      default:
-        if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI, GEMV_DEPTH<EPI>>(a, s, lane, wid, W, xs, red, best, rope);
-        break;
-    }
-  }
+  for (int s = 1; s < nseg; ++s) run_any<FMTMASK, R, EPI, false>(a, s, lane, wid, W, xs, red, best, rope, XPre{});
   if constexpr (EPI == EPI_LOGITS) {
     // one atomic per workgroup: lane 0 of each wave holds the wave's best key
     __shared__ unsigned long long wbest[NW];
