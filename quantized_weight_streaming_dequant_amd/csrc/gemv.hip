@@ -1156,6 +1156,12 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
     if (threadIdx.x < 64) rope[threadIdx.x] = rope_cs(a.rope_theta, a.pos, threadIdx.x);
   }
   const int t0 = (int)blockIdx.x * sa.tpw, t1 = min(sa.tasks, t0 + sa.tpw);
+  // The waves of a slice share its tasks: each starts with D fixed ones (t0 + sub + d rsub)
+  // and then takes the next untaken task of the slice from a counter in LDS, so that waves
+  // slowed by their place in the memory queues do fewer tasks instead of finishing last.
+  __shared__ int next_task[ST_MAX_WAVES];
+  if ((int)threadIdx.x < sa.ns) next_task[threadIdx.x] = t0 + D * sa.rsub;
+  __syncthreads();
 
   // ---- x slice into registers, issued first so that it arrives first
   const int c0 = KF ? sl * ST_SLICE_COLS_K + 64 * lane : sl * ST_SLICE_COLS_B + 32 * lane;
@@ -1171,8 +1177,12 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
   }
   __builtin_amdgcn_sched_barrier(0);
   // ---- the first D tasks of this wave in flight (every wave has a slice and a share of tasks)
+  int tslot[D];  // the task in each ring slot (t1 or more: none)
 #pragma unroll
-  for (int d = 0; d < D; ++d) st_issue<EPI, NI>(sc, min(t0 + sub + d * sa.rsub, t1 - 1), lane, ring + d * SLOT);
+  for (int d = 0; d < D; ++d) {
+    tslot[d] = t0 + sub + d * sa.rsub;
+    st_issue<EPI, NI>(sc, min(tslot[d], t1 - 1), lane, ring + d * SLOT);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // ---- RMSNorm prologue: scale from the sum of squares over all slices
   if (a.gain) {
@@ -1218,10 +1228,17 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
     for (int i = 0; i < 8; ++i) limb_digits(&x[32 * b + 4 * i], k, xq, 8 * b + i);
   }
 
-  // ---- the wave's tasks: t0 + sub, t0 + sub + rsub, ...
-  {
-    int d = 0;
-    for (int t = t0 + sub; t < t1; t += sa.rsub) {
+  // ---- the wave's tasks, in the order its ring slots were filled; every refill issues the
+  // same transfers (past the last task it re-reads the last row), so the wait is static
+  // (the ring is unrolled, so that the slots' tasks stay in registers)
+  for (bool more = true; more;) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int t = tslot[d];
+      if (t >= t1) {  // tasks are taken in increasing order: the later slots hold none either
+        more = false;
+        break;
+      }
       uint8_t* slot = ring + d * SLOT;
       wait_vm<NI * (D - 1)>();
       int seg, row;
@@ -1236,15 +1253,18 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
           else v = Q40_S::dot(slot, lane, xq, xsc, xs);
         }
       }
-      // the slot has been read: refill it with the task D steps ahead
+      // the slot has been read: refill it with the slice's next untaken task
+      int tn = 0;
+      if (lane == 0) tn = atomicAdd(&next_task[sl], 1);
+      tn = __builtin_amdgcn_readfirstlane(tn);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      st_issue<EPI, NI>(sc, min(t + D * sa.rsub, t1 - 1), lane, slot);
+      st_issue<EPI, NI>(sc, min(tn, t1 - 1), lane, slot);
+      tslot[d] = tn;
       v = row16_sum(v);
       if ((lane & 15) == 0) part[(((t - t0) * sa.ns + sl) << 2) + (lane >> 4)] = v;
-      d = (d + 1 == D) ? 0 : d + 1;
     }
-    wait_vm<0>();
   }
+  wait_vm<0>();
   __syncthreads();
 
   // ---- epilogue: one thread per task (per pair for SWIGLU and QKV)
