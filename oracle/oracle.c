@@ -19,6 +19,9 @@
  *   Q4_0 (18 B / 32): d fp16 @0, nibbles[16] @2;           w = d*(n-8), weight i<16 is the low
  *                      nibble of byte i, weight i>=16 the high nibble of byte i-16
  *   Q4_K (144 B / 256): d @0, dmin @2, scales[12] @4, nibbles[128] @16; w = d*sc_j*q - dmin*m_j
+ *   Q5_K (176 B / 256): d @0, dmin @2, scales[12] @4 (packed as in Q4_K), high bits[32] @16,
+ *                      nibbles[128] @48; q = nibble + 16 * (bit j of high byte i mod 32),
+ *                      w = d*sc_j*q - dmin*m_j
  *   Q6_K (210 B / 256): low nibbles[128] @0, 2-bit highs[64] @128, int8 s[16] @192, d @208;
  *                      w = d*s_(i/16)*(q-32)
  * With these fields every weight is an exact fp64 number (at most 32
@@ -35,12 +38,12 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3 };
+enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_K = 4 };
 
 int or_block_elems(int fmt) {
   switch (fmt) {
     case OR_Q8_0: case OR_Q4_0: return 32;
-    case OR_Q4_K: case OR_Q6_K: return 256;
+    case OR_Q4_K: case OR_Q6_K: case OR_Q5_K: return 256;
   }
   return -1;
 }
@@ -51,6 +54,7 @@ int or_block_bytes(int fmt) {
     case OR_Q4_0: return 18;
     case OR_Q4_K: return 144;
     case OR_Q6_K: return 210;
+    case OR_Q5_K: return 176;
   }
   return -1;
 }
@@ -107,6 +111,22 @@ static void dequant_block(int fmt, const uint8_t* b, double* w) {
       for (int i = 0; i < 256; ++i) {
         int j = i / 32, g = i / 64, l = i % 32;
         int q = (qs[32 * g + l] >> (4 * (j % 2))) & 15;
+        int s, m;
+        q4k_scale_min(sc, j, &s, &m);
+        w[i] = d * (double)s * (double)q - dmin * (double)m;
+      }
+      break;
+    }
+    case OR_Q5_K: {
+      /* as Q4_K, with a fifth code bit: weight i of sub-block j takes bit j of
+       * high-bit byte i mod 32, worth 16 */
+      double d = rd16(b), dmin = rd16(b + 2);
+      const uint8_t* sc = b + 4;
+      const uint8_t* qh = b + 16;
+      const uint8_t* qs = b + 48;
+      for (int i = 0; i < 256; ++i) {
+        int j = i / 32, g = i / 64, l = i % 32;
+        int q = ((qs[32 * g + l] >> (4 * (j % 2))) & 15) + 16 * ((qh[l] >> j) & 1);
         int s, m;
         q4k_scale_min(sc, j, &s, &m);
         w[i] = d * (double)s * (double)q - dmin * (double)m;

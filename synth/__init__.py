@@ -8,8 +8,8 @@ entries.  It computes nothing the decode path computes.  The C generator in
 Weights follow the distributions of the workloads on the ntransformer pages'
 formats (ntransformer overview, de.news.hada.io, "Überblick über NTransformer":
 GGUF formats Q4_0, Q8_0, Q4_K_M, Q5_K, Q6_K): every fp16 super-scale ~ U[0.001, 0.01],
-Q8_0 codes ~ U{-127..127}, Q4_0/Q4_K nibbles and Q4_K 6-bit scales/mins ~ uniform,
-Q6_K 6-bit codes ~ uniform and int8 sub-scales ~ U{-64..63}.
+Q8_0 codes ~ U{-127..127}, Q4_0/Q4_K/Q5_K nibbles, Q5_K high bits and Q4_K/Q5_K 6-bit
+scales/mins ~ uniform, Q6_K 6-bit codes ~ uniform and int8 sub-scales ~ U{-64..63}.
 """
 from __future__ import annotations
 
@@ -24,10 +24,10 @@ _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
 # format ids, block geometry (weights per block, bytes per block)
-Q8_0, Q4_0, Q4_K, Q6_K = 0, 1, 2, 3
-FORMAT_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
-BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210}
+Q8_0, Q4_0, Q4_K, Q6_K, Q5_K = 0, 1, 2, 3, 4
+FORMAT_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_K: "Q5_K"}
+BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256, Q5_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210, Q5_K: 176}
 
 DLO, DHI = 0.001, 0.01
 
@@ -51,7 +51,7 @@ def lib():
             build()
         L = ctypes.CDLL(_LIB)
         i64, u64, vp, dbl = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_double
-        for name in ("synth_fill_q8_0", "synth_fill_q4_0", "synth_fill_q4_k", "synth_fill_q6_k"):
+        for name in ("synth_fill_q8_0", "synth_fill_q4_0", "synth_fill_q4_k", "synth_fill_q6_k", "synth_fill_q5_k"):
             f = getattr(L, name)
             f.argtypes = [vp, i64, i64, u64, u64, dbl, dbl]
             f.restype = None
@@ -87,7 +87,7 @@ def fill_blocks(buf, fmt: int, n_blocks: int, seed: int, stream: int, block0: in
                 dlo: float = DLO, dhi: float = DHI) -> None:
     """Write n_blocks blocks of format fmt (blocks block0.. of the stream) at buf."""
     fn = {Q8_0: lib().synth_fill_q8_0, Q4_0: lib().synth_fill_q4_0,
-          Q4_K: lib().synth_fill_q4_k, Q6_K: lib().synth_fill_q6_k}[fmt]
+          Q4_K: lib().synth_fill_q4_k, Q6_K: lib().synth_fill_q6_k, Q5_K: lib().synth_fill_q5_k}[fmt]
     fn(_ptr(buf), block0, n_blocks, seed, stream, dlo, dhi)
 
 

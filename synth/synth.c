@@ -18,6 +18,7 @@
  *   Q4_0  18 B / 32 weights : d fp16 @0, packed nibbles[16] @2
  *   Q4_K 144 B / 256 weights: d fp16 @0, dmin fp16 @2, packed 6-bit scales[12] @4, nibbles[128] @16
  *   Q6_K 210 B / 256 weights: low nibbles[128] @0, high 2-bit fields[64] @128, int8 scales[16] @192, d fp16 @208
+ *   Q5_K 176 B / 256 weights: d fp16 @0, dmin fp16 @2, packed 6-bit scales[12] @4, high bits[32] @16, nibbles[128] @48
  * Packed bit fields are filled with uniform random bytes, which makes every
  * field (4-bit, 6-bit, 2-bit) uniform over its full range, as the workloads ask.
  */
@@ -122,6 +123,19 @@ void synth_fill_q4_k(uint8_t* out, int64_t b0, int64_t nb, uint64_t seed, uint64
     put_u16(blk + 0, scale_f16(draw(key, c), dlo, dhi));
     put_u16(blk + 2, scale_f16(draw(key, c + 1), dlo, dhi));
     fill_bytes(blk + 4, 140, key, c + 2); /* 12 scale bytes + 128 nibble bytes */
+  }
+}
+
+/* Q5_K: d, dmin ~ U[dlo, dhi] fp16; 6-bit scales/mins, high bits and nibbles uniform. */
+void synth_fill_q5_k(uint8_t* out, int64_t b0, int64_t nb, uint64_t seed, uint64_t stream, double dlo, double dhi) {
+  uint64_t key = stream_key(seed, stream);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nb; ++i) {
+    uint64_t c = (uint64_t)(b0 + i) * BLOCK_COUNTERS;
+    uint8_t* blk = out + i * 176;
+    put_u16(blk + 0, scale_f16(draw(key, c), dlo, dhi));
+    put_u16(blk + 2, scale_f16(draw(key, c + 1), dlo, dhi));
+    fill_bytes(blk + 4, 172, key, c + 2); /* 12 scale bytes + 32 high-bit bytes + 128 nibble bytes */
   }
 }
 

@@ -30,14 +30,8 @@ def pack_q4_0(d: float, n) -> bytes:
     return struct.pack("<H", f16_bits(d)) + qs
 
 
-def pack_q4_k(d: float, dmin: float, sc, m, q) -> bytes:
-    """sc, m: 8 six-bit values (one per 32-weight sub-block); q: 256 nibbles.
-    Weight i = d*sc[i//32]*q[i] - dmin*m[i//32]."""
-    sc = [int(v) for v in sc]
-    m = [int(v) for v in m]
-    q = [int(v) for v in q]
-    assert len(sc) == 8 and len(m) == 8 and len(q) == 256
-    assert all(0 <= v < 64 for v in sc + m) and all(0 <= v < 16 for v in q)
+def _pack_k_scales(sc, m) -> bytes:
+    """The 12 bytes holding 8 six-bit (scale, min) pairs, as Q4_K and Q5_K store them."""
     s = [0] * 12
     for j in range(4):
         s[j] = sc[j] & 63          # low 6 bits: scale of sub-block j
@@ -46,12 +40,43 @@ def pack_q4_k(d: float, dmin: float, sc, m, q) -> bytes:
         s[j + 4] = (sc[j] & 15) | ((m[j] & 15) << 4)   # low nibbles of scale/min of sub-block j
         s[j - 4] |= (sc[j] >> 4) << 6                  # top two bits of the scale
         s[j] |= (m[j] >> 4) << 6                       # top two bits of the min
+    return bytes(s)
+
+
+def _pack_nibbles(q) -> bytes:
+    """128 bytes: weight i of sub-block j = i // 32 is nibble j % 2 of byte 32 (j // 2) + i % 32."""
     qs = [0] * 128
     for i in range(256):
         j, l = i // 32, i % 32
-        byte = 32 * (j // 2) + l
-        qs[byte] |= q[i] << (4 * (j % 2))
-    return struct.pack("<HH", f16_bits(d), f16_bits(dmin)) + bytes(s) + bytes(qs)
+        qs[32 * (j // 2) + l] |= (q[i] & 15) << (4 * (j % 2))
+    return bytes(qs)
+
+
+def pack_q4_k(d: float, dmin: float, sc, m, q) -> bytes:
+    """sc, m: 8 six-bit values (one per 32-weight sub-block); q: 256 nibbles.
+    Weight i = d*sc[i//32]*q[i] - dmin*m[i//32]."""
+    sc = [int(v) for v in sc]
+    m = [int(v) for v in m]
+    q = [int(v) for v in q]
+    assert len(sc) == 8 and len(m) == 8 and len(q) == 256
+    assert all(0 <= v < 64 for v in sc + m) and all(0 <= v < 16 for v in q)
+    return struct.pack("<HH", f16_bits(d), f16_bits(dmin)) + _pack_k_scales(sc, m) + _pack_nibbles(q)
+
+
+def pack_q5_k(d: float, dmin: float, sc, m, q) -> bytes:
+    """sc, m: 8 six-bit values (one per 32-weight sub-block); q: 256 five-bit codes.
+    Weight i = d*sc[i//32]*q[i] - dmin*m[i//32]; the fifth bit of weight i sits in bit
+    i // 32 of high-bit byte i % 32."""
+    sc = [int(v) for v in sc]
+    m = [int(v) for v in m]
+    q = [int(v) for v in q]
+    assert len(sc) == 8 and len(m) == 8 and len(q) == 256
+    assert all(0 <= v < 64 for v in sc + m) and all(0 <= v < 32 for v in q)
+    qh = [0] * 32
+    for i in range(256):
+        qh[i % 32] |= (q[i] >> 4) << (i // 32)
+    return (struct.pack("<HH", f16_bits(d), f16_bits(dmin)) + _pack_k_scales(sc, m) + bytes(qh) +
+            _pack_nibbles(q))
 
 
 def pack_q6_k(d: float, s, q) -> bytes:

@@ -19,7 +19,7 @@ import torch
 import oracle
 import synth
 from synth import recipes
-from tests.blockpack import f16_bits, pack_q4_0, pack_q4_k, pack_q6_k, pack_q8_0
+from tests.blockpack import f16_bits, pack_q4_0, pack_q4_k, pack_q5_k, pack_q6_k, pack_q8_0
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(12345)
@@ -106,9 +106,11 @@ def test_q4_k_hand_block():
     assert np.array_equal(w, exp)
 
 
-def test_q4_k_scale_min_packing_exhaustive():
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q5_K])
+def test_k_scale_min_packing_exhaustive(fmt):
     """Every (scale, min) pair in 0..63 x 0..63 at every sub-block decodes back."""
-    q = [(7 * i + 3 + i // 32) % 16 for i in range(256)]
+    pack = pack_q4_k if fmt == synth.Q4_K else pack_q5_k
+    q = [(7 * i + 3 + i // 32) % (16 if fmt == synth.Q4_K else 32) for i in range(256)]
     base_sc = [5, 9, 17, 33, 40, 51, 62, 1]
     base_m = [60, 2, 30, 44, 8, 19, 63, 27]
     d, dmin = 0.25, 0.125
@@ -119,9 +121,9 @@ def test_q4_k_scale_min_packing_exhaustive():
             sc = list(base_sc)
             m = list(base_m)
             sc[j], m[j] = s, mm
-            blocks.append(pack_q4_k(d, dmin, sc, m, q))
+            blocks.append(pack(d, dmin, sc, m, q))
         buf = np.frombuffer(b"".join(blocks), np.uint8)
-        w = oracle.dequant_exact(synth.Q4_K, len(pairs), 256, buf)
+        w = oracle.dequant_exact(fmt, len(pairs), 256, buf)
         qa = np.array(q, dtype=np.float64)
         for r, (s, mm) in enumerate(pairs):
             sc = list(base_sc)
@@ -129,6 +131,45 @@ def test_q4_k_scale_min_packing_exhaustive():
             sc[j], m[j] = s, mm
             exp = np.array([d * sc[i // 32] * qa[i] - dmin * m[i // 32] for i in range(256)])
             assert np.array_equal(w[r], exp), (j, s, mm)
+
+
+def test_q5_k_hand_block():
+    # d = 1, dmin = 0.5, scale of sub-block j = j+1, min = 2j, code_i = (i + 5j) mod 32
+    # -> w_i = (j+1)((i + 5j) mod 32) - j; codes 16..31 set the fifth bit
+    sc = [j + 1 for j in range(8)]
+    m = [2 * j for j in range(8)]
+    code = lambda i: (i + 5 * (i // 32)) % 32
+    blk = pack_q5_k(1.0, 0.5, sc, m, [code(i) for i in range(256)])
+    assert len(blk) == 176
+    w = oracle.dequant_exact(synth.Q5_K, 1, 256, np.frombuffer(blk, np.uint8))[0]
+    exp = np.array([(i // 32 + 1) * code(i) - i // 32 for i in range(256)], dtype=np.float64)
+    assert np.array_equal(w, exp)
+
+
+def test_q5_k_every_code_at_every_position():
+    sc = [3, 7, 11, 13, 17, 19, 23, 29]
+    code = lambda i, c: (i + c + 7 * (i // 32)) % 32
+    blocks = [pack_q5_k(1.0, 0.0, sc, [0] * 8, [code(i, c) for i in range(256)]) for c in range(32)]
+    w = oracle.dequant_exact(synth.Q5_K, 32, 256, np.frombuffer(b"".join(blocks), np.uint8))
+    for c in range(32):
+        exp = np.array([sc[i // 32] * code(i, c) for i in range(256)], dtype=np.float64)
+        assert np.array_equal(w[c], exp)
+
+
+def test_q5_k_is_q4_k_plus_sixteen_per_high_bit():
+    """With its high bits clear a Q5_K block decodes like the Q4_K block with the same fields;
+    each set high bit adds exactly 16 d sc_j to its weight and nothing elsewhere."""
+    rng = np.random.default_rng(55)
+    for _ in range(20):
+        d, dmin = (float(np.float16(v)) for v in rng.uniform(0.001, 0.01, 2))
+        sc, m = rng.integers(0, 64, 8), rng.integers(0, 64, 8)
+        lo = rng.integers(0, 16, 256)
+        hi = rng.integers(0, 2, 256)
+        w4 = oracle.dequant_exact(synth.Q4_K, 1, 256, np.frombuffer(pack_q4_k(d, dmin, sc, m, lo), np.uint8))[0]
+        w5_0 = oracle.dequant_exact(synth.Q5_K, 1, 256, np.frombuffer(pack_q5_k(d, dmin, sc, m, lo), np.uint8))[0]
+        w5 = oracle.dequant_exact(synth.Q5_K, 1, 256, np.frombuffer(pack_q5_k(d, dmin, sc, m, lo + 16 * hi), np.uint8))[0]
+        assert np.array_equal(w5_0, w4)
+        assert np.array_equal(w5 - w4, 16.0 * d * np.repeat(sc, 32) * hi)
 
 
 def test_q6_k_hand_block():
@@ -164,7 +205,7 @@ def test_q4_0_and_q8_0_every_code():
         assert np.array_equal(w[c], np.array([((i + 32 * c) % 256) - 128 for i in range(32)], dtype=np.float64))
 
 
-@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K])
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K])
 def test_dequant_f32_is_one_rounding_of_exact(fmt):
     """fp32 output = RNE(exact rational value), checked with Fractions."""
     rows, cols = 3, 512
@@ -215,7 +256,7 @@ def test_format_sizes_match_page_figures():
 
 def test_bits_per_weight():
     bpw = {f: 8 * synth.BLOCK_BYTES[f] / synth.BLOCK_ELEMS[f] for f in synth.BLOCK_BYTES}
-    assert bpw == {synth.Q8_0: 8.5, synth.Q4_0: 4.5, synth.Q4_K: 4.5, synth.Q6_K: 6.5625}
+    assert bpw == {synth.Q8_0: 8.5, synth.Q4_0: 4.5, synth.Q4_K: 4.5, synth.Q6_K: 6.5625, synth.Q5_K: 5.5}
     for f in synth.BLOCK_BYTES:
         assert oracle.block_bytes(f) == synth.BLOCK_BYTES[f]
         assert oracle.block_elems(f) == synth.BLOCK_ELEMS[f]
@@ -223,7 +264,7 @@ def test_bits_per_weight():
 
 # ---------------------------------------------------------------- GEMV
 
-@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K])
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K])
 def test_gemv_exact_rational_brute_force(fmt):
     rows, cols = 4, 512
     blocks = synth.quant_matrix(fmt, rows, cols, seed=3, stream=10 + fmt)
@@ -237,7 +278,7 @@ def test_gemv_exact_rational_brute_force(fmt):
         assert abs(Fraction(nrm[r]) - n_exact) <= Fraction(cols) * Fraction(2) ** -52 * n_exact
 
 
-@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K])
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K])
 def test_gemv_one_hot_picks_a_column(fmt):
     rows, cols = 5, 512
     blocks = synth.quant_matrix(fmt, rows, cols, seed=4, stream=30 + fmt)

@@ -18,7 +18,7 @@ def test_reproducible_and_stream_separated():
 
 
 def test_rows_regenerate_alone():
-    for fmt in (synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K):
+    for fmt in (synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K):
         full = synth.quant_matrix(fmt, 12, 1024, seed=0, stream=9).reshape(12, -1)
         part = synth.quant_rows(fmt, 1024, [11, 0, 5], seed=0, stream=9)
         assert np.array_equal(part, full[[11, 0, 5]])
@@ -51,6 +51,18 @@ def test_q4_k_and_q6_k_fields_uniform():
     # decoded codes are uniform over 0..63 (decode through the checker)
     w = oracle.dequant_exact(synth.Q6_K, 4, 8192, q6[:4 * 32].ravel())
     assert np.isfinite(w).all()
+
+
+def test_q5_k_fields_uniform():
+    blk = synth.quant_matrix(synth.Q5_K, 64, 8192, seed=0, stream=11).reshape(-1, 176)
+    d = blk[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+    dmin = blk[:, 2:4].copy().view(np.float16).astype(np.float64).ravel()
+    assert 0.0009 < d.min() and d.max() < 0.0101 and 0.0009 < dmin.min() and dmin.max() < 0.0101
+    bits = np.unpackbits(blk[:, 16:48].ravel())
+    assert abs(bits.mean() - 0.5) < 0.01
+    nib = np.concatenate([blk[:, 48:] & 15, blk[:, 48:] >> 4]).ravel()
+    cnt = np.bincount(nib, minlength=16)
+    assert cnt.min() > 0.95 * cnt.mean()
 
 
 def test_normals_and_gains():
