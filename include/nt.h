@@ -47,8 +47,11 @@ extern "C" {
  *            nibbles[128] @16                                               w = d*sc*q - dmin*m
  *   NT_Q6_K 210 B / 256 weights: low nibbles[128] @0, 2-bit highs[64] @128, int8 scales[16] @192,
  *            d fp16 @208                                                    w = d*s*(q-32)
+ *   NT_Q5_K 176 B / 256 weights: d @0, dmin @2, scales and mins packed as in NT_Q4_K @4,
+ *            high bits[32] @16, nibbles[128] @48; the fifth code bit of weight i of sub-block
+ *            j = i/32 is bit j of high byte i%32                              w = d*sc*q - dmin*m
  */
-typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3 } nt_format;
+typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4 } nt_format;
 
 typedef enum {
   NT_OK = 0,

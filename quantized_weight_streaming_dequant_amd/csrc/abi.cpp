@@ -36,7 +36,7 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(NT_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_Q6_K; }
+bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_Q5_K; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -7,11 +7,11 @@
 
 namespace nt {
 
-enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3 };
+enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4 };
 
 __host__ __device__ constexpr int block_elems(int f) { return f <= FMT_Q4_0 ? 32 : 256; }
 __host__ __device__ constexpr int block_bytes(int f) {
-  return f == FMT_Q8_0 ? 34 : f == FMT_Q4_0 ? 18 : f == FMT_Q4_K ? 144 : 210;
+  return f == FMT_Q8_0 ? 34 : f == FMT_Q4_0 ? 18 : f == FMT_Q4_K ? 144 : f == FMT_Q5_K ? 176 : 210;
 }
 
 // 4-byte-aligned 128/64-bit vector types: global_load_dwordx4/x2 only need dword alignment,

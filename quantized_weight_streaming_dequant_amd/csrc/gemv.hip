@@ -1,25 +1,27 @@
 // Fused dequantize-and-GEMV over GGML-style block-quantized weights, batch 1, gfx950.
 //
 // The decode path reads every weight once per token (70B PCIe P2P article,
-// blog.hotdry.top, §传统数据路径的性能瓶颈分析), so this kernel is an HBM stream with a
-// tight ALU budget (about 2.8 VALU lane-operations per 4.5-bit weight at 8 TB/s):
-//  * persistent workgroups, as many as stay resident: each stages the activation vector
-//    x (optionally RMS-normalised on the way in) into LDS once, with per-16-column sums;
-//  * the work is groups of R consecutive rows (2R rows for the paired gate/up launch)
-//    dealt round-robin to every wave of the launch, so waves finish together; a wave
-//    walks its rows' blocks in steps, a lane taking one fixed slice of a block per step
-//    (a Q8_0/Q4_0 block, a quarter of a Q4_K/Q6_K superblock) with dword-aligned 128-bit
-//    loads, and the loads of the next step are in flight while the current one computes;
-//  * blocks of 34, 18 and 210 bytes sit at 2-byte phases: the step order visits even and
-//    odd blocks separately so that the phase is uniform per row and step, and a scalar
-//    branch realigns with v_alignbyte;
-//  * 4- and 6-bit codes become exact fp16 values 1024 + q (or 1024 + 16q) by OR-ing the
-//    exponent bits in, and v_fma_mix_f32 multiplies them with the fp32 activation in one
-//    instruction; the 1024 offsets come back out through the per-16-column sums of x;
-//  * scale factors are applied once per 16 or 32 weights, lane sums are reduced with
-//    cross-lane shuffles, and epilogues fuse the residual add, SwiGLU, RoPE + fp16 KV
-//    append, or the greedy argmax.
+// blog.hotdry.top, §传统数据路径的性能瓶颈分析), so these kernels are an HBM stream with a
+// tight ALU budget.  Two paths:
+//  * register path (gemv_kernel): persistent workgroups, as many as stay resident; each
+//    stages the activation vector x (optionally RMS-normalised on the way in) into LDS
+//    once, as signed 8-bit limbs with a power-of-two scale per 32 columns and exact fp32
+//    sums per 16 columns; the work is groups of R rows (a gate/up row pair for the SwiGLU
+//    launch) dealt round-robin to every wave; a wave walks its rows' blocks in steps, a
+//    lane taking one fixed slice of a block (a Q8_0/Q4_0 block, a quarter of a
+//    Q4_K/Q5_K superblock, an eighth of a Q6_K one) with 128-bit loads, the loads of the
+//    next step in flight while the current one computes;
+//  * streamed path (gemv_stream_kernel, Q6_K and the 32-weight formats): waves split the
+//    columns into slices, hold their x slice in registers and stream their rows' bytes
+//    HBM -> LDS with global->LDS transfers.
+// Codes become bytes (nibble masks; high bits rotated into place) and meet the limbs in
+// v_dot4_i32_i8, four exact 8-bit products per instruction; each 16- or 32-column integer
+// sum is scaled once; offsets and mins use the fp32 x sums.  Blocks of 34, 18 and 210
+// bytes sit at 2-byte phases, realigned with v_alignbyte.  Epilogues fuse the residual
+// add, SwiGLU, RoPE + fp16 KV append, or the greedy argmax.
 // No matrix cores: at batch 1 this is not a dense contraction.
+#include <type_traits>
+
 #include "common.h"
 #include "gemv.h"
 
@@ -386,6 +388,82 @@ struct Q4_KF {
       const uint32_t Y = raw[k].hd.y, Z = raw[k].hd.z, W = raw[k].hd.w;
       const uint32_t yz = __builtin_amdgcn_perm(Z, Y, sel);
       const uint32_t lo = upper ? __builtin_amdgcn_perm(W >> 4, W, sel) : yz;  // [W p, W p+1, W p>>4, W p+1>>4]
+      const uint32_t sm = and_or(yz >> 2, mtop, lo & mlow);
+      const float d = h2f(raw[k].hd.x), dmin = h2f(raw[k].hd.x >> 16);
+      acc[k] += (d * sA * ub0(sm)) * limb_sum(da[k]);
+      acc[k] += (d * sB * ub1(sm)) * limb_sum(db[k]);
+      acc[k] -= dmin * (ub2(sm) * xa + ub3(sm) * xb);
+    }
+  }
+};
+
+// Q5_K: the Q4_K lane layout over a 176-byte superblock (16-byte aligned: no phases), with
+// a fifth code bit worth 16: column l (0..31) of sub-block j has it in bit j of high-bit byte
+// l (bytes 16..47, which all four lanes of the superblock read).  Run h of the quarter takes
+// high-bit bytes 16 (h & 1) .. +15 and bit 2g + (h >> 1); the nibbles sit at 48 + 32 g.
+// The bit is rotated into bit 4 of each byte and OR-ed onto the nibble: codes 0..31.
+struct Q5_KF {
+  struct Raw {
+    u32x4 hd, ha, hb, qa, qb;
+  };
+  static __device__ __forceinline__ int steps(int cols) { return ((cols >> 8) + 15) / 16; }
+  static __device__ __forceinline__ Raw load(const uint8_t* rowp, int cols, int step, int lane) {
+    const int nsb = cols >> 8;
+    int sb = step * 16 + (lane >> 2);
+    sb = sb < nsb ? sb : 0;
+    const int g = lane & 3;
+    const uint8_t* p = rowp + (size_t)sb * 176;
+    Raw r;
+    r.hd = wld16(p);
+    r.ha = wld16(p + 16);
+    r.hb = wld16(p + 32);
+    r.qa = wld16(p + 48 + 32 * g);
+    r.qb = wld16(p + 64 + 32 * g);
+    return r;
+  }
+  template <int NR>
+  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane, const XLimbs& xs,
+                                             float (&acc)[NR]) {
+    const int nsb = cols >> 8;
+    const int sb = step * 16 + (lane >> 2);
+    if (sb >= nsb) return;
+    const int g = lane & 3;
+    const int c0 = (sb << 8) + (g << 6);
+    const uint32_t m0f = vreg(0x0F0F0F0Fu), m10 = vreg(0x10101010u);
+    // rotations that bring bit 2g (runs 0, 1) and bit 2g + 1 (runs 2, 3) of each byte to bit 4
+    const uint32_t rot_a = (uint32_t)(2 * g + 28) & 31u, rot_b = (uint32_t)(2 * g + 29) & 31u;
+    int da[NR][XL], db[NR][XL];
+    zero_limbs(da);
+    zero_limbs(db);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const XRun x = x_run(xs, c0 + 16 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const uint32_t v = (h & 1) ? raw[k].qb[i] : raw[k].qa[i];
+          const uint32_t hv = (h & 1) ? raw[k].hb[i] : raw[k].ha[i];
+          if (h < 2)
+            dot_limbs(and_or(__builtin_amdgcn_alignbit(hv, hv, rot_a), m10, v & m0f), x, i, da[k]);
+          else
+            dot_limbs(and_or(__builtin_amdgcn_alignbit(hv, hv, rot_b), m10, (v >> 4) & m0f), x, i, db[k]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float sA = xs.sc[c0 >> 5], sB = xs.sc[(c0 >> 5) + 1];
+    const float xa = xs.s16[c0 >> 4] + xs.s16[(c0 >> 4) + 1];
+    const float xb = xs.s16[(c0 >> 4) + 2] + xs.s16[(c0 >> 4) + 3];
+    // scales and mins exactly as Q4_K's (same 12-byte packing at bytes 4..15)
+    const uint32_t p = 2u * (uint32_t)(g & 1);
+    const uint32_t sel = p | ((p + 1) << 8) | ((p + 4) << 16) | ((p + 5) << 24);
+    const bool upper = g >= 2;
+    const uint32_t mlow = vreg(upper ? 0x0F0F0F0Fu : 0x3F3F3F3Fu), mtop = vreg(upper ? 0x30303030u : 0u);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const uint32_t Y = raw[k].hd.y, Z = raw[k].hd.z, W = raw[k].hd.w;
+      const uint32_t yz = __builtin_amdgcn_perm(Z, Y, sel);
+      const uint32_t lo = upper ? __builtin_amdgcn_perm(W >> 4, W, sel) : yz;
       const uint32_t sm = and_or(yz >> 2, mtop, lo & mlow);
       const float d = h2f(raw[k].hd.x), dmin = h2f(raw[k].hd.x >> 16);
       acc[k] += (d * sA * ub0(sm)) * limb_sum(da[k]);
@@ -845,9 +923,10 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
   }
 }
 
-// Format "mask" of the kernel instantiated for q/k/v launches whose segments are Q4_K, Q4_K,
-// Q6_K in that order (the common Q4_K_M layer).
+// Format "masks" of the kernels instantiated for q/k/v launches whose segments are Q4_K,
+// Q4_K, Q6_K or Q5_K, Q5_K, Q6_K in that order (the Q4_K_M and Q5_K_M layers).
 constexpr int FMTS_Q4K_Q4K_Q6K = 1 << 8;
+constexpr int FMTS_Q5K_Q5K_Q6K = 1 << 9;
 
 // Segment s with its format's work loop (STAGE: the first segment, which stages x).
 template <int FMTMASK, int R, int EPI, bool STAGE>
@@ -863,6 +942,9 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
       break;
     case FMT_Q4_K:
       if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      break;
+    case FMT_Q5_K:
+      if constexpr ((FMTMASK >> FMT_Q5_K) & 1) run_segment<Q5_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
       break;
     default:
       if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
@@ -893,12 +975,13 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   // x is loaded first (its loads then complete before the weights'); the first segment
   // stages it after issuing its first weight loads
   const XPre xpre = stage_x_load(a);
-  if constexpr (FMTMASK == FMTS_Q4K_Q4K_Q6K) {
+  if constexpr (FMTMASK == FMTS_Q4K_Q4K_Q6K || FMTMASK == FMTS_Q5K_Q5K_Q6K) {
     // the three segments' formats fixed at compile time: straight-line code, so registers
     // are allocated per segment rather than for every format at every segment
     constexpr int D = GEMV_DEPTH<EPI>;
-    run_segment<Q4_KF, R, EPI, D, true>(a, 0, lane, wid, W, xs, red, best, rope, xpre);
-    run_segment<Q4_KF, R, EPI, D, false>(a, 1, lane, wid, W, xs, red, best, rope, XPre{});
+    using FK = std::conditional_t<FMTMASK == FMTS_Q4K_Q4K_Q6K, Q4_KF, Q5_KF>;
+    run_segment<FK, R, EPI, D, true>(a, 0, lane, wid, W, xs, red, best, rope, xpre);
+    run_segment<FK, R, EPI, D, false>(a, 1, lane, wid, W, xs, red, best, rope, XPre{});
     run_segment<Q6_KF, R, EPI, D, false>(a, 2, lane, wid, W, xs, red, best, rope, XPre{});
   } else {
     run_any<FMTMASK, R, EPI, true>(a, 0, lane, wid, W, xs, red, best, rope, xpre);
@@ -1430,13 +1513,20 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
     case 1 << FMT_Q4_0: return launch_nw<1 << FMT_Q4_0, EPI>(plan, n_groups, a, s);
     case 1 << FMT_Q4_K: return launch_nw<1 << FMT_Q4_K, EPI>(plan, n_groups, a, s);
     case 1 << FMT_Q6_K: return launch_nw<1 << FMT_Q6_K, EPI>(plan, n_groups, a, s);
+    case 1 << FMT_Q5_K: return launch_nw<1 << FMT_Q5_K, EPI>(plan, n_groups, a, s);
+    case (1 << FMT_Q5_K) | (1 << FMT_Q6_K):
+      if constexpr (EPI == EPI_QKV) {
+        if (a.nseg == 3 && a.seg[0].fmt == FMT_Q5_K && a.seg[1].fmt == FMT_Q5_K && a.seg[2].fmt == FMT_Q6_K)
+          return launch_nw<FMTS_Q5K_Q5K_Q6K, EPI>(plan, n_groups, a, s);
+      }
+      return launch_nw<(1 << FMT_Q5_K) | (1 << FMT_Q6_K), EPI>(plan, n_groups, a, s);
     case (1 << FMT_Q4_K) | (1 << FMT_Q6_K):
       if constexpr (EPI == EPI_QKV) {
         if (a.nseg == 3 && a.seg[0].fmt == FMT_Q4_K && a.seg[1].fmt == FMT_Q4_K && a.seg[2].fmt == FMT_Q6_K)
           return launch_nw<FMTS_Q4K_Q4K_Q6K, EPI>(plan, n_groups, a, s);
       }
       return launch_nw<(1 << FMT_Q4_K) | (1 << FMT_Q6_K), EPI>(plan, n_groups, a, s);
-    default: return launch_nw<15, EPI>(plan, n_groups, a, s);
+    default: return launch_nw<31, EPI>(plan, n_groups, a, s);
   }
 }
 
@@ -1481,8 +1571,8 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) 
     const GemvSeg& g = a.seg[i];
     if (st_family(g.fmt) != kf) return hipErrorNotSupported;
     // Q4_K measured faster on the register path (also with integer dot products here:
-    // 64.7 vs 49.9 us for the 70B gate/up pair)
-    if (g.fmt == FMT_Q4_K) return hipErrorNotSupported;
+    // 64.7 vs 49.9 us for the 70B gate/up pair); Q5_K, its 5-bit sibling, has only that path
+    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q5_K) return hipErrorNotSupported;
     if ((reinterpret_cast<uintptr_t>(g.w) & 15) || (g.row_bytes & 15) || g.rows <= 0) return hipErrorNotSupported;
   }
   if ((reinterpret_cast<uintptr_t>(a.x) & 15) || (a.gain && (reinterpret_cast<uintptr_t>(a.gain) & 15)))

@@ -26,8 +26,8 @@ __device__ void dequant_group(int fmt, const uint8_t* blk, int grp, float* out) 
       const int n = i < 16 ? (blk[2 + i] & 15) : (blk[2 + i - 16] >> 4);
       out[i] = d * (float)(n - 8);
     }
-  } else if (fmt == FMT_Q4_K) {
-    // grp = sub-block j (32 weights)
+  } else if (fmt == FMT_Q4_K || fmt == FMT_Q5_K) {
+    // grp = sub-block j (32 weights); Q5_K adds bit j of high byte l, worth 16
     const int j = grp;
     const float d = f16_at(blk), dmin = f16_at(blk + 2);
     const uint8_t* S = blk + 4;
@@ -40,9 +40,14 @@ __device__ void dequant_group(int fmt, const uint8_t* blk, int grp, float* out) 
       m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
     }
     const float dsc = d * (float)sc, dm = dmin * (float)m;
-    const uint8_t* Q = blk + 16 + 32 * (j >> 1);
+    const bool k5 = fmt == FMT_Q5_K;
+    const uint8_t* Q = blk + (k5 ? 48 : 16) + 32 * (j >> 1);
+    const uint8_t* H = blk + 16;
     const int shift = 4 * (j & 1);
-    for (int l = 0; l < 32; ++l) out[l] = dsc * (float)((Q[l] >> shift) & 15) - dm;
+    for (int l = 0; l < 32; ++l) {
+      const int q = ((Q[l] >> shift) & 15) + (k5 ? 16 * ((H[l] >> j) & 1) : 0);
+      out[l] = dsc * (float)q - dm;
+    }
   } else {
     // Q6_K, grp = 32-weight run: h = grp/4, t = grp%4
     const int h = grp >> 2, t = grp & 3;

@@ -4,7 +4,8 @@ Shapes are the public Llama-3-8B and Llama-3.1-70B dimensions.  The pages run
 Llama 8B in Q8_0 and Llama 3.1 70B in Q6_K and Q4_K_M (ntransformer overview,
 de.news.hada.io, "Roadmap der Entwicklungsphasen" and "Leistung und
 Caching-Struktur"; the 70B PCIe P2P article, blog.hotdry.top, §性能数据与瓶颈分析).
-The Q4_K_M mix is read as Q4_K everywhere except Q6_K for attn_v and ffn_down.
+The Q4_K_M mix is read as Q4_K everywhere except Q6_K for attn_v and ffn_down; the
+Q5_K_M mix (a format the overview lists, not a measured workload) the same with Q5_K.
 
 Every tensor has its own seed stream, so any tensor (or any row of it) can be
 regenerated alone, on either side of the comparison.
@@ -15,7 +16,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import (BLOCK_BYTES, BLOCK_ELEMS, Q4_K, Q6_K, Q8_0, fill_blocks, fill_normal_f16,
+from . import (BLOCK_BYTES, BLOCK_ELEMS, Q4_K, Q5_K, Q6_K, Q8_0, fill_blocks, fill_normal_f16,
                fill_uniform_f32, matrix_bytes, normal_f32, uniform_index)
 
 TENSORS = ("q", "k", "v", "o", "gate", "up", "down")
@@ -56,6 +57,7 @@ VOCAB_70B = 128256
 MIX_Q8_0 = {n: Q8_0 for n in TENSORS}
 MIX_Q6_K = {n: Q6_K for n in TENSORS}
 MIX_Q4_K_M = {n: (Q6_K if n in ("v", "down") else Q4_K) for n in TENSORS}
+MIX_Q5_K_M = {n: (Q6_K if n in ("v", "down") else Q5_K) for n in TENSORS}
 
 
 @dataclass

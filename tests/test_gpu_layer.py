@@ -110,11 +110,17 @@ def test_layer_70b_q6_k_full_size():
     run_layer_and_check(recipes.LLAMA31_70B, recipes.MIX_Q6_K, pos=4200, n_slots=4096, layer=3)
 
 
+def test_layer_70b_q5_k_m_full_size():
+    """The 70B-shaped layer in the Q5_K_M mix (Q5_K, with Q6_K for attn_v and ffn_down)."""
+    run_layer_and_check(recipes.LLAMA31_70B, recipes.MIX_Q5_K_M, pos=4100, n_slots=4096, layer=5)
+
+
 SMALL = recipes.LayerShape(dim=1024, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn_dim=2816, max_ctx=96)
 
 
 @pytest.mark.parametrize("mix,pos", [(recipes.MIX_Q4_K_M, 0), (recipes.MIX_Q8_0, 50), (recipes.MIX_Q6_K, 95),
-                                     ({n: synth.Q4_0 for n in recipes.TENSORS}, 17)])
+                                     ({n: synth.Q4_0 for n in recipes.TENSORS}, 17), (recipes.MIX_Q5_K_M, 33),
+                                     ({n: synth.Q5_K for n in recipes.TENSORS}, 64)])
 def test_layer_small_shapes(mix, pos):
     run_layer_and_check(SMALL, mix, pos=pos, n_slots=96)
 

@@ -14,13 +14,13 @@ import oracle
 import quantized_weight_streaming_dequant_amd as nt
 import synth
 from synth import recipes
-from tests.blockpack import pack_q4_0, pack_q4_k, pack_q6_k, pack_q8_0
+from tests.blockpack import pack_q4_0, pack_q4_k, pack_q5_k, pack_q6_k, pack_q8_0
 from tests.gpu_util import v_to_device, check_rel, dev, host, same_value, say, stream
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K]
-NAMES = {synth.Q8_0: "Q8_0", synth.Q4_0: "Q4_0", synth.Q4_K: "Q4_K", synth.Q6_K: "Q6_K"}
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K]
+NAMES = {synth.Q8_0: "Q8_0", synth.Q4_0: "Q4_0", synth.Q4_K: "Q4_K", synth.Q6_K: "Q6_K", synth.Q5_K: "Q5_K"}
 
 
 def gpu_gemv(fmt, rows, cols, blocks, x):
@@ -59,6 +59,9 @@ def test_dequant_hand_blocks_bit_exact():
          pack_q4_k(-2.0, 6.1e-5, list(range(56, 64)), list(range(8)), [(i * 7) % 16 for i in range(256)])),
         (synth.Q6_K, pack_q6_k(0.01, [-128, 127] * 8, [i % 64 for i in range(256)]) +
          pack_q6_k(-6.0e-8, [-64 + 8 * k for k in range(16)], [(i * 5 + 3) % 64 for i in range(256)])),
+        (synth.Q5_K, pack_q5_k(0.001, 0.01, [63] * 8, [63] * 8, [i % 32 for i in range(256)]) +
+         pack_q5_k(-2.0, 6.1e-5, list(range(56, 64)), list(range(8)), [(i * 7 + 16 * (i // 32 % 2)) % 32
+                                                                      for i in range(256)])),
     ]
     for fmt, raw in cases:
         blocks = np.frombuffer(raw, np.uint8)
@@ -81,6 +84,8 @@ GEMV_SHAPES = {
     synth.Q4_K: [(1, 256), (23, 1280), (130, 4352), (3, 12288), (8192, 8192), (1024, 8192), (28672, 8192),
                  (8192, 28672)],
     synth.Q6_K: [(1, 256), (19, 768), (77, 2304), (77, 6144), (5, 2048), (8192, 8192), (1024, 8192), (28672, 8192),
+                 (8192, 28672)],
+    synth.Q5_K: [(1, 256), (23, 1280), (130, 4352), (3, 12288), (8192, 8192), (1024, 8192), (28672, 8192),
                  (8192, 28672)],
 }
 GEMV_CASES = [(f, r, c) for f in FMTS for (r, c) in GEMV_SHAPES[f]]
