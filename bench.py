@@ -10,7 +10,7 @@ decode layers, final norm, LM head and argmax, every kernel in libnt.so.
 Prints one JSON line.  Other workloads (--config) print their own line for measurement
 runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B GEMV
 shapes in Q4_K, Q6_K and Q5_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
-host memory.
+host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes.
 """
 from __future__ import annotations
 
@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--layers", type=int, default=80, help="layers of the 70B model (measurement runs only)")
@@ -423,6 +423,57 @@ def bench_gemv_shapes(args, torch, nt, tg):
     }
 
 
+def bench_gemm_tokens(args, torch, nt, tg):
+    """The k-token GEMM (nt_gemm_q) at the 70B shapes for k = 1, 2, 4, 8: each weight read
+    once per call for all k tokens.  value = weight bytes per second at k = 4 on the
+    28672 x 8192 Q4_K shape; every (shape, k) is listed with its GEMV time beside it."""
+    import synth
+    steps = args.steps or 60
+    warmup = args.warmup if args.warmup is not None else 6
+    cs = torch.cuda.current_stream().cuda_stream
+    out = []
+    for fmt, rows, cols in ((synth.Q4_K, 28672, 8192), (synth.Q4_K, 8192, 8192), (synth.Q6_K, 8192, 28672),
+                            (synth.Q5_K, 28672, 8192)):
+        nbytes = synth.matrix_bytes(fmt, rows, cols)
+        copies = max(2, int(np.ceil(600e6 / nbytes)))
+        hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        ws = []
+        for k in range(copies):
+            synth.fill_blocks(hb.data_ptr(), fmt, nbytes // synth.BLOCK_BYTES[fmt], 0, 50 + k)
+            ws.append(hb.cuda())
+        gemv = rotating_gemv(torch, nt, fmt, rows, cols, copies, steps, warmup)
+        for k in (1, 2, 4, 8):
+            x = torch.from_numpy(np.stack([synth.normal_f32(cols, 0, 60 + t) for t in range(k)])).cuda()
+            y = torch.empty(k * rows, dtype=torch.float32, device="cuda")
+
+            def run(n):
+                for i in range(n):
+                    nt.nt_gemm_q(fmt, rows, cols, k, ws[i % copies].data_ptr(), x.data_ptr(), y.data_ptr(), cs)
+
+            run(warmup)
+            torch.cuda.synchronize()
+            r = timed_class(nt, torch, nt.K_GEMM, lambda: run(steps), nbytes + 4 * k * (rows + cols))
+            r.update({"format": synth.FORMAT_NAMES[fmt], "rows": rows, "cols": cols, "tokens": k,
+                      "gemv_us": gemv["avg_us"], "time_vs_gemv": r["avg_us"] / gemv["avg_us"],
+                      "token_rows_per_us": k * rows / r["avg_us"]})
+            log(f"  {r['format']} {rows}x{cols} k={k}: {r['avg_us']:.2f} us ({r['time_vs_gemv']:.2f}x the GEMV's "
+                f"{gemv['avg_us']:.2f} us), weights at {r['GBps']:.0f} GB/s")
+            out.append(r)
+        del ws
+        torch.cuda.empty_cache()
+    head = next(r for r in out if r["format"] == "Q4_K" and r["rows"] == 28672 and r["tokens"] == 4)
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": head["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": head["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "quantized weights, f32 math", "data": "synthetic",
+        "config": {"workload": "k-token quantized GEMM (self-speculative verification), 70B shapes, k = 1, 2, 4, 8"},
+        "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["GBps"] / HBM_PEAK_GBS, "traffic": None},
+        "gemm": out,
+    }
+
+
 def bench_layer_8b(args, torch, nt, tg):
     import synth
     from synth import recipes
@@ -556,6 +607,8 @@ def main():
         res = bench_gemv_shapes(args, torch, nt, tg)
     elif args.config == 2:
         res = bench_layer_8b(args, torch, nt, tg)
+    elif args.config == 6:
+        res = bench_gemm_tokens(args, torch, nt, tg)
     else:
         res = bench_stream_70b(args, torch, nt, tg)
     print(json.dumps(res), flush=True)

@@ -88,6 +88,21 @@ int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w
  * (fp32 accumulation, scale factors applied per block). */
 int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream);
 
+/* Largest token count of nt_gemm_q. */
+#define NT_GEMM_MAX_TOK 8
+
+/* y[t*rows + r] = sum_c W[r][c] x[t*cols + c] for t < n_tok: the GEMV for n_tok tokens
+ * at once, reading each weight once.  This is the weight-bound step of the verification
+ * pass of self-speculative decoding, where the draft tokens proposed by the VRAM-resident
+ * layers meet the whole model in one pass (ntransformer overview, "Hauptfunktionen").
+ * 1 <= n_tok <= NT_GEMM_MAX_TOK; x: n_tok x cols fp32, 16-byte aligned; y: n_tok x rows
+ * fp32, overwritten, must not overlap x or blocks; blocks: 16-byte aligned; cols a positive
+ * multiple of the block size (any width: wide matrices run as several launches over column
+ * chunks, each adding into y); rows <= 2^31 - 1.  Per token, the accuracy of nt_gemv_q.
+ * Errors as nt_gemv_q, and NT_ESHAPE for n_tok out of range; nothing is enqueued then. */
+int nt_gemm_q(int fmt, int64_t rows, int64_t cols, int n_tok, const void* blocks, const float* x, float* y,
+              void* stream);
+
 /* RMSNorm: y_i = gain_i * x_i / sqrt(mean_j x_j^2 + eps)  (eps inside the root).
  * ntransformer overview, "Hauptfunktionen" (RMSNorm).  y may equal x.  n <= 2^24. */
 int nt_rmsnorm(int64_t n, const float* x, const float* gain, float eps, float* y, void* stream);
@@ -261,8 +276,8 @@ size_t nt_decode_token_ws_bytes(const nt_layer_shape* shp);
  * on the launching stream (adds small gaps; for measurement runs only).  The first
  * five are the launches of a decode layer, NT_K_LM_HEAD the LM head of
  * nt_decode_token / nt_model_head; NT_K_ATTN also covers nt_attn_decode and
- * NT_K_GEMV covers nt_gemv_q. */
-enum { NT_K_ATTN_IN = 0, NT_K_ATTN, NT_K_O, NT_K_FFN_UP, NT_K_FFN_DOWN, NT_K_LM_HEAD, NT_K_GEMV, NT_K_COUNT };
+ * NT_K_GEMV covers nt_gemv_q, NT_K_GEMM nt_gemm_q (one interval per call). */
+enum { NT_K_ATTN_IN = 0, NT_K_ATTN, NT_K_O, NT_K_FFN_UP, NT_K_FFN_DOWN, NT_K_LM_HEAD, NT_K_GEMV, NT_K_GEMM, NT_K_COUNT };
 /* Start timing launches of kernel class kclass (one class at a time); up to
  * max_launches launches are recorded.  Creates events on the current device. */
 int nt_timing_begin(int kclass, int max_launches);

@@ -142,6 +142,18 @@ def gemv(fmt: int, rows: int, cols: int, blocks, x, row_idx=None):
     return y, nrm
 
 
+def gemm(fmt: int, rows: int, cols: int, blocks, X, row_idx=None):
+    """(Y, NRM) in fp64 for n_tok tokens at once: row t of X (n_tok x cols) is token t's
+    activation vector, and Y[t], NRM[t] are gemv() of it.  The verification pass of
+    self-speculative decoding (ntransformer overview, "Hauptfunktionen") applies every
+    weight matrix to all draft tokens; per token this is the plain GEMV."""
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    if X.shape[1] != cols:
+        raise ValueError("X has the wrong width")
+    out = [gemv(fmt, rows, cols, blocks, X[t], row_idx) for t in range(X.shape[0])]
+    return np.stack([o[0] for o in out]), np.stack([o[1] for o in out])
+
+
 def rmsnorm(x, g, eps: float) -> np.ndarray:
     x = _c(x, np.float64).ravel()
     g = _c(g, np.float64).ravel()

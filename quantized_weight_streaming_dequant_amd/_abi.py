@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libnt.so")
 Q8_0, Q4_0, Q4_K, Q6_K, Q5_K = 0, 1, 2, 3, 4
 NT_OK, NT_EINVAL, NT_EFORMAT, NT_ESHAPE, NT_EALIGN, NT_EHOSTMEM, NT_EHIP = 0, -1, -2, -3, -4, -5, -6
 W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN, W_COUNT = range(8)
-K_ATTN_IN, K_ATTN, K_O, K_FFN_UP, K_FFN_DOWN, K_LM_HEAD, K_GEMV = range(7)
+K_ATTN_IN, K_ATTN, K_O, K_FFN_UP, K_FFN_DOWN, K_LM_HEAD, K_GEMV, K_GEMM = range(8)
+GEMM_MAX_TOK = 8
 GEMV_MAX_COLS = NT_GEMV_MAX_COLS = 32768
 NT_MAX_CTX = 524288  # cache capacity limit (slots); KV cache max_ctx must also be a multiple of 8
 
@@ -65,7 +66,7 @@ class ModelHead(ctypes.Structure):
 _lib = None
 
 EXPORTS = [
-    "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q",
+    "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q", "nt_gemm_q",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
     "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
     "nt_stream_destroy", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_timing_begin",
@@ -91,6 +92,7 @@ def load(path: str = LIB_PATH):
         "nt_matrix_bytes": ([i, i64, i64], i64),
         "nt_dequant": ([i, i64, i64, vp, vp, vp], i),
         "nt_gemv_q": ([i, i64, i64, vp, vp, vp, vp], i),
+        "nt_gemm_q": ([i, i64, i64, i, vp, vp, vp, vp], i),
         "nt_rmsnorm": ([i64, vp, vp, f, vp, vp], i),
         "nt_rope": ([i, i, i, f, vp, vp], i),
         "nt_attn_decode": ([i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp], i),
@@ -151,6 +153,10 @@ def nt_dequant(fmt, rows, cols, blocks, w, stream=None):
 
 def nt_gemv_q(fmt, rows, cols, blocks, x, y, stream=None):
     return _check(load().nt_gemv_q(fmt, rows, cols, blocks, x, y, stream))
+
+
+def nt_gemm_q(fmt, rows, cols, n_tok, blocks, x, y, stream=None):
+    return _check(load().nt_gemm_q(fmt, rows, cols, n_tok, blocks, x, y, stream))
 
 
 def nt_rmsnorm(n, x, gain, eps, y, stream=None):

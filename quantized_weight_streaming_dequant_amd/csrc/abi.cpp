@@ -296,6 +296,20 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
   return e == hipSuccess ? NT_OK : hip_fail(e, "gemv launch");
 }
 
+int nt_gemm_q(int fmt, int64_t rows, int64_t cols, int n_tok, const void* blocks, const float* x, float* y,
+              void* stream) {
+  if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
+  if (rows <= 0 || rows > 0x7FFFFFFF || cols <= 0 || cols > 0x7FFFFFFF || cols % block_elems(fmt))
+    return fail(NT_ESHAPE, "need 0 < rows < 2^31 and cols a positive multiple of %d (got %lld x %lld)", block_elems(fmt),
+                (long long)rows, (long long)cols);
+  if (n_tok < 1 || n_tok > NT_GEMM_MAX_TOK) return fail(NT_ESHAPE, "n_tok must be in [1, %d]", NT_GEMM_MAX_TOK);
+  if (!blocks || !x || !y) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return fail(NT_EALIGN, "blocks and x must be 16-byte aligned, y 4-byte");
+  TimedLaunch tl(NT_K_GEMM, (hipStream_t)stream);
+  hipError_t e = gemm_launch(fmt, reinterpret_cast<const uint8_t*>(blocks), rows, cols, n_tok, x, y, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "gemm launch");
+}
+
 int nt_rmsnorm(int64_t n, const float* x, const float* gain, float eps, float* y, void* stream) {
   if (n <= 0 || n > (1 << 24)) return fail(NT_ESHAPE, "n must be in [1, 2^24]");
   if (!x || !gain || !y) return fail(NT_EINVAL, "null pointer");

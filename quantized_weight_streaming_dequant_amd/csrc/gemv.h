@@ -55,4 +55,12 @@ int gemv_groups(const GemvPlan& p, int rows);
 // launch's row groups over all segments.
 hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s);
 
+// k-token GEMM: y[t][r] = sum_c W[r][c] x[t][c] for t < n_tok (1..GEMM_MAX_TOK), x [n_tok][cols],
+// y [n_tok][rows], all device fp32; one launch per column chunk (the weights are read once).
+constexpr int GEMM_MAX_TOK = 8;
+hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int n_tok, const float* x, float* y,
+                       hipStream_t s);
+// Columns per launch for n_tok tokens (a multiple of the block size); exposed for the tests.
+int gemm_chunk_cols(int n_tok, int cols, int block_elems);
+
 }  // namespace nt

@@ -106,6 +106,11 @@ static_assert(XL == 2 || XL == 3, "two or three limbs");
 
 __host__ __device__ __forceinline__ int xq_off(int c) { return c + ((c >> 6) << 4); }
 __host__ __device__ __forceinline__ int xq_plane(int cols) { return (xq_off(cols) + 15) & ~15; }
+// LDS bytes of one token's staged chunk in the k-token GEMM: limb planes, a scale per 32
+// columns and a sum per 16, rounded to 16 bytes
+__host__ __device__ __forceinline__ size_t gemm_lds_per_token(int cols) {
+  return ((size_t)XL * xq_plane(cols) + sizeof(float) * (size_t)((cols >> 5) + (cols >> 4)) + 15) & ~(size_t)15;
+}
 
 // The staged activation vector, as the register-path kernels see it in LDS.
 struct XLimbs {
@@ -1003,6 +1008,232 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
 }
 
 
+// ================================================================== k-token GEMM
+//
+// Y[t] = W X[t] for t < n_tok tokens at once (the verification pass of self-speculative
+// decoding: the draft tokens, which come from the VRAM-resident layers, meet every weight
+// of the full model in one pass; ntransformer overview, de.news.hada.io,
+// "Hauptfunktionen").  The register path with a token dimension: a workgroup stages the
+// NT activation vectors as limbs, one LDS region each; a wave's row blocks are loaded once
+// per step and dotted with every token's limbs (the code unpacking is shared: it depends
+// on the loaded bytes only), so the weights are read once for all NT tokens.  Tokens past
+// n_tok are staged as zeros and never stored.  A launch covers a column chunk: the host
+// splits wide matrices so that NT chunks of x fit in LDS, and every chunk after the first
+// adds into Y (stream order separates the chunks).
+
+struct GemmArgs {
+  const uint8_t* w;  // first block of the chunk in row 0
+  int64_t row_bytes; // of the whole matrix
+  int rows;
+  int cols;          // of the chunk
+  int n_tok;
+  const float* x;    // token 0's chunk; token t at x + t * xld
+  int64_t xld;
+  float* y;          // token t's outputs at y + t * yld
+  int64_t yld;
+  int accum;         // add into y
+};
+
+// Q4_K and Q5_K in the k-token GEMM: an item's codes (four 8-bit codes per dword, per run
+// of 16 columns) and its scale factors d sc and dmin m are decoded once and then dotted
+// with each token's limbs, so that the unpacking is not repeated per token.
+template <int NR>
+struct KDec {
+  uint32_t code[NR][4][4];  // [row][run h][dword]
+  float dA[NR], dB[NR], mA[NR], mB[NR];  // d sc and dmin m of sub-blocks 2g and 2g + 1
+  int c0;
+  bool ok;
+};
+
+template <typename F, int NR>
+__device__ __forceinline__ void kdecode(const typename F::Raw (&raw)[NR], int cols, int step, int lane, KDec<NR>& D) {
+  constexpr bool K5 = std::is_same<F, Q5_KF>::value;
+  const int sb = step * 16 + (lane >> 2);
+  D.ok = sb < (cols >> 8);
+  const int g = lane & 3;
+  D.c0 = (sb << 8) + (g << 6);
+  const uint32_t m0f = 0x0F0F0F0Fu, m10 = 0x10101010u;
+  const uint32_t rot_a = (uint32_t)(2 * g + 28) & 31u, rot_b = (uint32_t)(2 * g + 29) & 31u;
+#pragma unroll
+  for (int k = 0; k < NR; ++k)
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t v = (h & 1) ? raw[k].qb[i] : raw[k].qa[i];
+        uint32_t c = h < 2 ? (v & m0f) : ((v >> 4) & m0f);
+        if constexpr (K5) {
+          const uint32_t hv = (h & 1) ? raw[k].hb[i] : raw[k].ha[i];
+          c = and_or(__builtin_amdgcn_alignbit(hv, hv, h < 2 ? rot_a : rot_b), m10, c);
+        }
+        D.code[k][h][i] = c;
+      }
+  // the 6-bit scales and mins of sub-blocks 2g, 2g + 1, gathered as in the GEMV formats
+  const uint32_t p = 2u * (uint32_t)(g & 1);
+  const uint32_t sel = p | ((p + 1) << 8) | ((p + 4) << 16) | ((p + 5) << 24);
+  const bool upper = g >= 2;
+  const uint32_t mlow = upper ? 0x0F0F0F0Fu : 0x3F3F3F3Fu, mtop = upper ? 0x30303030u : 0u;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const uint32_t Y = raw[k].hd.y, Z = raw[k].hd.z, W = raw[k].hd.w;
+    const uint32_t yz = __builtin_amdgcn_perm(Z, Y, sel);
+    const uint32_t lo = upper ? __builtin_amdgcn_perm(W >> 4, W, sel) : yz;
+    const uint32_t sm = and_or(yz >> 2, mtop, lo & mlow);
+    const float d = h2f(raw[k].hd.x), dmin = h2f(raw[k].hd.x >> 16);
+    D.dA[k] = d * ub0(sm);
+    D.dB[k] = d * ub1(sm);
+    D.mA[k] = dmin * ub2(sm);
+    D.mB[k] = dmin * ub3(sm);
+  }
+}
+
+template <int NR>
+__device__ __forceinline__ void kapply(const KDec<NR>& D, const XLimbs& xs, float (&acc)[NR]) {
+  if (!D.ok) return;
+  int da[NR][XL], db[NR][XL];
+  zero_limbs(da);
+  zero_limbs(db);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const XRun x = x_run(xs, D.c0 + 16 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < NR; ++k) dot_limbs(D.code[k][h][i], x, i, h < 2 ? da[k] : db[k]);
+  }
+  const float sA = xs.sc[D.c0 >> 5], sB = xs.sc[(D.c0 >> 5) + 1];
+  const float xa = xs.s16[D.c0 >> 4] + xs.s16[(D.c0 >> 4) + 1];
+  const float xb = xs.s16[(D.c0 >> 4) + 2] + xs.s16[(D.c0 >> 4) + 3];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    acc[k] += (D.dA[k] * sA) * limb_sum(da[k]);
+    acc[k] += (D.dB[k] * sB) * limb_sum(db[k]);
+    acc[k] -= D.mA[k] * xa + D.mB[k] * xb;
+  }
+}
+
+template <typename F, int NT, int R>
+__device__ __forceinline__ void gemm_rows(const GemmArgs& a, const XLimbs (&xs)[NT], int lane, int wid, int W) {
+  typedef typename F::Raw Raw;
+  const int n_groups = (a.rows + R - 1) / R;
+  const int nsteps = F::steps(a.cols);
+  const int n_items = wid < n_groups ? ((n_groups - 1 - wid) / W + 1) * nsteps : 0;
+  if (n_items == 0) return;
+  int lk = wid, lt = 0;
+  auto issue = [&](Raw (&buf)[R]) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int r = min(lk * R + j, a.rows - 1);  // past-the-end rows re-read the last row; results dropped
+      buf[j] = F::load(a.w + (size_t)r * a.row_bytes, a.cols, lt, lane);
+    }
+    if (++lt == nsteps) {
+      lt = 0;
+      lk += W;
+    }
+  };
+  Raw b0[R], b1[R];
+  issue(b0);
+  float acc[NT][R];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[t][j] = 0.f;
+  int ck = wid, ct = 0, item = 0;
+  auto step = [&](const Raw (&cur)[R], Raw (&refill)[R]) -> bool {
+    issue(refill);  // unconditional: the wait for this item leaves the next one in flight
+    if constexpr (std::is_same<F, Q4_KF>::value || std::is_same<F, Q5_KF>::value) {
+      KDec<R> dec;
+      kdecode<F, R>(cur, a.cols, ct, lane, dec);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) kapply<R>(dec, xs[t], acc[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) F::template fma<R>(cur, a.cols, ct, lane, xs[t], acc[t]);
+    }
+    if (ct == nsteps - 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[t][j] = wave_sum(acc[t][j]);
+        const int r = ck * R + lane;
+        if (t < a.n_tok && lane < R && r < a.rows) {
+          float v = acc[t][0];
+#pragma unroll
+          for (int j = 1; j < R; ++j) v = (lane == j) ? acc[t][j] : v;
+          float* yp = a.y + (size_t)t * a.yld + r;
+          *yp = a.accum ? *yp + v : v;
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[t][j] = 0.f;
+      }
+    }
+    if (++ct == nsteps) {
+      ct = 0;
+      ck += W;
+    }
+    return ++item < n_items;
+  };
+  for (;;) {
+    if (!step(b0, b1)) break;
+    if (!step(b1, b0)) break;
+  }
+}
+
+// Stage token t's chunk of x (zeros for t >= n_tok) into its limb region: a thread takes
+// 16 columns per round, as stage_x does, without a norm.
+__device__ __forceinline__ void gemm_stage(const GemmArgs& a, int t, const XLimbs& xs, int nthreads) {
+  const int ng = a.cols >> 4;
+  const float* x = a.x + (size_t)t * a.xld;
+  for (int gi = (int)threadIdx.x; gi < ng; gi += nthreads) {
+    float v[16];
+    if (t < a.n_tok) {
+      const float4* src = reinterpret_cast<const float4*>(x + gi * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 q = src[i];
+        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.f;
+    }
+    stage_group(xs, gi, v);
+  }
+}
+
+// Rows per item: two, or one where two rows' loads in both ring buffers, the decoded codes
+// and NT tokens' accumulators would not fit the registers (Q5_K: five 128-bit loads per row;
+// Q4_K from two tokens on; Q6_K at 8 tokens).
+template <int FMT, int NT>
+constexpr int GEMM_ROWS = (FMT == FMT_Q5_K || (FMT == FMT_Q4_K && NT >= 2) || (FMT == FMT_Q6_K && NT == 8)) ? 1 : 2;
+
+template <int FMT, int NT, int NW>
+__global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
+  extern __shared__ float4 smem4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wid = (int)blockIdx.x * NW + wave;
+  const int W = (int)gridDim.x * NW;
+  const size_t per_tok = gemm_lds_per_token(a.cols);
+  XLimbs xs[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    uint8_t* base = reinterpret_cast<uint8_t*>(smem4) + t * per_tok;
+    xs[t].q = base;
+    xs[t].plane = xq_plane(a.cols);
+    xs[t].sc = reinterpret_cast<float*>(base + XL * xs[t].plane);
+    xs[t].s16 = xs[t].sc + (a.cols >> 5);
+    gemm_stage(a, t, xs[t], NW * 64);
+  }
+  __syncthreads();
+  constexpr int R = GEMM_ROWS<FMT, NT>;
+  if constexpr (FMT == FMT_Q8_0) gemm_rows<Q8_0F, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_Q4_0) gemm_rows<Q4_0F, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_Q4_K) gemm_rows<Q4_KF, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_Q5_K) gemm_rows<Q5_KF, NT, R>(a, xs, lane, wid, W);
+  else gemm_rows<Q6_KF, NT, R>(a, xs, lane, wid, W);
+}
+
 // ================================================================== streamed GEMV
 //
 // Column-stationary layout for shapes whose rows are 16-byte aligned.  A workgroup owns a
@@ -1652,4 +1883,75 @@ hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups
   }
 }
 
+// ---- k-token GEMM launcher
+constexpr size_t GEMM_LDS_MAX = 160 * 1024 - 1024;  // dynamic LDS budget (static LDS on top)
+
+template <int FMT, int NT>
+static hipError_t gemm_launch_nt(const GemmArgs& a, hipStream_t s) {
+  constexpr int NW = 16;
+  auto kern = gemm_kernel<FMT, NT, NW>;
+  static bool raised = false;
+  if (!raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)GEMM_LDS_MAX);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  const size_t lds = (size_t)NT * gemm_lds_per_token(a.cols);
+  constexpr int R = GEMM_ROWS<FMT, NT>;
+  const int groups = (a.rows + R - 1) / R;
+  const int grid = max(1, min((groups + NW - 1) / NW, num_cu()));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t gemm_launch_fmt(int nt, const GemmArgs& a, hipStream_t s) {
+  if (nt <= 1) return gemm_launch_nt<FMT, 1>(a, s);
+  if (nt <= 2) return gemm_launch_nt<FMT, 2>(a, s);
+  if (nt <= 4) return gemm_launch_nt<FMT, 4>(a, s);
+  return gemm_launch_nt<FMT, 8>(a, s);
+}
+
+int gemm_chunk_cols(int n_tok, int cols, int be) {
+  const int nt = n_tok <= 1 ? 1 : n_tok <= 2 ? 2 : n_tok <= 4 ? 4 : 8;
+  // the widest multiple of 256 columns (a superblock, eight 32-weight blocks) whose NT
+  // limb regions fit, and no wider than the matrix
+  int c = 256;
+  while (c + 256 <= cols && (size_t)nt * gemm_lds_per_token(c + 256) <= GEMM_LDS_MAX) c += 256;
+  if (c > cols) c = cols;
+  return c - c % be;
+}
+
+hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int n_tok, const float* x, float* y,
+                       hipStream_t s) {
+  const int be = block_elems(fmt), bb = block_bytes(fmt);
+  const int chunk = gemm_chunk_cols(n_tok, (int)cols, be);
+  if (chunk <= 0) return hipErrorInvalidValue;
+  GemmArgs a;
+  a.row_bytes = (int64_t)(cols / be) * bb;
+  a.rows = (int)rows;
+  a.n_tok = n_tok;
+  a.xld = cols;
+  a.y = y;
+  a.yld = rows;
+  for (int64_t c0 = 0; c0 < cols; c0 += chunk) {
+    a.cols = (int)(cols - c0 < chunk ? cols - c0 : chunk);
+    a.w = w + (c0 / be) * bb;
+    a.x = x + c0;
+    a.accum = c0 > 0;
+    hipError_t e;
+    switch (fmt) {
+      case FMT_Q8_0: e = gemm_launch_fmt<FMT_Q8_0>(n_tok, a, s); break;
+      case FMT_Q4_0: e = gemm_launch_fmt<FMT_Q4_0>(n_tok, a, s); break;
+      case FMT_Q4_K: e = gemm_launch_fmt<FMT_Q4_K>(n_tok, a, s); break;
+      case FMT_Q5_K: e = gemm_launch_fmt<FMT_Q5_K>(n_tok, a, s); break;
+      default: e = gemm_launch_fmt<FMT_Q6_K>(n_tok, a, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace nt
+

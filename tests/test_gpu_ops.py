@@ -102,6 +102,54 @@ def test_gemv_matches_oracle(fmt, rows, cols):
     say(f"  worst rel err {worst:.2e}")
 
 
+def gpu_gemm(fmt, rows, cols, n_tok, blocks, X):
+    wb = dev(blocks)
+    xd = dev(np.ascontiguousarray(X, dtype=np.float32).ravel())
+    y = torch.full((n_tok * rows,), float("nan"), dtype=torch.float32, device="cuda")
+    nt.nt_gemm_q(fmt, rows, cols, n_tok, wb.data_ptr(), xd.data_ptr(), y.data_ptr(), stream())
+    return host(y).reshape(n_tok, rows)
+
+
+GEMM_CASES = [
+    # (format, rows, cols, tokens): single blocks, ragged row counts, token counts that fill
+    # the kernels' 1/2/4/8-token variants partly, the 70B shapes, and widths that run as
+    # several column chunks (each adding into y)
+    (synth.Q8_0, 1, 32, 8), (synth.Q8_0, 37, 2144, 3), (synth.Q8_0, 4096, 14336, 5), (synth.Q4_0, 29, 1440, 6),
+    (synth.Q4_K, 1, 256, 1), (synth.Q4_K, 130, 4352, 2), (synth.Q4_K, 8192, 8192, 4), (synth.Q4_K, 1024, 8192, 8),
+    (synth.Q4_K, 28672, 8192, 4), (synth.Q4_K, 8192, 28672, 7),
+    (synth.Q6_K, 77, 2304, 7), (synth.Q6_K, 8192, 28672, 8), (synth.Q6_K, 1024, 8192, 3),
+    (synth.Q5_K, 23, 1280, 6), (synth.Q5_K, 8192, 8192, 8), (synth.Q5_K, 28672, 8192, 2),
+]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,n_tok", GEMM_CASES)
+def test_gemm_matches_oracle(fmt, rows, cols, n_tok):
+    say(f"gemm {NAMES[fmt]} {rows}x{cols} x {n_tok} tokens")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=8, stream=700 + fmt)
+    X = np.stack([synth.normal_f32(cols, seed=8, stream=800 + t) for t in range(n_tok)])
+    Y = gpu_gemm(fmt, rows, cols, n_tok, blocks, X)
+    ref, nrm = oracle.gemm(fmt, rows, cols, blocks, X.astype(np.float64))
+    worst = 0.0
+    for t in range(n_tok):
+        worst = max(worst, check_rel(Y[t], ref[t], nrm[t], what=f"{NAMES[fmt]} {rows}x{cols} token {t}"))
+    say(f"  worst rel err {worst:.2e}")
+
+
+def test_gemm_one_token_matches_gemv_and_tokens_are_independent():
+    """A token's outputs do not depend on the other tokens of the call, and one token gives
+    what the GEMV gives (both are within the tolerance of the same exact values)."""
+    fmt, rows, cols = synth.Q4_K, 512, 8192
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=9, stream=900)
+    X = np.stack([synth.normal_f32(cols, seed=9, stream=901 + t) for t in range(4)])
+    Y4 = gpu_gemm(fmt, rows, cols, 4, blocks, X)
+    Y2 = gpu_gemm(fmt, rows, cols, 2, blocks, X[2:])
+    assert np.array_equal(Y4[2:], Y2)
+    y1 = gpu_gemv(fmt, rows, cols, blocks, X[1])
+    ref, nrm = oracle.gemv(fmt, rows, cols, blocks, X[1].astype(np.float64))
+    check_rel(y1, ref, nrm, what="gemv")
+    check_rel(Y4[1], ref, nrm, what="gemm token 1")
+
+
 OUTLIER_KINDS = {
     # multiplier per column on top of N(0, 1): one channel per 32 columns at 100x, a single
     # channel at 10^4x, three channels at 2000x (the shapes of large outlier activations)

@@ -291,6 +291,23 @@ def test_gemv_one_hot_picks_a_column(fmt):
         assert np.array_equal(nrm, np.abs(w[:, j]))
 
 
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q8_0])
+def test_gemm_token_t_is_row_t(fmt):
+    """Token t of X is X's row t and lands in Y's row t: one-hot tokens pick their columns."""
+    rows, cols = 6, 512
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=6, stream=50 + fmt)
+    w = oracle.dequant_exact(fmt, rows, cols, blocks)
+    picks = [5, 300, 0, 511, 37]
+    X = np.zeros((len(picks), cols))
+    for t, c in enumerate(picks):
+        X[t, c] = 2.0 ** -t
+    Y, N = oracle.gemm(fmt, rows, cols, blocks, X)
+    assert Y.shape == (len(picks), rows)
+    for t, c in enumerate(picks):
+        assert np.array_equal(Y[t], w[:, c] * 2.0 ** -t)
+        assert np.array_equal(N[t], np.abs(w[:, c]) * 2.0 ** -t)
+
+
 def test_gemv_constant_blocks_and_zero_x():
     # every weight equal: y = w * sum(x)
     blk = pack_q8_0(0.25, [3] * 32)
