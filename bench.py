@@ -10,7 +10,8 @@ decode layers, final norm, LM head and argmax, every kernel in libnt.so.
 Prints one JSON line.  Other workloads (--config) print their own line for measurement
 runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B GEMV
 shapes in Q4_K, Q6_K and Q5_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
-host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes.
+host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes, 7 = the 70B model with
+cosine-based layer skip (--skip layers, default 20 of 80).
 """
 from __future__ import annotations
 
@@ -39,7 +40,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6])
+    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6, 7])
+    p.add_argument("--skip", type=int, default=20, help="layers to skip in --config 7")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--layers", type=int, default=80, help="layers of the 70B model (measurement runs only)")
@@ -185,7 +187,7 @@ class Model70B:
         torch.cuda.synchronize()
         log(f"  model ready in {time.time() - t0:.1f}s")
 
-    def plan(self):
+    def plan(self, skip=()):
         tg, nt = self.tg, self.nt
         shp = tg.layer_shape(self.shape)
         lay = tg.layer_layout(self.lay.offset_list(), self.lay.fmt_list(), self.lay.nbytes)
@@ -195,7 +197,7 @@ class Model70B:
                 ents.append((self.dev_blobs[l].data_ptr(), True, self.kc[l].data_ptr(), self.vc[l].data_ptr()))
             else:
                 ents.append((self.host_blobs[l].data_ptr(), False, self.kc[l].data_ptr(), self.vc[l].data_ptr()))
-        return tg.model_plan(shp, lay, ents)
+        return tg.model_plan(shp, lay, ents, skip)
 
     def layer_weights(self, l):
         """nt_layer_weights of resident layer l (pointers into its blob)."""
@@ -474,6 +476,70 @@ def bench_gemm_tokens(args, torch, nt, tg):
     }
 
 
+def bench_layer_skip_70b(args, torch, nt, tg):
+    """Cosine-based layer skip on the resident 70B Q4_K_M model: one calibration token runs the
+    layers one by one and records cos(h before, h after) per layer (nt_layer_cosine); the
+    args.skip layers with the highest similarity are then skipped while decoding.  With random
+    weights only the mechanism and its speed are meaningful, not the choice of layers."""
+    from synth import recipes
+    steps = args.steps if args.steps is not None else 128
+    warmup = args.warmup if args.warmup is not None else 4
+    mix = recipes.MIX_Q4_K_M
+    n_layers = args.layers
+    log(f"config 7: 70B Q4_K_M, {n_layers} layers, the {args.skip} most input-like layers skipped")
+    m = Model70B(torch, nt, tg, mix, n_layers, range(n_layers))
+    head = m.head()
+    shp = tg.layer_shape(m.shape)
+    wsb = nt.nt_decode_token_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(m.shape.dim, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(m.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cs = torch.cuda.current_stream().cuda_stream
+    # calibration: the first token's embedding row through the layers at pos 4096, one at a time
+    tok.fill_(m.first_token)
+    nt.nt_embed_row(m.embd_fmt, m.vocab, m.shape.dim, m.embd.data_ptr(), tok.data_ptr(), h.data_ptr(), cs)
+    cos = torch.zeros(n_layers, dtype=torch.float32, device="cuda")
+    h_in = torch.empty_like(h)
+    for l in range(n_layers):
+        h_in.copy_(h)
+        nt.nt_decode_layer(m.layer_weights(l), shp, 4096, h.data_ptr(), m.kc[l].data_ptr(), m.vc[l].data_ptr(),
+                           ws.data_ptr(), wsb, cs)
+        nt.nt_layer_cosine(m.shape.dim, h_in.data_ptr(), h.data_ptr(), cos[l:].data_ptr(), cs)
+    torch.cuda.synchronize()
+    cv = cos.cpu().numpy()
+    skip = sorted(int(i) for i in np.argsort(-cv, kind="stable")[:args.skip])
+    plan, keep = m.plan(skip=set(skip))
+    full, keep_full = m.plan()
+
+    def run(p, n):
+        tok.fill_(m.first_token)
+        for i in range(n):
+            nt.nt_decode_token(None, p, head, 4096 + i, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                               ws.data_ptr(), wsb, cs, cs, None)
+
+    res_t = {}
+    for name, p in (("all layers", full), ("skipping", plan)):
+        run(p, warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(p, steps)
+        torch.cuda.synchronize()
+        res_t[name] = steps / (time.perf_counter() - t0)
+        log(f"  {name}: {res_t[name]:.2f} tok/s")
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": res_t["skipping"], "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": 1e3 / res_t["skipping"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4_k/q6_k weights, f32 math, f16 kv", "data": "synthetic (seeded, random weights of the named shape)",
+        "config": {"workload": f"llama3.1-70b-shape Q4_K_M resident decode with cosine layer skip ({args.skip} of "
+                               f"{n_layers} layers), 4096-slot fp16 KV prefill, greedy, batch 1",
+                   "layers": n_layers, "skipped": skip},
+        "tok_s_all_layers": res_t["all layers"],
+        "layer_cosine": [float(v) for v in cv],
+    }
+
+
 def bench_layer_8b(args, torch, nt, tg):
     import synth
     from synth import recipes
@@ -609,6 +675,8 @@ def main():
         res = bench_layer_8b(args, torch, nt, tg)
     elif args.config == 6:
         res = bench_gemm_tokens(args, torch, nt, tg)
+    elif args.config == 7:
+        res = bench_layer_skip_70b(args, torch, nt, tg)
     else:
         res = bench_stream_70b(args, torch, nt, tg)
     print(json.dumps(res), flush=True)

@@ -201,6 +201,14 @@ int nt_embed_row(int fmt, int64_t n_vocab, int64_t dim, const void* table, const
 /* *out_index = first index of the maximum of v[0..n) (greedy pick; ties -> lowest index). */
 int nt_argmax(int64_t n, const float* v, int32_t* out_index, void* stream);
 
+/* *out = sum_i a_i b_i / sqrt(sum_i a_i^2 * sum_i b_i^2), or 0 if a or b is all zeros: the
+ * cosine similarity of a layer's input and output hidden states, by which cosine-based layer
+ * skip ranks layers (ntransformer overview, "Leistung und Caching-Struktur": 20 of 80 layers
+ * skipped).  Sums in fp64; |error| below 1e-6.  a, b: device [n], n in [1, 2^24]; out:
+ * device, one float.  A calibration pass keeps a copy of h before each layer, runs the
+ * layer, and calls this on (copy, h). */
+int nt_layer_cosine(int64_t n, const float* a, const float* b, float* out, void* stream);
+
 /* ------------------------------------------------------- models, streaming */
 
 /* Where each tensor of a layer sits in one contiguous layer blob (bytes). */
@@ -215,6 +223,10 @@ typedef struct {
   int resident;         /* 1: run in place; 0: stream through a staging buffer */
   uint16_t* k_cache;    /* device, fp16, the KV cache layout above */
   uint16_t* v_cache;
+  int skip;             /* 1: layer skip: the layer is not run (h passes through unchanged, its
+                           cache is not written, a streamed blob is not copied); the caller picks
+                           the layers, e.g. those whose nt_layer_cosine of input and output is
+                           highest (ntransformer overview, "Leistung und Caching-Struktur") */
 } nt_layer_entry;
 
 typedef struct {

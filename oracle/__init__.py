@@ -190,6 +190,16 @@ def swiglu(gate, up):
     return out, nrm
 
 
+def cosine(a, b) -> float:
+    """sum a b / sqrt(sum a^2 sum b^2) in fp64, 0 if a or b is all zeros: the similarity of a
+    layer's input and output by which cosine-based layer skip ranks layers (ntransformer
+    overview, "Leistung und Caching-Struktur")."""
+    a = _c(a, np.float64).ravel()
+    b = _c(b, np.float64).ravel()
+    den = np.sqrt(np.dot(a, a) * np.dot(b, b))
+    return float(np.dot(a, b) / den) if den > 0 else 0.0
+
+
 def argmax(v) -> int:
     v = _c(v, np.float64).ravel()
     return int(lib().or_argmax(v.size, v.ctypes.data))

@@ -251,7 +251,7 @@ struct nt_streamer {
   hipEvent_t ready[2], freed[2];
   bool freed_recorded[2];
   const void* plan_layers;  // identity of the plan the sequence counters belong to
-  int n_streamed;
+  std::vector<int> streamed;  // and its streamed, unskipped layers
   int64_t c_run;    // next streamed-layer sequence number to run
   int64_t c_issue;  // next streamed-layer sequence number to copy
 };
@@ -421,6 +421,14 @@ int nt_argmax(int64_t n, const float* v, int32_t* out_index, void* stream) {
   return e == hipSuccess ? NT_OK : hip_fail(e, "argmax launch");
 }
 
+int nt_layer_cosine(int64_t n, const float* a, const float* b, float* out, void* stream) {
+  if (n <= 0 || n > (1 << 24)) return fail(NT_ESHAPE, "n must be in [1, 2^24]");
+  if (!a || !b || !out) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(out, 4)) return fail(NT_EALIGN, "a, b and out must be 4-byte aligned");
+  hipError_t e = cosine_launch(n, a, b, out, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "cosine launch");
+}
+
 int nt_stream_create(void* staging0, void* staging1, size_t staging_bytes, nt_streamer** out) {
   if (!out) return fail(NT_EINVAL, "out is null");
   *out = nullptr;
@@ -441,7 +449,6 @@ int nt_stream_create(void* staging0, void* staging1, size_t staging_bytes, nt_st
     st->freed_recorded[b] = false;
   }
   st->plan_layers = nullptr;
-  st->n_streamed = 0;
   st->c_run = st->c_issue = 0;
   *out = st;
   return NT_OK;
@@ -500,11 +507,11 @@ static int stream_issue(nt_streamer* st, const nt_model_plan* plan, const std::v
 
 static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, uint8_t* ws,
                               hipStream_t compute, hipStream_t copy, nt_stream_stats* stats) {
-  std::vector<int> streamed;
+  std::vector<int> streamed;  // the layers copied through the staging buffers, in order
   for (int l = 0; l < plan->n_layers; ++l)
-    if (!plan->layers[l].resident) streamed.push_back(l);
+    if (!plan->layers[l].resident && !plan->layers[l].skip) streamed.push_back(l);
   if (st && !streamed.empty()) {
-    if (st->plan_layers != (const void*)plan->layers || st->n_streamed != (int)streamed.size()) {
+    if (st->plan_layers != (const void*)plan->layers || st->streamed != streamed) {
       // a new plan: drain what the streamer had in flight, then restart its sequence
       for (int b = 0; b < 2; ++b) {
         (void)hipEventSynchronize(st->ready[b]);
@@ -512,7 +519,7 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
         st->freed_recorded[b] = false;
       }
       st->plan_layers = plan->layers;
-      st->n_streamed = (int)streamed.size();
+      st->streamed = streamed;
       st->c_run = st->c_issue = 0;
     }
   }
@@ -522,6 +529,7 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
       if ((rc = stream_issue(st, plan, streamed, copy, stats))) return rc;
   for (int l = 0; l < plan->n_layers; ++l) {
     const nt_layer_entry& ent = plan->layers[l];
+    if (ent.skip) continue;
     if (ent.resident) {
       const nt_layer_weights w = weights_in_blob(reinterpret_cast<const uint8_t*>(ent.blob), plan->layout);
       if ((rc = run_layer(w, plan->shape, pos, h, ent.k_cache, ent.v_cache, ws, compute))) return rc;

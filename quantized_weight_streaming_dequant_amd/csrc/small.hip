@@ -220,4 +220,44 @@ hipError_t token_from_key_launch(const unsigned long long* key, int32_t* token, 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ cosine similarity
+// out = sum a b / sqrt(sum a^2 sum b^2), 0 if either vector is zero: the similarity of a
+// layer's input and output that cosine-based layer skip ranks layers by (ntransformer
+// overview, "Leistung und Caching-Struktur").  One workgroup; the sums in fp64, so the
+// result is the exact value to within a few units of fp32 rounding.
+__global__ __launch_bounds__(256) void cosine_kernel(int64_t n, const float* __restrict__ a, const float* __restrict__ b,
+                                                     float* out) {
+  __shared__ double red[3][4];
+  double ab = 0.0, aa = 0.0, bb = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    const double x = a[i], y = b[i];
+    ab += x * y;
+    aa += x * x;
+    bb += y * y;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    ab += __shfl_xor(ab, off, 64);
+    aa += __shfl_xor(aa, off, 64);
+    bb += __shfl_xor(bb, off, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = ab;
+    red[1][w] = aa;
+    red[2][w] = bb;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s[3];
+    for (int k = 0; k < 3; ++k) s[k] = (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]);
+    const double den = sqrt(s[1] * s[2]);
+    out[0] = den > 0.0 ? (float)(s[0] / den) : 0.f;
+  }
+}
+
+hipError_t cosine_launch(int64_t n, const float* a, const float* b, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(cosine_kernel, dim3(1), dim3(256), 0, s, n, a, b, out);
+  return hipGetLastError();
+}
+
 }  // namespace nt

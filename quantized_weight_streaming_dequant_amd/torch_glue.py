@@ -44,14 +44,16 @@ def layer_layout(offsets: list[int], fmts: list[int], blob_bytes: int) -> _abi.L
     return lay
 
 
-def model_plan(shape: _abi.LayerShape, layout: _abi.LayerLayout, entries: list[tuple[int, bool, int, int]]):
-    """entries: (blob address, resident, k_cache address, v_cache address) per layer.
-    Returns (plan, keepalive); keep the second value alive while the plan is used."""
+def model_plan(shape: _abi.LayerShape, layout: _abi.LayerLayout, entries: list[tuple], skip=()):
+    """entries: (blob address, resident, k_cache address, v_cache address) per layer; skip:
+    the layers to skip.  Returns (plan, keepalive); keep the second value alive while the
+    plan is used (its entries' skip fields may be changed in place)."""
     arr = (_abi.LayerEntry * len(entries))()
     for i, (blob, resident, kc, vc) in enumerate(entries):
         arr[i].blob = blob
         arr[i].resident = 1 if resident else 0
         arr[i].k_cache = kc
         arr[i].v_cache = vc
+        arr[i].skip = 1 if i in skip else 0
     plan = _abi.ModelPlan(shape, layout, len(entries), ctypes.cast(arr, ctypes.POINTER(_abi.LayerEntry)))
     return plan, arr

@@ -173,26 +173,28 @@ class Model:
         return ([dev(k) for k in self.kc0],
                 [dev(v_to_device(v, self.shape.n_kv_heads, self.shape.max_ctx)) for v in self.vc0])
 
-    def plan(self, kcs, vcs, streamed=None):
+    def plan(self, kcs, vcs, streamed=None, skip=(), layers=None):
+        """layers: the layer indices the plan lists (default all), in order."""
         streamed = self.streamed if streamed is None else streamed
+        layers = range(self.n_layers) if layers is None else layers
         shp = tg.layer_shape(self.shape)
         lay = tg.layer_layout(self.lay.offset_list(), self.lay.fmt_list(), self.lay.nbytes)
         ents = []
-        for l in range(self.n_layers):
+        for l in layers:
             if l in streamed:
                 ents.append((self.blobs_host[l].data_ptr(), False, kcs[l].data_ptr(), vcs[l].data_ptr()))
             else:
                 ents.append((self.blobs_dev[l].data_ptr(), True, kcs[l].data_ptr(), vcs[l].data_ptr()))
-        return tg.model_plan(shp, lay, ents)
+        return tg.model_plan(shp, lay, ents, skip={i for i, l in enumerate(layers) if l in skip})
 
     def head(self):
         return nt.ModelHead(synth.Q4_K, self.embd_d.data_ptr(), self.vocab, self.onorm_d.data_ptr(), synth.Q4_K,
                             self.out_d.data_ptr())
 
 
-def decode_tokens(model, streamed, tok0, pos0, n_tokens, staging=None):
+def decode_tokens(model, streamed, tok0, pos0, n_tokens, staging=None, skip=(), layers=None):
     kcs, vcs = model.caches()
-    plan, keep = model.plan(kcs, vcs, streamed)
+    plan, keep = model.plan(kcs, vcs, streamed, skip, layers)
     shp = tg.layer_shape(model.shape)
     wsb = nt.nt_decode_token_ws_bytes(shp)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
@@ -274,6 +276,66 @@ def test_token_step_matches_layer_calls():
     assert same_value(host(h), hs[0])
     for l in range(3):
         assert same_value(host(kd[l]), kcs[l]) and same_value(host(vd[l]), vcs[l])
+
+
+def test_layer_skip_equals_leaving_the_layers_out():
+    """Skipped layers are not run: decoding with layers 1 and 2 of 4 skipped gives bit for bit
+    what a plan listing only layers 0 and 3 gives, the skipped layers' caches are untouched,
+    and a skipped streamed layer is not copied (layers 2 and 3 streamed, 2 skipped)."""
+    say("layer skip vs a plan without the layers")
+    m = Model(TINY, recipes.MIX_Q4_K_M, 4, vocab=1000, n_slots=32)
+    tok0 = synth.uniform_index(1000, 0, 78)
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    a = decode_tokens(m, set(), tok0, 32, 3, skip={1, 2})
+    b = decode_tokens(m, set(), tok0, 32, 3, layers=[0, 3])
+    c = decode_tokens(m, {2, 3}, tok0, 32, 3, staging, skip={1, 2})
+    assert a[0] == b[0] == c[0]
+    for x, y, z in zip(a[1] + a[2], b[1] + b[2], c[1] + c[2]):
+        assert same_value(x, y) and same_value(x, z)
+    kc0 = [dev(k) for k in m.kc0]
+    for l in (1, 2):
+        assert same_value(a[3][l], host(kc0[l])) and same_value(c[3][l], host(kc0[l]))
+    assert same_value(a[3][3], c[3][3]) and not same_value(a[3][3], host(kc0[3]))
+    assert c[5].layers_streamed == 1
+    # the run is still the model's: the last token's logits against the checker on the GPU's h
+    n = oracle.rmsnorm(a[1][-1], m.onorm, TINY.eps)
+    ref, nrm = oracle.gemv(synth.Q4_K, 1000, TINY.dim, m.out, n)
+    check_rel(a[2][-1], ref, nrm, what="logits with layers skipped")
+
+
+def test_layer_cosine_calibration():
+    """The calibration pass: cos(h before, h after) per layer, on the GPU, matches the checker's
+    cosine of the same vectors; the kernel also meets the closed forms."""
+    say("layer cosine calibration")
+    for n, kind in ((1, "same"), (7, "neg"), (8192, "rand"), (28672, "rand"), (1 << 20, "rand"), (8192, "zero"),
+                    (8192, "orth")):
+        a = synth.normal_f32(n, 1, 7)
+        b = {"same": a, "neg": -a, "rand": synth.normal_f32(n, 1, 8), "zero": np.zeros(n, np.float32)}.get(kind)
+        if kind == "orth":
+            r = synth.normal_f32(n, 1, 9).astype(np.float64)
+            b = (r - a * (r @ a) / (a @ a.astype(np.float64))).astype(np.float32)
+        out = torch.zeros(1, dtype=torch.float32, device="cuda")
+        ad, bd = dev(a), dev(b)  # both alive across the call
+        nt.nt_layer_cosine(n, ad.data_ptr(), bd.data_ptr(), out.data_ptr(), stream())
+        got, ref = float(host(out)[0]), oracle.cosine(a, b)
+        assert abs(got - ref) <= 1e-6, (n, kind, got, ref)
+    m = Model(TINY, recipes.MIX_Q4_K_M, 3, vocab=100, n_slots=16)
+    kd, vd = m.caches()
+    shp = tg.layer_shape(TINY)
+    wsb = nt.nt_decode_layer_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = dev(recipes.hidden_input(TINY.dim))
+    cos = torch.zeros(3, dtype=torch.float32, device="cuda")
+    for l in range(3):
+        blob = m.blobs_dev[l]
+        mats = [blob[m.lay.offsets[nm]:] for nm in recipes.TENSORS]
+        w = tg.layer_weights(m.lay.fmt_list(), mats, blob[m.lay.offsets["attn_norm"]:].view(torch.float32),
+                             blob[m.lay.offsets["ffn_norm"]:].view(torch.float32))
+        h_in = h.clone()
+        nt.nt_decode_layer(w, shp, 16, h.data_ptr(), kd[l].data_ptr(), vd[l].data_ptr(), ws.data_ptr(), wsb, stream())
+        nt.nt_layer_cosine(TINY.dim, h_in.data_ptr(), h.data_ptr(), cos[l:].data_ptr(), stream())
+        torch.cuda.synchronize()
+        assert abs(float(host(cos)[l]) - oracle.cosine(host(h_in), host(h))) <= 1e-6
 
 
 def test_streaming_70b_q6_k_layer_bit_identical():

@@ -461,6 +461,25 @@ def test_swiglu_matches_torch_silu_and_limits():
     assert np.all(nrm >= np.abs(out))
 
 
+def test_cosine_closed_forms():
+    a = RNG.normal(size=1000)
+    assert abs(oracle.cosine(a, a) - 1.0) < 1e-15
+    assert abs(oracle.cosine(a, -a) + 1.0) < 1e-15
+    assert abs(oracle.cosine(3.0 * a, 0.5 * a) - 1.0) < 1e-15
+    assert oracle.cosine(a, np.zeros(1000)) == 0.0 and oracle.cosine(np.zeros(3), np.zeros(3)) == 0.0
+    # the angle in a plane
+    for th in (0.0, 0.3, 1.0, math.pi / 2, 2.5, math.pi):
+        assert abs(oracle.cosine([1.0, 0.0], [math.cos(th), math.sin(th)]) - math.cos(th)) < 1e-15
+    # orthogonal by construction: b minus its projection on a
+    b = RNG.normal(size=1000)
+    b -= a * (b @ a) / (a @ a)
+    assert abs(oracle.cosine(a, b)) < 1e-12
+    # scale invariance and symmetry on unrelated vectors, against the textbook formula by hand
+    c = RNG.normal(size=1000)
+    ref = sum(x * y for x, y in zip(a, c)) / math.sqrt(sum(x * x for x in a) * sum(y * y for y in c))
+    assert abs(oracle.cosine(a, c) - ref) < 1e-12 and abs(oracle.cosine(c, 7.0 * a) - ref) < 1e-12
+
+
 def test_argmax_ties_lowest():
     assert oracle.argmax([1.0, 3.0, 3.0, -1.0]) == 1
     assert oracle.argmax([-5.0]) == 0
