@@ -11,7 +11,8 @@ Prints one JSON line.  Other workloads (--config) print their own line for measu
 runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B GEMV
 shapes in Q4_K, Q6_K and Q5_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
 host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes, 7 = the 70B model with
-cosine-based layer skip (--skip layers, default 20 of 80).
+cosine-based layer skip (--skip layers, default 20 of 80), 8 = 70B Q6_K layers read from a file
+(--file-layers, default 8) through page-locked bounce buffers.
 """
 from __future__ import annotations
 
@@ -40,8 +41,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6, 7])
+    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     p.add_argument("--skip", type=int, default=20, help="layers to skip in --config 7")
+    p.add_argument("--file-layers", type=int, default=8, help="layers read from a file in --config 8")
+    p.add_argument("--read-threads", type=int, default=8, help="reader threads per blob in --config 8")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--layers", type=int, default=80, help="layers of the 70B model (measurement runs only)")
@@ -651,6 +654,89 @@ def bench_stream_70b(args, torch, nt, tg):
     }
 
 
+def bench_file_tier_70b(args, torch, nt, tg):
+    """The file tier: 70B Q6_K layer blobs written to one file, then decoded with every layer read
+    through the page cache into page-locked bounce buffers (args.read_threads pread threads per
+    blob), copied to the staging buffers and run; the same layers from pinned host memory beside
+    it.  value = file-tier bytes per second (read + H2D, overlapped with compute)."""
+    import tempfile
+    from synth import recipes
+    steps = args.steps or 3
+    warmup = args.warmup if args.warmup is not None else 1
+    mix = recipes.MIX_Q6_K
+    n_layers = args.file_layers
+    log(f"config 8: 70B Q6_K, {n_layers} layers read from a file (page cache), {args.read_threads} readers per blob")
+    m = Model70B(torch, nt, tg, mix, n_layers, [])
+    nb = m.lay.nbytes
+    stride = (nb + 4095) // 4096 * 4096
+    fdir = os.environ.get("TMPDIR", "/tmp")
+    f = tempfile.NamedTemporaryFile(dir=fdir, prefix="nt_layers_", suffix=".bin", delete=False)
+    path = f.name
+    try:
+        for l in range(n_layers):
+            f.seek(l * stride)
+            f.write(memoryview(m.host_blobs[l].numpy()))
+        f.close()
+        fd = os.open(path, os.O_RDONLY)
+        shp = tg.layer_shape(m.shape)
+        lay = tg.layer_layout(m.lay.offset_list(), m.lay.fmt_list(), nb)
+        ents = [(0, nt.TIER_FILE, m.kc[l].data_ptr(), m.vc[l].data_ptr(), fd, l * stride) for l in range(n_layers)]
+        fplan, keep_f = tg.model_plan(shp, lay, ents)
+        pplan, keep_p = m.plan()
+        head = m.head()
+        wsb = nt.nt_decode_token_ws_bytes(shp)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        h = torch.zeros(m.shape.dim, dtype=torch.float32, device="cuda")
+        logits = torch.zeros(m.vocab, dtype=torch.float32, device="cuda")
+        tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+        staging = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        bounce = []
+        for _ in range(2):
+            t = torch.empty(nb + 4096, dtype=torch.uint8, pin_memory=True)
+            off = (-t.data_ptr()) % 4096
+            bounce.append(t[off:off + nb])
+        st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), nb)
+        nt.nt_stream_set_bounce(st, bounce[0].data_ptr(), bounce[1].data_ptr(), nb, args.read_threads)
+        compute = torch.cuda.current_stream()
+        copy = torch.cuda.Stream()
+        stats = nt.StreamStats()
+        res = {}
+        try:
+            for name, plan in (("file", fplan), ("pinned", pplan)):
+                def run(n):
+                    tok.fill_(m.first_token)
+                    tot = 0
+                    for i in range(n):
+                        nt.nt_decode_token(st, plan, head, 4096 + i, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                                           ws.data_ptr(), wsb, compute.cuda_stream, copy.cuda_stream, stats)
+                        tot += stats.h2d_bytes
+                    return tot
+
+                run(warmup)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                moved = run(steps)
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                res[name] = {"tok_s": steps / dt, "GBps": moved / dt / 1e9, "bytes_per_token": moved / steps}
+                log(f"  {name}: {steps / dt:.2f} tok/s, {moved / dt / 1e9:.1f} GB/s of layer blobs")
+        finally:
+            torch.cuda.synchronize()
+            nt.nt_stream_destroy(st)
+            os.close(fd)
+    finally:
+        os.unlink(path)
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": res["file"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": 1e3 / res["file"]["tok_s"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q6_k weights, f32 math, f16 kv", "data": "synthetic",
+        "config": {"workload": f"llama3.1-70b-shape Q6_K, {n_layers} layers read from a file through the page cache, "
+                               f"{args.read_threads} readers per blob", "layers": n_layers},
+        "file_tier": res["file"], "pinned_tier": res["pinned"],
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -677,6 +763,8 @@ def main():
         res = bench_gemm_tokens(args, torch, nt, tg)
     elif args.config == 7:
         res = bench_layer_skip_70b(args, torch, nt, tg)
+    elif args.config == 8:
+        res = bench_file_tier_70b(args, torch, nt, tg)
     else:
         res = bench_stream_70b(args, torch, nt, tg)
     print(json.dumps(res), flush=True)

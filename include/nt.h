@@ -218,15 +218,24 @@ typedef struct {
   int64_t blob_bytes;
 } nt_layer_layout;
 
+/* Where a layer's blob lives (ntransformer overview, "Leistung und Caching-Struktur": VRAM-
+ * resident layers, pinned RAM for H2D transfers, and a file fallback; "Hauptfunktionen": the
+ * data path picks the fastest tier that holds the layer). */
+enum { NT_TIER_PINNED = 0, NT_TIER_RESIDENT = 1, NT_TIER_FILE = 2 };
+
 typedef struct {
-  const void* blob;     /* device pointer if resident, else page-locked HOST pointer */
-  int resident;         /* 1: run in place; 0: stream through a staging buffer */
+  const void* blob;     /* device pointer if resident, page-locked HOST pointer if pinned, unused for a file */
+  int resident;         /* NT_TIER_RESIDENT: run in place; NT_TIER_PINNED: copied from host memory into a
+                           staging buffer; NT_TIER_FILE: read from fd at file_offset into the streamer's
+                           page-locked bounce buffers, then copied into a staging buffer */
   uint16_t* k_cache;    /* device, fp16, the KV cache layout above */
   uint16_t* v_cache;
   int skip;             /* 1: layer skip: the layer is not run (h passes through unchanged, its
                            cache is not written, a streamed blob is not copied); the caller picks
                            the layers, e.g. those whose nt_layer_cosine of input and output is
                            highest (ntransformer overview, "Leistung und Caching-Struktur") */
+  int fd;               /* NT_TIER_FILE: an open file descriptor readable with pread */
+  int64_t file_offset;  /* NT_TIER_FILE: byte offset of the blob in that file */
 } nt_layer_entry;
 
 typedef struct {
@@ -251,14 +260,24 @@ typedef struct nt_streamer nt_streamer;
 int nt_stream_create(void* staging0, void* staging1, size_t staging_bytes, nt_streamer** out);
 void nt_stream_destroy(nt_streamer* st);
 
+/* Give a streamer the page-locked host bounce buffers (bounce_bytes each, caller-owned,
+ * 4096-byte aligned) that NT_TIER_FILE layers are read into before their H2D copy, and the
+ * number of host threads (1..64) that read each blob in parallel pieces with pread.  The
+ * three stages of a file layer -- read into a bounce buffer, copy to a staging buffer,
+ * compute -- overlap across layers: while the GPU runs layer n, the calling thread reads
+ * layer n + 2 (70B PCIe P2P article, §gpu-nvme-direct的实现架构: a three-stage pipeline;
+ * here through the page cache, without the raw-device path). */
+int nt_stream_set_bounce(nt_streamer* st, void* bounce0, void* bounce1, size_t bounce_bytes, int n_threads);
+
 /* Run all plan->n_layers layers for the token at pos over h (in/out, [dim]).
  * Resident layers run in place on `compute`.  A streamed layer's blob is copied
  * by hipMemcpyAsync on `copy` into a free staging buffer as soon as that buffer
  * frees (the compute stream records "free" events, the copy stream "ready"
  * events), so copies run ahead of compute and across calls: at the end of a
  * call the first streamed layers of the next token are already in flight.
- * Streamed blobs must be page-locked host memory (NT_EHOSTMEM otherwise) and
- * fit staging_bytes.  ws as for nt_decode_layer.  compute != copy.  stats nullable.
+ * Pinned blobs must be page-locked host memory (NT_EHOSTMEM otherwise); file layers need
+ * bounce buffers (nt_stream_set_bounce; NT_EINVAL otherwise), and a short or failed read is
+ * NT_EHOSTMEM.  Every streamed blob must fit staging_bytes.  ws as for nt_decode_layer.  compute != copy.  stats nullable.
  * A streamer must be used with one plan at a time, from one host thread. */
 int nt_stream_layers(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, void* ws, size_t ws_bytes,
                      void* compute, void* copy, nt_stream_stats* stats);

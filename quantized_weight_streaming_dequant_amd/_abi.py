@@ -18,6 +18,7 @@ NT_OK, NT_EINVAL, NT_EFORMAT, NT_ESHAPE, NT_EALIGN, NT_EHOSTMEM, NT_EHIP = 0, -1
 W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN, W_COUNT = range(8)
 K_ATTN_IN, K_ATTN, K_O, K_FFN_UP, K_FFN_DOWN, K_LM_HEAD, K_GEMV, K_GEMM = range(8)
 GEMM_MAX_TOK = 8
+TIER_PINNED, TIER_RESIDENT, TIER_FILE = 0, 1, 2
 GEMV_MAX_COLS = NT_GEMV_MAX_COLS = 32768
 NT_MAX_CTX = 524288  # cache capacity limit (slots); KV cache max_ctx must also be a multiple of 8
 
@@ -46,7 +47,8 @@ class LayerLayout(ctypes.Structure):
 
 class LayerEntry(ctypes.Structure):
     _fields_ = [("blob", ctypes.c_void_p), ("resident", ctypes.c_int), ("k_cache", ctypes.c_void_p),
-                ("v_cache", ctypes.c_void_p), ("skip", ctypes.c_int)]
+                ("v_cache", ctypes.c_void_p), ("skip", ctypes.c_int), ("fd", ctypes.c_int),
+                ("file_offset", ctypes.c_int64)]
 
 
 class ModelPlan(ctypes.Structure):
@@ -69,7 +71,7 @@ EXPORTS = [
     "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q", "nt_gemm_q", "nt_layer_cosine",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
     "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
-    "nt_stream_destroy", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_timing_begin",
+    "nt_stream_destroy", "nt_stream_set_bounce", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_timing_begin",
     "nt_timing_end",
 ]
 
@@ -107,6 +109,7 @@ def load(path: str = LIB_PATH):
         "nt_argmax": ([i64, vp, vp, vp], i),
         "nt_stream_create": ([vp, vp, sz, ctypes.POINTER(vp)], i),
         "nt_stream_destroy": ([vp], None),
+        "nt_stream_set_bounce": ([vp, vp, vp, sz, i], i),
         "nt_stream_layers": ([vp, ctypes.POINTER(ModelPlan), i, vp, vp, sz, vp, vp, ctypes.POINTER(StreamStats)], i),
         "nt_decode_token": ([vp, ctypes.POINTER(ModelPlan), ctypes.POINTER(ModelHead), i, vp, vp, vp, vp, sz, vp, vp,
                              ctypes.POINTER(StreamStats)], i),
@@ -221,6 +224,10 @@ def nt_stream_create(staging0, staging1, staging_bytes) -> int:
 
 def nt_stream_destroy(st) -> None:
     load().nt_stream_destroy(st)
+
+
+def nt_stream_set_bounce(st, bounce0, bounce1, bounce_bytes, n_threads=4):
+    return _check(load().nt_stream_set_bounce(st, bounce0, bounce1, bounce_bytes, n_threads))
 
 
 def nt_stream_layers(st, plan: ModelPlan, pos, h, ws, ws_bytes, compute, copy, stats: StreamStats | None = None):

@@ -6,8 +6,12 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <errno.h>
+#include <unistd.h>
+
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/nt.h"
@@ -250,6 +254,11 @@ struct nt_streamer {
   size_t bytes;
   hipEvent_t ready[2], freed[2];
   bool freed_recorded[2];
+  uint8_t* bounce[2];       // page-locked host buffers for file-tier layers (null: none)
+  size_t bounce_bytes;
+  int n_threads;            // readers per blob
+  hipEvent_t bounce_free[2];  // recorded after the H2D copy out of bounce[b]
+  bool bounce_recorded[2];
   const void* plan_layers;  // identity of the plan the sequence counters belong to
   std::vector<int> streamed;  // and its streamed, unskipped layers
   int64_t c_run;    // next streamed-layer sequence number to run
@@ -448,9 +457,48 @@ int nt_stream_create(void* staging0, void* staging1, size_t staging_bytes, nt_st
     }
     st->freed_recorded[b] = false;
   }
+  st->bounce[0] = st->bounce[1] = nullptr;
+  st->bounce_bytes = 0;
+  st->n_threads = 1;
+  st->bounce_recorded[0] = st->bounce_recorded[1] = false;
   st->plan_layers = nullptr;
   st->c_run = st->c_issue = 0;
   *out = st;
+  return NT_OK;
+}
+
+int nt_stream_set_bounce(nt_streamer* st, void* bounce0, void* bounce1, size_t bounce_bytes, int n_threads) {
+  if (!st) return fail(NT_EINVAL, "null streamer");
+  if (!bounce0 || !bounce1 || bounce0 == bounce1) return fail(NT_EINVAL, "need two distinct bounce buffers");
+  if (!aligned(bounce0, 4096) || !aligned(bounce1, 4096)) return fail(NT_EALIGN, "bounce buffers must be 4096-byte aligned");
+  if (bounce_bytes == 0) return fail(NT_EINVAL, "bounce_bytes is 0");
+  if (n_threads < 1 || n_threads > 64) return fail(NT_EINVAL, "n_threads must be in [1, 64]");
+  for (void* p : {bounce0, bounce1}) {
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof(attr));
+    hipError_t he = hipPointerGetAttributes(&attr, p);
+    if (he != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(NT_EHOSTMEM, "bounce buffers must be page-locked host memory");
+    }
+  }
+  if (!st->bounce[0]) {
+    for (int b = 0; b < 2; ++b) {
+      hipError_t e = hipEventCreateWithFlags(&st->bounce_free[b], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        if (b == 1) (void)hipEventDestroy(st->bounce_free[0]);
+        return hip_fail(e, "hipEventCreate");
+      }
+    }
+  } else {
+    for (int b = 0; b < 2; ++b)
+      if (st->bounce_recorded[b]) (void)hipEventSynchronize(st->bounce_free[b]);  // the old buffers' copies are done
+  }
+  st->bounce[0] = reinterpret_cast<uint8_t*>(bounce0);
+  st->bounce[1] = reinterpret_cast<uint8_t*>(bounce1);
+  st->bounce_bytes = bounce_bytes;
+  st->n_threads = n_threads;
+  st->bounce_recorded[0] = st->bounce_recorded[1] = false;
   return NT_OK;
 }
 
@@ -462,20 +510,37 @@ void nt_stream_destroy(nt_streamer* st) {
     (void)hipEventDestroy(st->ready[b]);
     (void)hipEventDestroy(st->freed[b]);
   }
+  if (st->bounce[0]) {
+    for (int b = 0; b < 2; ++b) {
+      (void)hipEventSynchronize(st->bounce_free[b]);
+      (void)hipEventDestroy(st->bounce_free[b]);
+    }
+  }
   delete st;
 }
 
-static int check_plan(const nt_model_plan* plan, bool need_resident) {
+static int check_plan(const nt_model_plan* plan, const nt_streamer* st) {
   if (!plan || !plan->layers || plan->n_layers <= 0) return fail(NT_EINVAL, "empty plan");
   int rc = check_shape(&plan->shape);
   if (rc) return rc;
   if ((rc = check_layout(plan->shape, plan->layout))) return rc;
   for (int l = 0; l < plan->n_layers; ++l) {
     const nt_layer_entry& e = plan->layers[l];
-    if (!e.blob || !e.k_cache || !e.v_cache) return fail(NT_EINVAL, "layer %d has a null pointer", l);
+    if (e.resident != NT_TIER_PINNED && e.resident != NT_TIER_RESIDENT && e.resident != NT_TIER_FILE)
+      return fail(NT_EINVAL, "layer %d has an unknown tier %d", l, e.resident);
+    if (!e.k_cache || !e.v_cache) return fail(NT_EINVAL, "layer %d has a null cache pointer", l);
+    if (e.resident != NT_TIER_RESIDENT && !st)
+      return fail(NT_EINVAL, "layer %d is not resident and no streamer was given", l);
+    if (e.resident == NT_TIER_FILE) {
+      if (e.fd < 0 || e.file_offset < 0) return fail(NT_EINVAL, "layer %d: bad file descriptor or offset", l);
+      if (!st->bounce[0]) return fail(NT_EINVAL, "layer %d is read from a file but the streamer has no bounce buffers", l);
+      if ((size_t)plan->layout.blob_bytes > st->bounce_bytes)
+        return fail(NT_EINVAL, "layer blob larger than the bounce buffers");
+      continue;
+    }
+    if (!e.blob) return fail(NT_EINVAL, "layer %d has a null blob", l);
     if (!aligned(e.blob, 256)) return fail(NT_EALIGN, "layer %d blob must be 256-byte aligned", l);
-    if (!e.resident) {
-      if (need_resident) return fail(NT_EINVAL, "layer %d is not resident and no streamer was given", l);
+    if (e.resident == NT_TIER_PINNED) {
       hipPointerAttribute_t attr;
       memset(&attr, 0, sizeof(attr));
       hipError_t he = hipPointerGetAttributes(&attr, e.blob);
@@ -488,17 +553,71 @@ static int check_plan(const nt_model_plan* plan, bool need_resident) {
   return NT_OK;
 }
 
+// Read n bytes at offset off of fd into dst with t threads, each taking one contiguous piece
+// (a multiple of 4096 bytes but the last) and repeating pread until it is done.  False on a
+// read error or an early end of file.
+static bool read_blob(int fd, int64_t off, uint8_t* dst, size_t n, int t) {
+  auto piece = [fd, off, dst](size_t a, size_t b, bool* ok) {
+    while (a < b) {
+      const ssize_t r = pread(fd, dst + a, b - a, (off_t)(off + (int64_t)a));
+      if (r < 0 && errno == EINTR) continue;
+      if (r <= 0) {
+        *ok = false;
+        return;
+      }
+      a += (size_t)r;
+    }
+    *ok = true;
+  };
+  const size_t step = ((n + (size_t)t - 1) / (size_t)t + 4095) & ~(size_t)4095;
+  std::vector<std::thread> th;
+  bool ok[64];
+  int k = 0;
+  for (size_t a = 0; a < n; a += step, ++k) {
+    const size_t b = a + step < n ? a + step : n;
+    bool spawned = false;
+    if (a + step < n) {
+      try {
+        th.emplace_back(piece, a, b, &ok[k]);
+        spawned = true;
+      } catch (...) {
+        // no thread to be had: read this piece here
+      }
+    }
+    if (!spawned) piece(a, b, &ok[k]);  // the last piece (or one no thread took) on this thread
+  }
+  for (auto& x : th) x.join();
+  for (int i = 0; i < k; ++i)
+    if (!ok[i]) return false;
+  return true;
+}
+
 static int stream_issue(nt_streamer* st, const nt_model_plan* plan, const std::vector<int>& streamed, hipStream_t copy,
                         nt_stream_stats* stats) {
   const int64_t q = st->c_issue;
   const int b = (int)(q & 1);
   const int layer = streamed[(size_t)(q % (int64_t)streamed.size())];
+  const nt_layer_entry& ent = plan->layers[layer];
+  const size_t nbytes = (size_t)plan->layout.blob_bytes;
   hipError_t e;
+  const void* src = ent.blob;
+  if (ent.resident == NT_TIER_FILE) {
+    // the bounce buffer's previous copy (two issues ago) must be done before it is refilled
+    if (st->bounce_recorded[b] && (e = hipEventSynchronize(st->bounce_free[b])) != hipSuccess)
+      return hip_fail(e, "hipEventSynchronize(bounce)");
+    if (!read_blob(ent.fd, ent.file_offset, st->bounce[b], nbytes, st->n_threads))
+      return fail(NT_EHOSTMEM, "layer %d: short or failed read of %zu bytes at offset %lld", layer, nbytes,
+                  (long long)ent.file_offset);
+    src = st->bounce[b];
+  }
   if (st->freed_recorded[b] && (e = hipStreamWaitEvent(copy, st->freed[b], 0)) != hipSuccess)
     return hip_fail(e, "hipStreamWaitEvent(copy)");
-  const size_t nbytes = (size_t)plan->layout.blob_bytes;
-  if ((e = hipMemcpyAsync(st->staging[b], plan->layers[layer].blob, nbytes, hipMemcpyHostToDevice, copy)) != hipSuccess)
+  if ((e = hipMemcpyAsync(st->staging[b], src, nbytes, hipMemcpyHostToDevice, copy)) != hipSuccess)
     return hip_fail(e, "hipMemcpyAsync");
+  if (ent.resident == NT_TIER_FILE) {
+    if ((e = hipEventRecord(st->bounce_free[b], copy)) != hipSuccess) return hip_fail(e, "hipEventRecord(bounce)");
+    st->bounce_recorded[b] = true;
+  }
   if ((e = hipEventRecord(st->ready[b], copy)) != hipSuccess) return hip_fail(e, "hipEventRecord(ready)");
   if (stats) stats->h2d_bytes += (int64_t)nbytes;
   st->c_issue = q + 1;
@@ -509,7 +628,7 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
                               hipStream_t compute, hipStream_t copy, nt_stream_stats* stats) {
   std::vector<int> streamed;  // the layers copied through the staging buffers, in order
   for (int l = 0; l < plan->n_layers; ++l)
-    if (!plan->layers[l].resident && !plan->layers[l].skip) streamed.push_back(l);
+    if (plan->layers[l].resident != NT_TIER_RESIDENT && !plan->layers[l].skip) streamed.push_back(l);
   if (st && !streamed.empty()) {
     if (st->plan_layers != (const void*)plan->layers || st->streamed != streamed) {
       // a new plan: drain what the streamer had in flight, then restart its sequence
@@ -530,7 +649,7 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
   for (int l = 0; l < plan->n_layers; ++l) {
     const nt_layer_entry& ent = plan->layers[l];
     if (ent.skip) continue;
-    if (ent.resident) {
+    if (ent.resident == NT_TIER_RESIDENT) {
       const nt_layer_weights w = weights_in_blob(reinterpret_cast<const uint8_t*>(ent.blob), plan->layout);
       if ((rc = run_layer(w, plan->shape, pos, h, ent.k_cache, ent.v_cache, ws, compute))) return rc;
       continue;
@@ -556,7 +675,7 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
 int nt_stream_layers(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, void* ws, size_t ws_bytes,
                      void* compute, void* copy, nt_stream_stats* stats) {
   if (stats) stats->layers_streamed = stats->h2d_bytes = 0;
-  int rc = check_plan(plan, st == nullptr);
+  int rc = check_plan(plan, st);
   if (rc) return rc;
   if (pos < 0 || pos >= plan->shape.max_ctx) return fail(NT_ESHAPE, "pos %d outside [0, max_ctx)", pos);
   if (!h || !ws) return fail(NT_EINVAL, "null pointer");
@@ -576,7 +695,7 @@ int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_h
                     float* logits, float* h, void* ws, size_t ws_bytes, void* compute, void* copy,
                     nt_stream_stats* stats) {
   if (stats) stats->layers_streamed = stats->h2d_bytes = 0;
-  int rc = check_plan(plan, st == nullptr);
+  int rc = check_plan(plan, st);
   if (rc) return rc;
   if (!head || !head->token_embd || !head->output_norm || !head->output || !token || !logits || !h || !ws)
     return fail(NT_EINVAL, "null pointer");

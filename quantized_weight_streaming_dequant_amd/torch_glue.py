@@ -45,15 +45,19 @@ def layer_layout(offsets: list[int], fmts: list[int], blob_bytes: int) -> _abi.L
 
 
 def model_plan(shape: _abi.LayerShape, layout: _abi.LayerLayout, entries: list[tuple], skip=()):
-    """entries: (blob address, resident, k_cache address, v_cache address) per layer; skip:
-    the layers to skip.  Returns (plan, keepalive); keep the second value alive while the
-    plan is used (its entries' skip fields may be changed in place)."""
+    """entries: (blob address, tier, k_cache address, v_cache address[, fd, file offset]) per
+    layer, tier a _abi.TIER_* value (True / False mean resident / pinned); skip: the layers to
+    skip.  Returns (plan, keepalive); keep the second value alive while the plan is used (its
+    entries' skip fields may be changed in place)."""
     arr = (_abi.LayerEntry * len(entries))()
-    for i, (blob, resident, kc, vc) in enumerate(entries):
-        arr[i].blob = blob
-        arr[i].resident = 1 if resident else 0
+    for i, ent in enumerate(entries):
+        blob, tier, kc, vc = ent[:4]
+        arr[i].blob = blob or 0
+        arr[i].resident = int(tier)
         arr[i].k_cache = kc
         arr[i].v_cache = vc
         arr[i].skip = 1 if i in skip else 0
+        arr[i].fd = ent[4] if len(ent) > 4 else -1
+        arr[i].file_offset = ent[5] if len(ent) > 5 else 0
     plan = _abi.ModelPlan(shape, layout, len(entries), ctypes.cast(arr, ctypes.POINTER(_abi.LayerEntry)))
     return plan, arr

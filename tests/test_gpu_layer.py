@@ -173,15 +173,19 @@ class Model:
         return ([dev(k) for k in self.kc0],
                 [dev(v_to_device(v, self.shape.n_kv_heads, self.shape.max_ctx)) for v in self.vc0])
 
-    def plan(self, kcs, vcs, streamed=None, skip=(), layers=None):
-        """layers: the layer indices the plan lists (default all), in order."""
+    def plan(self, kcs, vcs, streamed=None, skip=(), layers=None, files=None):
+        """layers: the layer indices the plan lists (default all), in order; files: layer ->
+        (fd, offset) for layers read from a file."""
+        files = files or {}
         streamed = self.streamed if streamed is None else streamed
         layers = range(self.n_layers) if layers is None else layers
         shp = tg.layer_shape(self.shape)
         lay = tg.layer_layout(self.lay.offset_list(), self.lay.fmt_list(), self.lay.nbytes)
         ents = []
         for l in layers:
-            if l in streamed:
+            if l in files:
+                ents.append((0, nt.TIER_FILE, kcs[l].data_ptr(), vcs[l].data_ptr(), files[l][0], files[l][1]))
+            elif l in streamed:
                 ents.append((self.blobs_host[l].data_ptr(), False, kcs[l].data_ptr(), vcs[l].data_ptr()))
             else:
                 ents.append((self.blobs_dev[l].data_ptr(), True, kcs[l].data_ptr(), vcs[l].data_ptr()))
@@ -192,9 +196,9 @@ class Model:
                             self.out_d.data_ptr())
 
 
-def decode_tokens(model, streamed, tok0, pos0, n_tokens, staging=None, skip=(), layers=None):
+def decode_tokens(model, streamed, tok0, pos0, n_tokens, staging=None, skip=(), layers=None, files=None, bounce=None):
     kcs, vcs = model.caches()
-    plan, keep = model.plan(kcs, vcs, streamed, skip, layers)
+    plan, keep = model.plan(kcs, vcs, streamed, skip, layers, files)
     shp = tg.layer_shape(model.shape)
     wsb = nt.nt_decode_token_ws_bytes(shp)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
@@ -204,8 +208,10 @@ def decode_tokens(model, streamed, tok0, pos0, n_tokens, staging=None, skip=(), 
     compute = torch.cuda.Stream()
     copy = torch.cuda.Stream()
     st = None
-    if streamed:
+    if streamed or files:
         st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), staging[0].numel())
+    if files:
+        nt.nt_stream_set_bounce(st, bounce[0].data_ptr(), bounce[1].data_ptr(), bounce[0].numel(), 3)
     toks, hs, lgs = [], [], []
     stats = nt.StreamStats()
     try:
@@ -301,6 +307,46 @@ def test_layer_skip_equals_leaving_the_layers_out():
     n = oracle.rmsnorm(a[1][-1], m.onorm, TINY.eps)
     ref, nrm = oracle.gemv(synth.Q4_K, 1000, TINY.dim, m.out, n)
     check_rel(a[2][-1], ref, nrm, what="logits with layers skipped")
+
+
+def _pinned_page_aligned(nbytes):
+    """A page-locked host tensor of at least nbytes whose data starts on a 4096-byte boundary."""
+    t = torch.empty(nbytes + 4096, dtype=torch.uint8, pin_memory=True)
+    off = (-t.data_ptr()) % 4096
+    return t[off:off + nbytes]
+
+
+def test_file_tier_bit_identical(tmp_path):
+    """Layers read from a file through page-locked bounce buffers (layers 1 and 3), next to a
+    pinned one (2) and a resident one (0), decode bit for bit as the all-resident model."""
+    import os
+    say("file tier: layers 1 and 3 from a file")
+    m = Model(TINY, recipes.MIX_Q4_K_M, 4, vocab=1000, n_slots=32)
+    stride = (m.lay.nbytes + 4095) // 4096 * 4096
+    path = tmp_path / "layers.bin"
+    with open(path, "wb") as f:
+        for l in (3, 1):  # file order unlike layer order
+            f.write(m.blobs_host[l].numpy().tobytes())
+            f.write(b"\0" * (stride - m.lay.nbytes))
+    fd = os.open(path, os.O_RDONLY)
+    try:
+        files = {3: (fd, 0), 1: (fd, stride)}
+        staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        bounce = [_pinned_page_aligned(m.lay.nbytes) for _ in range(2)]
+        tok0 = synth.uniform_index(1000, 0, 79)
+        a = decode_tokens(m, set(), tok0, 32, 3)
+        b = decode_tokens(m, {2}, tok0, 32, 3, staging, files=files, bounce=bounce)
+        assert a[0] == b[0]
+        for x, y in zip(a[1] + a[2] + a[3] + a[4], b[1] + b[2] + b[3] + b[4]):
+            assert same_value(x, y)
+        assert b[5].layers_streamed == 3 and b[5].h2d_bytes >= 3 * m.lay.nbytes
+        # a blob past the end of the file is a host-side error, reported before its copy
+        bad = {3: (fd, 0), 1: (fd, 4 * stride)}
+        with pytest.raises(nt.NtError) as ei:
+            decode_tokens(m, set(), tok0, 32, 1, staging, files=bad, bounce=bounce)
+        assert ei.value.code == nt.NT_EHOSTMEM
+    finally:
+        os.close(fd)
 
 
 def test_layer_cosine_calibration():
