@@ -20,11 +20,11 @@
 // [n_kv][max_ctx/8][128][8], so that one 16-byte load gives a lane the 8 consecutive
 // slots of one dimension that the B operand of p V wants.
 //
-// Work split: workgroup (split, kv head) covers 128 slots, each of its four waves 32.
+// Work split: workgroup (split, kv head) covers 256 slots, each of its eight waves 32.
 // A wave's two 16-slot score tiles map MFMA row r to slot 8(r/4) + 4 tile + r%4, so
 // that the output layout (lane l: rows 4(l/16)..+3, column l%16) leaves each lane
 // the eight consecutive slots 8(l/16)..+7 of its column: exactly its A operand for
-// p V, with no data movement.  The four waves merge through LDS into one (max, sum,
+// p V, with no data movement.  The eight waves merge through LDS into one (max, sum,
 // unnormalised output) partial per head; a second kernel merges the splits.  With a
 // single split the first kernel writes the normalised output itself.
 #include "attn.h"
@@ -36,7 +36,10 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int HD = 128;
-constexpr int AW = 4;              // waves per workgroup
+#ifndef NT_ATTN_WAVES
+#define NT_ATTN_WAVES 8
+#endif
+constexpr int AW = NT_ATTN_WAVES;  // waves per workgroup
 constexpr int SW = 32;             // cache slots per wave
 constexpr int SWG = AW * SW;       // cache slots per workgroup (one split)
 constexpr int QPAD = HD + 8;       // halves per staged query row
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
   }
   __syncthreads();
 
-  // ---- 5. merge the four waves (rows h and h + 8 of a column block are one head's hi and lo)
+  // ---- 5. merge the waves (rows h and h + 8 of a column block are one head's hi and lo)
   for (int idx = threadIdx.x; idx < G * HD; idx += AW * 64) {
     const int h = idx >> 7, d = idx & (HD - 1);
     const int cb = h >> 3, hr = h & 7;
