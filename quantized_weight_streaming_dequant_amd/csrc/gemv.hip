@@ -19,7 +19,8 @@
 // sum is scaled once; offsets and mins use the fp32 x sums.  Blocks of 34, 18 and 210
 // bytes sit at 2-byte phases, realigned with v_alignbyte.  Epilogues fuse the residual
 // add, SwiGLU, RoPE + fp16 KV append, or the greedy argmax.
-// No matrix cores: at batch 1 this is not a dense contraction.
+// No matrix cores in the GEMVs: at batch 1 this is not a dense contraction (the k-token GEMM
+// below uses them for Q4_K at 3 to 8 tokens, where it is one).
 #include <type_traits>
 
 #include "common.h"
@@ -1234,6 +1235,197 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   else gemm_rows<Q6_KF, NT, R>(a, xs, lane, wid, W);
 }
 
+// ---- k-token GEMM on the matrix cores (Q4_K, 3 to 8 tokens)
+//
+// The GEMV's limb arithmetic on v_mfma_i32_16x16x32_i8.  For one 32-column sub-block of a
+// Q4_K superblock the A operand holds 16 rows of staged activation digits, row 4u + l being
+// limb l of token 4m + u (row 4u + 3 is unused), and the B operand the 4-bit codes (as
+// bytes) of 16 weight rows, so one instruction forms the exact integer sums
+// D[(token, limb)][row] = sum over the 32 columns of digit * code for 16 weight rows and
+// four tokens (|D| <= 32 * 128 * 15: exact in int32 and in fp32).  An A fragment is read
+// from LDS once per wave and sub-block and serves 16 weight rows, where the VALU kernel
+// reads every token's digits again for every row (its LDS-read bound).  A lane's four D
+// values are the limbs of one token for its own weight row, so they combine in the lane
+// exactly as the GEMV's limb_sum does, the row's d sc and dmin m are decoded once per lane,
+// and each sub-block costs the lane one scaled FMA per token plus the min term (dmin m
+// times the block's fp32 x sum, as in the GEMV).
+//
+// Operand layouts (8 bytes per lane): A lane l holds row l % 16 at k = 8 (l / 16) .. +7, B
+// lane l column l % 16 at the same k, and D lane l rows 4 (l / 16) .. +3 of column l % 16.
+// A and B only need the same assignment of the sub-block's 32 columns to (lane group q,
+// byte): q takes bytes 8q .. 8q + 7 of the sub-block pair's 32 code bytes (low nibbles are
+// sub-block 2g, high nibbles 2g + 1) and the digits of the same 8 columns.
+//
+// Work: one workgroup of 16 waves per CU walks 16-row tiles; the waves split a tile's
+// superblocks (wave w takes superblocks w and w + 16 of a column chunk of at most 32) and
+// write their per-(row, token) sums to LDS (two buffers, so one barrier per tile); 16 NT
+// threads then add the 16 waves' sums and store the tile.  The next tile's loads are issued
+// before the current tile is computed; one loop iteration is one tile, with the barrier in
+// one place, so that the registers of the two tiles stay fixed (an unrolled ring of steps
+// with the barrier in each step was merged back into one step by the compiler, which then
+// waited for every load in flight at the top of the loop).
+
+struct MmRaw {
+  u32x2 q[4];  // code bytes 16 + 32 g + 8 q_lane .. +7 of the lane's row, g = 0..3
+  u32x4 hd;    // d, dmin and the 12 packed scale/min bytes
+};
+
+__host__ __device__ __forceinline__ size_t mm_lds_bytes(int nt, int cols) {
+  const size_t xs = (size_t)nt * gemm_lds_per_token(cols);
+  const size_t tr = (size_t)2 * sizeof(float) * (size_t)(cols >> 5) * (size_t)nt;
+  const size_t red = (size_t)2 * 16 * 16 * (size_t)nt * sizeof(float);
+  return xs + ((tr + 15) & ~(size_t)15) + red;
+}
+
+template <int NT, int S>
+__global__ __launch_bounds__(1024, 1) void gemm_q4k_mfma_kernel(const GemmArgs a) {
+  static_assert(NT == 4 || NT == 8, "four tokens per MFMA");
+  static_assert(S == 1 || S == 2, "superblocks per wave and tile");
+  constexpr int NW = 16, NM = NT / 4;
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  extern __shared__ float4 smem4[];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem4);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int iw = lane & 15, q = lane >> 4;
+  const size_t per_tok = gemm_lds_per_token(a.cols);
+  const int plane = xq_plane(a.cols);
+  const int nblk = a.cols >> 5;
+  // ---- stage every token's chunk of x as limbs (16 columns of one token per thread and
+  // round, at most four rounds: NT * cols <= 2^16; every round's loads issued first), then
+  // the digit scales and x sums per (32-column block, token), token-minor
+  {
+    const int ng = a.cols >> 4, total = NT * ng;  // ng even: a DPP pair stays in one token
+    float v[4][16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = (int)threadIdx.x + NW * 64 * u, t = i / ng, gi = i % ng;
+      if (i < total && t < a.n_tok) {
+        const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)t * a.xld + gi * 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 f = src[k];
+          v[u][4 * k] = f.x; v[u][4 * k + 1] = f.y; v[u][4 * k + 2] = f.z; v[u][4 * k + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[u][k] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = (int)threadIdx.x + NW * 64 * u, t = i / ng, gi = i % ng;
+      if (i < total) {
+        XLimbs xs;
+        xs.q = lds + t * per_tok;
+        xs.plane = plane;
+        xs.sc = reinterpret_cast<float*>(xs.q + XL * plane);
+        xs.s16 = xs.sc + nblk;
+        stage_group(xs, gi, v[u]);
+      }
+    }
+  }
+  __syncthreads();
+  float* scT = reinterpret_cast<float*>(lds + NT * per_tok);
+  float* xsT = scT + nblk * NT;
+  float* red = reinterpret_cast<float*>(lds + NT * per_tok + (((size_t)2 * sizeof(float) * nblk * NT + 15) & ~(size_t)15));
+  for (int i = threadIdx.x; i < nblk * NT; i += NW * 64) {
+    const int b = i / NT, t = i % NT;
+    const float* sc = reinterpret_cast<const float*>(lds + t * per_tok + XL * plane);
+    scT[i] = sc[b];
+    xsT[i] = sc[nblk + 2 * b] + sc[nblk + 2 * b + 1];
+  }
+  __syncthreads();
+
+  // ---- this lane's A rows: token 4m + iw / 4, limb iw % 4 (the unused fourth reads limb
+  // XL - 1: real digits, whose sums are dropped); its outputs: token 4m + q
+  const uint8_t* abase[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+    abase[m] = lds + (4 * m + (iw >> 2)) * per_tok + min(iw & 3, XL - 1) * plane + 8 * q;
+
+  const int nsb = a.cols >> 8;  // at most NW * S
+  const int ntiles = (a.rows + 15) >> 4;
+  if ((int)blockIdx.x >= ntiles) return;
+  const uint32_t m0f = 0x0F0F0F0Fu;
+  // this wave's S superblocks of tile t (past the chunk's last superblock or the last row:
+  // valid addresses whose results are dropped)
+  auto issue = [&](MmRaw (&r)[S], int t) {
+    const int row = min(t * 16 + iw, a.rows - 1);
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const int sb = min(wave + NW * k, nsb - 1);
+      const uint8_t* p = a.w + (size_t)row * a.row_bytes + (size_t)sb * 144;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) r[k].q[g] = wld8(p + 16 + 32 * g + 8 * q);
+      r[k].hd = wld16(p);
+    }
+  };
+  MmRaw cur[S], nxt[S];
+  int ct = blockIdx.x, buf = 0;
+  issue(cur, ct);
+  for (;;) {
+    const int tn = ct + (int)gridDim.x;
+    issue(nxt, min(tn, ntiles - 1));  // in flight while this tile is computed
+    float acc[NM], am[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = am[m] = 0.f;
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const int sb = wave + NW * k;
+      if (sb >= nsb) continue;
+      const MmRaw& c = cur[k];
+      const float d = h2f(c.hd.x), dmin = h2f(c.hd.x >> 16);
+      const uint32_t Y = c.hd.y, Z = c.hd.z, W = c.hd.w;
+      const uint32_t scA = Y & 0x3F3F3F3Fu, mA = Z & 0x3F3F3F3Fu;
+      const uint32_t scB = (W & m0f) | ((Y >> 2) & 0x30303030u);
+      const uint32_t mB = ((W >> 4) & m0f) | ((Z >> 2) & 0x30303030u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sw = j < 4 ? scA : scB, mw = j < 4 ? mA : mB;
+        const int sh = 8 * (j & 3);
+        const float dsc = d * (float)((sw >> sh) & 0xFFu), dm = dmin * (float)((mw >> sh) & 0xFFu);
+        const u32x2 v = c.q[j >> 1];
+        const uint32_t c0 = (j & 1) ? ((v.x >> 4) & m0f) : (v.x & m0f);
+        const uint32_t c1 = (j & 1) ? ((v.y >> 4) & m0f) : (v.y & m0f);
+        const long B = (long)(((uint64_t)c1 << 32) | c0);
+        const int cc = 256 * sb + 32 * j;  // first column of the sub-block in the chunk
+        const int xo = xq_off(cc);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const long A = *reinterpret_cast<const long*>(abase[m] + xo);
+          const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+          const int ti = (cc >> 5) * NT + 4 * m + q;
+          const int dl[XL] = {D[0], D[1], D[XL - 1]};
+          acc[m] = fmaf(dsc * scT[ti], limb_sum(dl), acc[m]);
+          am[m] = fmaf(dm, xsT[ti], am[m]);
+        }
+      }
+    }
+    // ---- every lane holds its row's sums for tokens 4m + q; the waves meet in LDS
+    float* rb = red + (size_t)buf * (NW * 16 * NT);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) rb[(wave * 16 + iw) * NT + 4 * m + q] = acc[m] - am[m];
+    __syncthreads();
+    if ((int)threadIdx.x < 16 * NT) {
+      const int rr = threadIdx.x / NT, t = threadIdx.x % NT;
+      const int row = ct * 16 + rr;
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) y += rb[(w * 16 + rr) * NT + t];
+      if (row < a.rows && t < a.n_tok) {
+        float* yp = a.y + (size_t)t * a.yld + row;
+        *yp = a.accum ? *yp + y : y;
+      }
+    }
+    buf ^= 1;  // the other buffer: the next tile's writes cannot meet this tile's reads
+    ct = tn;
+    if (ct >= ntiles) break;
+    cur[0] = nxt[0];
+    if constexpr (S == 2) cur[1] = nxt[1];
+  }
+}
+
 // ================================================================== streamed GEMV
 //
 // Column-stationary layout for shapes whose rows are 16-byte aligned.  A workgroup owns a
@@ -1913,6 +2105,35 @@ static hipError_t gemm_launch_fmt(int nt, const GemmArgs& a, hipStream_t s) {
   return gemm_launch_nt<FMT, 8>(a, s);
 }
 
+#ifndef NT_GEMM_MFMA
+#define NT_GEMM_MFMA 1  // Q4_K with 3 to 8 tokens on the matrix cores
+#endif
+static bool gemm_use_mfma(int fmt, int n_tok) { return NT_GEMM_MFMA && fmt == FMT_Q4_K && n_tok >= 3; }
+
+template <int NT, int S>
+static hipError_t gemm_mfma_launch_nt(const GemmArgs& a, hipStream_t s) {
+  auto kern = gemm_q4k_mfma_kernel<NT, S>;
+  static bool raised = false;
+  if (!raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)GEMM_LDS_MAX);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  const int ntiles = (a.rows + 15) / 16;
+  const int grid = max(1, min(ntiles, num_cu()));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), mm_lds_bytes(NT, a.cols), s, a);
+  return hipGetLastError();
+}
+
+static int gemm_mfma_chunk_cols(int n_tok, int cols) {
+  const int nt = n_tok <= 4 ? 4 : 8;
+  int c = 256;  // at most 32 superblocks (two per wave) and NT * c <= 2^16 (four staging rounds)
+  while (c + 256 <= cols && c + 256 <= 32 * 256 && nt * (c + 256) <= 65536 && mm_lds_bytes(nt, c + 256) <= GEMM_LDS_MAX)
+    c += 256;
+  return c > cols ? cols : c;
+}
+
 int gemm_chunk_cols(int n_tok, int cols, int be) {
   const int nt = n_tok <= 1 ? 1 : n_tok <= 2 ? 2 : n_tok <= 4 ? 4 : 8;
   // the widest multiple of 256 columns (a superblock, eight 32-weight blocks) whose NT
@@ -1926,7 +2147,8 @@ int gemm_chunk_cols(int n_tok, int cols, int be) {
 hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int n_tok, const float* x, float* y,
                        hipStream_t s) {
   const int be = block_elems(fmt), bb = block_bytes(fmt);
-  const int chunk = gemm_chunk_cols(n_tok, (int)cols, be);
+  const bool mm = gemm_use_mfma(fmt, n_tok);
+  const int chunk = mm ? gemm_mfma_chunk_cols(n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, be);
   if (chunk <= 0) return hipErrorInvalidValue;
   GemmArgs a;
   a.row_bytes = (int64_t)(cols / be) * bb;
@@ -1941,6 +2163,13 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
     a.x = x + c0;
     a.accum = c0 > 0;
     hipError_t e;
+    if (mm) {
+      const bool s2 = a.cols > 16 * 256;  // superblocks per wave and tile
+      e = n_tok <= 4 ? (s2 ? gemm_mfma_launch_nt<4, 2>(a, s) : gemm_mfma_launch_nt<4, 1>(a, s))
+                     : (s2 ? gemm_mfma_launch_nt<8, 2>(a, s) : gemm_mfma_launch_nt<8, 1>(a, s));
+      if (e != hipSuccess) return e;
+      continue;
+    }
     switch (fmt) {
       case FMT_Q8_0: e = gemm_launch_fmt<FMT_Q8_0>(n_tok, a, s); break;
       case FMT_Q4_0: e = gemm_launch_fmt<FMT_Q4_0>(n_tok, a, s); break;

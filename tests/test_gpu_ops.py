@@ -119,6 +119,10 @@ GEMM_CASES = [
     (synth.Q4_K, 28672, 8192, 4), (synth.Q4_K, 8192, 28672, 7),
     (synth.Q6_K, 77, 2304, 7), (synth.Q6_K, 8192, 28672, 8), (synth.Q6_K, 1024, 8192, 3),
     (synth.Q5_K, 23, 1280, 6), (synth.Q5_K, 8192, 8192, 8), (synth.Q5_K, 28672, 8192, 2),
+    # the matrix-core path (Q4_K, 3 to 8 tokens): 16-row tiles cut short, chunks of fewer
+    # superblocks than waves, a one-superblock last chunk, one row
+    (synth.Q4_K, 37, 2304, 3), (synth.Q4_K, 17, 512, 4), (synth.Q4_K, 1, 256, 8), (synth.Q4_K, 130, 4352, 5),
+    (synth.Q4_K, 300, 16640, 6), (synth.Q4_K, 1000, 12288, 8),
 ]
 
 
@@ -140,10 +144,20 @@ def test_gemm_one_token_matches_gemv_and_tokens_are_independent():
     what the GEMV gives (both are within the tolerance of the same exact values)."""
     fmt, rows, cols = synth.Q4_K, 512, 8192
     blocks = synth.quant_matrix(fmt, rows, cols, seed=9, stream=900)
-    X = np.stack([synth.normal_f32(cols, seed=9, stream=901 + t) for t in range(4)])
-    Y4 = gpu_gemm(fmt, rows, cols, 4, blocks, X)
-    Y2 = gpu_gemm(fmt, rows, cols, 2, blocks, X[2:])
-    assert np.array_equal(Y4[2:], Y2)
+    X = np.stack([synth.normal_f32(cols, seed=9, stream=901 + t) for t in range(8)])
+    Xo = np.stack([synth.normal_f32(cols, seed=9, stream=951 + t) for t in range(8)])
+    # token 2 kept, every other token replaced: its outputs are bit for bit the same, on the
+    # VALU kernel (2 tokens) and on the matrix-core kernel (4 and 8 token slots)
+    for n in (3, 4, 5, 8):
+        Xb = Xo[:n].copy()
+        Xb[2] = X[2]
+        Ya = gpu_gemm(fmt, rows, cols, n, blocks, X[:n])
+        Yb = gpu_gemm(fmt, rows, cols, n, blocks, Xb)
+        assert np.array_equal(Ya[2], Yb[2]), f"{n} tokens"
+    Y2 = gpu_gemm(fmt, rows, cols, 2, blocks, X[:2])
+    Y2b = gpu_gemm(fmt, rows, cols, 2, blocks, np.stack([X[0], Xo[1]]))
+    assert np.array_equal(Y2[0], Y2b[0])
+    Y4 = gpu_gemm(fmt, rows, cols, 4, blocks, X[:4])
     y1 = gpu_gemv(fmt, rows, cols, blocks, X[1])
     ref, nrm = oracle.gemv(fmt, rows, cols, blocks, X[1].astype(np.float64))
     check_rel(y1, ref, nrm, what="gemv")
@@ -174,6 +188,21 @@ def test_gemv_outlier_activations(fmt, kind):
     check_rel(y, ref, nrm, what=f"{NAMES[fmt]} {kind}")
     worst = check_rel(y, ref, nrm, tol=1e-5, what=f"{NAMES[fmt]} {kind} (limb precision)")
     say(f"  worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("kind", list(OUTLIER_KINDS))
+def test_gemm_outlier_activations(kind):
+    """The same outlier channels in every token of the matrix-core GEMM (Q4_K, 5 tokens, one
+    token without outliers): the digits are the GEMV's, so the same 1e-5 bound holds."""
+    fmt, rows, cols, n = synth.Q4_K, 512, 8192, 5
+    say(f"gemm outliers {kind}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=4, stream=520)
+    X = np.stack([synth.normal_f32(cols, seed=4, stream=620 + t) * (OUTLIER_KINDS[kind](cols) if t != 3 else 1.0)
+                  for t in range(n)]).astype(np.float32)
+    Y = gpu_gemm(fmt, rows, cols, n, blocks, X)
+    ref, nrm = oracle.gemm(fmt, rows, cols, blocks, X.astype(np.float64))
+    for t in range(n):
+        check_rel(Y[t], ref[t], nrm[t], tol=1e-5, what=f"{kind} token {t} (limb precision)")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
