@@ -1270,18 +1270,24 @@ struct MmRaw {
   u32x4 hd;    // d, dmin and the 12 packed scale/min bytes
 };
 
+#ifndef NT_MM_WAVES
+#define NT_MM_WAVES 16
+#endif
+constexpr int MM_NW = NT_MM_WAVES;  // waves per workgroup of the matrix-core GEMM
+constexpr int MM_SMAX = 32 / MM_NW;  // superblocks per wave and tile at the widest chunk (32)
+
 __host__ __device__ __forceinline__ size_t mm_lds_bytes(int nt, int cols) {
   const size_t xs = (size_t)nt * gemm_lds_per_token(cols);
   const size_t tr = (size_t)2 * sizeof(float) * (size_t)(cols >> 5) * (size_t)nt;
-  const size_t red = (size_t)2 * 16 * 16 * (size_t)nt * sizeof(float);
+  const size_t red = (size_t)2 * MM_NW * 16 * (size_t)nt * sizeof(float);
   return xs + ((tr + 15) & ~(size_t)15) + red;
 }
 
 template <int NT, int S>
-__global__ __launch_bounds__(1024, 1) void gemm_q4k_mfma_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(MM_NW * 64, 1) void gemm_q4k_mfma_kernel(const GemmArgs a) {
   static_assert(NT == 4 || NT == 8, "four tokens per MFMA");
-  static_assert(S == 1 || S == 2, "superblocks per wave and tile");
-  constexpr int NW = 16, NM = NT / 4;
+  static_assert(S >= 1 && S <= 4, "superblocks per wave and tile");
+  constexpr int NW = MM_NW, NM = NT / 4;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   extern __shared__ float4 smem4[];
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem4);
@@ -1422,7 +1428,9 @@ __global__ __launch_bounds__(1024, 1) void gemm_q4k_mfma_kernel(const GemmArgs a
     ct = tn;
     if (ct >= ntiles) break;
     cur[0] = nxt[0];
-    if constexpr (S == 2) cur[1] = nxt[1];
+    if constexpr (S >= 2) cur[1] = nxt[1];
+    if constexpr (S >= 3) cur[2] = nxt[2];
+    if constexpr (S >= 4) cur[3] = nxt[3];
   }
 }
 
@@ -2122,14 +2130,15 @@ static hipError_t gemm_mfma_launch_nt(const GemmArgs& a, hipStream_t s) {
   }
   const int ntiles = (a.rows + 15) / 16;
   const int grid = max(1, min(ntiles, num_cu()));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), mm_lds_bytes(NT, a.cols), s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(MM_NW * 64), mm_lds_bytes(NT, a.cols), s, a);
   return hipGetLastError();
 }
 
 static int gemm_mfma_chunk_cols(int n_tok, int cols) {
   const int nt = n_tok <= 4 ? 4 : 8;
-  int c = 256;  // at most 32 superblocks (two per wave) and NT * c <= 2^16 (four staging rounds)
-  while (c + 256 <= cols && c + 256 <= 32 * 256 && nt * (c + 256) <= 65536 && mm_lds_bytes(nt, c + 256) <= GEMM_LDS_MAX)
+  int c = 256;  // at most 32 superblocks and NT * c <= 64 MM_NW * 64 (four staging rounds of 16 columns)
+  while (c + 256 <= cols && c + 256 <= 32 * 256 && nt * (c + 256) <= 64 * MM_NW * 64 &&
+         mm_lds_bytes(nt, c + 256) <= GEMM_LDS_MAX)
     c += 256;
   return c > cols ? cols : c;
 }
@@ -2164,9 +2173,11 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
     a.accum = c0 > 0;
     hipError_t e;
     if (mm) {
-      const bool s2 = a.cols > 16 * 256;  // superblocks per wave and tile
-      e = n_tok <= 4 ? (s2 ? gemm_mfma_launch_nt<4, 2>(a, s) : gemm_mfma_launch_nt<4, 1>(a, s))
-                     : (s2 ? gemm_mfma_launch_nt<8, 2>(a, s) : gemm_mfma_launch_nt<8, 1>(a, s));
+      // superblocks per wave and tile: the chunk's superblocks over the workgroup's waves
+      const bool wide = a.cols > MM_NW / 2 * 256 * MM_SMAX;
+      constexpr int SW = MM_SMAX, SN = MM_SMAX / 2;
+      e = n_tok <= 4 ? (wide ? gemm_mfma_launch_nt<4, SW>(a, s) : gemm_mfma_launch_nt<4, SN>(a, s))
+                     : (wide ? gemm_mfma_launch_nt<8, SW>(a, s) : gemm_mfma_launch_nt<8, SN>(a, s));
       if (e != hipSuccess) return e;
       continue;
     }
