@@ -98,6 +98,28 @@ def copy_calibration(torch):
     return {"copy_bytes": n, "copies": 10}
 
 
+def read_probe(torch, nt, nbytes=4 << 30, reps=20):
+    """The achievable HBM read rate: nt_read_probe (plain 16-byte loads over a buffer far
+    larger than the 256 MB last-level cache), HIP events around `reps` back-to-back calls."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cs = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        nt.nt_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), cs)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        nt.nt_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), cs)
+    ev1.record()
+    ev1.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / reps
+    del buf
+    return {"GBps": nbytes / (us * 1e-6) / 1e9, "bytes": nbytes, "avg_us": us, "reps": reps,
+            "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "kernel": "nt_read_probe: 16-byte loads, 2 in flight per thread, 32 workgroups of 256 per CU"}
+
+
 def host_threads() -> int:
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
@@ -363,6 +385,10 @@ def bench_decode_70b(args, torch, nt, tg):
         "kernels": kern,
         "last_token": last_tok,
     }
+    # the yardstick next to the published peak: what plain reads achieve on this part
+    rp = read_probe(torch, nt)
+    res["read_probe"] = rp
+    res["roofline"]["frac_of_read_probe"] = res["roofline"]["achieved"] / rp["GBps"]
     if not args.no_cpu_baseline:
         log("cpu baseline (checker on a bounded sample)...")
         del m

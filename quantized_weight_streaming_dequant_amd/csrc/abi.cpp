@@ -438,6 +438,14 @@ int nt_layer_cosine(int64_t n, const float* a, const float* b, float* out, void*
   return e == hipSuccess ? NT_OK : hip_fail(e, "cosine launch");
 }
 
+int nt_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes <= 0 || bytes % 16) return fail(NT_ESHAPE, "bytes must be a positive multiple of 16");
+  if (!buf || !sink) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(NT_EALIGN, "buf must be 16-byte aligned, sink 4-byte");
+  hipError_t e = read_probe_launch(buf, bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "read probe launch");
+}
+
 int nt_stream_create(void* staging0, void* staging1, size_t staging_bytes, nt_streamer** out) {
   if (!out) return fail(NT_EINVAL, "out is null");
   *out = nullptr;

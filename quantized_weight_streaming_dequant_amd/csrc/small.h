@@ -15,5 +15,6 @@ hipError_t swiglu_launch(int64_t n, const float* gate, const float* up, float* o
 hipError_t argmax_launch(int64_t n, const float* v, int32_t* out, hipStream_t s);
 hipError_t token_from_key_launch(const unsigned long long* key, int32_t* token, hipStream_t s);
 hipError_t cosine_launch(int64_t n, const float* a, const float* b, float* out, hipStream_t s);
+hipError_t read_probe_launch(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace nt

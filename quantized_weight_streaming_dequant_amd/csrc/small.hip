@@ -255,6 +255,51 @@ __global__ __launch_bounds__(256) void cosine_kernel(int64_t n, const float* __r
   }
 }
 
+// ------------------------------------------------------------ read probe
+// A plain stream of 16-byte loads over a buffer, two in flight per thread, 32 workgroups of
+// 256 per CU (the fastest of a sweep of 2-32 workgroups per CU and 2-16 loads per thread,
+// 5.3-5.8 TB/s over a 4 GiB buffer; the default reads 5.77 TB/s), the data folded
+// into one word per thread that is stored only if it equals a value the caller never uses
+// (so the loads cannot be dropped): the achievable HBM read rate of the part, next to which
+// the GEMVs' rates can be read.
+#ifndef NT_PROBE_WG_PER_CU
+#define NT_PROBE_WG_PER_CU 32
+#endif
+#ifndef NT_PROBE_UNROLL
+#define NT_PROBE_UNROLL 2
+#endif
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ p, int64_t n16, uint32_t* sink) {
+  constexpr int U = NT_PROBE_UNROLL;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+hipError_t read_probe_launch(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s) {
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t n16 = bytes / 16;
+  const int64_t want = (n16 + 255) / 256;
+  const int64_t cap = (int64_t)ncu * NT_PROBE_WG_PER_CU;
+  const int grid = (int)(want < cap ? (want > 0 ? want : 1) : cap);
+  hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<const u32x4*>(buf), n16, sink);
+  return hipGetLastError();
+}
+
 hipError_t cosine_launch(int64_t n, const float* a, const float* b, float* out, hipStream_t s) {
   hipLaunchKernelGGL(cosine_kernel, dim3(1), dim3(256), 0, s, n, a, b, out);
   return hipGetLastError();

@@ -56,6 +56,10 @@ def test_block_geometry():
     (lambda: nt.nt_layer_cosine((1 << 24) + 1, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_layer_cosine(16, None, 16, 16), nt.NT_EINVAL),
     (lambda: nt.nt_layer_cosine(16, 16, 18, 16), nt.NT_EALIGN),
+    (lambda: nt.nt_read_probe(16, 0, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_read_probe(16, 24, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_read_probe(None, 16, 16), nt.NT_EINVAL),
+    (lambda: nt.nt_read_probe(8, 16, 16), nt.NT_EALIGN),
     (lambda: nt.nt_gemm_q(5, 16, 256, 2, 16, 16, 16), nt.NT_EFORMAT),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, 0, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, nt.GEMM_MAX_TOK + 1, 16, 16, 16), nt.NT_ESHAPE),

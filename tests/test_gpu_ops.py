@@ -386,3 +386,15 @@ def test_embed_row_and_argmax():
         o = torch.zeros(1, dtype=torch.int32, device="cuda")
         nt.nt_argmax(n, vd.data_ptr(), o.data_ptr(), stream())
         assert int(host(o)[0]) == oracle.argmax(v)
+
+
+def test_read_probe_runs_and_leaves_the_sink():
+    """The read-rate probe streams a buffer and discards it: it returns, and the sink keeps
+    its value unless the folded data hits the one constant it stores on (not these bytes)."""
+    n = 64 << 20
+    buf = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    nt.nt_read_probe(buf.data_ptr(), n, sink.data_ptr(), stream())
+    nt.nt_read_probe(buf.data_ptr(), 16, sink.data_ptr(), stream())  # a single 16-byte piece
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
