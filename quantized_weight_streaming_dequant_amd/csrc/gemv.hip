@@ -20,7 +20,7 @@
 // bytes sit at 2-byte phases, realigned with v_alignbyte.  Epilogues fuse the residual
 // add, SwiGLU, RoPE + fp16 KV append, or the greedy argmax.
 // No matrix cores in the GEMVs: at batch 1 this is not a dense contraction (the k-token GEMM
-// below uses them for Q4_K at 3 to 8 tokens, where it is one).
+// below uses them for Q4_K and Q6_K at 3 to 8 tokens, where it is one).
 #include <type_traits>
 
 #include "common.h"
@@ -1235,7 +1235,7 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   else gemm_rows<Q6_KF, NT, R>(a, xs, lane, wid, W);
 }
 
-// ---- k-token GEMM on the matrix cores (Q4_K, 3 to 8 tokens)
+// ---- k-token GEMM on the matrix cores (Q4_K and Q6_K, 3 to 8 tokens)
 //
 // The GEMV's limb arithmetic on v_mfma_i32_16x16x32_i8.  For one 32-column sub-block of a
 // Q4_K superblock the A operand holds 16 rows of staged activation digits, row 4u + l being
@@ -1265,9 +1265,26 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
 // with the barrier in each step was merged back into one step by the compiler, which then
 // waited for every load in flight at the top of the loop).
 
-struct MmRaw {
+template <int FMT>
+struct MmRaw;
+template <>
+struct MmRaw<FMT_Q4_K> {
   u32x2 q[4];  // code bytes 16 + 32 g + 8 q_lane .. +7 of the lane's row, g = 0..3
   u32x4 hd;    // d, dmin and the 12 packed scale/min bytes
+};
+// Q6_K: the lane's eight columns 8 q_lane .. +7 of each 32-column pair p of sub-blocks take
+// low-bit bytes 64 h + 32 e + 8 q_lane .. +7 (h = p / 4, e = p % 2; nibble p / 2 % 2) and
+// high-bit bytes 128 + 32 h + 8 q_lane .. +7 (bits 2 (p % 4) ..); superblocks sit at 2-byte
+// phases (210 = 2 mod 4) and are read with loads at 2-byte alignment, which the runtime's
+// unaligned access mode serves (a whole 16-byte piece where one straddles a line)
+typedef uint32_t u32x2a2 __attribute__((ext_vector_type(2), aligned(2)));
+typedef uint32_t u32x4a2 __attribute__((ext_vector_type(4), aligned(2)));
+template <>
+struct MmRaw<FMT_Q6_K> {
+  u32x2 ql[4];  // [2 h + e]
+  u32x2 qh[2];  // [h]
+  u32x4 sc;     // the 16 int8 sub-block scales
+  uint32_t d;   // fp16 d in the low half
 };
 
 #ifndef NT_MM_WAVES
@@ -1276,15 +1293,20 @@ struct MmRaw {
 constexpr int MM_NW = NT_MM_WAVES;  // waves per workgroup of the matrix-core GEMM
 constexpr int MM_SMAX = 32 / MM_NW;  // superblocks per wave and tile at the widest chunk (32)
 
-__host__ __device__ __forceinline__ size_t mm_lds_bytes(int nt, int cols) {
+// LDS: the tokens' limb regions, the digit scales per (32-column block, token), the x sums
+// per (32-column block, token) for Q4_K's mins or per (16-column block, token) for Q6_K's
+// offset, and two buffers of per-(wave, row, token) sums
+__host__ __device__ __forceinline__ size_t mm_lds_bytes(int fmt, int nt, int cols) {
   const size_t xs = (size_t)nt * gemm_lds_per_token(cols);
-  const size_t tr = (size_t)2 * sizeof(float) * (size_t)(cols >> 5) * (size_t)nt;
+  const size_t tr = (size_t)(fmt == FMT_Q6_K ? 3 : 2) * sizeof(float) * (size_t)(cols >> 5) * (size_t)nt;
   const size_t red = (size_t)2 * MM_NW * 16 * (size_t)nt * sizeof(float);
   return xs + ((tr + 15) & ~(size_t)15) + red;
 }
 
-template <int NT, int S>
-__global__ __launch_bounds__(MM_NW * 64, 1) void gemm_q4k_mfma_kernel(const GemmArgs a) {
+template <int FMT, int NT, int S>
+__global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs a) {
+  static_assert(FMT == FMT_Q4_K || FMT == FMT_Q6_K, "Q4_K or Q6_K");
+  constexpr bool K6 = FMT == FMT_Q6_K;
   static_assert(NT == 4 || NT == 8, "four tokens per MFMA");
   static_assert(S >= 1 && S <= 4, "superblocks per wave and tile");
   constexpr int NW = MM_NW, NM = NT / 4;
@@ -1333,13 +1355,19 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_q4k_mfma_kernel(const Gemm
   }
   __syncthreads();
   float* scT = reinterpret_cast<float*>(lds + NT * per_tok);
-  float* xsT = scT + nblk * NT;
-  float* red = reinterpret_cast<float*>(lds + NT * per_tok + (((size_t)2 * sizeof(float) * nblk * NT + 15) & ~(size_t)15));
+  float* xsT = scT + nblk * NT;  // per 32 columns (Q4_K) or per 16 (Q6_K)
+  float* red = reinterpret_cast<float*>(
+      lds + NT * per_tok + (((size_t)(K6 ? 3 : 2) * sizeof(float) * nblk * NT + 15) & ~(size_t)15));
   for (int i = threadIdx.x; i < nblk * NT; i += NW * 64) {
     const int b = i / NT, t = i % NT;
     const float* sc = reinterpret_cast<const float*>(lds + t * per_tok + XL * plane);
     scT[i] = sc[b];
-    xsT[i] = sc[nblk + 2 * b] + sc[nblk + 2 * b + 1];
+    if constexpr (K6) {
+      xsT[2 * b * NT + t] = sc[nblk + 2 * b];
+      xsT[(2 * b + 1) * NT + t] = sc[nblk + 2 * b + 1];
+    } else {
+      xsT[i] = sc[nblk + 2 * b] + sc[nblk + 2 * b + 1];
+    }
   }
   __syncthreads();
 
@@ -1356,18 +1384,31 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_q4k_mfma_kernel(const Gemm
   const uint32_t m0f = 0x0F0F0F0Fu;
   // this wave's S superblocks of tile t (past the chunk's last superblock or the last row:
   // valid addresses whose results are dropped)
-  auto issue = [&](MmRaw (&r)[S], int t) {
+  auto issue = [&](MmRaw<FMT> (&r)[S], int t) {
     const int row = min(t * 16 + iw, a.rows - 1);
 #pragma unroll
     for (int k = 0; k < S; ++k) {
       const int sb = min(wave + NW * k, nsb - 1);
-      const uint8_t* p = a.w + (size_t)row * a.row_bytes + (size_t)sb * 144;
+      const uint8_t* p = a.w + (size_t)row * a.row_bytes + (size_t)sb * (K6 ? 210 : 144);
+      if constexpr (K6) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) r[k].q[g] = wld8(p + 16 + 32 * g + 8 * q);
-      r[k].hd = wld16(p);
+        for (int i = 0; i < 4; ++i) r[k].ql[i] = *NT_GPTR(u32x2a2, p + 64 * (i >> 1) + 32 * (i & 1) + 8 * q);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) r[k].qh[h] = *NT_GPTR(u32x2a2, p + 128 + 32 * h + 8 * q);
+        r[k].sc = *NT_GPTR(u32x4a2, p + 192);
+        r[k].d = wld2(p + 208);
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) r[k].q[g] = wld8(p + 16 + 32 * g + 8 * q);
+        r[k].hd = wld16(p);
+      }
     }
   };
-  MmRaw cur[S], nxt[S];
+  // lanes of lane groups 0-1 carry the first sub-block of a Q6_K pair, 2-3 the second
+  const uint64_t half_a = q < 2 ? ~0ull : 0ull, half_b = ~half_a;
+  (void)half_a;
+  (void)half_b;
+  MmRaw<FMT> cur[S], nxt[S];
   int ct = blockIdx.x, buf = 0;
   issue(cur, ct);
   for (;;) {
@@ -1380,7 +1421,40 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_q4k_mfma_kernel(const Gemm
     for (int k = 0; k < S; ++k) {
       const int sb = wave + NW * k;
       if (sb >= nsb) continue;
-      const MmRaw& c = cur[k];
+      if constexpr (K6) {
+        const MmRaw<FMT_Q6_K>& c = cur[k];
+        const float d = h2f(c.d);
+        const uint32_t m30 = 0x30303030u;
+#pragma unroll
+        for (int pp = 0; pp < 8; ++pp) {  // pair of sub-blocks 2 pp, 2 pp + 1: columns 32 pp ..
+          const int h = pp >> 2, kk = pp & 3;
+          const u32x2 lv = c.ql[2 * h + (kk & 1)], hv = c.qh[h];
+          const uint32_t sl = 4u * (uint32_t)(kk >> 1), rot = (uint32_t)(2 * kk + 28) & 31u;
+          const uint32_t c0 = and_or(__builtin_amdgcn_alignbit(hv.x, hv.x, rot), m30, (lv.x >> sl) & m0f);
+          const uint32_t c1 = and_or(__builtin_amdgcn_alignbit(hv.y, hv.y, rot), m30, (lv.y >> sl) & m0f);
+          const uint64_t code = ((uint64_t)c1 << 32) | c0;
+          const long BA = (long)(code & half_a), BB = (long)(code & half_b);
+          const uint32_t sw = pp < 2 ? c.sc.x : pp < 4 ? c.sc.y : pp < 6 ? c.sc.z : c.sc.w;
+          const int sh = 16 * (pp & 1);
+          const float dsa = d * (float)(int)(int8_t)(sw >> sh), dsb = d * (float)(int)(int8_t)(sw >> (sh + 8));
+          const int cc = 256 * sb + 32 * pp;
+          const int xo = xq_off(cc);
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const long A = *reinterpret_cast<const long*>(abase[m] + xo);
+            const i32x4 DA = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, BA, i32x4{0, 0, 0, 0}, 0, 0, 0);
+            const i32x4 DB = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, BB, i32x4{0, 0, 0, 0}, 0, 0, 0);
+            const int ti = (cc >> 5) * NT + 4 * m + q, t16 = (cc >> 4) * NT + 4 * m + q;
+            const int la[XL] = {DA[0], DA[1], DA[XL - 1]}, lb[XL] = {DB[0], DB[1], DB[XL - 1]};
+            const float sx = scT[ti];
+            acc[m] = fmaf(dsa * sx, limb_sum(la), acc[m]);
+            acc[m] = fmaf(dsb * sx, limb_sum(lb), acc[m]);
+            am[m] = fmaf(dsa, xsT[t16], am[m]);  // w = d s (q - 32): the offset times the x sums
+            am[m] = fmaf(dsb, xsT[t16 + NT], am[m]);
+          }
+        }
+      } else {
+      const MmRaw<FMT_Q4_K>& c = cur[k];
       const float d = h2f(c.hd.x), dmin = h2f(c.hd.x >> 16);
       const uint32_t Y = c.hd.y, Z = c.hd.z, W = c.hd.w;
       const uint32_t scA = Y & 0x3F3F3F3Fu, mA = Z & 0x3F3F3F3Fu;
@@ -1407,11 +1481,12 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_q4k_mfma_kernel(const Gemm
           am[m] = fmaf(dm, xsT[ti], am[m]);
         }
       }
+      }
     }
     // ---- every lane holds its row's sums for tokens 4m + q; the waves meet in LDS
     float* rb = red + (size_t)buf * (NW * 16 * NT);
 #pragma unroll
-    for (int m = 0; m < NM; ++m) rb[(wave * 16 + iw) * NT + 4 * m + q] = acc[m] - am[m];
+    for (int m = 0; m < NM; ++m) rb[(wave * 16 + iw) * NT + 4 * m + q] = acc[m] - (K6 ? 32.f : 1.f) * am[m];
     __syncthreads();
     if ((int)threadIdx.x < 16 * NT) {
       const int rr = threadIdx.x / NT, t = threadIdx.x % NT;
@@ -2114,13 +2189,15 @@ static hipError_t gemm_launch_fmt(int nt, const GemmArgs& a, hipStream_t s) {
 }
 
 #ifndef NT_GEMM_MFMA
-#define NT_GEMM_MFMA 1  // Q4_K with 3 to 8 tokens on the matrix cores
+#define NT_GEMM_MFMA 1  // Q4_K and Q6_K with 3 to 8 tokens on the matrix cores
 #endif
-static bool gemm_use_mfma(int fmt, int n_tok) { return NT_GEMM_MFMA && fmt == FMT_Q4_K && n_tok >= 3; }
+static bool gemm_use_mfma(int fmt, int n_tok) {
+  return NT_GEMM_MFMA && (fmt == FMT_Q4_K || fmt == FMT_Q6_K) && n_tok >= 3;
+}
 
-template <int NT, int S>
+template <int FMT, int NT, int S>
 static hipError_t gemm_mfma_launch_nt(const GemmArgs& a, hipStream_t s) {
-  auto kern = gemm_q4k_mfma_kernel<NT, S>;
+  auto kern = gemm_mfma_kernel<FMT, NT, S>;
   static bool raised = false;
   if (!raised) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -2130,15 +2207,15 @@ static hipError_t gemm_mfma_launch_nt(const GemmArgs& a, hipStream_t s) {
   }
   const int ntiles = (a.rows + 15) / 16;
   const int grid = max(1, min(ntiles, num_cu()));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(MM_NW * 64), mm_lds_bytes(NT, a.cols), s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(MM_NW * 64), mm_lds_bytes(FMT, NT, a.cols), s, a);
   return hipGetLastError();
 }
 
-static int gemm_mfma_chunk_cols(int n_tok, int cols) {
+static int gemm_mfma_chunk_cols(int fmt, int n_tok, int cols) {
   const int nt = n_tok <= 4 ? 4 : 8;
   int c = 256;  // at most 32 superblocks and NT * c <= 64 MM_NW * 64 (four staging rounds of 16 columns)
   while (c + 256 <= cols && c + 256 <= 32 * 256 && nt * (c + 256) <= 64 * MM_NW * 64 &&
-         mm_lds_bytes(nt, c + 256) <= GEMM_LDS_MAX)
+         mm_lds_bytes(fmt, nt, c + 256) <= GEMM_LDS_MAX)
     c += 256;
   return c > cols ? cols : c;
 }
@@ -2157,7 +2234,7 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
                        hipStream_t s) {
   const int be = block_elems(fmt), bb = block_bytes(fmt);
   const bool mm = gemm_use_mfma(fmt, n_tok);
-  const int chunk = mm ? gemm_mfma_chunk_cols(n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, be);
+  const int chunk = mm ? gemm_mfma_chunk_cols(fmt, n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, be);
   if (chunk <= 0) return hipErrorInvalidValue;
   GemmArgs a;
   a.row_bytes = (int64_t)(cols / be) * bb;
@@ -2176,8 +2253,12 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
       // superblocks per wave and tile: the chunk's superblocks over the workgroup's waves
       const bool wide = a.cols > MM_NW / 2 * 256 * MM_SMAX;
       constexpr int SW = MM_SMAX, SN = MM_SMAX / 2;
-      e = n_tok <= 4 ? (wide ? gemm_mfma_launch_nt<4, SW>(a, s) : gemm_mfma_launch_nt<4, SN>(a, s))
-                     : (wide ? gemm_mfma_launch_nt<8, SW>(a, s) : gemm_mfma_launch_nt<8, SN>(a, s));
+      if (fmt == FMT_Q4_K)
+        e = n_tok <= 4 ? (wide ? gemm_mfma_launch_nt<FMT_Q4_K, 4, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q4_K, 4, SN>(a, s))
+                       : (wide ? gemm_mfma_launch_nt<FMT_Q4_K, 8, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q4_K, 8, SN>(a, s));
+      else
+        e = n_tok <= 4 ? (wide ? gemm_mfma_launch_nt<FMT_Q6_K, 4, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q6_K, 4, SN>(a, s))
+                       : (wide ? gemm_mfma_launch_nt<FMT_Q6_K, 8, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q6_K, 8, SN>(a, s));
       if (e != hipSuccess) return e;
       continue;
     }

@@ -123,6 +123,9 @@ GEMM_CASES = [
     # superblocks than waves, a one-superblock last chunk, one row
     (synth.Q4_K, 37, 2304, 3), (synth.Q4_K, 17, 512, 4), (synth.Q4_K, 1, 256, 8), (synth.Q4_K, 130, 4352, 5),
     (synth.Q4_K, 300, 16640, 6), (synth.Q4_K, 1000, 12288, 8),
+    # Q6_K on the matrix cores: odd superblock counts (chunks that start 2 bytes past a
+    # 4-byte boundary), one row, a short tile
+    (synth.Q6_K, 17, 512, 4), (synth.Q6_K, 1, 256, 8), (synth.Q6_K, 130, 4352, 6), (synth.Q6_K, 300, 16640, 5),
 ]
 
 
@@ -190,13 +193,14 @@ def test_gemv_outlier_activations(fmt, kind):
     say(f"  worst rel err {worst:.2e}")
 
 
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q6_K])
 @pytest.mark.parametrize("kind", list(OUTLIER_KINDS))
-def test_gemm_outlier_activations(kind):
-    """The same outlier channels in every token of the matrix-core GEMM (Q4_K, 5 tokens, one
-    token without outliers): the digits are the GEMV's, so the same 1e-5 bound holds."""
-    fmt, rows, cols, n = synth.Q4_K, 512, 8192, 5
+def test_gemm_outlier_activations(kind, fmt):
+    """The same outlier channels in every token of the matrix-core GEMM (5 tokens, one token
+    without outliers): the digits are the GEMV's, so the same 1e-5 bound holds."""
+    rows, cols, n = 512, 8192, 5
     say(f"gemm outliers {kind}")
-    blocks = synth.quant_matrix(fmt, rows, cols, seed=4, stream=520)
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=4, stream=520 + fmt)
     X = np.stack([synth.normal_f32(cols, seed=4, stream=620 + t) * (OUTLIER_KINDS[kind](cols) if t != 3 else 1.0)
                   for t in range(n)]).astype(np.float32)
     Y = gpu_gemm(fmt, rows, cols, n, blocks, X)
