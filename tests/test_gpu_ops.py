@@ -89,6 +89,8 @@ GEMV_SHAPES = {
                  (8192, 28672)],
 }
 GEMV_CASES = [(f, r, c) for f in FMTS for (r, c) in GEMV_SHAPES[f]]
+# the widest x the header allows (NT_GEMV_MAX_COLS columns)
+GEMV_CASES += [(f, 64, nt.NT_GEMV_MAX_COLS) for f in FMTS]
 
 
 @pytest.mark.parametrize("fmt,rows,cols", GEMV_CASES)
@@ -126,6 +128,8 @@ GEMM_CASES = [
     # Q6_K on the matrix cores: odd superblock counts (chunks that start 2 bytes past a
     # 4-byte boundary), one row, a short tile
     (synth.Q6_K, 17, 512, 4), (synth.Q6_K, 1, 256, 8), (synth.Q6_K, 130, 4352, 6), (synth.Q6_K, 300, 16640, 5),
+    # the widest x the header allows: many column chunks adding into y
+    (synth.Q4_K, 40, 32768, 8), (synth.Q6_K, 40, 32768, 4), (synth.Q8_0, 40, 32768, 3),
 ]
 
 
@@ -294,6 +298,7 @@ ATTN_CASES = [  # n_q, n_kv, n_ctx, max_ctx, q scale
     (64, 8, 1, 4224, 1.0), (64, 8, 65, 128, 1.0), (64, 8, 128, 128, 1.0), (64, 8, 129, 136, 1.0),
     (8, 8, 300, 512, 1.0), (16, 8, 77, 96, 2.0), (16, 1, 333, 400, 1.0), (128, 8, 1000, 1024, 1.0),
     (64, 8, 16384, 16384, 1.0), (64, 8, 9001, 16384, 1e-6), (64, 8, 2049, 2560, 30.0),
+    (8, 1, nt.NT_MAX_CTX, nt.NT_MAX_CTX, 1.0),  # the longest cache the header allows
 ]
 
 
