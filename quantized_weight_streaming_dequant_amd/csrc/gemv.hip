@@ -48,6 +48,9 @@ namespace nt {
 #ifndef NT_GEMV_DEPTH_PAIR
 #define NT_GEMV_DEPTH_PAIR 2  // the same for the gate/up pair
 #endif
+#ifndef NT_GEMV_DEPTH_QKV
+#define NT_GEMV_DEPTH_QKV 2  // the same for the q/k/v launch
+#endif
 #ifndef NT_GEMV_STREAM
 #define NT_GEMV_STREAM 1  // the streamed (global->LDS) path wherever the shape allows it
 #endif
@@ -585,7 +588,7 @@ struct Q6_KF {
 // Rows per work item and items in flight per wave on the register path: the gate/up pair
 // carries two rows already; the q/k/v launch needs RoPE pairs (2 rows) in one item.
 template <int EPI>
-constexpr int GEMV_DEPTH = EPI == EPI_QKV ? 2 : EPI == EPI_SWIGLU ? NT_GEMV_DEPTH_PAIR : NT_GEMV_DEPTH;
+constexpr int GEMV_DEPTH = EPI == EPI_QKV ? NT_GEMV_DEPTH_QKV : EPI == EPI_SWIGLU ? NT_GEMV_DEPTH_PAIR : NT_GEMV_DEPTH;
 template <int EPI>
 constexpr int GEMV_ROWS = (EPI == EPI_SWIGLU) ? 1 : (EPI == EPI_QKV) ? 2 : NT_GEMV_ROWS;
 
