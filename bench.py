@@ -371,7 +371,7 @@ def bench_decode_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q4_k/q6_k weights, f32 math, f16 kv", "data": "synthetic (seeded, random weights of the named shape)",
+        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q4_k/q6_k weights)", "data": "synthetic (seeded, random weights of the named shape)",
         "config": {"workload": "llama3.1-70b-shape Q4_K_M resident decode, 128256 vocab, 4096-slot fp16 KV prefill, "
                                "greedy, batch 1", "layers": n_layers, "global_batch": 1, "seq_len": 4096 + steps,
                    "parallelism": "none (1 GPU)"},
@@ -459,7 +459,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": best["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": best["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "quantized weights, f32 math", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots, f32 scales (quantized weights)", "data": "synthetic",
         "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K and Q5_K"},
         "roofline": {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": best["frac_of_peak"], "traffic": None},
@@ -512,7 +512,7 @@ def bench_gemm_tokens(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": head["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": head["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "quantized weights, f32 math", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots, f32 scales (quantized weights)", "data": "synthetic",
         "config": {"workload": "k-token quantized GEMM (self-speculative verification), 70B shapes, k = 1, 2, 4, 8"},
         "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["GBps"] / HBM_PEAK_GBS, "traffic": None},
@@ -575,7 +575,7 @@ def bench_layer_skip_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": res_t["skipping"], "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": 1e3 / res_t["skipping"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q4_k/q6_k weights, f32 math, f16 kv", "data": "synthetic (seeded, random weights of the named shape)",
+        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q4_k/q6_k weights)", "data": "synthetic (seeded, random weights of the named shape)",
         "config": {"workload": f"llama3.1-70b-shape Q4_K_M resident decode with cosine layer skip ({args.skip} of "
                                f"{n_layers} layers), 4096-slot fp16 KV prefill, greedy, batch 1",
                    "layers": n_layers, "skipped": skip},
@@ -622,7 +622,7 @@ def bench_layer_8b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": tok_s, "unit": "tok/s (derived: 32 layers + Q8_0 LM head)", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": t_layer * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "q8_0 weights, f32 math, f16 kv", "data": "synthetic",
+        "vs_baseline": None, "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q8_0 weights)", "data": "synthetic",
         "config": {"workload": "llama3-8b-shape Q8_0 decode layer, pos 1023, 1024-slot fp16 KV"},
         "layer_us": t_layer * 1e6, "layer_GBps": lb / t_layer / 1e9, "layer_frac_of_peak": lb / t_layer / 1e9 / HBM_PEAK_GBS,
         "lm_head": lm,
@@ -687,7 +687,7 @@ def bench_stream_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": steps / dt, "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q6_k weights, f32 math, f16 kv", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q6_k weights)", "data": "synthetic",
         "config": {"workload": "llama3.1-70b-shape Q6_K, 26 layers resident, 54 streamed from pinned host memory",
                    "layers": n_layers},
         "h2d_GBps": h2d / dt / 1e9, "pinned_copy_ceiling_GBps": ceil, "pcie_gen5_x16_GBps": 63.0,
@@ -771,7 +771,7 @@ def bench_file_tier_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": res["file"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": 1e3 / res["file"]["tok_s"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q6_k weights, f32 math, f16 kv", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q6_k weights)", "data": "synthetic",
         "config": {"workload": f"llama3.1-70b-shape Q6_K, {n_layers} layers read from a file through the page cache, "
                                f"{args.read_threads} readers per blob", "layers": n_layers},
         "file_tier": res["file"], "pinned_tier": res["pinned"],
