@@ -213,6 +213,40 @@ def test_gemm_outlier_activations(kind, fmt):
         check_rel(Y[t], ref[t], nrm[t], tol=1e-5, what=f"{kind} token {t} (limb precision)")
 
 
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_non_finite_activation(fmt, bad):
+    """One NaN or inf in x: the exact result of every row is non-finite (a nonzero weight times
+    inf, or zero times inf), and so is the kernel's (the 32-column block holding it is staged with
+    a NaN scale)."""
+    rows, cols = 96, 2048
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=6, stream=540 + fmt)
+    x = synth.normal_f32(cols, seed=6, stream=640 + fmt).copy()
+    x[777] = bad
+    ref, _ = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+    assert not np.isfinite(ref).any()
+    y = gpu_gemv(fmt, rows, cols, blocks, x)
+    assert not np.isfinite(y).any()
+
+
+@pytest.mark.parametrize("fmt,n_tok", [(synth.Q4_K, 4), (synth.Q4_K, 7), (synth.Q6_K, 5), (synth.Q4_K, 2), (synth.Q8_0, 3)])
+def test_gemm_non_finite_token_is_isolated(fmt, n_tok):
+    """A NaN in one token's x makes that token's outputs non-finite and leaves every other
+    token's outputs bit for bit as without it (the matrix-core kernel puts four tokens' digits
+    in one MFMA operand; each output row still meets one token's digits and scales only)."""
+    rows, cols = 130, 4096
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=7, stream=560 + fmt)
+    X = np.stack([synth.normal_f32(cols, seed=7, stream=660 + t) for t in range(n_tok)])
+    Y = gpu_gemm(fmt, rows, cols, n_tok, blocks, X)
+    Xb = X.copy()
+    Xb[1, 1000] = float("nan")
+    Yb = gpu_gemm(fmt, rows, cols, n_tok, blocks, Xb)
+    assert not np.isfinite(Yb[1]).any()
+    for t in range(n_tok):
+        if t != 1:
+            assert np.array_equal(Y[t], Yb[t]), f"token {t}"
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_one_hot_and_zero(fmt):
     """One-hot x picks a dequantized column exactly; all-zero blocks give exact zeros."""
