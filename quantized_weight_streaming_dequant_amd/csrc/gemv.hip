@@ -1583,14 +1583,20 @@ struct Q6K_S {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int l = 0; l < XL; ++l) dg[j][l] = 0;
+    // the low-bit bytes' nibble is taken from the two aligned words around each word with one
+    // funnel shift by 8 phase + 4 hi, which realigns and shifts at once
+    const uint32_t lsh = 8u * ph + sl;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      uint32_t L[8];
-      lds_run<8>(p + 64 * n + 32 * half, ph, L);
+      uint32_t Lw[9];
+      const uint8_t* lp = p + 64 * n + 32 * half - ph;
+#pragma unroll
+      for (int k = 0; k <= 8; ++k) Lw[k] = lds4(lp + 4 * k);
       const uint32_t rot = (sl + 2u * (uint32_t)half + 28u) & 31u;  // top bits 4hi + 2half -> bit 4
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const uint32_t code = and_or(__builtin_amdgcn_alignbit(H[k], H[k], rot), m30, (L[k] >> sl) & m0f);
+        const uint32_t lo = __builtin_amdgcn_alignbit(Lw[k + 1], Lw[k], lsh) & m0f;
+        const uint32_t code = and_or(__builtin_amdgcn_alignbit(H[k], H[k], rot), m30, lo);
         int(&d)[XL] = dg[2 * half + (k >> 2)];
 #pragma unroll
         for (int l = 0; l < XL; ++l) d[l] = sdot4(code, xq[l][8 * half + k], d[l]);
