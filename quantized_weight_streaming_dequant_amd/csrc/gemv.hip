@@ -1572,8 +1572,17 @@ struct Q6K_S {
     const int s = lane >> 2, g = lane & 3, n = g >> 1, hi = g & 1;
     const uint8_t* p = slot + s * 210;
     const uint32_t ph = (uint32_t)(s & 1) * 2u;
-    uint32_t H[8], S[1], D[1];
-    lds_run<8>(p + 128 + 32 * n, ph, H);
+    uint32_t S[1], D[1];
+    // high-bit bytes: the nine aligned words around the eight the lane needs; a lane whose
+    // rotation moves bits left (hi = 0) at phase 0 takes them one word earlier, so that for
+    // every lane one funnel shift of words k + 1, k by (8 phase + rotation) mod 32 realigns and
+    // rotates at once (the bits that come from the other word are masked off)
+    uint32_t Hw[9];
+    {
+      const uint8_t* hp = p + 128 + 32 * n - ph - ((ph == 0 && hi == 0) ? 4 : 0);
+#pragma unroll
+      for (int k = 0; k <= 8; ++k) Hw[k] = lds4(hp + 4 * k);
+    }
     lds_run<1>(p + 192 + 8 * n + 4 * hi, ph, S);
     lds_run<1>(p + 208, ph, D);
     const uint32_t m0f = vreg(0x0F0F0F0Fu), m30 = vreg(0x30303030u);
@@ -1593,10 +1602,11 @@ struct Q6K_S {
 #pragma unroll
       for (int k = 0; k <= 8; ++k) Lw[k] = lds4(lp + 4 * k);
       const uint32_t rot = (sl + 2u * (uint32_t)half + 28u) & 31u;  // top bits 4hi + 2half -> bit 4
+      const uint32_t hsh = (8u * ph + rot) & 31u;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const uint32_t lo = __builtin_amdgcn_alignbit(Lw[k + 1], Lw[k], lsh) & m0f;
-        const uint32_t code = and_or(__builtin_amdgcn_alignbit(H[k], H[k], rot), m30, lo);
+        const uint32_t code = and_or(__builtin_amdgcn_alignbit(Hw[k + 1], Hw[k], hsh), m30, lo);
         int(&d)[XL] = dg[2 * half + (k >> 2)];
 #pragma unroll
         for (int l = 0; l < XL; ++l) d[l] = sdot4(code, xq[l][8 * half + k], d[l]);
