@@ -333,6 +333,8 @@ ATTN_CASES = [  # n_q, n_kv, n_ctx, max_ctx, q scale
     (8, 8, 300, 512, 1.0), (16, 8, 77, 96, 2.0), (16, 1, 333, 400, 1.0), (128, 8, 1000, 1024, 1.0),
     (64, 8, 16384, 16384, 1.0), (64, 8, 9001, 16384, 1e-6), (64, 8, 2049, 2560, 30.0),
     (8, 1, nt.NT_MAX_CTX, nt.NT_MAX_CTX, 1.0),  # the longest cache the header allows
+    # the 256-slot split boundaries: one full split (one kernel), one slot into a second, two full
+    (64, 8, 256, 256, 1.0), (64, 8, 257, 264, 1.0), (32, 8, 512, 512, 3.0), (16, 2, 255, 256, 1.0),
 ]
 
 
