@@ -99,7 +99,7 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
  * fp32, overwritten, must not overlap x or blocks; blocks: 16-byte aligned; cols a positive
  * multiple of the block size (any width: wide matrices run as several launches over column
  * chunks, each adding into y); rows <= 2^31 - 1.  Per token, the accuracy of nt_gemv_q.
- * Q4_K and Q6_K with 3 to 8 tokens run on the matrix cores (8-bit integer MFMA of activation digits
+ * Q4_K, Q5_K and Q6_K with 3 to 8 tokens run on the matrix cores (8-bit integer MFMA of activation digits
  * and weight codes, exact in int32); the other cases on the vector ALUs.  A token's outputs
  * do not depend on the other tokens of the call.
  * Errors as nt_gemv_q, and NT_ESHAPE for n_tok out of range; nothing is enqueued then. */

@@ -20,7 +20,7 @@
 // bytes sit at 2-byte phases, realigned with v_alignbyte.  Epilogues fuse the residual
 // add, SwiGLU, RoPE + fp16 KV append, or the greedy argmax.
 // No matrix cores in the GEMVs: at batch 1 this is not a dense contraction (the k-token GEMM
-// below uses them for Q4_K and Q6_K at 3 to 8 tokens, where it is one).
+// below uses them for Q4_K, Q5_K and Q6_K at 3 to 8 tokens, where it is one).
 #include <type_traits>
 
 #include "common.h"
@@ -1238,7 +1238,7 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   else gemm_rows<Q6_KF, NT, R>(a, xs, lane, wid, W);
 }
 
-// ---- k-token GEMM on the matrix cores (Q4_K and Q6_K, 3 to 8 tokens)
+// ---- k-token GEMM on the matrix cores (Q4_K, Q5_K and Q6_K, 3 to 8 tokens)
 //
 // The GEMV's limb arithmetic on v_mfma_i32_16x16x32_i8.  For one 32-column sub-block of a
 // Q4_K superblock the A operand holds 16 rows of staged activation digits, row 4u + l being
@@ -1275,6 +1275,15 @@ struct MmRaw<FMT_Q4_K> {
   u32x2 q[4];  // code bytes 16 + 32 g + 8 q_lane .. +7 of the lane's row, g = 0..3
   u32x4 hd;    // d, dmin and the 12 packed scale/min bytes
 };
+// Q5_K: Q4_K's fields with the nibbles at 48 + 32 g and the fifth code bit of column l of
+// sub-block j in bit j of high-bit byte 16 + l (the lane's columns 8 q_lane .. +7 of every
+// sub-block share its eight high-bit bytes)
+template <>
+struct MmRaw<FMT_Q5_K> {
+  u32x2 q[4];
+  u32x2 qh;
+  u32x4 hd;
+};
 // Q6_K: the lane's eight columns 8 q_lane .. +7 of each 32-column pair p of sub-blocks take
 // low-bit bytes 64 h + 32 e + 8 q_lane .. +7 (h = p / 4, e = p % 2; nibble p / 2 % 2) and
 // high-bit bytes 128 + 32 h + 8 q_lane .. +7 (bits 2 (p % 4) ..); superblocks sit at 2-byte
@@ -1308,8 +1317,8 @@ __host__ __device__ __forceinline__ size_t mm_lds_bytes(int fmt, int nt, int col
 
 template <int FMT, int NT, int S>
 __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs a) {
-  static_assert(FMT == FMT_Q4_K || FMT == FMT_Q6_K, "Q4_K or Q6_K");
-  constexpr bool K6 = FMT == FMT_Q6_K;
+  static_assert(FMT == FMT_Q4_K || FMT == FMT_Q5_K || FMT == FMT_Q6_K, "Q4_K, Q5_K or Q6_K");
+  constexpr bool K6 = FMT == FMT_Q6_K, K5 = FMT == FMT_Q5_K;
   static_assert(NT == 4 || NT == 8, "four tokens per MFMA");
   static_assert(S >= 1 && S <= 4, "superblocks per wave and tile");
   constexpr int NW = MM_NW, NM = NT / 4;
@@ -1392,7 +1401,7 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs
 #pragma unroll
     for (int k = 0; k < S; ++k) {
       const int sb = min(wave + NW * k, nsb - 1);
-      const uint8_t* p = a.w + (size_t)row * a.row_bytes + (size_t)sb * (K6 ? 210 : 144);
+      const uint8_t* p = a.w + (size_t)row * a.row_bytes + (size_t)sb * (K6 ? 210 : K5 ? 176 : 144);
       if constexpr (K6) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[k].ql[i] = *NT_GPTR(u32x2a2, p + 64 * (i >> 1) + 32 * (i & 1) + 8 * q);
@@ -1402,7 +1411,8 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs
         r[k].d = wld2(p + 208);
       } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) r[k].q[g] = wld8(p + 16 + 32 * g + 8 * q);
+        for (int g = 0; g < 4; ++g) r[k].q[g] = wld8(p + (K5 ? 48 : 16) + 32 * g + 8 * q);
+        if constexpr (K5) r[k].qh = wld8(p + 16 + 8 * q);
         r[k].hd = wld16(p);
       }
     }
@@ -1457,7 +1467,7 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs
           }
         }
       } else {
-      const MmRaw<FMT_Q4_K>& c = cur[k];
+      const MmRaw<FMT>& c = cur[k];
       const float d = h2f(c.hd.x), dmin = h2f(c.hd.x >> 16);
       const uint32_t Y = c.hd.y, Z = c.hd.z, W = c.hd.w;
       const uint32_t scA = Y & 0x3F3F3F3Fu, mA = Z & 0x3F3F3F3Fu;
@@ -1469,8 +1479,13 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs
         const int sh = 8 * (j & 3);
         const float dsc = d * (float)((sw >> sh) & 0xFFu), dm = dmin * (float)((mw >> sh) & 0xFFu);
         const u32x2 v = c.q[j >> 1];
-        const uint32_t c0 = (j & 1) ? ((v.x >> 4) & m0f) : (v.x & m0f);
-        const uint32_t c1 = (j & 1) ? ((v.y >> 4) & m0f) : (v.y & m0f);
+        uint32_t c0 = (j & 1) ? ((v.x >> 4) & m0f) : (v.x & m0f);
+        uint32_t c1 = (j & 1) ? ((v.y >> 4) & m0f) : (v.y & m0f);
+        if constexpr (K5) {  // bit j of each high-bit byte rotated into bit 4: codes 0..31
+          const uint32_t m10 = 0x10101010u, rj = (uint32_t)(j + 28) & 31u;
+          c0 = and_or(__builtin_amdgcn_alignbit(c.qh.x, c.qh.x, rj), m10, c0);
+          c1 = and_or(__builtin_amdgcn_alignbit(c.qh.y, c.qh.y, rj), m10, c1);
+        }
         const long B = (long)(((uint64_t)c1 << 32) | c0);
         const int cc = 256 * sb + 32 * j;  // first column of the sub-block in the chunk
         const int xo = xq_off(cc);
@@ -2208,10 +2223,10 @@ static hipError_t gemm_launch_fmt(int nt, const GemmArgs& a, hipStream_t s) {
 }
 
 #ifndef NT_GEMM_MFMA
-#define NT_GEMM_MFMA 1  // Q4_K and Q6_K with 3 to 8 tokens on the matrix cores
+#define NT_GEMM_MFMA 1  // Q4_K, Q5_K and Q6_K with 3 to 8 tokens on the matrix cores
 #endif
 static bool gemm_use_mfma(int fmt, int n_tok) {
-  return NT_GEMM_MFMA && (fmt == FMT_Q4_K || fmt == FMT_Q6_K) && n_tok >= 3;
+  return NT_GEMM_MFMA && (fmt == FMT_Q4_K || fmt == FMT_Q5_K || fmt == FMT_Q6_K) && n_tok >= 3;
 }
 
 template <int FMT, int NT, int S>
@@ -2275,6 +2290,9 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
       if (fmt == FMT_Q4_K)
         e = n_tok <= 4 ? (wide ? gemm_mfma_launch_nt<FMT_Q4_K, 4, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q4_K, 4, SN>(a, s))
                        : (wide ? gemm_mfma_launch_nt<FMT_Q4_K, 8, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q4_K, 8, SN>(a, s));
+      else if (fmt == FMT_Q5_K)
+        e = n_tok <= 4 ? (wide ? gemm_mfma_launch_nt<FMT_Q5_K, 4, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q5_K, 4, SN>(a, s))
+                       : (wide ? gemm_mfma_launch_nt<FMT_Q5_K, 8, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q5_K, 8, SN>(a, s));
       else
         e = n_tok <= 4 ? (wide ? gemm_mfma_launch_nt<FMT_Q6_K, 4, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q6_K, 4, SN>(a, s))
                        : (wide ? gemm_mfma_launch_nt<FMT_Q6_K, 8, SW>(a, s) : gemm_mfma_launch_nt<FMT_Q6_K, 8, SN>(a, s));

@@ -130,6 +130,8 @@ GEMM_CASES = [
     (synth.Q6_K, 17, 512, 4), (synth.Q6_K, 1, 256, 8), (synth.Q6_K, 130, 4352, 6), (synth.Q6_K, 300, 16640, 5),
     # the widest x the header allows: many column chunks adding into y
     (synth.Q4_K, 40, 32768, 8), (synth.Q6_K, 40, 32768, 4), (synth.Q8_0, 40, 32768, 3),
+    # Q5_K on the matrix cores: short tiles, one row, chunks of fewer superblocks than waves, the widest x
+    (synth.Q5_K, 37, 2304, 3), (synth.Q5_K, 1, 256, 8), (synth.Q5_K, 300, 16640, 6), (synth.Q5_K, 40, 32768, 5),
 ]
 
 
@@ -197,7 +199,7 @@ def test_gemv_outlier_activations(fmt, kind):
     say(f"  worst rel err {worst:.2e}")
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q6_K])
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q5_K, synth.Q6_K])
 @pytest.mark.parametrize("kind", list(OUTLIER_KINDS))
 def test_gemm_outlier_activations(kind, fmt):
     """The same outlier channels in every token of the matrix-core GEMM (5 tokens, one token
@@ -229,7 +231,8 @@ def test_gemv_non_finite_activation(fmt, bad):
     assert not np.isfinite(y).any()
 
 
-@pytest.mark.parametrize("fmt,n_tok", [(synth.Q4_K, 4), (synth.Q4_K, 7), (synth.Q6_K, 5), (synth.Q4_K, 2), (synth.Q8_0, 3)])
+@pytest.mark.parametrize("fmt,n_tok", [(synth.Q4_K, 4), (synth.Q4_K, 7), (synth.Q6_K, 5), (synth.Q5_K, 8), (synth.Q4_K, 2),
+                                       (synth.Q8_0, 3)])
 def test_gemm_non_finite_token_is_isolated(fmt, n_tok):
     """A NaN in one token's x makes that token's outputs non-finite and leaves every other
     token's outputs bit for bit as without it (the matrix-core kernel puts four tokens' digits
