@@ -21,6 +21,7 @@
 // add, SwiGLU, RoPE + fp16 KV append, or the greedy argmax.
 // No matrix cores in the GEMVs: at batch 1 this is not a dense contraction (the k-token GEMM
 // below uses them for Q4_K, Q5_K and Q6_K at 3 to 8 tokens, where it is one).
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1983,18 +1984,22 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
 
 // ------------------------------------------------------------------ host side
 
+// Host-side state is set up once, with C++ static initialisation (thread-safe), or kept in
+// one atomic word, so that concurrent calls from several host threads cannot race on it.
+
+// compute units of the device current at the first call (one MI355X: 256)
 static int num_cu() {
-  static int n_cu = 0;
-  if (n_cu == 0) {
+  static const int n_cu = [] {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      n_cu = n;
-    else
-      n_cu = 256;
-  }
+      return n;
+    return 256;
+  }();
   return n_cu;
 }
+
+constexpr size_t GEMV_LDS_MAX = 160 * 1024 - 2048;  // dynamic LDS budget of the register path (static LDS on top)
 
 // limb planes, scales per 32 columns, sums per 16 columns, 16 floats of reduction space
 static size_t lds_for(int cols) {
@@ -2016,20 +2021,22 @@ template <int FMTMASK, int NW, int EPI>
 static hipError_t launch_one(const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s) {
   constexpr int R = GEMV_ROWS<EPI>;
   auto kern = gemv_kernel<FMTMASK, R, NW, EPI>;
-  // resident workgroups per CU at this LDS size, cached per instantiation
-  static int per_cu = 0;
-  static size_t per_cu_lds = 0;
-  if (per_cu == 0 || per_cu_lds != plan.lds_bytes) {
-    // the dynamic LDS this launch needs (static LDS of the kernel comes on top)
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)plan.lds_bytes);
-    if (e != hipSuccess) return e;
+  // the dynamic LDS limit, raised once to the whole budget (each launch passes its own size)
+  static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_LDS_MAX);
+  if (raised != hipSuccess) return raised;
+  if (plan.lds_bytes > GEMV_LDS_MAX) return hipErrorInvalidValue;
+  // resident workgroups per CU at this LDS size, cached per instantiation as (LDS bytes << 8 | count)
+  static std::atomic<uint64_t> cache{0};
+  const uint64_t c = cache.load(std::memory_order_relaxed);
+  int per_cu = (int)(c & 0xFF);
+  if (per_cu == 0 || (c >> 8) != (uint64_t)plan.lds_bytes) {
     int n = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NW * 64, plan.lds_bytes);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NW * 64, plan.lds_bytes);
     if (e != hipSuccess) return e;
-    per_cu = n > 0 ? n : 1;
+    per_cu = n > 0 ? (n < 255 ? n : 255) : 1;
     if (NT_GEMV_WG_PER_CU_MAX > 0 && per_cu > NT_GEMV_WG_PER_CU_MAX) per_cu = NT_GEMV_WG_PER_CU_MAX;
-    per_cu_lds = plan.lds_bytes;
+    cache.store(((uint64_t)plan.lds_bytes << 8) | (uint64_t)per_cu, std::memory_order_relaxed);
   }
   // as many resident waves as the chip holds, but no idle workgroups
   const int grid = max(1, min((n_groups + NW - 1) / NW, per_cu * num_cu()));
@@ -2078,13 +2085,9 @@ constexpr size_t ST_LDS_MAX = 160 * 1024 - 2048;  // dynamic LDS budget (static 
 template <int KF, int EPI, int D, int NI>
 static hipError_t st_launch(const StreamArgs& sa, int grid, int nw, size_t lds, hipStream_t s) {
   auto kern = gemv_stream_kernel<KF, EPI, D, NI>;
-  static bool raised = false;  // the dynamic LDS limit of this instantiation
-  if (!raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)ST_LDS_MAX);
-    if (e != hipSuccess) return e;
-    raised = true;
-  }
+  static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)ST_LDS_MAX);
+  if (raised != hipSuccess) return raised;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(nw * 64), lds, s, sa);
   return hipGetLastError();
 }
@@ -2199,13 +2202,9 @@ template <int FMT, int NT>
 static hipError_t gemm_launch_nt(const GemmArgs& a, hipStream_t s) {
   constexpr int NW = 16;
   auto kern = gemm_kernel<FMT, NT, NW>;
-  static bool raised = false;
-  if (!raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)GEMM_LDS_MAX);
-    if (e != hipSuccess) return e;
-    raised = true;
-  }
+  static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS_MAX);
+  if (raised != hipSuccess) return raised;
   const size_t lds = (size_t)NT * gemm_lds_per_token(a.cols);
   constexpr int R = GEMM_ROWS<FMT, NT>;
   const int groups = (a.rows + R - 1) / R;
@@ -2232,13 +2231,9 @@ static bool gemm_use_mfma(int fmt, int n_tok) {
 template <int FMT, int NT, int S>
 static hipError_t gemm_mfma_launch_nt(const GemmArgs& a, hipStream_t s) {
   auto kern = gemm_mfma_kernel<FMT, NT, S>;
-  static bool raised = false;
-  if (!raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)GEMM_LDS_MAX);
-    if (e != hipSuccess) return e;
-    raised = true;
-  }
+  static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS_MAX);
+  if (raised != hipSuccess) return raised;
   const int ntiles = (a.rows + 15) / 16;
   const int grid = max(1, min(ntiles, num_cu()));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(MM_NW * 64), mm_lds_bytes(FMT, NT, a.cols), s, a);

@@ -446,3 +446,41 @@ def test_read_probe_runs_and_leaves_the_sink():
     nt.nt_read_probe(buf.data_ptr(), 16, sink.data_ptr(), stream())  # a single 16-byte piece
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+def test_gemv_from_several_host_threads():
+    """Host threads on their own streams launch GEMVs of different widths (so of different LDS
+    sizes) at once; each result still matches the oracle.  The launchers' one-time state is set
+    up race-free, and the per-size occupancy cache is one atomic word."""
+    import threading
+    fmt = synth.Q4_K
+    shapes = [(300, 2048), (200, 8192), (129, 4096), (77, 12288)]
+    data = []
+    for i, (rows, cols) in enumerate(shapes):
+        blocks = synth.quant_matrix(fmt, rows, cols, seed=12, stream=900 + i)
+        x = synth.normal_f32(cols, seed=12, stream=950 + i)
+        ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+        data.append((rows, cols, dev(blocks), dev(x.astype(np.float32)), ref, nrm))
+    outs = [None] * len(shapes)
+    errors = []
+
+    def work(i):
+        try:
+            rows, cols, wb, xd, _, _ = data[i]
+            st = torch.cuda.Stream()
+            y = torch.empty(rows, dtype=torch.float32, device="cuda")
+            for _ in range(25):
+                nt.nt_gemv_q(fmt, rows, cols, wb.data_ptr(), xd.data_ptr(), y.data_ptr(), st.cuda_stream)
+            st.synchronize()
+            outs[i] = host(y)
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for i, (rows, cols, _, _, ref, nrm) in enumerate(data):
+        check_rel(outs[i], ref, nrm, what=f"thread {i} {rows}x{cols}")
