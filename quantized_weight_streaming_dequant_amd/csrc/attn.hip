@@ -45,7 +45,10 @@ constexpr int SWG = AW * SW;       // cache slots per workgroup (one split)
 constexpr int QPAD = HD + 8;       // halves per staged query row
 constexpr int OPAD = HD + 4;       // floats per staged output row
 constexpr float PSCALE = 4096.f;   // p is split at 2^12 p
-constexpr int CWV = 4;             // waves of the merge kernel
+#ifndef NT_ATTN_MERGE_WAVES
+#define NT_ATTN_MERGE_WAVES 4
+#endif
+constexpr int CWV = NT_ATTN_MERGE_WAVES;  // waves of the merge kernel
 constexpr int CK = 16;             // splits per merge wave per round of loads
 
 __device__ __forceinline__ h8 as_h8(u32x4 v) { return __builtin_bit_cast(h8, v); }
