@@ -477,7 +477,7 @@ def bench_gemm_tokens(args, torch, nt, tg):
     cs = torch.cuda.current_stream().cuda_stream
     out = []
     for fmt, rows, cols in ((synth.Q4_K, 28672, 8192), (synth.Q4_K, 8192, 8192), (synth.Q6_K, 8192, 28672),
-                            (synth.Q5_K, 28672, 8192)):
+                            (synth.Q5_K, 28672, 8192), (synth.Q8_0, 14336, 4096)):
         nbytes = synth.matrix_bytes(fmt, rows, cols)
         copies = max(2, int(np.ceil(600e6 / nbytes)))
         hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
@@ -513,7 +513,7 @@ def bench_gemm_tokens(args, torch, nt, tg):
         "value": head["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": head["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 x i8 -> i32 dots, f32 scales (quantized weights)", "data": "synthetic",
-        "config": {"workload": "k-token quantized GEMM (self-speculative verification), 70B shapes, k = 1, 2, 4, 8"},
+        "config": {"workload": "k-token quantized GEMM (self-speculative verification), 70B shapes and the 8B Q8_0 FFN shape, k = 1, 2, 4, 8"},
         "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["GBps"] / HBM_PEAK_GBS, "traffic": None},
         "gemm": out,

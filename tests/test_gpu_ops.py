@@ -132,6 +132,8 @@ GEMM_CASES = [
     (synth.Q4_K, 40, 32768, 8), (synth.Q6_K, 40, 32768, 4), (synth.Q8_0, 40, 32768, 3),
     # Q5_K on the matrix cores: short tiles, one row, chunks of fewer superblocks than waves, the widest x
     (synth.Q5_K, 37, 2304, 3), (synth.Q5_K, 1, 256, 8), (synth.Q5_K, 300, 16640, 6), (synth.Q5_K, 40, 32768, 5),
+    # Q8_0 at 3-8 tokens (the VALU kernel: its matrix-core form measured slower), the 8B FFN shape
+    (synth.Q8_0, 17, 512, 4), (synth.Q8_0, 1, 256, 8), (synth.Q8_0, 300, 4352, 6), (synth.Q8_0, 14336, 4096, 7),
 ]
 
 
@@ -199,7 +201,7 @@ def test_gemv_outlier_activations(fmt, kind):
     say(f"  worst rel err {worst:.2e}")
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q5_K, synth.Q6_K])
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.Q8_0])
 @pytest.mark.parametrize("kind", list(OUTLIER_KINDS))
 def test_gemm_outlier_activations(kind, fmt):
     """The same outlier channels in every token of the matrix-core GEMM (5 tokens, one token
