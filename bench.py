@@ -117,7 +117,7 @@ def read_probe(torch, nt, nbytes=4 << 30, reps=20):
     del buf
     return {"GBps": nbytes / (us * 1e-6) / 1e9, "bytes": nbytes, "avg_us": us, "reps": reps,
             "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "kernel": "nt_read_probe: 16-byte loads, 2 in flight per thread, 32 workgroups of 256 per CU"}
+            "kernel": "nt_read_probe: 16-byte nontemporal loads, 2 in flight per thread, 32 workgroups of 256 per CU"}
 
 
 def host_threads() -> int:

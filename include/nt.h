@@ -213,8 +213,8 @@ int nt_argmax(int64_t n, const float* v, int32_t* out_index, void* stream);
 int nt_layer_cosine(int64_t n, const float* a, const float* b, float* out, void* stream);
 
 /* Measurement helper, not a step of the decode: reads `bytes` of device memory at buf with
- * plain 16-byte vector loads (32 workgroups of 256 threads per CU, two loads in flight per
- * thread) and discards them, so that the time it takes is the achievable HBM read rate
+ * plain 16-byte nontemporal vector loads (32 workgroups of 256 threads per CU, two loads in
+ * flight per thread) and discards them, so that the time it takes is the achievable HBM read rate
  * of the part, the yardstick for the GEMVs' rates next to the published peak.  buf: device,
  * 16-byte aligned, bytes a positive multiple of 16; sink: device, 4 bytes, written only in
  * the (never expected) case that the folded data equals a fixed constant.  Errors: NT_ESHAPE,

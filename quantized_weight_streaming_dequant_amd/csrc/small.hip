@@ -256,14 +256,17 @@ __global__ __launch_bounds__(256) void cosine_kernel(int64_t n, const float* __r
 }
 
 // ------------------------------------------------------------ read probe
-// A plain stream of 16-byte loads over a buffer, two in flight per thread, 32 workgroups of
-// 256 per CU (the fastest of a sweep of 2-32 workgroups per CU and 2-16 loads per thread,
-// 5.3-5.8 TB/s over a 4 GiB buffer; the default reads 5.77 TB/s), the data folded
-// into one word per thread that is stored only if it equals a value the caller never uses
-// (so the loads cannot be dropped): the achievable HBM read rate of the part, next to which
-// the GEMVs' rates can be read.
+// A plain stream of 16-byte nontemporal loads over a buffer, two in flight per thread, 32
+// workgroups of 256 per CU (the fastest of a sweep of 2-32 workgroups per CU, 2-16 loads per
+// thread and cached or nontemporal loads: 6.4 TB/s over a 4 GiB buffer, against 5.3-5.8 TB/s
+// with cached loads), the data folded into one word per thread that is stored only if it
+// equals a value the caller never uses (so the loads cannot be dropped): the achievable HBM
+// read rate of the part, next to which the GEMVs' rates can be read.
 #ifndef NT_PROBE_WG_PER_CU
 #define NT_PROBE_WG_PER_CU 32
+#endif
+#ifndef NT_PROBE_NT
+#define NT_PROBE_NT 1  // nontemporal loads: 6.4 TB/s against 5.75 with cached ones
 #endif
 #ifndef NT_PROBE_UNROLL
 #define NT_PROBE_UNROLL 2
@@ -276,7 +279,13 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict
   for (; i + (U - 1) * stride < n16; i += U * stride) {
     u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < U; ++u) {
+#if NT_PROBE_NT
+      v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#else
+      v[u] = p[i + u * stride];
+#endif
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
