@@ -59,7 +59,8 @@ namespace nt {
 // Weight loads, through global-address-space pointers: a load the compiler can only prove
 // to be generic becomes a flat load, which also counts against the LDS wait counter, so every
 // wait for an LDS read would wait for the prefetched weights too.  Nontemporal loads were
-// measured slower on every GEMV shape here (by 10-30%), so plain cached loads are the default.
+// measured slower for these (20-45%: a lane's line is read by two instructions), so plain
+// cached loads are the default here; the streamed path's whole-line transfers do use them.
 #define NT_GPTR(T, p) ((const __attribute__((address_space(1))) T*)(p))
 #if NT_GEMV_NONTEMPORAL
 __device__ __forceinline__ u32x4 wld16(const uint8_t* p) { return __builtin_nontemporal_load(NT_GPTR(u32x4, p)); }
@@ -1549,8 +1550,15 @@ constexpr int ST_SLICE_COLS_K = 4096;
 constexpr int ST_SLICE_COLS_B = 2048;
 constexpr int ST_MAX_WAVES = 16;
 
+// The streamed path's global->LDS transfers read 1 KiB of consecutive bytes per instruction,
+// each line once, and take the nontemporal policy (cache-policy bits 2 = nt): the Q6_K down
+// GEMV 42.6 vs 44.9 us, an 8B Q8_0 layer 3% faster.  (The register path's weight loads touch
+// a line from two instructions and were 20-45% slower with it.)
+#ifndef NT_STREAM_CPOL
+#define NT_STREAM_CPOL 2
+#endif
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, NT_STREAM_CPOL);
 }
 __device__ __forceinline__ uint32_t lds4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 __device__ __forceinline__ u32x4 lds16a(const uint8_t* p) {
