@@ -72,6 +72,9 @@ int64_t nt_matrix_bytes(int fmt, int64_t rows, int64_t cols); /* bytes of a rows
 
 /* Largest cols accepted by the GEMV entry points (x is held in LDS, padded). */
 #define NT_GEMV_MAX_COLS 32768
+/* Largest rows (and vocabulary size) accepted anywhere: row and row-group indices stay in
+ * 32-bit integer range inside the kernels. */
+#define NT_MAX_ROWS (1 << 30)
 
 /* Dequantize a whole matrix to fp32: w[r*cols + c].  Every value equals the
  * block's exact weight rounded once (round-to-nearest-even) to fp32.
@@ -84,7 +87,7 @@ int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w
  * Codestruktur").  blocks: 16-byte aligned; x: 16-byte aligned, cols floats;
  * y: rows floats, overwritten, must not overlap x or blocks.
  * cols must be a multiple of the block size and <= NT_GEMV_MAX_COLS;
- * rows <= 2^31 - 1.  Accuracy: |y_r - sum_c w_rc x_c| <= 1e-3 * sum_c |w_rc x_c|
+ * rows <= NT_MAX_ROWS.  Accuracy: |y_r - sum_c w_rc x_c| <= 1e-3 * sum_c |w_rc x_c|
  * (fp32 accumulation, scale factors applied per block). */
 int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream);
 
@@ -98,7 +101,7 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
  * 1 <= n_tok <= NT_GEMM_MAX_TOK; x: n_tok x cols fp32, 16-byte aligned; y: n_tok x rows
  * fp32, overwritten, must not overlap x or blocks; blocks: 16-byte aligned; cols a positive
  * multiple of the block size (any width: wide matrices run as several launches over column
- * chunks, each adding into y); rows <= 2^31 - 1.  Per token, the accuracy of nt_gemv_q.
+ * chunks, each adding into y); rows and cols <= NT_MAX_ROWS.  Per token, the accuracy of nt_gemv_q.
  * Q4_K, Q5_K and Q6_K with 3 to 8 tokens run on the matrix cores (8-bit integer MFMA of activation digits
  * and weight codes, exact in int32); the other cases on the vector ALUs.  A token's outputs
  * do not depend on the other tokens of the call.
@@ -312,6 +315,23 @@ int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_h
                     float* logits, float* h, void* ws, size_t ws_bytes, void* compute, void* copy,
                     nt_stream_stats* stats);
 size_t nt_decode_token_ws_bytes(const nt_layer_shape* shp);
+
+/* Workspace bytes of nt_lm_head (the packed argmax key). */
+#define NT_LM_HEAD_WS_BYTES 256
+
+/* The greedy head on its own, the same launches nt_decode_token ends with (ntransformer
+ * overview, "Architektur und Codestruktur": the sampler after the model; "Hauptfunktionen":
+ * RMSNorm): logits = W_out RMSNorm(h, output_norm) with W_out an n_vocab x dim block
+ * matrix (the GEMV, its RMSNorm prologue and a fused argmax epilogue in one launch), then
+ * *token = the first index of the largest logit (ties -> lowest index; a NaN logit never
+ * wins).  h: device [dim] fp32, 16-byte aligned, read only; output: 16-byte aligned blocks;
+ * output_norm: device [dim], 16-byte aligned; logits: device [n_vocab] fp32, overwritten;
+ * token: device int32.  ws: NT_LM_HEAD_WS_BYTES bytes, 256-byte aligned, no initial contents
+ * required.  dim a positive multiple of 256 up to NT_GEMV_MAX_COLS; 1 <= n_vocab <= NT_MAX_ROWS.
+ * Errors: NT_EFORMAT, NT_ESHAPE, NT_EINVAL (null pointer, eps < 0, workspace too small),
+ * NT_EALIGN, NT_EHIP; nothing is enqueued then. */
+int nt_lm_head(int fmt, int64_t n_vocab, int64_t dim, const void* output, const float* output_norm, float eps,
+               const float* h, float* logits, int32_t* token, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------- measurement hook */
 

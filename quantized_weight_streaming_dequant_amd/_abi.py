@@ -20,6 +20,8 @@ K_ATTN_IN, K_ATTN, K_O, K_FFN_UP, K_FFN_DOWN, K_LM_HEAD, K_GEMV, K_GEMM = range(
 GEMM_MAX_TOK = 8
 TIER_PINNED, TIER_RESIDENT, TIER_FILE = 0, 1, 2
 GEMV_MAX_COLS = NT_GEMV_MAX_COLS = 32768
+NT_MAX_ROWS = 1 << 30  # largest rows / vocabulary anywhere
+NT_LM_HEAD_WS_BYTES = 256
 NT_MAX_CTX = 524288  # cache capacity limit (slots); KV cache max_ctx must also be a multiple of 8
 
 
@@ -71,7 +73,7 @@ EXPORTS = [
     "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q", "nt_gemm_q", "nt_layer_cosine", "nt_read_probe",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
     "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
-    "nt_stream_destroy", "nt_stream_set_bounce", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_timing_begin",
+    "nt_stream_destroy", "nt_stream_set_bounce", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_lm_head", "nt_timing_begin",
     "nt_timing_end",
 ]
 
@@ -115,6 +117,7 @@ def load(path: str = LIB_PATH):
         "nt_decode_token": ([vp, ctypes.POINTER(ModelPlan), ctypes.POINTER(ModelHead), i, vp, vp, vp, vp, sz, vp, vp,
                              ctypes.POINTER(StreamStats)], i),
         "nt_decode_token_ws_bytes": ([ctypes.POINTER(LayerShape)], sz),
+        "nt_lm_head": ([i, i64, i64, vp, vp, f, vp, vp, vp, vp, sz, vp], i),
         "nt_timing_begin": ([i, i], i),
         "nt_timing_end": ([ctypes.POINTER(i), ctypes.POINTER(ctypes.c_double)], i),
     }
@@ -249,6 +252,11 @@ def nt_decode_token(st, plan: ModelPlan, head: ModelHead, pos, token, logits, h,
 
 def nt_decode_token_ws_bytes(shape: LayerShape) -> int:
     return int(load().nt_decode_token_ws_bytes(ctypes.byref(shape)))
+
+
+def nt_lm_head(fmt, n_vocab, dim, output, output_norm, eps, h, logits, token, ws, ws_bytes, stream=None):
+    return _check(load().nt_lm_head(fmt, n_vocab, dim, output, output_norm, eps, h, logits, token, ws, ws_bytes,
+                                    stream))
 
 
 def nt_timing_begin(kclass: int, max_launches: int) -> None:

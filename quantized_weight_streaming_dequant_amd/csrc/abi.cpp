@@ -157,6 +157,27 @@ static hipError_t ffn_up_launch(const nt_layer_weights& w, const nt_layer_shape&
   return gemv_launch(1 << w.fmt[NT_W_GATE], EPI_SWIGLU, p, gemv_groups(p, s.ffn_dim), a, st);
 }
 
+// Enqueue the greedy head: logits = W_out RMSNorm(h, gain); the fused argmax folds into *key
+// (reset first), and *token takes the index it holds.
+static int lm_head_enqueue(int fmt, int64_t n_vocab, int dim, const void* output, const float* gain, float eps,
+                           const float* h, float* logits, unsigned long long* key, int32_t* token, bool reset,
+                           hipStream_t st) {
+  hipError_t e;
+  if (reset && (e = key_reset_launch(key, 1, st)) != hipSuccess) return hip_fail(e, "key reset launch");
+  {
+    const GemvPlan p = gemv_plan(EPI_LOGITS, dim);
+    GemvArgs a = blank_args();
+    a.x = h; a.gain = gain; a.eps = eps; a.cols = dim; a.nseg = 1;
+    a.seg[0] = make_seg(output, fmt, (int)n_vocab, dim, 0);
+    a.y = logits; a.amax = key;
+    TimedLaunch tl(NT_K_LM_HEAD, st);
+    if ((e = gemv_launch(1 << fmt, EPI_LOGITS, p, gemv_groups(p, (int)n_vocab), a, st)) != hipSuccess)
+      return hip_fail(e, "lm head launch");
+  }
+  if ((e = token_from_key_launch(key, token, st)) != hipSuccess) return hip_fail(e, "token launch");
+  return NT_OK;
+}
+
 // Enqueue one decode layer (arguments already checked).
 int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float* h, uint16_t* kc, uint16_t* vc,
               uint8_t* ws, hipStream_t st) {
@@ -290,8 +311,8 @@ int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w
 
 int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream) {
   if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
-  if (rows <= 0 || rows > 0x7FFFFFFF || cols <= 0 || cols % block_elems(fmt) || cols > NT_GEMV_MAX_COLS)
-    return fail(NT_ESHAPE, "need 0 < rows < 2^31 and cols a positive multiple of %d up to %d (got %lld x %lld)",
+  if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols % block_elems(fmt) || cols > NT_GEMV_MAX_COLS)
+    return fail(NT_ESHAPE, "need 0 < rows <= 2^30 and cols a positive multiple of %d up to %d (got %lld x %lld)",
                 block_elems(fmt), NT_GEMV_MAX_COLS, (long long)rows, (long long)cols);
   if (!blocks || !x || !y) return fail(NT_EINVAL, "null pointer");
   if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return fail(NT_EALIGN, "blocks and x must be 16-byte aligned, y 4-byte");
@@ -308,8 +329,8 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
 int nt_gemm_q(int fmt, int64_t rows, int64_t cols, int n_tok, const void* blocks, const float* x, float* y,
               void* stream) {
   if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
-  if (rows <= 0 || rows > 0x7FFFFFFF || cols <= 0 || cols > 0x7FFFFFFF || cols % block_elems(fmt))
-    return fail(NT_ESHAPE, "need 0 < rows < 2^31 and cols a positive multiple of %d (got %lld x %lld)", block_elems(fmt),
+  if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols > NT_MAX_ROWS || cols % block_elems(fmt))
+    return fail(NT_ESHAPE, "need 0 < rows, cols <= 2^30 and cols a multiple of %d (got %lld x %lld)", block_elems(fmt),
                 (long long)rows, (long long)cols);
   if (n_tok < 1 || n_tok > NT_GEMM_MAX_TOK) return fail(NT_ESHAPE, "n_tok must be in [1, %d]", NT_GEMM_MAX_TOK);
   if (!blocks || !x || !y) return fail(NT_EINVAL, "null pointer");
@@ -708,7 +729,7 @@ int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_h
   if (!head || !head->token_embd || !head->output_norm || !head->output || !token || !logits || !h || !ws)
     return fail(NT_EINVAL, "null pointer");
   if (!fmt_ok(head->embd_fmt) || !fmt_ok(head->out_fmt)) return fail(NT_EFORMAT, "unknown head format");
-  if (head->n_vocab <= 0 || head->n_vocab > 0x7FFFFFFF) return fail(NT_ESHAPE, "bad vocabulary size");
+  if (head->n_vocab <= 0 || head->n_vocab > NT_MAX_ROWS) return fail(NT_ESHAPE, "vocabulary size must be in [1, 2^30]");
   if (!aligned(head->output, 16) || !aligned(head->token_embd, 4) || !aligned(head->output_norm, 16) || !aligned(h, 16) ||
       !aligned(ws, 256))
     return fail(NT_EALIGN, "misaligned head, h or ws pointer");
@@ -726,18 +747,25 @@ int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_h
   if ((e = embed_launch(head->embd_fmt, head->n_vocab, plan->shape.dim, head->token_embd, token, h, key, cs)) != hipSuccess)
     return hip_fail(e, "embed launch");
   if ((rc = stream_layers_impl(st, plan, pos, h, wsb, cs, (hipStream_t)copy, stats))) return rc;
-  {
-    const GemvPlan p = gemv_plan(EPI_LOGITS, plan->shape.dim);
-    GemvArgs a = blank_args();
-    a.x = h; a.gain = head->output_norm; a.eps = plan->shape.eps; a.cols = plan->shape.dim; a.nseg = 1;
-    a.seg[0] = make_seg(head->output, head->out_fmt, (int)head->n_vocab, plan->shape.dim, 0);
-    a.y = logits; a.amax = key;
-    TimedLaunch tl(NT_K_LM_HEAD, cs);
-    if ((e = gemv_launch(1 << head->out_fmt, EPI_LOGITS, p, gemv_groups(p, (int)head->n_vocab), a, cs)) != hipSuccess)
-      return hip_fail(e, "lm head launch");
-  }
-  if ((e = token_from_key_launch(key, token, cs)) != hipSuccess) return hip_fail(e, "token launch");
-  return NT_OK;
+  // the embedding launch reset the key
+  return lm_head_enqueue(head->out_fmt, head->n_vocab, plan->shape.dim, head->output, head->output_norm,
+                         plan->shape.eps, h, logits, key, token, false, cs);
+}
+
+int nt_lm_head(int fmt, int64_t n_vocab, int64_t dim, const void* output, const float* output_norm, float eps,
+               const float* h, float* logits, int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
+  if (n_vocab <= 0 || n_vocab > NT_MAX_ROWS) return fail(NT_ESHAPE, "n_vocab must be in [1, %d]", NT_MAX_ROWS);
+  if (dim <= 0 || dim % 256 || dim > NT_GEMV_MAX_COLS)
+    return fail(NT_ESHAPE, "dim must be a positive multiple of 256 up to %d", NT_GEMV_MAX_COLS);
+  if (!output || !output_norm || !h || !logits || !token || !ws) return fail(NT_EINVAL, "null pointer");
+  if (!(eps >= 0.f)) return fail(NT_EINVAL, "eps must be >= 0");
+  if (!aligned(output, 16) || !aligned(output_norm, 16) || !aligned(h, 16) || !aligned(logits, 4) ||
+      !aligned(token, 4) || !aligned(ws, 256))
+    return fail(NT_EALIGN, "output, output_norm and h must be 16-byte aligned, logits and token 4-byte, ws 256-byte");
+  if (ws_bytes < NT_LM_HEAD_WS_BYTES) return fail(NT_EINVAL, "workspace too small (%zu < %d)", ws_bytes, NT_LM_HEAD_WS_BYTES);
+  return lm_head_enqueue(fmt, n_vocab, (int)dim, output, output_norm, eps, h, logits,
+                         reinterpret_cast<unsigned long long*>(ws), token, true, (hipStream_t)stream);
 }
 
 int nt_timing_begin(int kclass, int max_launches) {

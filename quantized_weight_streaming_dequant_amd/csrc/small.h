@@ -13,7 +13,10 @@ hipError_t rmsnorm_launch(int64_t n, const float* x, const float* g, float eps, 
 hipError_t rope_launch(int n_heads, int head_dim, int pos, double theta, float* qk, hipStream_t s);
 hipError_t swiglu_launch(int64_t n, const float* gate, const float* up, float* out, hipStream_t s);
 hipError_t argmax_launch(int64_t n, const float* v, int32_t* out, hipStream_t s);
-hipError_t token_from_key_launch(const unsigned long long* key, int32_t* token, hipStream_t s);
+// tokens[i] = index packed in key[i], for i < n (n <= 64)
+hipError_t token_from_key_launch(const unsigned long long* key, int32_t* token, hipStream_t s, int n = 1);
+// key[i] = 0 for i < n (n <= 64)
+hipError_t key_reset_launch(unsigned long long* key, int n, hipStream_t s);
 hipError_t cosine_launch(int64_t n, const float* a, const float* b, float* out, hipStream_t s);
 hipError_t read_probe_launch(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 

@@ -211,12 +211,26 @@ hipError_t argmax_launch(int64_t n, const float* v, int32_t* out, hipStream_t s)
   return hipGetLastError();
 }
 
-__global__ void token_from_key_kernel(const unsigned long long* key, int32_t* token) {
-  *token = (int32_t)(0xFFFFFFFFu - (uint32_t)(*key & 0xFFFFFFFFull));
+// The greedy pick of n tokens from their packed (value, index) keys, and the keys' reset
+// before a fused LM-head launch folds its maxima into them (a kernel rather than a memset,
+// so that callers may capture it in a graph).
+__global__ void token_from_key_kernel(const unsigned long long* key, int32_t* token, int n) {
+  const int i = (int)threadIdx.x;
+  if (i < n) token[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key[i] & 0xFFFFFFFFull));
 }
 
-hipError_t token_from_key_launch(const unsigned long long* key, int32_t* token, hipStream_t s) {
-  hipLaunchKernelGGL(token_from_key_kernel, dim3(1), dim3(1), 0, s, key, token);
+hipError_t token_from_key_launch(const unsigned long long* key, int32_t* token, hipStream_t s, int n) {
+  hipLaunchKernelGGL(token_from_key_kernel, dim3(1), dim3(64), 0, s, key, token, n);
+  return hipGetLastError();
+}
+
+__global__ void key_reset_kernel(unsigned long long* key, int n) {
+  const int i = (int)threadIdx.x;
+  if (i < n) key[i] = 0ull;
+}
+
+hipError_t key_reset_launch(unsigned long long* key, int n, hipStream_t s) {
+  hipLaunchKernelGGL(key_reset_kernel, dim3(1), dim3(64), 0, s, key, n);
   return hipGetLastError();
 }
 

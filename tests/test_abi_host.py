@@ -83,6 +83,19 @@ def test_block_geometry():
     (lambda: nt.nt_stream_create(None, 256, 1024), nt.NT_EINVAL),
     (lambda: nt.nt_stream_create(256, 256, 1024), nt.NT_EINVAL),
     (lambda: nt.nt_stream_create(256, 512 + 16, 1024), nt.NT_EALIGN),
+    # rows past 2^30 (row-group indices stay in 32-bit range inside the kernels)
+    (lambda: nt.nt_gemv_q(nt.Q4_0, nt.NT_MAX_ROWS + 1, 32, 16, 16, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_gemm_q(nt.Q4_0, nt.NT_MAX_ROWS + 1, 32, 2, 16, 16, 16), nt.NT_ESHAPE),
+    # the greedy head
+    (lambda: nt.nt_lm_head(9, 1000, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_EFORMAT),
+    (lambda: nt.nt_lm_head(nt.Q4_K, 1000, 1000, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_ESHAPE),
+    (lambda: nt.nt_lm_head(nt.Q4_K, 0, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_ESHAPE),
+    (lambda: nt.nt_lm_head(nt.Q4_K, nt.NT_MAX_ROWS + 1, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_ESHAPE),
+    (lambda: nt.nt_lm_head(nt.Q4_K, 1000, 1024, 256, None, 1e-5, 256, 256, 256, 256, 256), nt.NT_EINVAL),
+    (lambda: nt.nt_lm_head(nt.Q4_K, 1000, 1024, 256, 256, -1.0, 256, 256, 256, 256, 256), nt.NT_EINVAL),
+    (lambda: nt.nt_lm_head(nt.Q4_K, 1000, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 8), nt.NT_EINVAL),
+    (lambda: nt.nt_lm_head(nt.Q4_K, 1000, 1024, 264, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_EALIGN),
+    (lambda: nt.nt_lm_head(nt.Q4_K, 1000, 1024, 256, 256, 1e-5, 256, 256, 256, 128, 256), nt.NT_EALIGN),
 ])
 def test_bad_arguments_are_rejected(call, code):
     with pytest.raises(nt.NtError) as ei:
@@ -182,6 +195,8 @@ def test_layer_workspace_too_small():
 def test_header_constants_match_binding():
     import re
     text = open(HEADER).read()
-    for name in ("NT_MAX_CTX", "NT_GEMV_MAX_COLS"):
+    for name in ("NT_MAX_CTX", "NT_GEMV_MAX_COLS", "NT_LM_HEAD_WS_BYTES"):
         m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(nt, name), name
+    m = re.search(r"#define\s+NT_MAX_ROWS\s+\(1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == nt.NT_MAX_ROWS

@@ -20,7 +20,8 @@ import quantized_weight_streaming_dequant_amd as nt
 import synth
 from quantized_weight_streaming_dequant_amd import torch_glue as tg
 from synth import recipes
-from tests.gpu_util import check_rel, dev, host, same_value, say, stream, v_from_device, v_to_device
+from tests.gpu_util import (check_layer_stages, check_rel, dev, host, same_value, say, stream, v_from_device,
+                            v_to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,25 +71,8 @@ def run_layer_and_check(shape, mix, pos, n_slots, layer=0, sample_rows=None):
 
     st = oracle.decode_layer(L.host, mix, shape, pos, h0, L.kc_host, L.vc_host,
                              forced={"k16": g_k16, "v16": g_v16, "q": g_q, "o": g_o, "h1": g_h1, "a": g_a})
-    # RoPE mixes rows 2i and 2i+1: the pair's GEMV normalisers bound the rotated error
-    qn = np.repeat(st["q_nrm"][0::2] + st["q_nrm"][1::2], 2)
-    kn = np.repeat(st["k_nrm"][0::2] + st["k_nrm"][1::2], 2)
-    res = {}
-    # the cache holds RNE_fp16(v') for some v' within the GEMV tolerance of the exact value:
-    # |fp16 - exact| <= 1e-3 N + half a binary16 step at that value
-    for name, bits, exact, nrm in (("k16", g_k16, st["k"], kn), ("v16", g_v16, st["v"], st["v_nrm"])):
-        val = bits.view(np.float16).astype(np.float64)
-        half_step = np.spacing(np.abs(bits.view(np.float16))).astype(np.float64) / 2
-        err = np.abs(val - exact)
-        assert np.all(err <= 1e-3 * nrm + half_step), f"{name}: worst {np.max(err / (1e-3 * nrm + half_step)):.3f}"
-        res[name] = float(np.max(np.maximum(err - half_step, 0) / nrm))
-    res["q"] = check_rel(g_q, st["q"], qn, what="q")
-    res["o"] = check_rel(g_o, st["o"], st["o_nrm"], what="attention")
-    res["h1"] = check_rel(g_h1, st["h1"], st["h1_nrm"], what="h1")
-    # a = silu(g) u: with |dg| <= e N_g and |du| <= e N_u, |da| <= e (1.1 N_g |u| + |g| N_u) + O(e^2)
-    na = 1.1 * st["gate_nrm"] * np.abs(st["up"]) + (np.abs(st["gate"]) + 1e-3 * st["gate_nrm"]) * st["up_nrm"]
-    res["a"] = check_rel(g_a, st["a"], na, what="swiglu")
-    res["h2"] = check_rel(g_h2, st["h2"], st["h2_nrm"], what="h2")
+    res = check_layer_stages(st, {"k16": g_k16, "v16": g_v16, "q": g_q, "o": g_o, "h1": g_h1, "a": g_a,
+                                  "h2": g_h2})
     # free-running (no forcing) end-to-end error, reported only
     free = oracle.decode_layer(L.host, mix, shape, pos, h0, L.kc_host, L.vc_host)
     rel = np.max(np.abs(g_h2 - free["h2"]) / (free["h2_nrm"]))
