@@ -188,6 +188,23 @@ int nt_decode_layer(const nt_layer_weights* w, const nt_layer_shape* shp, int po
                     uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream);
 size_t nt_decode_layer_ws_bytes(const nt_layer_shape* shp);
 
+/* Bytes of the static workspace of nt_decode_layer_noalloc (per device). */
+#define NT_NOALLOC_WS_BYTES (8 << 20)
+
+/* nt_decode_layer for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same launches, with the
+ * workspace taken from a static device array of NT_NOALLOC_WS_BYTES that each device holds
+ * until the process ends, found on the first call on a device (with that device current)
+ * instead of a caller buffer.  The call allocates nothing.  Shapes whose
+ * nt_decode_layer_ws_bytes() exceeds NT_NOALLOC_WS_BYTES are rejected with NT_ESHAPE (the
+ * 70B shape at 4224 cache slots needs 0.8 MB; the limit is reached near 60000 slots).  Every
+ * call on a device shares that device's array: calls that overlap in time on one device
+ * (other streams, other host threads) race on it and must be ordered by the caller.  After
+ * the call the array holds the stage outputs nt_decode_layer leaves in its workspace.
+ * Arguments, results and errors otherwise as nt_decode_layer. */
+int nt_decode_layer_noalloc(const nt_layer_weights* w, const nt_layer_shape* shp, int pos, float* h,
+                            uint16_t* k_cache, uint16_t* v_cache, void* stream);
+
 /* The FFN input half of a decode layer on its own, the same launch nt_decode_layer makes:
  * a = SwiGLU(Wg n, Wu n) with n = RMSNorm(h, ffn_norm) (ntransformer overview,
  * "Hauptfunktionen": RMSNorm, SwiGLU).  h: device [dim] fp32, 16-byte aligned, read only;

@@ -22,6 +22,7 @@ TIER_PINNED, TIER_RESIDENT, TIER_FILE = 0, 1, 2
 GEMV_MAX_COLS = NT_GEMV_MAX_COLS = 32768
 NT_MAX_ROWS = 1 << 30  # largest rows / vocabulary anywhere
 NT_LM_HEAD_WS_BYTES = 256
+NT_NOALLOC_WS_BYTES = 8 << 20  # static workspace of nt_decode_layer_noalloc
 NT_MAX_CTX = 524288  # cache capacity limit (slots); KV cache max_ctx must also be a multiple of 8
 
 
@@ -72,7 +73,7 @@ _lib = None
 EXPORTS = [
     "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q", "nt_gemm_q", "nt_layer_cosine", "nt_read_probe",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
-    "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
+    "nt_decode_layer_noalloc", "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
     "nt_stream_destroy", "nt_stream_set_bounce", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_lm_head", "nt_timing_begin",
     "nt_timing_end",
 ]
@@ -106,6 +107,7 @@ def load(path: str = LIB_PATH):
         "nt_swiglu": ([i64, vp, vp, vp, vp], i),
         "nt_decode_layer": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerShape), i, vp, vp, vp, vp, sz, vp], i),
         "nt_decode_layer_ws_bytes": ([ctypes.POINTER(LayerShape)], sz),
+        "nt_decode_layer_noalloc": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerShape), i, vp, vp, vp, vp], i),
         "nt_ffn_up": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerShape), vp, vp, vp], i),
         "nt_decode_layer_ws_offsets": ([ctypes.POINTER(LayerShape), ctypes.POINTER(ctypes.c_int64)], i),
         "nt_embed_row": ([i, i64, i64, vp, vp, vp, vp], i),
@@ -200,6 +202,11 @@ def nt_swiglu(n, gate, up, out, stream=None):
 def nt_decode_layer(weights: LayerWeights, shape: LayerShape, pos, h, k_cache, v_cache, ws, ws_bytes, stream=None):
     return _check(load().nt_decode_layer(ctypes.byref(weights), ctypes.byref(shape), pos, h, k_cache, v_cache, ws,
                                          ws_bytes, stream))
+
+
+def nt_decode_layer_noalloc(weights: LayerWeights, shape: LayerShape, pos, h, k_cache, v_cache, stream=None):
+    return _check(load().nt_decode_layer_noalloc(ctypes.byref(weights), ctypes.byref(shape), pos, h, k_cache, v_cache,
+                                                 stream))
 
 
 def nt_ffn_up(weights: LayerWeights, shape: LayerShape, h, a, stream=None):

@@ -268,6 +268,11 @@ int check_layout(const nt_layer_shape& s, const nt_layer_layout& lay) {
 
 }  // namespace
 
+namespace nt {
+// The thread-local error message of nt_last_error(), for entry points in other files.
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace nt
+
 // ====================================================================== C ABI
 
 struct nt_streamer {
