@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--file-layers", type=int, default=8, help="layers read from a file in --config 8")
     p.add_argument("--read-threads", type=int, default=8, help="reader threads per blob in --config 8")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip the GEMV and 8B-layer measurements of the default run")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--layers", type=int, default=80, help="layers of the 70B model (measurement runs only)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -264,17 +265,16 @@ def ffn_up_bytes(mix, shape):
     return 2 * synth.matrix_bytes(mix["gate"], rows, cols) + 4 * (2 * cols + rows)
 
 
-def cpu_baseline_70b(mix, target_s):
-    """The checker (fp64, OpenMP over the host threads) on a bounded sample of one decode
-    token: whole layers until target_s of CPU work, plus a slice of the LM head; scaled
-    to one 80-layer token."""
+def _oracle_token_sample(mix, target_s, max_layers=80, head_rows=8192):
+    """Time the checker on whole 70B layers (pos 4096) until target_s of work, and on head_rows
+    LM-head rows; returns (seconds per 80-layer token, layers timed, rows, seconds of work)."""
     import oracle
     import synth
     from synth import recipes
     shp = recipes.LLAMA31_70B
     t_layers, n = 0.0, 0
     h = recipes.hidden_input(shp.dim)
-    while n < 80 and t_layers < 0.8 * target_s:
+    while n < max_layers and (n == 0 or t_layers < 0.8 * target_s):
         w = recipes.layer_arrays(shp, mix, n)
         kc = recipes.kv_cache_array(shp, n, "k", 4096)
         vc = recipes.kv_cache_array(shp, n, "v", 4096)
@@ -283,17 +283,59 @@ def cpu_baseline_70b(mix, target_s):
         t_layers += time.time() - t
         h = st["h2"]
         n += 1
-    rows = 8192
     head_fmt = synth.Q4_K if mix["q"] == synth.Q4_K else synth.Q6_K
-    out = synth.quant_rows(head_fmt, shp.dim, range(rows), 0,
+    out = synth.quant_rows(head_fmt, shp.dim, range(head_rows), 0,
                            recipes.stream_id(recipes.GLOBAL_LAYER, recipes.GID_OUTPUT))
     t = time.time()
-    oracle.gemv(head_fmt, rows, shp.dim, out, oracle.rmsnorm(h, np.ones(shp.dim), shp.eps))
-    t_head = (time.time() - t) * (128256 / rows)
-    s_per_tok = 80 * (t_layers / n) + t_head
-    return {"value": 1.0 / s_per_tok, "unit": "tok/s", "cores": host_threads(), "kind": "oracle",
+    oracle.gemv(head_fmt, head_rows, shp.dim, out, oracle.rmsnorm(h, np.ones(shp.dim), shp.eps))
+    t_rows = time.time() - t
+    s_per_tok = 80 * (t_layers / n) + t_rows * (128256 / head_rows)
+    return s_per_tok, n, head_rows, t_layers + t_rows
+
+
+def cpu_baseline_70b(mix, target_s):
+    """The checker (fp64, OpenMP) on a bounded sample of one decode token, scaled to one 80-layer
+    token: with every host thread (whole layers until target_s of work, plus 8192 LM-head rows),
+    then with one thread (one layer and 1024 rows)."""
+    import oracle
+    cores = host_threads()
+    s_all, n, rows, work = _oracle_token_sample(mix, target_s)
+    old = oracle.set_threads(1)
+    try:
+        s_one, n1, rows1, work1 = _oracle_token_sample(mix, target_s, max_layers=1, head_rows=1024)
+    finally:
+        oracle.set_threads(old)
+    return {"value": 1.0 / s_all, "unit": "tok/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of 80 decode layers (70B shape, pos 4096) and {rows} of 128256 LM-head rows, "
-                      f"fp64, scaled to one token ({t_layers + t_head * rows / 128256:.1f} s of CPU work)"}
+                      f"fp64, scaled to one token ({work:.1f} s of CPU work)",
+            "one_thread": {"value": 1.0 / s_one, "unit": "tok/s", "cores": 1,
+                           "sample": f"{n1} decode layer and {rows1} LM-head rows, scaled to one token "
+                                     f"({work1:.1f} s of CPU work)"}}
+
+
+def metric_extras(torch, nt, tg):
+    """The GEMV and 8B halves of the metric, measured in the default run: the Q8_0 4096x4096
+    GEMV, the 70B GEMV shapes in Q4_K and Q6_K (rotating weight copies past the 256 MB
+    last-level cache, HIP events around back-to-back launches) and one Llama-3-8B-shaped
+    Q8_0 layer with its derived tokens/s."""
+    import synth
+    keys = ("rows", "cols", "format", "avg_us", "GBps", "frac_of_peak", "algorithmic_bytes", "copies")
+    out = {}
+    g = rotating_gemv(torch, nt, synth.Q8_0, 4096, 4096, 34, 200, 10)
+    out["gemv_q8_0_4096x4096"] = {k: g[k] for k in keys}
+    torch.cuda.empty_cache()
+    lst = []
+    for fmt in (synth.Q4_K, synth.Q6_K):
+        for r, c in ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)):
+            nbytes = synth.matrix_bytes(fmt, r, c)
+            g = rotating_gemv(torch, nt, fmt, r, c, max(2, int(np.ceil(600e6 / nbytes))), 200, 10)
+            lst.append({k: g[k] for k in keys})
+            log(f"  {g['format']} {r}x{c}: {g['avg_us']:.2f} us, {g['GBps']:.0f} GB/s ({100 * g['frac_of_peak']:.1f}%)")
+            torch.cuda.empty_cache()
+    out["gemv_70b"] = lst
+    out["layer_8b_q8_0"] = layer_8b_measure(torch, nt, tg, 100, 10)
+    torch.cuda.empty_cache()
+    return out
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -371,7 +413,7 @@ def bench_decode_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q4_k/q6_k weights)", "data": "synthetic (seeded, random weights of the named shape)",
+        "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales, sums and activations, f16 kv (q4_k/q6_k weights)", "data": "synthetic (seeded, random weights of the named shape)",
         "config": {"workload": "llama3.1-70b-shape Q4_K_M resident decode, 128256 vocab, 4096-slot fp16 KV prefill, "
                                "greedy, batch 1", "layers": n_layers, "global_batch": 1, "seq_len": 4096 + steps,
                    "parallelism": "none (1 GPU)"},
@@ -389,10 +431,13 @@ def bench_decode_70b(args, torch, nt, tg):
     rp = read_probe(torch, nt)
     res["read_probe"] = rp
     res["roofline"]["frac_of_read_probe"] = res["roofline"]["achieved"] / rp["GBps"]
+    del m, lw, plan, keep
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        log("GEMV shapes and the 8B layer...")
+        res.update(metric_extras(torch, nt, tg))
     if not args.no_cpu_baseline:
         log("cpu baseline (checker on a bounded sample)...")
-        del m
-        torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline_70b(mix, args.cpu_seconds)
     return res
 
@@ -459,7 +504,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": best["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": best["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 dots, f32 scales (quantized weights)", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales and sums (quantized weights)", "data": "synthetic",
         "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K and Q5_K"},
         "roofline": {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": best["frac_of_peak"], "traffic": None},
@@ -512,7 +557,7 @@ def bench_gemm_tokens(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": head["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": head["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 dots, f32 scales (quantized weights)", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales and sums (quantized weights)", "data": "synthetic",
         "config": {"workload": "k-token quantized GEMM (self-speculative verification), 70B shapes and the 8B Q8_0 FFN shape, k = 1, 2, 4, 8"},
         "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["GBps"] / HBM_PEAK_GBS, "traffic": None},
@@ -575,7 +620,7 @@ def bench_layer_skip_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": res_t["skipping"], "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": 1e3 / res_t["skipping"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q4_k/q6_k weights)", "data": "synthetic (seeded, random weights of the named shape)",
+        "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales, sums and activations, f16 kv (q4_k/q6_k weights)", "data": "synthetic (seeded, random weights of the named shape)",
         "config": {"workload": f"llama3.1-70b-shape Q4_K_M resident decode with cosine layer skip ({args.skip} of "
                                f"{n_layers} layers), 4096-slot fp16 KV prefill, greedy, batch 1",
                    "layers": n_layers, "skipped": skip},
@@ -584,13 +629,14 @@ def bench_layer_skip_70b(args, torch, nt, tg):
     }
 
 
-def bench_layer_8b(args, torch, nt, tg):
+def layer_8b_measure(torch, nt, tg, steps, warmup):
+    """One Llama-3-8B-shaped Q8_0 decode layer at pos 1023 over a 1024-slot cache, over 4 distinct
+    layers' weights in rotation (past the 256 MB last-level cache), host-timed around the batch;
+    derived tokens/s = 1 / (32 layers + the Q8_0 128256 x 4096 LM head)."""
     import synth
     from synth import recipes
-    steps = args.steps or 100
-    warmup = args.warmup if args.warmup is not None else 10
     shape, mix = recipes.LLAMA3_8B, recipes.MIX_Q8_0
-    copies = 4  # 4 x 232 MB of distinct layers, past the 256 MB last-level cache
+    copies = 4
     lays = [recipes.layer_arrays(shape, mix, l) for l in range(copies)]
     dl = [{k: torch.from_numpy(v).cuda() for k, v in L.items()} for L in lays]
     ws_list = [tg.layer_weights([mix[n] for n in recipes.TENSORS], [d[n] for n in recipes.TENSORS], d["attn_norm"],
@@ -618,14 +664,25 @@ def bench_layer_8b(args, torch, nt, tg):
     lm = rotating_gemv(torch, nt, synth.Q8_0, 128256, 4096, 2, 50, 5)
     tok_s = 1.0 / (32 * t_layer + lm["avg_us"] * 1e-6)
     lb = recipes.layer_weight_bytes(shape, mix) + 2 * 8 * 1024 * 128 * 2
+    del dl, ws_list
+    return {"layer_us": t_layer * 1e6, "layer_GBps": lb / t_layer / 1e9, "layer_frac_of_peak": lb / t_layer / 1e9 / HBM_PEAK_GBS,
+            "layer_bytes": lb, "derived_tok_s": tok_s, "roofline_tok_s": 1.0 / ((32 * lb + lm["algorithmic_bytes"]) / (HBM_PEAK_GBS * 1e9)),
+            "lm_head_us": lm["avg_us"], "lm_head_GBps": lm["GBps"], "steps": steps}
+
+
+def bench_layer_8b(args, torch, nt, tg):
+    steps = args.steps or 100
+    warmup = args.warmup if args.warmup is not None else 10
+    r = layer_8b_measure(torch, nt, tg, steps, warmup)
     return {
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
-        "value": tok_s, "unit": "tok/s (derived: 32 layers + Q8_0 LM head)", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": t_layer * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q8_0 weights)", "data": "synthetic",
+        "value": r["derived_tok_s"], "unit": "tok/s (derived: 32 layers + Q8_0 LM head)", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": r["layer_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales, sums and activations, f16 kv (q8_0 weights)",
+        "data": "synthetic",
         "config": {"workload": "llama3-8b-shape Q8_0 decode layer, pos 1023, 1024-slot fp16 KV"},
-        "layer_us": t_layer * 1e6, "layer_GBps": lb / t_layer / 1e9, "layer_frac_of_peak": lb / t_layer / 1e9 / HBM_PEAK_GBS,
-        "lm_head": lm,
+        **r,
     }
 
 
@@ -687,7 +744,7 @@ def bench_stream_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": steps / dt, "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q6_k weights)", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales, sums and activations, f16 kv (q6_k weights)", "data": "synthetic",
         "config": {"workload": "llama3.1-70b-shape Q6_K, 26 layers resident, 54 streamed from pinned host memory",
                    "layers": n_layers},
         "h2d_GBps": h2d / dt / 1e9, "pinned_copy_ceiling_GBps": ceil, "pcie_gen5_x16_GBps": 63.0,
@@ -771,7 +828,7 @@ def bench_file_tier_70b(args, torch, nt, tg):
         "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
         "value": res["file"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": 1e3 / res["file"]["tok_s"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 dots, f32 scales and activations, f16 kv (q6_k weights)", "data": "synthetic",
+        "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales, sums and activations, f16 kv (q6_k weights)", "data": "synthetic",
         "config": {"workload": f"llama3.1-70b-shape Q6_K, {n_layers} layers read from a file through the page cache, "
                                f"{args.read_threads} readers per blob", "layers": n_layers},
         "file_tier": res["file"], "pinned_tier": res["pinned"],

@@ -81,8 +81,19 @@ def lib():
         L.or_swiglu.restype = None
         L.or_argmax.argtypes = [i64, vp]
         L.or_argmax.restype = i64
+        L.or_set_threads.argtypes = [ci]
+        L.or_set_threads.restype = None
+        L.or_get_threads.argtypes = []
+        L.or_get_threads.restype = ci
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> int:
+    """Set the checker's OpenMP thread count (for timing); returns the previous one."""
+    old = lib().or_get_threads()
+    lib().or_set_threads(int(n))
+    return old
 
 
 def _c(a, dtype):

@@ -34,11 +34,16 @@
  * routines on special cases).  See tests/test_oracle_pins.py.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_K = 4 };
+
+/* Threads of the OpenMP loops below (for timing the checker on a stated core count). */
+void or_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int or_get_threads(void) { return omp_get_max_threads(); }
 
 int or_block_elems(int fmt) {
   switch (fmt) {
