@@ -188,6 +188,26 @@ int nt_decode_layer(const nt_layer_weights* w, const nt_layer_shape* shp, int po
                     uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream);
 size_t nt_decode_layer_ws_bytes(const nt_layer_shape* shp);
 
+/* One decode layer for n_tok tokens at consecutive positions pos .. pos + n_tok - 1 at once:
+ * the verification pass of self-speculative decoding, where the draft tokens proposed by the
+ * VRAM-resident layers run through the whole model together (ntransformer overview,
+ * "Hauptfunktionen": self-speculative decoding; RMSNorm, RoPE, GQA, SwiGLU, KV cache).
+ * Token t is the single-token layer of nt_decode_layer at position pos + t: its k and v go to
+ * cache slot pos + t, and it attends over slots [0, pos + t] (the earlier draft tokens of the
+ * call included, the later ones not).  Each weight matrix is read once for all n_tok tokens
+ * (the k-token GEMM of nt_gemm_q; the residual adds accumulate into h).
+ * h: [n_tok][dim] fp32, in/out.  1 <= n_tok <= NT_GEMM_MAX_TOK; 0 <= pos, pos + n_tok <= max_ctx.
+ * ws: nt_decode_layer_k_ws_bytes() bytes, 256-byte aligned, no initial contents required; after
+ * the call it holds, as fp32 [n_tok][...] arrays at the offsets nt_decode_layer_k_ws_offsets
+ * gives (q, o, h1, a), each token's rotated query, attention output, h1 and SwiGLU output.
+ * Accuracy per token as nt_decode_layer; the results are those of n_tok sequential
+ * nt_decode_layer calls up to rounding.  Other constraints and errors as nt_decode_layer. */
+int nt_decode_layer_k(const nt_layer_weights* w, const nt_layer_shape* shp, int pos, int n_tok, float* h,
+                      uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream);
+size_t nt_decode_layer_k_ws_bytes(const nt_layer_shape* shp, int n_tok);  /* 0 for a bad shape or n_tok */
+/* off[0..3] = byte offsets of q, o, h1 and a ([n_tok][...] fp32 each) in that workspace */
+int nt_decode_layer_k_ws_offsets(const nt_layer_shape* shp, int n_tok, int64_t* off);
+
 /* Bytes of the static workspace of nt_decode_layer_noalloc (per device). */
 #define NT_NOALLOC_WS_BYTES (8 << 20)
 
@@ -263,7 +283,9 @@ typedef struct {
   uint16_t* k_cache;    /* device, fp16, the KV cache layout above */
   uint16_t* v_cache;
   int skip;             /* 1: layer skip: the layer is not run (h passes through unchanged, its
-                           cache is not written, a streamed blob is not copied); the caller picks
+                           cache is not written, a streamed blob is not copied, and its blob,
+                           caches and tier are not checked, so a plan whose streamed layers are
+                           all skipped runs without a streamer); the caller picks
                            the layers, e.g. those whose nt_layer_cosine of input and output is
                            highest (ntransformer overview, "Leistung und Caching-Struktur") */
   int fd;               /* NT_TIER_FILE: an open file descriptor readable with pread */
@@ -332,6 +354,23 @@ int nt_decode_token(nt_streamer* st, const nt_model_plan* plan, const nt_model_h
                     float* logits, float* h, void* ws, size_t ws_bytes, void* compute, void* copy,
                     nt_stream_stats* stats);
 size_t nt_decode_token_ws_bytes(const nt_layer_shape* shp);
+
+/* The verification pass of self-speculative decoding over the whole model (ntransformer
+ * overview, "Hauptfunktionen": the draft tokens of the VRAM-resident layers are checked by the
+ * full model in one pass): the n_tok input tokens tokens[t] at positions pos + t run through
+ * every layer of the plan together (nt_decode_layer_k; streamed layers as in nt_stream_layers,
+ * each blob copied once for all tokens), then the final RMSNorm and the LM head for every
+ * token (the k-token GEMM), and next[t] = the greedy pick after token t (first index of the
+ * largest logit).  A caller that drafted tokens[1..] from tokens[0] accepts the draft tokens
+ * while tokens[t + 1] == next[t], and continues from the first next[t] that differs.
+ * tokens, next: device int32[n_tok]; logits: device [n_tok][n_vocab] fp32; h: device
+ * [n_tok][dim] fp32 (the final hidden states on return).  ws: nt_verify_tokens_ws_bytes()
+ * bytes, 256-byte aligned.  1 <= n_tok <= NT_GEMM_MAX_TOK; pos + n_tok <= max_ctx.
+ * Other arguments, constraints and errors as nt_decode_token. */
+int nt_verify_tokens(nt_streamer* st, const nt_model_plan* plan, const nt_model_head* head, int pos, int n_tok,
+                     const int32_t* tokens, int32_t* next, float* logits, float* h, void* ws, size_t ws_bytes,
+                     void* compute, void* copy, nt_stream_stats* stats);
+size_t nt_verify_tokens_ws_bytes(const nt_layer_shape* shp, int n_tok);
 
 /* Workspace bytes of nt_lm_head (the packed argmax key). */
 #define NT_LM_HEAD_WS_BYTES 256

@@ -74,7 +74,9 @@ EXPORTS = [
     "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q", "nt_gemm_q", "nt_layer_cosine", "nt_read_probe",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
     "nt_decode_layer_noalloc", "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
-    "nt_stream_destroy", "nt_stream_set_bounce", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_lm_head", "nt_timing_begin",
+    "nt_stream_destroy", "nt_stream_set_bounce", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_lm_head", "nt_decode_layer_k",
+    "nt_decode_layer_k_ws_bytes", "nt_decode_layer_k_ws_offsets", "nt_verify_tokens", "nt_verify_tokens_ws_bytes",
+    "nt_timing_begin",
     "nt_timing_end",
 ]
 
@@ -120,6 +122,13 @@ def load(path: str = LIB_PATH):
                              ctypes.POINTER(StreamStats)], i),
         "nt_decode_token_ws_bytes": ([ctypes.POINTER(LayerShape)], sz),
         "nt_lm_head": ([i, i64, i64, vp, vp, f, vp, vp, vp, vp, sz, vp], i),
+        "nt_decode_layer_k": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerShape), i, i, vp, vp, vp, vp, sz, vp],
+                              i),
+        "nt_decode_layer_k_ws_bytes": ([ctypes.POINTER(LayerShape), i], sz),
+        "nt_decode_layer_k_ws_offsets": ([ctypes.POINTER(LayerShape), i, ctypes.POINTER(ctypes.c_int64)], i),
+        "nt_verify_tokens": ([vp, ctypes.POINTER(ModelPlan), ctypes.POINTER(ModelHead), i, i, vp, vp, vp, vp, vp, sz,
+                              vp, vp, ctypes.POINTER(StreamStats)], i),
+        "nt_verify_tokens_ws_bytes": ([ctypes.POINTER(LayerShape), i], sz),
         "nt_timing_begin": ([i, i], i),
         "nt_timing_end": ([ctypes.POINTER(i), ctypes.POINTER(ctypes.c_double)], i),
     }
@@ -259,6 +268,33 @@ def nt_decode_token(st, plan: ModelPlan, head: ModelHead, pos, token, logits, h,
 
 def nt_decode_token_ws_bytes(shape: LayerShape) -> int:
     return int(load().nt_decode_token_ws_bytes(ctypes.byref(shape)))
+
+
+def nt_decode_layer_k(weights: LayerWeights, shape: LayerShape, pos, n_tok, h, k_cache, v_cache, ws, ws_bytes,
+                      stream=None):
+    return _check(load().nt_decode_layer_k(ctypes.byref(weights), ctypes.byref(shape), pos, n_tok, h, k_cache, v_cache,
+                                           ws, ws_bytes, stream))
+
+
+def nt_decode_layer_k_ws_bytes(shape: LayerShape, n_tok: int) -> int:
+    return int(load().nt_decode_layer_k_ws_bytes(ctypes.byref(shape), n_tok))
+
+
+def nt_decode_layer_k_ws_offsets(shape: LayerShape, n_tok: int) -> dict:
+    off = (ctypes.c_int64 * 4)()
+    _check(load().nt_decode_layer_k_ws_offsets(ctypes.byref(shape), n_tok, off))
+    return {"q": off[0], "o": off[1], "h1": off[2], "a": off[3]}
+
+
+def nt_verify_tokens(st, plan: ModelPlan, head: ModelHead, pos, n_tok, tokens, next_tokens, logits, h, ws, ws_bytes,
+                     compute, copy, stats: StreamStats | None = None):
+    return _check(load().nt_verify_tokens(st, ctypes.byref(plan), ctypes.byref(head), pos, n_tok, tokens, next_tokens,
+                                          logits, h, ws, ws_bytes, compute, copy,
+                                          ctypes.byref(stats) if stats is not None else None))
+
+
+def nt_verify_tokens_ws_bytes(shape: LayerShape, n_tok: int) -> int:
+    return int(load().nt_verify_tokens_ws_bytes(ctypes.byref(shape), n_tok))
 
 
 def nt_lm_head(fmt, n_vocab, dim, output, output_norm, eps, h, logits, token, ws, ws_bytes, stream=None):

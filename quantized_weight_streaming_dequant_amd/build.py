@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnt.so")
 
-SOURCES = ["gemv.hip", "attn.hip", "small.hip", "abi.cpp", "noalloc.cpp"]
+SOURCES = ["gemv.hip", "attn.hip", "small.hip", "layer_k.hip", "abi.cpp", "noalloc.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -18,6 +18,7 @@
 #include "attn.h"
 #include "common.h"
 #include "gemv.h"
+#include "layer_k.h"
 #include "small.h"
 
 using namespace nt;
@@ -90,6 +91,33 @@ LayerWs layer_ws(const nt_layer_shape& s) {
   w.a = off; off = align256(off + 4 * (size_t)s.ffn_dim);
   w.part = off; off = align256(off + 4 * attn_part_floats(s.n_q_heads, s.max_ctx));
   w.key = off; off = align256(off + 8);
+  w.total = off;
+  return w;
+}
+
+// Workspace of the k-token layer: normalised rows, q, k, v, attention output, h1, gate, up,
+// SwiGLU output (each [k][...] fp32) and the attention partials of every token.
+struct LayerKWs {
+  size_t xn, q, kk, vv, o, h1, g, u, a, part, total;
+  size_t part_stride;  // floats of partials per token
+};
+
+LayerKWs layer_k_ws(const nt_layer_shape& s, int k) {
+  LayerKWs w;
+  size_t off = 0;
+  const size_t nq = (size_t)s.n_q_heads * s.head_dim, nkv = (size_t)s.n_kv_heads * s.head_dim;
+  const size_t kk = (size_t)k;
+  w.xn = off; off = align256(off + 4 * kk * (size_t)s.dim);
+  w.q = off; off = align256(off + 4 * kk * nq);
+  w.kk = off; off = align256(off + 4 * kk * nkv);
+  w.vv = off; off = align256(off + 4 * kk * nkv);
+  w.o = off; off = align256(off + 4 * kk * nq);
+  w.h1 = off; off = align256(off + 4 * kk * (size_t)s.dim);
+  w.g = off; off = align256(off + 4 * kk * (size_t)s.ffn_dim);
+  w.u = off; off = align256(off + 4 * kk * (size_t)s.ffn_dim);
+  w.a = off; off = align256(off + 4 * kk * (size_t)s.ffn_dim);
+  w.part_stride = (attn_part_floats(s.n_q_heads, s.max_ctx) + 63) & ~(size_t)63;
+  w.part = off; off = align256(off + 4 * kk * w.part_stride);
   w.total = off;
   return w;
 }
@@ -233,6 +261,71 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     TimedLaunch tl(NT_K_FFN_DOWN, st);
     if ((e = gemv_launch(1 << w.fmt[NT_W_DOWN], EPI_RESID, p, gemv_groups(p, s.dim), a, st)) != hipSuccess)
       return hip_fail(e, "down launch");
+  }
+  return NT_OK;
+}
+
+// Enqueue one decode layer for k tokens at positions pos .. pos + k - 1 (arguments already
+// checked): h [k][dim] in/out.  The GEMMs read each weight once for all k tokens; the residual
+// adds are the GEMMs accumulating into h; token t attends over slots [0, pos + t].
+int run_layer_k(const nt_layer_weights& w, const nt_layer_shape& s, int pos, int k, float* h, uint16_t* kc,
+                uint16_t* vc, uint8_t* ws, hipStream_t st) {
+  const LayerKWs L = layer_k_ws(s, k);
+  float* xn = reinterpret_cast<float*>(ws + L.xn);
+  float* q = reinterpret_cast<float*>(ws + L.q);
+  float* kk = reinterpret_cast<float*>(ws + L.kk);
+  float* vv = reinterpret_cast<float*>(ws + L.vv);
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  float* h1 = reinterpret_cast<float*>(ws + L.h1);
+  float* g = reinterpret_cast<float*>(ws + L.g);
+  float* u = reinterpret_cast<float*>(ws + L.u);
+  float* a = reinterpret_cast<float*>(ws + L.a);
+  const int nq = s.n_q_heads * s.head_dim, nkv = s.n_kv_heads * s.head_dim;
+  auto W = [&](int i) { return reinterpret_cast<const uint8_t*>(w.w[i]); };
+  hipError_t e;
+  // a1: n1 = RMSNorm(h)
+  if ((e = rmsnorm_rows_launch(k, s.dim, h, w.attn_norm, s.eps, xn, nullptr, st)) != hipSuccess)
+    return hip_fail(e, "rmsnorm launch");
+  {  // a2: q, k, v for every token
+    TimedLaunch tl(NT_K_ATTN_IN, st);
+    if ((e = gemm_launch(w.fmt[NT_W_Q], W(NT_W_Q), nq, s.dim, k, xn, q, st)) != hipSuccess ||
+        (e = gemm_launch(w.fmt[NT_W_K], W(NT_W_K), nkv, s.dim, k, xn, kk, st)) != hipSuccess ||
+        (e = gemm_launch(w.fmt[NT_W_V], W(NT_W_V), nkv, s.dim, k, xn, vv, st)) != hipSuccess)
+      return hip_fail(e, "q/k/v gemm launch");
+  }
+  // a3: RoPE at pos + t, fp16 k and v into slot pos + t
+  if ((e = rope_append_launch(k, s.n_q_heads, s.n_kv_heads, pos, s.rope_theta, q, kk, vv, kc, vc, s.max_ctx, st)) !=
+      hipSuccess)
+    return hip_fail(e, "rope/append launch");
+  {  // a4: token t attends over slots [0, pos + t]
+    AttnArgs at;
+    at.q = q; at.k_cache = kc; at.v_cache = vc; at.out = o;
+    at.part = reinterpret_cast<float*>(ws + L.part);
+    at.n_kv = s.n_kv_heads; at.n_ctx = pos + 1; at.max_ctx = s.max_ctx;
+    at.n_tok = k; at.q_stride = nq; at.out_stride = nq; at.part_stride = (int64_t)L.part_stride;
+    at.n_split = attn_n_split(pos + k);
+    TimedLaunch tl(NT_K_ATTN, st);
+    if ((e = attn_launch(at, s.n_q_heads / s.n_kv_heads, st)) != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  {  // a5: h1 = h + Wo o
+    TimedLaunch tl(NT_K_O, st);
+    if ((e = gemm_launch(w.fmt[NT_W_O], W(NT_W_O), s.dim, nq, k, o, h, st, true)) != hipSuccess)
+      return hip_fail(e, "o gemm launch");
+  }
+  // a6: n2 = RMSNorm(h1), h1 kept in the workspace
+  if ((e = rmsnorm_rows_launch(k, s.dim, h, w.ffn_norm, s.eps, xn, h1, st)) != hipSuccess)
+    return hip_fail(e, "rmsnorm launch");
+  {  // a7, a8: a = SwiGLU(Wg n2, Wu n2)
+    TimedLaunch tl(NT_K_FFN_UP, st);
+    if ((e = gemm_launch(w.fmt[NT_W_GATE], W(NT_W_GATE), s.ffn_dim, s.dim, k, xn, g, st)) != hipSuccess ||
+        (e = gemm_launch(w.fmt[NT_W_UP], W(NT_W_UP), s.ffn_dim, s.dim, k, xn, u, st)) != hipSuccess ||
+        (e = swiglu_launch((int64_t)k * s.ffn_dim, g, u, a, st)) != hipSuccess)
+      return hip_fail(e, "gate/up launch");
+  }
+  {  // a9: h2 = h1 + Wd a
+    TimedLaunch tl(NT_K_FFN_DOWN, st);
+    if ((e = gemm_launch(w.fmt[NT_W_DOWN], W(NT_W_DOWN), s.dim, s.ffn_dim, k, a, h, st, true)) != hipSuccess)
+      return hip_fail(e, "down gemm launch");
   }
   return NT_OK;
 }
@@ -562,6 +655,7 @@ static int check_plan(const nt_model_plan* plan, const nt_streamer* st) {
     const nt_layer_entry& e = plan->layers[l];
     if (e.resident != NT_TIER_PINNED && e.resident != NT_TIER_RESIDENT && e.resident != NT_TIER_FILE)
       return fail(NT_EINVAL, "layer %d has an unknown tier %d", l, e.resident);
+    if (e.skip) continue;  // never read: its blob, caches and tier need nothing
     if (!e.k_cache || !e.v_cache) return fail(NT_EINVAL, "layer %d has a null cache pointer", l);
     if (e.resident != NT_TIER_RESIDENT && !st)
       return fail(NT_EINVAL, "layer %d is not resident and no streamer was given", l);
@@ -658,8 +752,13 @@ static int stream_issue(nt_streamer* st, const nt_model_plan* plan, const std::v
   return NT_OK;
 }
 
+// n_tok 0: the single-token layer (nt_decode_layer's launches); n_tok >= 1: the k-token layer.
 static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, uint8_t* ws,
-                              hipStream_t compute, hipStream_t copy, nt_stream_stats* stats) {
+                              hipStream_t compute, hipStream_t copy, nt_stream_stats* stats, int n_tok = 0) {
+  auto layer = [&](const nt_layer_weights& w, const nt_layer_entry& ent) {
+    return n_tok == 0 ? run_layer(w, plan->shape, pos, h, ent.k_cache, ent.v_cache, ws, compute)
+                      : run_layer_k(w, plan->shape, pos, n_tok, h, ent.k_cache, ent.v_cache, ws, compute);
+  };
   std::vector<int> streamed;  // the layers copied through the staging buffers, in order
   for (int l = 0; l < plan->n_layers; ++l)
     if (plan->layers[l].resident != NT_TIER_RESIDENT && !plan->layers[l].skip) streamed.push_back(l);
@@ -685,7 +784,7 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
     if (ent.skip) continue;
     if (ent.resident == NT_TIER_RESIDENT) {
       const nt_layer_weights w = weights_in_blob(reinterpret_cast<const uint8_t*>(ent.blob), plan->layout);
-      if ((rc = run_layer(w, plan->shape, pos, h, ent.k_cache, ent.v_cache, ws, compute))) return rc;
+      if ((rc = layer(w, ent))) return rc;
       continue;
     }
     const int64_t q = st->c_run;
@@ -695,7 +794,7 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
     hipError_t e;
     if ((e = hipStreamWaitEvent(compute, st->ready[b], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(compute)");
     const nt_layer_weights w = weights_in_blob(st->staging[b], plan->layout);
-    if ((rc = run_layer(w, plan->shape, pos, h, ent.k_cache, ent.v_cache, ws, compute))) return rc;
+    if ((rc = layer(w, ent))) return rc;
     if ((e = hipEventRecord(st->freed[b], compute)) != hipSuccess) return hip_fail(e, "hipEventRecord(freed)");
     st->freed_recorded[b] = true;
     st->c_run = q + 1;
@@ -771,6 +870,83 @@ int nt_lm_head(int fmt, int64_t n_vocab, int64_t dim, const void* output, const 
   if (ws_bytes < NT_LM_HEAD_WS_BYTES) return fail(NT_EINVAL, "workspace too small (%zu < %d)", ws_bytes, NT_LM_HEAD_WS_BYTES);
   return lm_head_enqueue(fmt, n_vocab, (int)dim, output, output_norm, eps, h, logits,
                          reinterpret_cast<unsigned long long*>(ws), token, true, (hipStream_t)stream);
+}
+
+size_t nt_decode_layer_k_ws_bytes(const nt_layer_shape* shp, int n_tok) {
+  if (!shp || shp->head_dim != 128 || shp->n_q_heads <= 0 || shp->n_kv_heads <= 0 || shp->max_ctx <= 0 ||
+      n_tok < 1 || n_tok > NT_GEMM_MAX_TOK)
+    return 0;
+  return layer_k_ws(*shp, n_tok).total;
+}
+
+int nt_decode_layer_k_ws_offsets(const nt_layer_shape* shp, int n_tok, int64_t* off) {
+  int rc = check_shape(shp);
+  if (rc) return rc;
+  if (n_tok < 1 || n_tok > NT_GEMM_MAX_TOK) return fail(NT_ESHAPE, "n_tok must be in [1, %d]", NT_GEMM_MAX_TOK);
+  if (!off) return fail(NT_EINVAL, "null pointer");
+  const LayerKWs L = layer_k_ws(*shp, n_tok);
+  off[0] = (int64_t)L.q; off[1] = (int64_t)L.o; off[2] = (int64_t)L.h1; off[3] = (int64_t)L.a;
+  return NT_OK;
+}
+
+int nt_decode_layer_k(const nt_layer_weights* w, const nt_layer_shape* shp, int pos, int n_tok, float* h,
+                      uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shp);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (n_tok < 1 || n_tok > NT_GEMM_MAX_TOK) return fail(NT_ESHAPE, "n_tok must be in [1, %d]", NT_GEMM_MAX_TOK);
+  if (pos < 0 || pos + n_tok > shp->max_ctx)
+    return fail(NT_ESHAPE, "positions %d .. %d outside [0, max_ctx)", pos, pos + n_tok - 1);
+  if (!h || !k_cache || !v_cache || !ws) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(h, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(ws, 256))
+    return fail(NT_EALIGN, "h and caches must be 16-byte aligned, ws 256-byte");
+  const size_t need = layer_k_ws(*shp, n_tok).total;
+  if (ws_bytes < need) return fail(NT_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, need);
+  return run_layer_k(*w, *shp, pos, n_tok, h, k_cache, v_cache, reinterpret_cast<uint8_t*>(ws), (hipStream_t)stream);
+}
+
+size_t nt_verify_tokens_ws_bytes(const nt_layer_shape* shp, int n_tok) { return nt_decode_layer_k_ws_bytes(shp, n_tok); }
+
+int nt_verify_tokens(nt_streamer* st, const nt_model_plan* plan, const nt_model_head* head, int pos, int n_tok,
+                     const int32_t* tokens, int32_t* next, float* logits, float* h, void* ws, size_t ws_bytes,
+                     void* compute, void* copy, nt_stream_stats* stats) {
+  if (stats) stats->layers_streamed = stats->h2d_bytes = 0;
+  int rc = check_plan(plan, st);
+  if (rc) return rc;
+  if (n_tok < 1 || n_tok > NT_GEMM_MAX_TOK) return fail(NT_ESHAPE, "n_tok must be in [1, %d]", NT_GEMM_MAX_TOK);
+  if (!head || !head->token_embd || !head->output_norm || !head->output || !tokens || !next || !logits || !h || !ws)
+    return fail(NT_EINVAL, "null pointer");
+  if (!fmt_ok(head->embd_fmt) || !fmt_ok(head->out_fmt)) return fail(NT_EFORMAT, "unknown head format");
+  if (head->n_vocab <= 0 || head->n_vocab > NT_MAX_ROWS) return fail(NT_ESHAPE, "vocabulary size must be in [1, 2^30]");
+  if (!aligned(head->output, 16) || !aligned(head->token_embd, 4) || !aligned(head->output_norm, 16) || !aligned(h, 16) ||
+      !aligned(logits, 4) || !aligned(ws, 256))
+    return fail(NT_EALIGN, "misaligned head, h, logits or ws pointer");
+  if (pos < 0 || pos + n_tok > plan->shape.max_ctx)
+    return fail(NT_ESHAPE, "positions %d .. %d outside [0, max_ctx)", pos, pos + n_tok - 1);
+  const LayerKWs L = layer_k_ws(plan->shape, n_tok);
+  if (ws_bytes < L.total) return fail(NT_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, L.total);
+  if (st) {
+    if ((size_t)plan->layout.blob_bytes > st->bytes) return fail(NT_EINVAL, "layer blob larger than the staging buffers");
+    if (compute == copy) return fail(NT_EINVAL, "compute and copy streams must differ");
+  }
+  hipStream_t cs = (hipStream_t)compute;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  const int dim = plan->shape.dim;
+  hipError_t e;
+  if ((e = embed_launch(head->embd_fmt, head->n_vocab, dim, head->token_embd, tokens, h, nullptr, cs, n_tok)) != hipSuccess)
+    return hip_fail(e, "embed launch");
+  if ((rc = stream_layers_impl(st, plan, pos, h, wsb, cs, (hipStream_t)copy, stats, n_tok))) return rc;
+  float* xn = reinterpret_cast<float*>(wsb + L.xn);
+  if ((e = rmsnorm_rows_launch(n_tok, dim, h, head->output_norm, plan->shape.eps, xn, nullptr, cs)) != hipSuccess)
+    return hip_fail(e, "rmsnorm launch");
+  {
+    TimedLaunch tl(NT_K_LM_HEAD, cs);
+    if ((e = gemm_launch(head->out_fmt, reinterpret_cast<const uint8_t*>(head->output), head->n_vocab, dim, n_tok, xn,
+                         logits, cs)) != hipSuccess)
+      return hip_fail(e, "lm head gemm launch");
+  }
+  if ((e = argmax_launch(head->n_vocab, logits, next, cs, n_tok)) != hipSuccess) return hip_fail(e, "argmax launch");
+  return NT_OK;
 }
 
 int nt_timing_begin(int kclass, int max_launches) {

@@ -62,10 +62,13 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
   __shared__ float ol[AW][NB][16][OPAD];
   __shared__ float wml[AW][NB * 8][2];
 
-  const int split = blockIdx.x, g = blockIdx.y;
+  const int split = blockIdx.x, g = blockIdx.y, tok = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, qd = lane >> 4;
-  const int n_ctx = a.n_ctx;
+  const int n_ctx = a.n_ctx + tok;
+  const int n_split = (n_ctx + SWG - 1) / SWG;  // this token's splits
+  if (split >= n_split) return;                  // the whole workgroup, before any barrier
+  const float* qtok = a.q + (size_t)tok * a.q_stride;
   const int t0 = split * SWG + wave * SW;  // first slot of this wave
   const bool active = t0 < n_ctx;          // wave-uniform
 
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {  // unconditional (a wave past the group rereads its last head)
     const int hh = min(wave + AW * k, G - 1);
-    qv[k] = *reinterpret_cast<const float2*>(a.q + (size_t)(g * G + hh) * HD + 2 * lane);
+    qv[k] = *reinterpret_cast<const float2*>(qtok + (size_t)(g * G + hh) * HD + 2 * lane);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the cache loads
   // Unconditional, with slots clamped into [0, n_ctx): a branch here would make the
@@ -225,10 +228,10 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
       }
     }
     v *= 1.f / PSCALE;
-    if (a.n_split == 1) {
-      a.out[(size_t)(g * G + h) * HD + d] = v / L;
+    if (n_split == 1) {
+      a.out[(size_t)tok * a.out_stride + (size_t)(g * G + h) * HD + d] = v / L;
     } else {
-      float* po = a.part + (((size_t)g * a.n_split + split) * G + h) * (HD + 2);
+      float* po = a.part + (size_t)tok * a.part_stride + (((size_t)g * n_split + split) * G + h) * (HD + 2);
       po[d] = v;
       if (d == 0) {
         po[HD] = M;
@@ -247,11 +250,12 @@ __global__ __launch_bounds__(CWV * 64) void attn_combine_kernel(const AttnArgs a
   extern __shared__ float cm[];  // [n_split] maxima, then [n_split] sums
   __shared__ float red[CWV][HD];
   __shared__ float wred[CWV][2];
-  const int hq = blockIdx.x;
+  const int hq = blockIdx.x, tok = blockIdx.y;
   const int g = hq / G, hg = hq % G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ns = a.n_split;
-  const float* gp = a.part + ((size_t)g * ns * G + hg) * (HD + 2);
+  const int ns = (a.n_ctx + tok + SWG - 1) / SWG;  // this token's splits
+  if (ns == 1) return;  // the partial kernel wrote this token's output itself
+  const float* gp = a.part + (size_t)tok * a.part_stride + ((size_t)g * ns * G + hg) * (HD + 2);
   const size_t ss = (size_t)G * (HD + 2);
 
   float2 ov[CK];
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(CWV * 64) void attn_combine_kernel(const AttnArgs a
       L += wred[w][1];
       v += red[w][threadIdx.x];
     }
-    a.out[(size_t)hq * HD + threadIdx.x] = v / L;
+    a.out[(size_t)tok * a.out_stride + (size_t)hq * HD + threadIdx.x] = v / L;
   }
 }
 
@@ -320,15 +324,21 @@ size_t attn_part_floats(int n_q, int max_ctx) {
 
 template <int G>
 static hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_partial_kernel<G>, dim3(a.n_split, a.n_kv), dim3(AW * 64), 0, s, a);
+  hipLaunchKernelGGL(attn_partial_kernel<G>, dim3(a.n_split, a.n_kv, a.n_tok), dim3(AW * 64), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3(a.n_kv * G), dim3(CWV * 64), 2 * sizeof(float) * a.n_split, s, a);
+  if (e != hipSuccess || a.n_split == 1) return e;  // then every token has one split
+  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3(a.n_kv * G, a.n_tok), dim3(CWV * 64), 2 * sizeof(float) * a.n_split,
+                     s, a);
   return hipGetLastError();
 }
 
 hipError_t attn_launch(const AttnArgs& a, int group, hipStream_t s) {
-  if (a.n_split != attn_n_split(a.n_ctx) || a.n_split > attn_max_split() || a.max_ctx % 8) return hipErrorInvalidValue;
+  if (a.n_tok < 1 || a.n_split != attn_n_split(a.n_ctx + a.n_tok - 1) || a.n_split > attn_max_split() ||
+      a.max_ctx % 8 || a.n_ctx + a.n_tok - 1 > a.max_ctx)
+    return hipErrorInvalidValue;
+  if (a.n_tok > 1 && (a.q_stride < (int64_t)a.n_kv * group * HD || a.out_stride < (int64_t)a.n_kv * group * HD ||
+                      a.part_stride < (int64_t)attn_part_floats(a.n_kv * group, a.n_ctx + a.n_tok - 1)))
+    return hipErrorInvalidValue;
   switch (group) {
     case 1: return launch_g<1>(a, s);
     case 2: return launch_g<2>(a, s);

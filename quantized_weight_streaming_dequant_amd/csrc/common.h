@@ -92,6 +92,17 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
 }
 
+// cos and sin of the RoPE angle of pair i of a head of head_dim values at position pos: the
+// angle pos * theta^(-2i/head_dim) is formed and reduced to [-pi, pi] in fp64, then rounded.
+__device__ __forceinline__ float2 rope_cs(double theta, int pos, int i, int head_dim) {
+  const double f = pow(theta, -2.0 * (double)i / (double)head_dim);
+  double ang = (double)pos * f;
+  ang -= 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
+  float sn, cs;
+  sincosf((float)ang, &sn, &cs);
+  return make_float2(cs, sn);
+}
+
 // Activation vector layout in LDS: 4 pad floats after every 64 columns and 4 more after
 // every 512, so that lanes reading runs 64 columns apart (Q8_0, Q4_0, Q4_K slices) and
 // runs 512 columns apart (Q6_K slices of alternate superblocks) with 128-bit reads

@@ -58,8 +58,9 @@ hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups
 // k-token GEMM: y[t][r] = sum_c W[r][c] x[t][c] for t < n_tok (1..GEMM_MAX_TOK), x [n_tok][cols],
 // y [n_tok][rows], all device fp32; one launch per column chunk (the weights are read once).
 constexpr int GEMM_MAX_TOK = 8;
+// accum: add W X into y (the residual add of a decode layer) instead of overwriting it.
 hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int n_tok, const float* x, float* y,
-                       hipStream_t s);
+                       hipStream_t s, bool accum = false);
 // Columns per launch for n_tok tokens (a multiple of the block size); exposed for the tests.
 int gemm_chunk_cols(int n_tok, int cols, int block_elems);
 

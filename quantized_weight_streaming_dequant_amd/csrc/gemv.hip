@@ -762,17 +762,6 @@ __device__ __forceinline__ unsigned long long logit_key(float v, int r) {
   return ((unsigned long long)order_key(v) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)r);
 }
 
-// cos and sin of the RoPE angle of pair i (0..63) of a 128-wide head at position pos: the
-// angle pos * theta^(-2i/128) is formed and reduced to [-pi, pi] in fp64, then rounded.
-__device__ __forceinline__ float2 rope_cs(double theta, int pos, int i) {
-  const double f = pow(theta, -2.0 * (double)i / 128.0);
-  double ang = (double)pos * f;
-  ang -= 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
-  float sn, cs;
-  sincosf((float)ang, &sn, &cs);
-  return make_float2(cs, sn);
-}
-
 template <int R, int EPI>
 __device__ __forceinline__ void epilogue(const GemvArgs& a, int s, const GemvSeg& sg, int row0, int lane,
                                          const float* acc, unsigned long long& best, const float2* rope) {
@@ -981,7 +970,7 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   // RoPE table for this position (visible after the barrier inside the staging of x)
   __shared__ float2 rope[64];
   if constexpr (EPI == EPI_QKV) {
-    if (threadIdx.x < 64) rope[threadIdx.x] = rope_cs(a.rope_theta, a.pos, threadIdx.x);
+    if (threadIdx.x < 64) rope[threadIdx.x] = rope_cs(a.rope_theta, a.pos, threadIdx.x, 128);
   }
   // x is loaded first (its loads then complete before the weights'); the first segment
   // stages it after issuing its first weight loads
@@ -1803,7 +1792,7 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
   __shared__ float2 rope[64];
   __shared__ unsigned long long wbest[ST_MAX_WAVES];
   if constexpr (EPI == EPI_QKV) {
-    if (threadIdx.x < 64) rope[threadIdx.x] = rope_cs(a.rope_theta, a.pos, threadIdx.x);
+    if (threadIdx.x < 64) rope[threadIdx.x] = rope_cs(a.rope_theta, a.pos, threadIdx.x, 128);
   }
   const int t0 = (int)blockIdx.x * sa.tpw, t1 = min(sa.tasks, t0 + sa.tpw);
   // The waves of a slice share its tasks: each starts with D fixed ones (t0 + sub + d rsub)
@@ -2268,7 +2257,7 @@ int gemm_chunk_cols(int n_tok, int cols, int be) {
 }
 
 hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int n_tok, const float* x, float* y,
-                       hipStream_t s) {
+                       hipStream_t s, bool accum) {
   const int be = block_elems(fmt), bb = block_bytes(fmt);
   const bool mm = gemm_use_mfma(fmt, n_tok);
   const int chunk = mm ? gemm_mfma_chunk_cols(fmt, n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, be);
@@ -2284,7 +2273,7 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
     a.cols = (int)(cols - c0 < chunk ? cols - c0 : chunk);
     a.w = w + (c0 / be) * bb;
     a.x = x + c0;
-    a.accum = c0 > 0;
+    a.accum = accum || c0 > 0;
     hipError_t e;
     if (mm) {
       // superblocks per wave and tile: the chunk's superblocks over the workgroup's waves

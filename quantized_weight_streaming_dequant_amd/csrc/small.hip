@@ -94,8 +94,10 @@ hipError_t dequant_launch(int fmt, int64_t rows, int64_t cols, const void* block
 __global__ void embed_kernel(int fmt, int64_t n_vocab, int64_t dim, const uint8_t* __restrict__ table,
                              const int32_t* __restrict__ token, float* __restrict__ h,
                              unsigned long long* __restrict__ amax_reset) {
-  const int tok = *token;
-  if (amax_reset && blockIdx.x == 0 && threadIdx.x == 0) *amax_reset = 0ull;
+  // row blockIdx.y of a batch of tokens
+  const int tok = token[blockIdx.y];
+  h += (int64_t)blockIdx.y * dim;
+  if (amax_reset && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *amax_reset = 0ull;
   const int be = block_elems(fmt), bb = block_bytes(fmt);
   const int64_t ngroups = dim / 32;
   for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < ngroups; gi += (int64_t)gridDim.x * blockDim.x) {
@@ -112,10 +114,10 @@ __global__ void embed_kernel(int fmt, int64_t n_vocab, int64_t dim, const uint8_
 }
 
 hipError_t embed_launch(int fmt, int64_t n_vocab, int64_t dim, const void* table, const int32_t* token, float* h,
-                        unsigned long long* amax_reset, hipStream_t s) {
+                        unsigned long long* amax_reset, hipStream_t s, int n_tok) {
   const int64_t ng = dim / 32;
   const int grid = (int)((ng + 63) / 64);
-  hipLaunchKernelGGL(embed_kernel, dim3(grid), dim3(64), 0, s, fmt, n_vocab, dim,
+  hipLaunchKernelGGL(embed_kernel, dim3(grid, n_tok), dim3(64), 0, s, fmt, n_vocab, dim,
                      reinterpret_cast<const uint8_t*>(table), token, h, amax_reset);
   return hipGetLastError();
 }
@@ -146,11 +148,8 @@ __global__ void rope_kernel(int n_heads, int head_dim, int pos, double theta, fl
   const int npairs = n_heads * (head_dim / 2);
   for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < npairs; p += gridDim.x * blockDim.x) {
     const int head = p / (head_dim / 2), i = p % (head_dim / 2);
-    const double f = pow(theta, -2.0 * (double)i / (double)head_dim);
-    double ang = (double)pos * f;
-    ang -= 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
-    float sn, cs;
-    sincosf((float)ang, &sn, &cs);
+    const float2 c = rope_cs(theta, pos, i, head_dim);
+    const float cs = c.x, sn = c.y;
     float* v = qk + (int64_t)head * head_dim + 2 * i;
     const float x0 = v[0], x1 = v[1];
     v[0] = x0 * cs - x1 * sn;
@@ -186,6 +185,9 @@ __device__ __forceinline__ uint32_t okey(float v) {
 
 __global__ __launch_bounds__(1024) void argmax_kernel(int64_t n, const float* __restrict__ v, int32_t* out) {
   __shared__ unsigned long long red[16];
+  // row blockIdx.x of a batch of rows of n
+  v += (int64_t)blockIdx.x * n;
+  out += blockIdx.x;
   unsigned long long best = 0;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
     const float x = v[i] != v[i] ? -INFINITY : v[i];
@@ -206,8 +208,8 @@ __global__ __launch_bounds__(1024) void argmax_kernel(int64_t n, const float* __
   }
 }
 
-hipError_t argmax_launch(int64_t n, const float* v, int32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_kernel, dim3(1), dim3(1024), 0, s, n, v, out);
+hipError_t argmax_launch(int64_t n, const float* v, int32_t* out, hipStream_t s, int n_rows) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(n_rows), dim3(1024), 0, s, n, v, out);
   return hipGetLastError();
 }
 

@@ -175,6 +175,24 @@ def test_ffn_up_checks(shape_kw, wfix, code):
     assert ei.value.code == code
 
 
+def test_layer_k_checks():
+    shp = _shape()
+    w = _weights()
+    for pos, k, code in ((0, 0, nt.NT_ESHAPE), (0, nt.GEMM_MAX_TOK + 1, nt.NT_ESHAPE), (1020, 5, nt.NT_ESHAPE),
+                         (-1, 2, nt.NT_ESHAPE)):
+        with pytest.raises(nt.NtError) as ei:
+            nt.nt_decode_layer_k(w, shp, pos, k, 4096, 4096, 4096, 4096, 1 << 30)
+        assert ei.value.code == code, (pos, k)
+    with pytest.raises(nt.NtError) as ei:
+        nt.nt_decode_layer_k(w, shp, 0, 4, 4096, 4096, 4096, 4096, 1024)
+    assert ei.value.code == nt.NT_EINVAL  # workspace too small
+    assert nt.nt_decode_layer_k_ws_bytes(shp, 0) == 0 and nt.nt_decode_layer_k_ws_bytes(shp, 9) == 0
+    # the k-token workspace holds k rows of every stage and k tokens' attention partials
+    assert nt.nt_decode_layer_k_ws_bytes(shp, 8) > 8 * 4 * (4096 + 14336)
+    off = nt.nt_decode_layer_k_ws_offsets(shp, 4)
+    assert all(v % 256 == 0 for v in off.values())
+
+
 def test_workspace_sizes_and_offsets():
     shp = _shape()
     ws = nt.nt_decode_layer_ws_bytes(shp)
