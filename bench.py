@@ -12,7 +12,9 @@ runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B
 shapes in Q4_K, Q6_K and Q5_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
 host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes, 7 = the 70B model with
 cosine-based layer skip (--skip layers, default 20 of 80), 8 = 70B Q6_K layers read from a file
-(--file-layers, default 8) through page-locked bounce buffers.
+(--file-layers, default 8) through page-locked bounce buffers, 9 = the self-speculative
+verification pass (k-token layer and whole-model verify at k = 2, 4, 8) at the 70B shape, 10 =
+self-speculative decoding over the streamed 70B Q6_K model (resident layers draft, --spec-k).
 """
 from __future__ import annotations
 
@@ -41,7 +43,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+    p.add_argument("--spec-k", type=int, default=4, help="tokens per verify pass in --config 10")
     p.add_argument("--skip", type=int, default=20, help="layers to skip in --config 7")
     p.add_argument("--file-layers", type=int, default=8, help="layers read from a file in --config 8")
     p.add_argument("--read-threads", type=int, default=8, help="reader threads per blob in --config 8")
@@ -835,6 +838,171 @@ def bench_file_tier_70b(args, torch, nt, tg):
     }
 
 
+def bench_verify_70b(args, torch, nt, tg):
+    """The verification pass of self-speculative decoding at the 70B Q4_K_M shape, all layers
+    resident: one decode layer for k = 1, 2, 4, 8 tokens at once (nt_decode_layer_k) against
+    the single-token layer (nt_decode_layer), each over the 80 layers' weights in turn (HIP
+    events around the batch), and the whole-model verify pass (nt_verify_tokens) against k
+    single-token steps (nt_decode_token).  value = token positions per second of the k = 4
+    verify pass."""
+    from synth import recipes
+    steps = args.steps if args.steps is not None else 3
+    warmup = args.warmup if args.warmup is not None else 1
+    mix = recipes.MIX_Q4_K_M
+    n_layers = args.layers
+    m = Model70B(torch, nt, tg, mix, n_layers, range(n_layers))
+    shp = tg.layer_shape(m.shape)
+    cs = torch.cuda.current_stream().cuda_stream
+    lw = [m.layer_weights(l) for l in range(n_layers)]
+    D = m.shape.dim
+    pos = 4096
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(run):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(steps):
+            run()
+        ev1.record()
+        ev1.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / steps
+
+    layers = {}
+    ws1 = torch.zeros(nt.nt_decode_layer_ws_bytes(shp), dtype=torch.uint8, device="cuda")
+    h1 = torch.from_numpy(recipes.hidden_input(D)).cuda()
+    us = timed(lambda: [nt.nt_decode_layer(lw[l], shp, pos, h1.data_ptr(), m.kc[l].data_ptr(), m.vc[l].data_ptr(),
+                                           ws1.data_ptr(), ws1.numel(), cs) for l in range(n_layers)])
+    t1 = us / n_layers
+    layers["single"] = {"us_per_layer": t1}
+    for k in (1, 2, 4, 8):
+        wsk = torch.zeros(nt.nt_decode_layer_k_ws_bytes(shp, k), dtype=torch.uint8, device="cuda")
+        hk = torch.from_numpy(np.tile(recipes.hidden_input(D), k)).cuda()
+        us = timed(lambda: [nt.nt_decode_layer_k(lw[l], shp, pos, k, hk.data_ptr(), m.kc[l].data_ptr(),
+                                                 m.vc[l].data_ptr(), wsk.data_ptr(), wsk.numel(), cs)
+                            for l in range(n_layers)])
+        layers[f"k{k}"] = {"us_per_layer": us / n_layers, "vs_k_single_layers": (us / n_layers) / (k * t1)}
+        log(f"  layer x{k}: {us / n_layers:.1f} us ({(us / n_layers) / (k * t1):.2f} of {k} single-token layers)")
+        del wsk
+    plan, keep = m.plan()
+    head = m.head()
+    passes = {}
+    wst = torch.zeros(nt.nt_decode_token_ws_bytes(shp), dtype=torch.uint8, device="cuda")
+    h = torch.zeros(D, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(m.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.full((1,), m.first_token, dtype=torch.int32, device="cuda")
+    t_tok = timed(lambda: nt.nt_decode_token(None, plan, head, pos, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                                             wst.data_ptr(), wst.numel(), cs, cs, None))
+    passes["single_token_step_us"] = t_tok
+    for k in (2, 4, 8):
+        wsv = torch.zeros(nt.nt_verify_tokens_ws_bytes(shp, k), dtype=torch.uint8, device="cuda")
+        hv = torch.zeros(k * D, dtype=torch.float32, device="cuda")
+        lv = torch.zeros(k * m.vocab, dtype=torch.float32, device="cuda")
+        tin = torch.full((k,), m.first_token, dtype=torch.int32, device="cuda")
+        nxt = torch.zeros(k, dtype=torch.int32, device="cuda")
+        us = timed(lambda: nt.nt_verify_tokens(None, plan, head, pos, k, tin.data_ptr(), nxt.data_ptr(), lv.data_ptr(),
+                                               hv.data_ptr(), wsv.data_ptr(), wsv.numel(), cs, cs, None))
+        passes[f"verify_k{k}_us"] = us
+        passes[f"verify_k{k}_vs_k_steps"] = us / (k * t_tok)
+        log(f"  verify pass x{k}: {us / 1e3:.2f} ms ({us / (k * t_tok):.2f} of {k} single-token steps)")
+        del wsv, hv, lv
+    v4 = 4 / (passes["verify_k4_us"] * 1e-6)
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": v4, "unit": "token positions/s (k = 4 verify pass)", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": passes["verify_k4_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8 x i8 -> i32 dots (integer MFMA for Q4_K/Q6_K at k >= 3), f32 scales and activations, f16 kv",
+        "data": "synthetic",
+        "config": {"workload": "llama3.1-70b-shape Q4_K_M resident, self-speculative verification pass at pos 4096",
+                   "layers": n_layers},
+        "layers": layers, "passes": passes,
+    }
+
+
+def bench_speculative_stream_70b(args, torch, nt, tg):
+    """Self-speculative decoding over the streamed 70B Q6_K model (26 layers resident, 54 streamed
+    from pinned host memory): the resident layers draft k - 1 tokens (the streamed ones skipped,
+    nothing copied), then the whole model verifies the current token and the drafts in one pass,
+    each streamed layer copied once for all k tokens.  value = emitted tokens/s.  With random
+    weights the drafts agree with the full model (later layers barely turn the hidden state), so
+    the acceptance here measures the mechanism, not a real draft model's quality."""
+    from synth import recipes
+    k = args.spec_k
+    n_out = args.steps if args.steps is not None else 32
+    mix = recipes.MIX_Q6_K
+    n_layers = args.layers
+    n_res = min(26, n_layers)
+    m = Model70B(torch, nt, tg, mix, n_layers, range(n_res))
+    streamed = set(range(n_res, n_layers))
+    full, keep_f = m.plan()
+    draft, keep_d = m.plan(skip=streamed)
+    head = m.head()
+    shp = tg.layer_shape(m.shape)
+    D = m.shape.dim
+    wst = torch.zeros(nt.nt_decode_token_ws_bytes(shp), dtype=torch.uint8, device="cuda")
+    h = torch.zeros(D, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(m.vocab, dtype=torch.float32, device="cuda")
+    dt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wsv = torch.zeros(nt.nt_verify_tokens_ws_bytes(shp, k), dtype=torch.uint8, device="cuda")
+    hv = torch.zeros(k * D, dtype=torch.float32, device="cuda")
+    lv = torch.zeros(k * m.vocab, dtype=torch.float32, device="cuda")
+    tin = torch.zeros(k, dtype=torch.int32, device="cuda")
+    nxt = torch.zeros(k, dtype=torch.int32, device="cuda")
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), m.lay.nbytes)
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    stats = nt.StreamStats()
+
+    def run(n_emit, pos0):
+        out, acc, h2d = [], [], 0
+        cur, pos = m.first_token, pos0
+        while len(out) < n_emit:
+            dt.fill_(cur)
+            drafts = []
+            for i in range(k - 1):
+                nt.nt_decode_token(None, draft, head, pos + i, dt.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                                   wst.data_ptr(), wst.numel(), compute.cuda_stream, copy.cuda_stream, None)
+                drafts.append(int(dt.item()))
+            tin.copy_(torch.tensor([cur] + drafts, dtype=torch.int32))
+            nt.nt_verify_tokens(st, full, head, pos, k, tin.data_ptr(), nxt.data_ptr(), lv.data_ptr(), hv.data_ptr(),
+                                wsv.data_ptr(), wsv.numel(), compute.cuda_stream, copy.cuda_stream, stats)
+            h2d += stats.h2d_bytes
+            v = nxt.tolist()
+            n = 0
+            while n < k - 1 and drafts[n] == v[n]:
+                n += 1
+            out += v[:n + 1]
+            acc.append(n)
+            cur, pos = v[n], pos + n + 1
+        return out, acc, h2d
+
+    try:
+        run(k, 4096)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out, acc, h2d = run(n_out, 4096)
+        torch.cuda.synchronize()
+        dt_s = time.perf_counter() - t0
+    finally:
+        torch.cuda.synchronize()
+        nt.nt_stream_destroy(st)
+    return {
+        "metric": "quant-GEMV HBM GB/s (% of peak); decode tokens/s at 8B and 70B shapes",
+        "value": len(out) / dt_s, "unit": "tok/s (emitted)", "n_gpus": 1, "steps": len(out), "warmup": k,
+        "ms_per_step": dt_s / len(out) * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8 x i8 -> i32 dots (integer MFMA for Q6_K at k >= 3), f32 scales and activations, f16 kv",
+        "data": "synthetic (random weights: draft acceptance is an artifact of them)",
+        "config": {"workload": f"llama3.1-70b-shape Q6_K, 26 layers resident (the draft model), 54 streamed, "
+                               f"self-speculative decoding with k = {k}", "layers": n_layers},
+        "verify_passes": len(acc), "accepted_drafts_per_pass": float(np.mean(acc)), "h2d_GBps": h2d / dt_s / 1e9,
+        "s_per_pass": dt_s / len(acc),
+        "full_acceptance_bound_tok_s": k / (dt_s / len(acc)),  # k tokens per pass if every draft were accepted
+        "h2d_bytes_per_emitted_token": h2d / len(out),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -863,6 +1031,10 @@ def main():
         res = bench_layer_skip_70b(args, torch, nt, tg)
     elif args.config == 8:
         res = bench_file_tier_70b(args, torch, nt, tg)
+    elif args.config == 9:
+        res = bench_verify_70b(args, torch, nt, tg)
+    elif args.config == 10:
+        res = bench_speculative_stream_70b(args, torch, nt, tg)
     else:
         res = bench_stream_70b(args, torch, nt, tg)
     print(json.dumps(res), flush=True)

@@ -201,7 +201,8 @@ size_t nt_decode_layer_ws_bytes(const nt_layer_shape* shp);
  * the call it holds, as fp32 [n_tok][...] arrays at the offsets nt_decode_layer_k_ws_offsets
  * gives (q, o, h1, a), each token's rotated query, attention output, h1 and SwiGLU output.
  * Accuracy per token as nt_decode_layer; the results are those of n_tok sequential
- * nt_decode_layer calls up to rounding.  Other constraints and errors as nt_decode_layer. */
+ * nt_decode_layer calls up to rounding (n_tok = 1 runs nt_decode_layer's own launches, bit for
+ * bit).  Other constraints and errors as nt_decode_layer. */
 int nt_decode_layer_k(const nt_layer_weights* w, const nt_layer_shape* shp, int pos, int n_tok, float* h,
                       uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes, void* stream);
 size_t nt_decode_layer_k_ws_bytes(const nt_layer_shape* shp, int n_tok);  /* 0 for a bad shape or n_tok */

@@ -268,8 +268,13 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
 // Enqueue one decode layer for k tokens at positions pos .. pos + k - 1 (arguments already
 // checked): h [k][dim] in/out.  The GEMMs read each weight once for all k tokens; the residual
 // adds are the GEMMs accumulating into h; token t attends over slots [0, pos + t].
+int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float* h, uint16_t* kc, uint16_t* vc,
+              uint8_t* ws, hipStream_t st);
+
 int run_layer_k(const nt_layer_weights& w, const nt_layer_shape& s, int pos, int k, float* h, uint16_t* kc,
                 uint16_t* vc, uint8_t* ws, hipStream_t st) {
+  // one token: the single-token layer's fused launches (its workspace layout fits in this one)
+  if (k == 1) return run_layer(w, s, pos, h, kc, vc, ws, st);
   const LayerKWs L = layer_k_ws(s, k);
   float* xn = reinterpret_cast<float*>(ws + L.xn);
   float* q = reinterpret_cast<float*>(ws + L.q);
@@ -884,6 +889,11 @@ int nt_decode_layer_k_ws_offsets(const nt_layer_shape* shp, int n_tok, int64_t* 
   if (rc) return rc;
   if (n_tok < 1 || n_tok > NT_GEMM_MAX_TOK) return fail(NT_ESHAPE, "n_tok must be in [1, %d]", NT_GEMM_MAX_TOK);
   if (!off) return fail(NT_EINVAL, "null pointer");
+  if (n_tok == 1) {  // the single-token layer's workspace layout
+    const LayerWs L1 = layer_ws(*shp);
+    off[0] = (int64_t)L1.q; off[1] = (int64_t)L1.o; off[2] = (int64_t)L1.h1; off[3] = (int64_t)L1.a;
+    return NT_OK;
+  }
   const LayerKWs L = layer_k_ws(*shp, n_tok);
   off[0] = (int64_t)L.q; off[1] = (int64_t)L.o; off[2] = (int64_t)L.h1; off[3] = (int64_t)L.a;
   return NT_OK;
@@ -935,7 +945,11 @@ int nt_verify_tokens(nt_streamer* st, const nt_model_plan* plan, const nt_model_
   hipError_t e;
   if ((e = embed_launch(head->embd_fmt, head->n_vocab, dim, head->token_embd, tokens, h, nullptr, cs, n_tok)) != hipSuccess)
     return hip_fail(e, "embed launch");
-  if ((rc = stream_layers_impl(st, plan, pos, h, wsb, cs, (hipStream_t)copy, stats, n_tok))) return rc;
+  if ((rc = stream_layers_impl(st, plan, pos, h, wsb, cs, (hipStream_t)copy, stats, n_tok == 1 ? 0 : n_tok))) return rc;
+  if (n_tok == 1)  // the single-token head: RMSNorm prologue, GEMV and fused argmax in one launch
+    return lm_head_enqueue(head->out_fmt, head->n_vocab, dim, head->output, head->output_norm, plan->shape.eps, h,
+                           logits, reinterpret_cast<unsigned long long*>(wsb + layer_ws(plan->shape).key), next, true,
+                           cs);
   float* xn = reinterpret_cast<float*>(wsb + L.xn);
   if ((e = rmsnorm_rows_launch(n_tok, dim, h, head->output_norm, plan->shape.eps, xn, nullptr, cs)) != hipSuccess)
     return hip_fail(e, "rmsnorm launch");

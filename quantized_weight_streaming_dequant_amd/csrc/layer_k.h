@@ -8,7 +8,7 @@
 namespace nt {
 
 // y[t] = gain * x[t] / sqrt(mean(x[t]^2) + eps) for rows t < n_rows of n floats (x and y
-// [n_rows][n]); copy (nullable) also gets x[t].
+// [n_rows][n], 16-byte aligned; n a multiple of 4 up to 32768); copy (nullable) also gets x[t].
 hipError_t rmsnorm_rows_launch(int n_rows, int n, const float* x, const float* gain, float eps, float* y, float* copy,
                                hipStream_t s);
 

@@ -8,29 +8,52 @@
 
 namespace nt {
 
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int n, const float* __restrict__ x,
-                                                           const float* __restrict__ g, float eps, float* __restrict__ y,
-                                                           float* __restrict__ copy) {
-  __shared__ float red[4];
+// one workgroup of 1024 threads per row: each thread holds up to RN_V float4 of its row in
+// registers, so x is read once, with all of a thread's loads in flight together
+constexpr int RN_T = 1024;
+constexpr int RN_V = 8;  // rows up to RN_T * RN_V * 4 = 32768 floats
+
+__global__ __launch_bounds__(RN_T) void rmsnorm_rows_kernel(int n, const float* __restrict__ x,
+                                                            const float* __restrict__ g, float eps,
+                                                            float* __restrict__ y, float* __restrict__ copy) {
+  __shared__ float red[RN_T / 64];
   const size_t row = (size_t)blockIdx.x * n;
-  const float* xr = x + row;
+  const float4* xr = reinterpret_cast<const float4*>(x + row);
+  const int n4 = n >> 2;
+  float4 v[RN_V];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ss += xr[i] * xr[i];
+#pragma unroll
+  for (int j = 0; j < RN_V; ++j) {
+    const int i = (int)threadIdx.x + j * RN_T;
+    v[j] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int j = 0; j < RN_V; ++j) ss += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < RN_T / 64; ++w) tot += red[w];
   const float scale = 1.0f / sqrtf(tot / (float)n + eps);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const float v = xr[i];
-    y[row + i] = v * scale * g[i];
-    if (copy) copy[row + i] = v;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  float4* y4 = reinterpret_cast<float4*>(y + row);
+  float4* c4 = copy ? reinterpret_cast<float4*>(copy + row) : nullptr;
+#pragma unroll
+  for (int j = 0; j < RN_V; ++j) {
+    const int i = (int)threadIdx.x + j * RN_T;
+    if (i < n4) {
+      const float4 gg = g4[i];
+      y4[i] = make_float4(v[j].x * scale * gg.x, v[j].y * scale * gg.y, v[j].z * scale * gg.z, v[j].w * scale * gg.w);
+      if (c4) c4[i] = v[j];
+    }
   }
 }
 
 hipError_t rmsnorm_rows_launch(int n_rows, int n, const float* x, const float* gain, float eps, float* y, float* copy,
                                hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(n_rows), dim3(256), 0, s, n, x, gain, eps, y, copy);
+  if (n % 4 || n > RN_T * RN_V * 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(n_rows), dim3(RN_T), 0, s, n, x, gain, eps, y, copy);
   return hipGetLastError();
 }
 

@@ -128,11 +128,16 @@ def test_verify_tokens_match_sequential_greedy(k):
         check_rel(LG[t], ref, nrm, what=f"logits of token {t}")
         assert ref[nxt[t]] >= ref.max() - 1e-3 * nrm[nxt[t]]
         assert nxt[t] == int(np.argmax(LG[t]))
-    # every layer's cache holds the k new slots, within rounding of the sequential run's
+    # every layer's cache holds the k new slots: the same values as the sequential run's up to
+    # rounding (normwise; each entry is judged against the checker in the layer tests)
     for l in range(4):
-        a16 = host(kcs[l]).view(np.float16).astype(np.float64)
-        b16 = kref[l].view(np.float16).astype(np.float64)
-        assert np.allclose(a16, b16, rtol=2e-3, atol=2e-3)
+        for got_c, ref_c in ((host(kcs[l]), kref[l]), (host(vcs[l]), vref[l])):
+            a16 = got_c.view(np.float16).astype(np.float64)
+            b16 = ref_c.view(np.float16).astype(np.float64)
+            rel = np.linalg.norm(a16 - b16) / np.linalg.norm(b16)
+            worst = np.unravel_index(np.argmax(np.abs(a16 - b16)), a16.shape)
+            say(f"  layer {l}: cache normwise rel diff {rel:.1e}, worst at {worst}: {a16[worst]} vs {b16[worst]}")
+            assert rel < 1e-3  # the GEMV tolerance; the two runs differ by fp16 rounding flips
 
 
 def test_verify_tokens_streamed_equals_resident():
