@@ -24,6 +24,8 @@
  *                      w = d*sc_j*q - dmin*m_j
  *   Q6_K (210 B / 256): low nibbles[128] @0, 2-bit highs[64] @128, int8 s[16] @192, d @208;
  *                      w = d*s_(i/16)*(q-32)
+ *   F16 (2 B / 1), F32 (4 B / 1): the weight itself, IEEE binary16 / binary32 (GGUF's
+ *                      unquantized tensor types, listed by the overview beside the quant formats)
  * With these fields every weight is an exact fp64 number (at most 32
  * significant bits), so dequantization to fp32 is a single RNE rounding of the
  * exact value, and every dot product here is accumulated in fp64.
@@ -39,7 +41,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_K = 4 };
+enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_K = 4, OR_F16 = 5, OR_F32 = 6 };
 
 /* Threads of the OpenMP loops below (for timing the checker on a stated core count). */
 void or_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
@@ -49,6 +51,7 @@ int or_block_elems(int fmt) {
   switch (fmt) {
     case OR_Q8_0: case OR_Q4_0: return 32;
     case OR_Q4_K: case OR_Q6_K: case OR_Q5_K: return 256;
+    case OR_F16: case OR_F32: return 1;  /* unquantized: one weight per "block" */
   }
   return -1;
 }
@@ -60,6 +63,8 @@ int or_block_bytes(int fmt) {
     case OR_Q4_K: return 144;
     case OR_Q6_K: return 210;
     case OR_Q5_K: return 176;
+    case OR_F16: return 2;
+    case OR_F32: return 4;
   }
   return -1;
 }
@@ -96,6 +101,15 @@ static void q4k_scale_min(const uint8_t* s, int j, int* sc, int* m) {
 /* Exact value of every weight of one block, in fp64. */
 static void dequant_block(int fmt, const uint8_t* b, double* w) {
   switch (fmt) {
+    case OR_F16:  /* IEEE binary16, little-endian */
+      w[0] = rd16(b);
+      break;
+    case OR_F32: {  /* IEEE binary32, little-endian; every binary32 value is exact in fp64 */
+      float f;
+      memcpy(&f, b, 4);
+      w[0] = (double)f;
+      break;
+    }
     case OR_Q8_0: {
       double d = rd16(b);
       for (int i = 0; i < 32; ++i) w[i] = d * (double)(int8_t)b[2 + i];

@@ -9,7 +9,8 @@ Weights follow the distributions of the workloads on the ntransformer pages'
 formats (ntransformer overview, de.news.hada.io, "Überblick über NTransformer":
 GGUF formats Q4_0, Q8_0, Q4_K_M, Q5_K, Q6_K): every fp16 super-scale ~ U[0.001, 0.01],
 Q8_0 codes ~ U{-127..127}, Q4_0/Q4_K/Q5_K nibbles, Q5_K high bits and Q4_K/Q5_K 6-bit
-scales/mins ~ uniform, Q6_K 6-bit codes ~ uniform and int8 sub-scales ~ U{-64..63}.
+scales/mins ~ uniform, Q6_K 6-bit codes ~ uniform and int8 sub-scales ~ U{-64..63}; F16 and
+F32 weights ~ N(0, 0.02), rounded to the format.
 """
 from __future__ import annotations
 
@@ -24,10 +25,14 @@ _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
 # format ids, block geometry (weights per block, bytes per block)
-Q8_0, Q4_0, Q4_K, Q6_K, Q5_K = 0, 1, 2, 3, 4
-FORMAT_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_K: "Q5_K"}
-BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256, Q5_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210, Q5_K: 176}
+Q8_0, Q4_0, Q4_K, Q6_K, Q5_K, F16, F32 = 0, 1, 2, 3, 4, 5, 6
+FORMAT_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_K: "Q5_K", F16: "F16", F32: "F32"}
+# F16 and F32 tensors hold one weight per "block" (GGUF's unquantized types)
+BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256, Q5_K: 256, F16: 1, F32: 1}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210, Q5_K: 176, F16: 2, F32: 4}
+# unquantized weights ~ N(0, F_STD): about the spread of trained Llama weight matrices (a reading:
+# the pages give no distribution for them)
+F_STD = 0.02
 
 DLO, DHI = 0.001, 0.01
 
@@ -86,6 +91,12 @@ def _ptr(buf) -> int:
 def fill_blocks(buf, fmt: int, n_blocks: int, seed: int, stream: int, block0: int = 0,
                 dlo: float = DLO, dhi: float = DHI) -> None:
     """Write n_blocks blocks of format fmt (blocks block0.. of the stream) at buf."""
+    if fmt == F16:
+        lib().synth_fill_normal_f16(_ptr(buf), block0, n_blocks, seed, stream, 0.0, F_STD)
+        return
+    if fmt == F32:
+        lib().synth_fill_normal_f32(_ptr(buf), block0, n_blocks, seed, stream, 0.0, F_STD)
+        return
     fn = {Q8_0: lib().synth_fill_q8_0, Q4_0: lib().synth_fill_q4_0,
           Q4_K: lib().synth_fill_q4_k, Q6_K: lib().synth_fill_q6_k, Q5_K: lib().synth_fill_q5_k}[fmt]
     fn(_ptr(buf), block0, n_blocks, seed, stream, dlo, dhi)

@@ -262,9 +262,47 @@ def test_bits_per_weight():
         assert oracle.block_elems(f) == synth.BLOCK_ELEMS[f]
 
 
+# ---------------------------------------------------------------- F16 / F32 weights
+
+def test_f16_weights_every_code_is_its_binary16_value():
+    """An F16 tensor is its weights as IEEE binary16: every one of the 65536 codes decodes to
+    numpy's value (NaNs as NaN, both zeros), and the fp32 dequantization is that value exactly."""
+    codes = np.arange(65536, dtype=np.uint16)
+    w = oracle.dequant_exact(synth.F16, 1, 65536, codes.view(np.uint8))[0]
+    ref = codes.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(w), nan) and np.array_equal(w[~nan], ref[~nan])
+    assert math.copysign(1.0, w[0x8000]) == -1.0 and w[0x7C00] == math.inf and w[0xFC00] == -math.inf
+    w32 = oracle.dequant_f32(synth.F16, 256, 256, codes.view(np.uint8))
+    ref32 = codes.view(np.float16).astype(np.float32).reshape(256, 256)
+    assert np.array_equal(np.isnan(w32), np.isnan(ref32))
+    assert np.array_equal(w32[~np.isnan(ref32)], ref32[~np.isnan(ref32)])
+
+
+def test_f32_weights_hand_values():
+    vals = np.array([1.0, -2.5, 3.4028234663852886e38, 1.401298464324817e-45, -0.0, 0.1, 65504.0, -1e-30,
+                     np.float32(np.pi)], dtype=np.float32)
+    w = oracle.dequant_exact(synth.F32, 1, vals.size, vals.view(np.uint8))[0]
+    assert np.array_equal(w, vals.astype(np.float64)) and math.copysign(1.0, w[4]) == -1.0
+    assert w[2] == 2.0 ** 128 - 2.0 ** 104 and w[3] == 2.0 ** -149  # largest normal, smallest subnormal
+    rnd = synth.quant_matrix(synth.F32, 3, 1000, seed=1, stream=3)
+    assert np.array_equal(oracle.dequant_f32(synth.F32, 3, 1000, rnd), rnd.view(np.float32).reshape(3, 1000))
+
+
+def test_f16_f32_geometry_and_generator():
+    assert (oracle.block_elems(synth.F16), oracle.block_bytes(synth.F16)) == (1, 2)
+    assert (oracle.block_elems(synth.F32), oracle.block_bytes(synth.F32)) == (1, 4)
+    w = synth.quant_matrix(synth.F16, 64, 4096, seed=0, stream=5).view(np.float16).astype(np.float64)
+    assert abs(w.std() - synth.F_STD) < 0.02 * synth.F_STD and abs(w.mean()) < 0.02 * synth.F_STD
+    # rows regenerate alone
+    rows = synth.quant_rows(synth.F32, 512, [3, 17], 0, 9)
+    full = synth.quant_matrix(synth.F32, 20, 512, 0, 9).reshape(20, -1)
+    assert np.array_equal(rows[0], full[3]) and np.array_equal(rows[1], full[17])
+
+
 # ---------------------------------------------------------------- GEMV
 
-@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K])
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32])
 def test_gemv_exact_rational_brute_force(fmt):
     rows, cols = 4, 512
     blocks = synth.quant_matrix(fmt, rows, cols, seed=3, stream=10 + fmt)
@@ -278,7 +316,7 @@ def test_gemv_exact_rational_brute_force(fmt):
         assert abs(Fraction(nrm[r]) - n_exact) <= Fraction(cols) * Fraction(2) ** -52 * n_exact
 
 
-@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K])
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32])
 def test_gemv_one_hot_picks_a_column(fmt):
     rows, cols = 5, 512
     blocks = synth.quant_matrix(fmt, rows, cols, seed=4, stream=30 + fmt)
