@@ -9,7 +9,7 @@ decode layers, final norm, LM head and argmax, every kernel in libnt.so.
 
 Prints one JSON line.  Other workloads (--config) print their own line for measurement
 runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B GEMV
-shapes in Q4_K, Q6_K and Q5_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
+shapes in Q4_K, Q6_K, Q5_K, F16 and F32, 5 = the 70B Q6_K model with 54 layers streamed from pinned
 host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes, 7 = the 70B model with
 cosine-based layer skip (--skip layers, default 20 of 80), 8 = 70B Q6_K layers read from a file
 (--file-layers, default 8) through page-locked bounce buffers, 9 = the self-speculative
@@ -492,7 +492,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
     if args.config == 1:
         shapes = [(synth.Q8_0, 4096, 4096)]
     else:
-        shapes = [(f, r, c) for f in (synth.Q4_K, synth.Q6_K, synth.Q5_K)
+        shapes = [(f, r, c) for f in (synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32)
                   for (r, c) in ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672))]
     for fmt, r, c in shapes:
         nbytes = synth.matrix_bytes(fmt, r, c)
@@ -508,7 +508,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
         "value": best["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": best["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales and sums (quantized weights)", "data": "synthetic",
-        "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K and Q5_K"},
+        "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K, Q5_K, F16 and F32"},
         "roofline": {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": best["frac_of_peak"], "traffic": None},
         "gemv": out,

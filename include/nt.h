@@ -50,8 +50,13 @@ extern "C" {
  *   NT_Q5_K 176 B / 256 weights: d @0, dmin @2, scales and mins packed as in NT_Q4_K @4,
  *            high bits[32] @16, nibbles[128] @48; the fifth code bit of weight i of sub-block
  *            j = i/32 is bit j of high byte i%32                              w = d*sc*q - dmin*m
+ *   NT_F16    2 B / 1 weight   : the weight as IEEE binary16 (GGUF's F16 tensors)
+ *   NT_F32    4 B / 1 weight   : the weight as IEEE binary32 (GGUF's F32 tensors)
+ * (the overview's format list, "Überblick über NTransformer", names both beside the quant types).
+ * Every entry point that takes cols for NT_F16 / NT_F32 needs a multiple of 32 (so that rows
+ * keep the 16-byte alignment the loads use).
  */
-typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4 } nt_format;
+typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4, NT_F16 = 5, NT_F32 = 6 } nt_format;
 
 typedef enum {
   NT_OK = 0,

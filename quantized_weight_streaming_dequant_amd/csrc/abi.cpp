@@ -41,7 +41,7 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(NT_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_Q5_K; }
+bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_F32; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -175,7 +175,7 @@ GemvArgs blank_args() {
 // Enqueue the FFN input half of a layer: a = SwiGLU(Wg n, Wu n), n = RMSNorm(h, ffn_norm).
 static hipError_t ffn_up_launch(const nt_layer_weights& w, const nt_layer_shape& s, const float* h, float* out,
                                 hipStream_t st) {
-  const GemvPlan p = gemv_plan(EPI_SWIGLU, s.dim);
+  const GemvPlan p = gemv_plan(EPI_SWIGLU, s.dim, 1 << w.fmt[NT_W_GATE]);
   GemvArgs a = blank_args();
   a.x = h; a.gain = w.ffn_norm; a.eps = s.eps; a.cols = s.dim; a.nseg = 2;
   a.seg[0] = make_seg(w.w[NT_W_GATE], w.fmt[NT_W_GATE], s.ffn_dim, s.dim, 0);
@@ -193,7 +193,7 @@ static int lm_head_enqueue(int fmt, int64_t n_vocab, int dim, const void* output
   hipError_t e;
   if (reset && (e = key_reset_launch(key, 1, st)) != hipSuccess) return hip_fail(e, "key reset launch");
   {
-    const GemvPlan p = gemv_plan(EPI_LOGITS, dim);
+    const GemvPlan p = gemv_plan(EPI_LOGITS, dim, 1 << fmt);
     GemvArgs a = blank_args();
     a.x = h; a.gain = gain; a.eps = eps; a.cols = dim; a.nseg = 1;
     a.seg[0] = make_seg(output, fmt, (int)n_vocab, dim, 0);
@@ -218,7 +218,8 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
   hipError_t e;
 
   {  // a1-a3: RMSNorm prologue, q/k/v GEMV, RoPE + fp16 cache append epilogue
-    const GemvPlan p = gemv_plan(EPI_QKV, s.dim);
+    const int mask = (1 << w.fmt[NT_W_Q]) | (1 << w.fmt[NT_W_K]) | (1 << w.fmt[NT_W_V]);
+    const GemvPlan p = gemv_plan(EPI_QKV, s.dim, mask);
     GemvArgs a = blank_args();
     a.x = h; a.gain = w.attn_norm; a.eps = s.eps; a.cols = s.dim;
     a.nseg = 3;
@@ -227,7 +228,6 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     a.seg[1] = make_seg(w.w[NT_W_K], w.fmt[NT_W_K], nkv, s.dim, t); t += gemv_groups(p, nkv);
     a.seg[2] = make_seg(w.w[NT_W_V], w.fmt[NT_W_V], nkv, s.dim, t); t += gemv_groups(p, nkv);
     a.q_out = wq; a.k_cache = kc; a.v_cache = vc; a.pos = pos; a.max_ctx = s.max_ctx; a.rope_theta = s.rope_theta;
-    const int mask = (1 << w.fmt[NT_W_Q]) | (1 << w.fmt[NT_W_K]) | (1 << w.fmt[NT_W_V]);
     TimedLaunch tl(NT_K_ATTN_IN, st);
     if ((e = gemv_launch(mask, EPI_QKV, p, t, a, st)) != hipSuccess) return hip_fail(e, "attn_in launch");
   }
@@ -241,7 +241,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     if ((e = attn_launch(a, s.n_q_heads / s.n_kv_heads, st)) != hipSuccess) return hip_fail(e, "attention launch");
   }
   {  // a5: O GEMV + residual (h1 also kept in the workspace)
-    const GemvPlan p = gemv_plan(EPI_RESID, nq);
+    const GemvPlan p = gemv_plan(EPI_RESID, nq, 1 << w.fmt[NT_W_O]);
     GemvArgs a = blank_args();
     a.x = wo; a.cols = nq; a.nseg = 1;
     a.seg[0] = make_seg(w.w[NT_W_O], w.fmt[NT_W_O], s.dim, nq, 0);
@@ -253,7 +253,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
   // a6-a8: RMSNorm prologue, paired gate/up GEMV, SwiGLU epilogue
   if ((e = ffn_up_launch(w, s, h, wa, st)) != hipSuccess) return hip_fail(e, "gate/up launch");
   {  // a9: down GEMV + residual
-    const GemvPlan p = gemv_plan(EPI_RESID, s.ffn_dim);
+    const GemvPlan p = gemv_plan(EPI_RESID, s.ffn_dim, 1 << w.fmt[NT_W_DOWN]);
     GemvArgs a = blank_args();
     a.x = wa; a.cols = s.ffn_dim; a.nseg = 1;
     a.seg[0] = make_seg(w.w[NT_W_DOWN], w.fmt[NT_W_DOWN], s.dim, s.ffn_dim, 0);
@@ -405,7 +405,7 @@ int64_t nt_matrix_bytes(int fmt, int64_t rows, int64_t cols) {
 
 int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, void* stream) {
   if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
-  if (rows <= 0 || cols <= 0 || cols % block_elems(fmt)) return fail(NT_ESHAPE, "cols must be a positive multiple of %d", block_elems(fmt));
+  if (rows <= 0 || cols <= 0 || cols % col_unit(fmt)) return fail(NT_ESHAPE, "cols must be a positive multiple of %d", col_unit(fmt));
   if (!blocks || !w) return fail(NT_EINVAL, "null pointer");
   if (!aligned(blocks, 4) || !aligned(w, 4)) return fail(NT_EALIGN, "blocks and w must be 4-byte aligned");
   hipError_t e = dequant_launch(fmt, rows, cols, blocks, w, (hipStream_t)stream);
@@ -414,12 +414,12 @@ int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w
 
 int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream) {
   if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
-  if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols % block_elems(fmt) || cols > NT_GEMV_MAX_COLS)
+  if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols % col_unit(fmt) || cols > NT_GEMV_MAX_COLS)
     return fail(NT_ESHAPE, "need 0 < rows <= 2^30 and cols a positive multiple of %d up to %d (got %lld x %lld)",
-                block_elems(fmt), NT_GEMV_MAX_COLS, (long long)rows, (long long)cols);
+                col_unit(fmt), NT_GEMV_MAX_COLS, (long long)rows, (long long)cols);
   if (!blocks || !x || !y) return fail(NT_EINVAL, "null pointer");
   if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return fail(NT_EALIGN, "blocks and x must be 16-byte aligned, y 4-byte");
-  const GemvPlan p = gemv_plan(EPI_STORE, (int)cols);
+  const GemvPlan p = gemv_plan(EPI_STORE, (int)cols, 1 << fmt);
   GemvArgs a = blank_args();
   a.x = x; a.cols = (int)cols; a.nseg = 1;
   a.seg[0] = make_seg(blocks, fmt, (int)rows, (int)cols, 0);
@@ -432,8 +432,8 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
 int nt_gemm_q(int fmt, int64_t rows, int64_t cols, int n_tok, const void* blocks, const float* x, float* y,
               void* stream) {
   if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
-  if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols > NT_MAX_ROWS || cols % block_elems(fmt))
-    return fail(NT_ESHAPE, "need 0 < rows, cols <= 2^30 and cols a multiple of %d (got %lld x %lld)", block_elems(fmt),
+  if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols > NT_MAX_ROWS || cols % col_unit(fmt))
+    return fail(NT_ESHAPE, "need 0 < rows, cols <= 2^30 and cols a multiple of %d (got %lld x %lld)", col_unit(fmt),
                 (long long)rows, (long long)cols);
   if (n_tok < 1 || n_tok > NT_GEMM_MAX_TOK) return fail(NT_ESHAPE, "n_tok must be in [1, %d]", NT_GEMM_MAX_TOK);
   if (!blocks || !x || !y) return fail(NT_EINVAL, "null pointer");
@@ -540,7 +540,7 @@ int nt_ffn_up(const nt_layer_weights* w, const nt_layer_shape* shp, const float*
 int nt_embed_row(int fmt, int64_t n_vocab, int64_t dim, const void* table, const int32_t* token, float* h,
                  void* stream) {
   if (!fmt_ok(fmt)) return fail(NT_EFORMAT, "unknown format %d", fmt);
-  if (n_vocab <= 0 || dim <= 0 || dim % block_elems(fmt)) return fail(NT_ESHAPE, "bad embedding shape");
+  if (n_vocab <= 0 || dim <= 0 || dim % col_unit(fmt)) return fail(NT_ESHAPE, "bad embedding shape");
   if (!table || !token || !h) return fail(NT_EINVAL, "null pointer");
   if (!aligned(table, 4)) return fail(NT_EALIGN, "table must be 4-byte aligned");
   hipError_t e = embed_launch(fmt, n_vocab, dim, table, token, h, nullptr, (hipStream_t)stream);

@@ -7,12 +7,19 @@
 
 namespace nt {
 
-enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4 };
+// F16 and F32 are unquantized weight tensors: one weight per "block".
+enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4, FMT_F16 = 5, FMT_F32 = 6 };
+constexpr int FMT_COUNT = 7;
 
-__host__ __device__ constexpr int block_elems(int f) { return f <= FMT_Q4_0 ? 32 : 256; }
+__host__ __device__ constexpr bool is_float_fmt(int f) { return f == FMT_F16 || f == FMT_F32; }
+__host__ __device__ constexpr int block_elems(int f) { return f <= FMT_Q4_0 ? 32 : is_float_fmt(f) ? 1 : 256; }
 __host__ __device__ constexpr int block_bytes(int f) {
-  return f == FMT_Q8_0 ? 34 : f == FMT_Q4_0 ? 18 : f == FMT_Q4_K ? 144 : f == FMT_Q5_K ? 176 : 210;
+  return f == FMT_Q8_0 ? 34 : f == FMT_Q4_0 ? 18 : f == FMT_Q4_K ? 144 : f == FMT_Q5_K ? 176 : f == FMT_F16 ? 2
+         : f == FMT_F32 ? 4 : 210;
 }
+// Column granularity of the kernels: a block, and at least 32 columns (one scale block of the
+// staged activations; F16 and F32 rows are then 64- and 128-byte multiples).
+__host__ __device__ constexpr int col_unit(int f) { return block_elems(f) < 32 ? 32 : block_elems(f); }
 
 // 4-byte-aligned 128/64-bit vector types: global_load_dwordx4/x2 only need dword alignment,
 // and telling the compiler the true alignment keeps it from splitting or assuming more.

@@ -47,8 +47,8 @@ struct GemvPlan {
   size_t lds_bytes;
 };
 
-// Launch geometry for a format mix and shape.
-GemvPlan gemv_plan(int epi, int cols);
+// Launch geometry for a format mix (bit f set for every format present) and shape.
+GemvPlan gemv_plan(int epi, int cols, int fmt_mask);
 // Row groups (of rows_per_wave rows) a segment of `rows` rows makes under `plan`.
 int gemv_groups(const GemvPlan& p, int rows);
 // Enqueue.  fmt_mask: bit f set for every format present in the segments; n_groups: the
@@ -61,7 +61,7 @@ constexpr int GEMM_MAX_TOK = 8;
 // accum: add W X into y (the residual add of a decode layer) instead of overwriting it.
 hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int n_tok, const float* x, float* y,
                        hipStream_t s, bool accum = false);
-// Columns per launch for n_tok tokens (a multiple of the block size); exposed for the tests.
-int gemm_chunk_cols(int n_tok, int cols, int block_elems);
+// Columns per launch of the vector-ALU k-token GEMM for n_tok tokens of format fmt.
+int gemm_chunk_cols(int n_tok, int cols, int fmt);
 
 }  // namespace nt

@@ -114,16 +114,19 @@ __host__ __device__ __forceinline__ int xq_off(int c) { return c + ((c >> 6) << 
 __host__ __device__ __forceinline__ int xq_plane(int cols) { return (xq_off(cols) + 15) & ~15; }
 // LDS bytes of one token's staged chunk in the k-token GEMM: limb planes, a scale per 32
 // columns and a sum per 16, rounded to 16 bytes
-__host__ __device__ __forceinline__ size_t gemm_lds_per_token(int cols) {
-  return ((size_t)XL * xq_plane(cols) + sizeof(float) * (size_t)((cols >> 5) + (cols >> 4)) + 15) & ~(size_t)15;
+// (fp32 x instead of the limb planes for the unquantized formats, f)
+__host__ __device__ __forceinline__ size_t gemm_lds_per_token(int cols, bool f = false) {
+  return ((f ? sizeof(float) * (size_t)cols : (size_t)XL * xq_plane(cols)) +
+          sizeof(float) * (size_t)((cols >> 5) + (cols >> 4)) + 15) & ~(size_t)15;
 }
 
 // The staged activation vector, as the register-path kernels see it in LDS.
 struct XLimbs {
-  uint8_t* q;   // XL planes of xq_plane(cols) bytes
-  int plane;
-  float* sc;    // scale s / 256^(XL-1) per 32 columns
-  float* s16;   // sum of x per 16 columns (fp32)
+  uint8_t* q = nullptr;   // XL planes of xq_plane(cols) bytes (null: not staged, no quantized format in the launch)
+  int plane = 0;
+  float* sc = nullptr;    // scale s / 256^(XL-1) per 32 columns
+  float* s16 = nullptr;   // sum of x per 16 columns (fp32)
+  float* xf = nullptr;    // x itself, fp32, for the unquantized formats (null: not staged)
 };
 
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
@@ -585,6 +588,67 @@ struct Q6_KF {
   }
 };
 
+// F16 / F32: unquantized rows (GGUF's F16 and F32 tensors).  Lane = 16 consecutive bytes per
+// load, four loads per step at 1 KiB apart, so each load instruction reads 1 KiB of the row:
+// F16 columns 2048 step + 512 i + 8 lane .. +7, F32 columns 1024 step + 256 i + 4 lane .. +3.
+// The products are fp32 FMAs against the fp32 copy of x (w is exact in fp32).  Columns are a
+// multiple of 32, so a load is wholly inside or wholly past the row.
+template <bool H>
+struct FloatF {
+  static constexpr int CPL = H ? 8 : 4;  // columns per 16-byte load
+  static constexpr int SHIFT = H ? 11 : 10;  // log2 of the columns of a step
+  struct Raw {
+    u32x4 v[4];
+  };
+  static __device__ __forceinline__ int col(int step, int i, int lane) {
+    return (step << SHIFT) + i * 64 * CPL + lane * CPL;
+  }
+  static __device__ __forceinline__ int steps(int cols) { return (cols + (1 << SHIFT) - 1) >> SHIFT; }
+  static __device__ __forceinline__ Raw load(const uint8_t* rowp, int cols, int step, int lane) {
+    Raw r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = col(step, i, lane);
+      c = c < cols ? c : 0;  // past the row end: reread its start (dropped)
+      r.v[i] = wld16(rowp + (size_t)c * (H ? 2 : 4));
+    }
+    return r;
+  }
+  template <int NR>
+  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane, const XLimbs& xs,
+                                             float (&acc)[NR]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = col(step, i, lane);
+      if (c >= cols) break;  // the later loads of the step are past the end too
+      if constexpr (H) {
+        const float4 x0 = *reinterpret_cast<const float4*>(xs.xf + c);
+        const float4 x1 = *reinterpret_cast<const float4*>(xs.xf + c + 4);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const u32x4 w = raw[k].v[i];
+          float t0 = h2f(w.x) * x0.x, t1 = h2f(w.x >> 16) * x0.y;
+          t0 = fmaf(h2f(w.y), x0.z, t0); t1 = fmaf(h2f(w.y >> 16), x0.w, t1);
+          t0 = fmaf(h2f(w.z), x1.x, t0); t1 = fmaf(h2f(w.z >> 16), x1.y, t1);
+          t0 = fmaf(h2f(w.w), x1.z, t0); t1 = fmaf(h2f(w.w >> 16), x1.w, t1);
+          acc[k] += t0 + t1;
+        }
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4*>(xs.xf + c);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const u32x4 w = raw[k].v[i];
+          float t0 = __uint_as_float(w.x) * x0.x, t1 = __uint_as_float(w.y) * x0.y;
+          t0 = fmaf(__uint_as_float(w.z), x0.z, t0); t1 = fmaf(__uint_as_float(w.w), x0.w, t1);
+          acc[k] += t0 + t1;
+        }
+      }
+    }
+  }
+};
+typedef FloatF<true> F16F;
+typedef FloatF<false> F32F;
+
 // ------------------------------------------------------------------ kernel
 
 // Rows per work item and items in flight per wave on the register path: the gate/up pair
@@ -670,6 +734,11 @@ __device__ __forceinline__ XPre stage_x_load(const GemvArgs& a) {
 // One group of 16 columns (already normalised) into the limb planes, its sum and, from the
 // even thread of each pair, the pair's scale.
 __device__ __forceinline__ void stage_group(const XLimbs& xs, int gi, const float (&v)[16]) {
+  if (xs.xf) {
+    float4* d = reinterpret_cast<float4*>(xs.xf + gi * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  }
   float sum = 0.f;
   uint32_t mb = 0;  // max of |x| as bit patterns: a NaN orders above every number
 #pragma unroll
@@ -682,6 +751,7 @@ __device__ __forceinline__ void stage_group(const XLimbs& xs, int gi, const floa
   float s, k;
   limb_scale(mb, s, k);
   if ((gi & 1) == 0) xs.sc[gi >> 1] = s;
+  if (!xs.q) return;
   uint32_t w[XL][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) limb_digits(&v[4 * i], k, w, i);
@@ -946,6 +1016,12 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
     case FMT_Q5_K:
       if constexpr ((FMTMASK >> FMT_Q5_K) & 1) run_segment<Q5_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
       break;
+    case FMT_F16:
+      if constexpr ((FMTMASK >> FMT_F16) & 1) run_segment<F16F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      break;
+    case FMT_F32:
+      if constexpr ((FMTMASK >> FMT_F32) & 1) run_segment<F32F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      break;
     default:
       if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
       break;
@@ -953,13 +1029,22 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
 }
 
 // At least four waves per SIMD (at most 128 VGPRs): the stream needs many waves in flight.
+// Which staged forms of x a launch's formats read: the limbs (quantized formats) and/or the
+// fp32 copy (F16, F32).
+constexpr bool mask_has_q(int m) { return (m & (0x1F | FMTS_Q4K_Q4K_Q6K | FMTS_Q5K_Q5K_Q6K)) != 0; }
+constexpr bool mask_has_f(int m) { return (m & ((1 << FMT_F16) | (1 << FMT_F32))) != 0; }
+
 template <int FMTMASK, int R, int NW, int EPI>
 __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   extern __shared__ float4 smem4[];
   XLimbs xs;
-  xs.q = reinterpret_cast<uint8_t*>(smem4);
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem4);
   xs.plane = xq_plane(a.cols);
-  xs.sc = reinterpret_cast<float*>(xs.q + XL * xs.plane);
+  xs.q = mask_has_q(FMTMASK) ? lds : nullptr;
+  lds += mask_has_q(FMTMASK) ? XL * xs.plane : 0;
+  xs.xf = mask_has_f(FMTMASK) ? reinterpret_cast<float*>(lds) : nullptr;
+  lds += mask_has_f(FMTMASK) ? 4 * a.cols : 0;
+  xs.sc = reinterpret_cast<float*>(lds);
   xs.s16 = xs.sc + (a.cols >> 5);
   float* red = xs.s16 + (a.cols >> 4);
   const int lane = threadIdx.x & 63;
@@ -1209,14 +1294,16 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wid = (int)blockIdx.x * NW + wave;
   const int W = (int)gridDim.x * NW;
-  const size_t per_tok = gemm_lds_per_token(a.cols);
+  constexpr bool FF = is_float_fmt(FMT);
+  const size_t per_tok = gemm_lds_per_token(a.cols, FF);
   XLimbs xs[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     uint8_t* base = reinterpret_cast<uint8_t*>(smem4) + t * per_tok;
-    xs[t].q = base;
     xs[t].plane = xq_plane(a.cols);
-    xs[t].sc = reinterpret_cast<float*>(base + XL * xs[t].plane);
+    xs[t].q = FF ? nullptr : base;
+    xs[t].xf = FF ? reinterpret_cast<float*>(base) : nullptr;
+    xs[t].sc = reinterpret_cast<float*>(base + (FF ? sizeof(float) * a.cols : (size_t)XL * xs[t].plane));
     xs[t].s16 = xs[t].sc + (a.cols >> 5);
     gemm_stage(a, t, xs[t], NW * 64);
   }
@@ -1226,6 +1313,8 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   else if constexpr (FMT == FMT_Q4_0) gemm_rows<Q4_0F, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q4_K) gemm_rows<Q4_KF, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q5_K) gemm_rows<Q5_KF, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_F16) gemm_rows<F16F, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_F32) gemm_rows<F32F, NT, R>(a, xs, lane, wid, W);
   else gemm_rows<Q6_KF, NT, R>(a, xs, lane, wid, W);
 }
 
@@ -1998,15 +2087,30 @@ static int num_cu() {
 
 constexpr size_t GEMV_LDS_MAX = 160 * 1024 - 2048;  // dynamic LDS budget of the register path (static LDS on top)
 
-// limb planes, scales per 32 columns, sums per 16 columns, 16 floats of reduction space
-static size_t lds_for(int cols) {
-  return (size_t)XL * xq_plane(cols) + sizeof(float) * (size_t)((cols >> 5) + (cols >> 4) + 16);
+// limb planes (quantized formats), fp32 x (unquantized formats), scales per 32 columns, sums
+// per 16 columns, 16 floats of reduction space
+static size_t lds_for(int cols, int inst) {
+  return (mask_has_q(inst) ? (size_t)XL * xq_plane(cols) : 0) + (mask_has_f(inst) ? sizeof(float) * (size_t)cols : 0) +
+         sizeof(float) * (size_t)((cols >> 5) + (cols >> 4) + 16);
 }
 
-GemvPlan gemv_plan(int epi, int cols) {
+// The kernel instantiation a launch's format mask selects (launch_mask; the fixed q/k/v format
+// variants stage what their general masks stage).
+static int inst_mask(int m) {
+  switch (m) {
+    case 1 << FMT_Q8_0: case 1 << FMT_Q4_0: case 1 << FMT_Q4_K: case 1 << FMT_Q6_K: case 1 << FMT_Q5_K:
+    case 1 << FMT_F16: case 1 << FMT_F32:
+    case (1 << FMT_Q5_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_K) | (1 << FMT_Q6_K):
+      return m;
+    default:
+      return (1 << FMT_COUNT) - 1;
+  }
+}
+
+GemvPlan gemv_plan(int epi, int cols, int fmt_mask) {
   GemvPlan p;
   p.rows_per_wave = (epi == EPI_SWIGLU) ? 1 : (epi == EPI_QKV) ? 2 : NT_GEMV_ROWS;
-  p.lds_bytes = lds_for(cols);
+  p.lds_bytes = lds_for(cols, inst_mask(fmt_mask));
   // one copy of x per workgroup: when only one fits in a CU's LDS, make it 16 waves
   p.waves = p.lds_bytes > 80 * 1024 ? 16 : 8;
   return p;
@@ -2022,7 +2126,8 @@ static hipError_t launch_one(const GemvPlan& plan, int n_groups, const GemvArgs&
   static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_LDS_MAX);
   if (raised != hipSuccess) return raised;
-  if (plan.lds_bytes > GEMV_LDS_MAX) return hipErrorInvalidValue;
+  // the plan must hold what this instantiation stages
+  if (plan.lds_bytes > GEMV_LDS_MAX || plan.lds_bytes < lds_for(a.cols, FMTMASK)) return hipErrorInvalidValue;
   // resident workgroups per CU at this LDS size, cached per instantiation as (LDS bytes << 8 | count)
   static std::atomic<uint64_t> cache{0};
   const uint64_t c = cache.load(std::memory_order_relaxed);
@@ -2058,6 +2163,8 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
     case 1 << FMT_Q4_K: return launch_nw<1 << FMT_Q4_K, EPI>(plan, n_groups, a, s);
     case 1 << FMT_Q6_K: return launch_nw<1 << FMT_Q6_K, EPI>(plan, n_groups, a, s);
     case 1 << FMT_Q5_K: return launch_nw<1 << FMT_Q5_K, EPI>(plan, n_groups, a, s);
+    case 1 << FMT_F16: return launch_nw<1 << FMT_F16, EPI>(plan, n_groups, a, s);
+    case 1 << FMT_F32: return launch_nw<1 << FMT_F32, EPI>(plan, n_groups, a, s);
     case (1 << FMT_Q5_K) | (1 << FMT_Q6_K):
       if constexpr (EPI == EPI_QKV) {
         if (a.nseg == 3 && a.seg[0].fmt == FMT_Q5_K && a.seg[1].fmt == FMT_Q5_K && a.seg[2].fmt == FMT_Q6_K)
@@ -2070,7 +2177,7 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
           return launch_nw<FMTS_Q4K_Q4K_Q6K, EPI>(plan, n_groups, a, s);
       }
       return launch_nw<(1 << FMT_Q4_K) | (1 << FMT_Q6_K), EPI>(plan, n_groups, a, s);
-    default: return launch_nw<31, EPI>(plan, n_groups, a, s);
+    default: return launch_nw<(1 << FMT_COUNT) - 1, EPI>(plan, n_groups, a, s);
   }
 }
 
@@ -2112,7 +2219,7 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) 
     if (st_family(g.fmt) != kf) return hipErrorNotSupported;
     // Q4_K measured faster on the register path (also with integer dot products here:
     // 64.7 vs 49.9 us for the 70B gate/up pair); Q5_K, its 5-bit sibling, has only that path
-    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q5_K) return hipErrorNotSupported;
+    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q5_K || is_float_fmt(g.fmt)) return hipErrorNotSupported;
     if ((reinterpret_cast<uintptr_t>(g.w) & 15) || (g.row_bytes & 15) || g.rows <= 0) return hipErrorNotSupported;
   }
   if ((reinterpret_cast<uintptr_t>(a.x) & 15) || (a.gain && (reinterpret_cast<uintptr_t>(a.gain) & 15)))
@@ -2202,7 +2309,7 @@ static hipError_t gemm_launch_nt(const GemmArgs& a, hipStream_t s) {
   static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS_MAX);
   if (raised != hipSuccess) return raised;
-  const size_t lds = (size_t)NT * gemm_lds_per_token(a.cols);
+  const size_t lds = (size_t)NT * gemm_lds_per_token(a.cols, is_float_fmt(FMT));
   constexpr int R = GEMM_ROWS<FMT, NT>;
   const int groups = (a.rows + R - 1) / R;
   const int grid = max(1, min((groups + NW - 1) / NW, num_cu()));
@@ -2246,21 +2353,22 @@ static int gemm_mfma_chunk_cols(int fmt, int n_tok, int cols) {
   return c > cols ? cols : c;
 }
 
-int gemm_chunk_cols(int n_tok, int cols, int be) {
+int gemm_chunk_cols(int n_tok, int cols, int fmt) {
   const int nt = n_tok <= 1 ? 1 : n_tok <= 2 ? 2 : n_tok <= 4 ? 4 : 8;
+  const bool f = is_float_fmt(fmt);
   // the widest multiple of 256 columns (a superblock, eight 32-weight blocks) whose NT
-  // limb regions fit, and no wider than the matrix
+  // staged regions fit, and no wider than the matrix
   int c = 256;
-  while (c + 256 <= cols && (size_t)nt * gemm_lds_per_token(c + 256) <= GEMM_LDS_MAX) c += 256;
+  while (c + 256 <= cols && (size_t)nt * gemm_lds_per_token(c + 256, f) <= GEMM_LDS_MAX) c += 256;
   if (c > cols) c = cols;
-  return c - c % be;
+  return c - c % col_unit(fmt);
 }
 
 hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int n_tok, const float* x, float* y,
                        hipStream_t s, bool accum) {
   const int be = block_elems(fmt), bb = block_bytes(fmt);
   const bool mm = gemm_use_mfma(fmt, n_tok);
-  const int chunk = mm ? gemm_mfma_chunk_cols(fmt, n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, be);
+  const int chunk = mm ? gemm_mfma_chunk_cols(fmt, n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, fmt);
   if (chunk <= 0) return hipErrorInvalidValue;
   GemmArgs a;
   a.row_bytes = (int64_t)(cols / be) * bb;
@@ -2296,6 +2404,8 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
       case FMT_Q4_0: e = gemm_launch_fmt<FMT_Q4_0>(n_tok, a, s); break;
       case FMT_Q4_K: e = gemm_launch_fmt<FMT_Q4_K>(n_tok, a, s); break;
       case FMT_Q5_K: e = gemm_launch_fmt<FMT_Q5_K>(n_tok, a, s); break;
+      case FMT_F16: e = gemm_launch_fmt<FMT_F16>(n_tok, a, s); break;
+      case FMT_F32: e = gemm_launch_fmt<FMT_F32>(n_tok, a, s); break;
       default: e = gemm_launch_fmt<FMT_Q6_K>(n_tok, a, s); break;
     }
     if (e != hipSuccess) return e;

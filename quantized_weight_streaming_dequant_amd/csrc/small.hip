@@ -17,7 +17,11 @@ __device__ __forceinline__ uint32_t byte_at(const uint8_t* p, int i) { return p[
 __device__ __forceinline__ float f16_at(const uint8_t* p) { return h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8)); }
 
 __device__ void dequant_group(int fmt, const uint8_t* blk, int grp, float* out) {
-  if (fmt == FMT_Q8_0) {
+  if (fmt == FMT_F16) {  // 32 consecutive binary16 weights at blk
+    for (int i = 0; i < 32; ++i) out[i] = f16_at(blk + 2 * i);
+  } else if (fmt == FMT_F32) {
+    for (int i = 0; i < 32; ++i) out[i] = *reinterpret_cast<const float*>(blk + 4 * i);
+  } else if (fmt == FMT_Q8_0) {
     const float d = f16_at(blk);
     for (int i = 0; i < 32; ++i) out[i] = d * (float)(int8_t)blk[2 + i];
   } else if (fmt == FMT_Q4_0) {

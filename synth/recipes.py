@@ -16,7 +16,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import (BLOCK_BYTES, BLOCK_ELEMS, Q4_K, Q5_K, Q6_K, Q8_0, fill_blocks, fill_normal_f16,
+from . import (BLOCK_BYTES, BLOCK_ELEMS, F16, F32, Q4_K, Q5_K, Q6_K, Q8_0, fill_blocks, fill_normal_f16,
                fill_uniform_f32, matrix_bytes, normal_f32, uniform_index)
 
 TENSORS = ("q", "k", "v", "o", "gate", "up", "down")
@@ -58,6 +58,8 @@ MIX_Q8_0 = {n: Q8_0 for n in TENSORS}
 MIX_Q6_K = {n: Q6_K for n in TENSORS}
 MIX_Q4_K_M = {n: (Q6_K if n in ("v", "down") else Q4_K) for n in TENSORS}
 MIX_Q5_K_M = {n: (Q6_K if n in ("v", "down") else Q5_K) for n in TENSORS}
+MIX_F16 = {n: F16 for n in TENSORS}  # unquantized layers (the overview lists F16 and F32 tensors)
+MIX_F32 = {n: F32 for n in TENSORS}
 
 
 @dataclass

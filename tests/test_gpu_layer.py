@@ -94,6 +94,11 @@ def test_layer_70b_q6_k_full_size():
     run_layer_and_check(recipes.LLAMA31_70B, recipes.MIX_Q6_K, pos=4200, n_slots=4096, layer=3)
 
 
+def test_layer_8b_f16_full_size():
+    """The Llama-3-8B-shaped layer with unquantized F16 weights (436 MB)."""
+    run_layer_and_check(recipes.LLAMA3_8B, recipes.MIX_F16, pos=1000, n_slots=1000)
+
+
 def test_layer_70b_q5_k_m_full_size():
     """The 70B-shaped layer in the Q5_K_M mix (Q5_K, with Q6_K for attn_v and ffn_down)."""
     run_layer_and_check(recipes.LLAMA31_70B, recipes.MIX_Q5_K_M, pos=4100, n_slots=4096, layer=5)
@@ -104,7 +109,12 @@ SMALL = recipes.LayerShape(dim=1024, n_q_heads=16, n_kv_heads=4, head_dim=128, f
 
 @pytest.mark.parametrize("mix,pos", [(recipes.MIX_Q4_K_M, 0), (recipes.MIX_Q8_0, 50), (recipes.MIX_Q6_K, 95),
                                      ({n: synth.Q4_0 for n in recipes.TENSORS}, 17), (recipes.MIX_Q5_K_M, 33),
-                                     ({n: synth.Q5_K for n in recipes.TENSORS}, 64)])
+                                     ({n: synth.Q5_K for n in recipes.TENSORS}, 64), (recipes.MIX_F16, 40),
+                                     (recipes.MIX_F32, 71),
+                                     # F16 attention projections over a Q4_K_M FFN, Q8_0 q/k with an F32 v
+                                     ({**recipes.MIX_Q4_K_M, "q": synth.F16, "k": synth.F16, "v": synth.F16,
+                                       "o": synth.F16}, 12),
+                                     ({**recipes.MIX_Q8_0, "v": synth.F32}, 90)])
 def test_layer_small_shapes(mix, pos):
     run_layer_and_check(SMALL, mix, pos=pos, n_slots=96)
 

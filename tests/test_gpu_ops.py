@@ -19,8 +19,8 @@ from tests.gpu_util import v_to_device, check_rel, dev, host, same_value, say, s
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K]
-NAMES = {synth.Q8_0: "Q8_0", synth.Q4_0: "Q4_0", synth.Q4_K: "Q4_K", synth.Q6_K: "Q6_K", synth.Q5_K: "Q5_K"}
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32]
+NAMES = synth.FORMAT_NAMES
 
 
 def gpu_gemv(fmt, rows, cols, blocks, x):
@@ -63,12 +63,28 @@ def test_dequant_hand_blocks_bit_exact():
          pack_q5_k(-2.0, 6.1e-5, list(range(56, 64)), list(range(8)), [(i * 7 + 16 * (i // 32 % 2)) % 32
                                                                       for i in range(256)])),
     ]
+    # F16 / F32: the IEEE values themselves, specials included
+    f16 = np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0x3C00, 0xC000, 0xFBFF, 0x3555] * 6 + [0x1234] * 4,
+                   dtype=np.uint16)
+    f32 = np.array([0.0, -0.0, 1.401298464324817e-45, 3.4028234663852886e38, -1.0, 0.1, -2.5e-30, 65504.0] * 8,
+                   dtype=np.float32)
+    cases += [(synth.F16, f16.tobytes()), (synth.F32, f32.tobytes())]
     for fmt, raw in cases:
         blocks = np.frombuffer(raw, np.uint8)
-        cols = synth.BLOCK_ELEMS[fmt] * 2
+        cols = synth.BLOCK_ELEMS[fmt] * 2 if synth.BLOCK_ELEMS[fmt] > 1 else len(raw) // synth.BLOCK_BYTES[fmt]
         got = gpu_dequant(fmt, 1, cols, blocks)
         ref = oracle.dequant_f32(fmt, 1, cols, blocks)
         assert same_value(got, ref), NAMES[fmt]
+
+
+def test_dequant_f16_every_code():
+    """All 65536 binary16 codes as one F16 matrix: each dequantizes to its value (NaN as NaN)."""
+    codes = np.arange(65536, dtype=np.uint16)
+    got = gpu_dequant(synth.F16, 64, 1024, codes.view(np.uint8))
+    ref = oracle.dequant_f32(synth.F16, 64, 1024, codes.view(np.uint8))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and same_value(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
 # ------------------------------------------------------------------ GEMV
@@ -87,6 +103,10 @@ GEMV_SHAPES = {
                  (8192, 28672)],
     synth.Q5_K: [(1, 256), (23, 1280), (130, 4352), (3, 12288), (8192, 8192), (1024, 8192), (28672, 8192),
                  (8192, 28672)],
+    # unquantized: one 32-column unit, a last step of one unit (2080 = 2048 + 32 for F16, 1024 + 1024 + 32
+    # for F32), the workload shapes
+    synth.F16: [(1, 32), (3, 96), (37, 2080), (130, 4352), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
+    synth.F32: [(1, 32), (3, 96), (37, 2080), (130, 4352), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
 }
 GEMV_CASES = [(f, r, c) for f in FMTS for (r, c) in GEMV_SHAPES[f]]
 # the widest x the header allows (NT_GEMV_MAX_COLS columns)
@@ -134,6 +154,9 @@ GEMM_CASES = [
     (synth.Q5_K, 37, 2304, 3), (synth.Q5_K, 1, 256, 8), (synth.Q5_K, 300, 16640, 6), (synth.Q5_K, 40, 32768, 5),
     # Q8_0 at 3-8 tokens (the VALU kernel: its matrix-core form measured slower), the 8B FFN shape
     (synth.Q8_0, 17, 512, 4), (synth.Q8_0, 1, 256, 8), (synth.Q8_0, 300, 4352, 6), (synth.Q8_0, 14336, 4096, 7),
+    # F16 / F32 (vector ALUs, fp32 x staged per token): ragged last steps, the 70B shape, several chunks
+    (synth.F16, 1, 32, 8), (synth.F16, 37, 2080, 3), (synth.F16, 8192, 8192, 4), (synth.F16, 40, 32768, 5),
+    (synth.F32, 3, 96, 2), (synth.F32, 130, 4352, 5), (synth.F32, 1024, 8192, 8), (synth.F32, 40, 32768, 7),
 ]
 
 
@@ -196,8 +219,9 @@ def test_gemv_outlier_activations(fmt, kind):
     x = (synth.normal_f32(cols, seed=3, stream=600 + fmt) * OUTLIER_KINDS[kind](cols)).astype(np.float32)
     y = gpu_gemv(fmt, rows, cols, blocks, x)
     ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
-    check_rel(y, ref, nrm, what=f"{NAMES[fmt]} {kind}")
-    worst = check_rel(y, ref, nrm, tol=1e-5, what=f"{NAMES[fmt]} {kind} (limb precision)")
+    worst = check_rel(y, ref, nrm, what=f"{NAMES[fmt]} {kind}")
+    if fmt not in (synth.F16, synth.F32):  # the unquantized formats read x in fp32, not as limbs
+        worst = check_rel(y, ref, nrm, tol=1e-5, what=f"{NAMES[fmt]} {kind} (limb precision)")
     say(f"  worst rel err {worst:.2e}")
 
 
