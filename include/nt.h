@@ -9,7 +9,11 @@
  *
  * Errors: every int-returning call returns NT_OK (0) or a negative nt_status;
  * on error nothing has been enqueued and nt_last_error() (thread-local)
- * describes the failure.
+ * describes the failure.  The one exception is an I/O failure while a file-tier
+ * layer is read (nt_stream_layers, nt_decode_token, nt_verify_tokens), which
+ * the host can only see mid-call: the file ranges are checked before anything is
+ * enqueued, but a read error or a file shrinking during the call returns
+ * NT_EHOSTMEM with the layers before that one enqueued (h partly updated).
  *
  * Ownership: the caller owns every buffer (weights, activations, caches,
  * workspaces).  The library allocates nothing on these paths and keeps no
@@ -338,7 +342,10 @@ int nt_stream_set_bounce(nt_streamer* st, void* bounce0, void* bounce1, size_t b
  * Pinned blobs must be page-locked host memory (NT_EHOSTMEM otherwise); file layers need
  * bounce buffers (nt_stream_set_bounce; NT_EINVAL otherwise), and a short or failed read is
  * NT_EHOSTMEM.  Every streamed blob must fit staging_bytes.  ws as for nt_decode_layer.  compute != copy.  stats nullable.
- * A streamer must be used with one plan at a time, from one host thread. */
+ * A streamer must be used with one plan at a time, from one host thread.  The copies it
+ * prefetches at the end of a call are used by the next call only if the plan's entries
+ * still name the same sources (blob, or file and offset); otherwise they are drained and
+ * the sequence restarts. */
 int nt_stream_layers(nt_streamer* st, const nt_model_plan* plan, int pos, float* h, void* ws, size_t ws_bytes,
                      void* compute, void* copy, nt_stream_stats* stats);
 

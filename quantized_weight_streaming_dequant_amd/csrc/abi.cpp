@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <errno.h>
+#include <sys/stat.h>
 #include <unistd.h>
 
 #include <mutex>
@@ -385,6 +386,14 @@ struct nt_streamer {
   bool bounce_recorded[2];
   const void* plan_layers;  // identity of the plan the sequence counters belong to
   std::vector<int> streamed;  // and its streamed, unskipped layers
+  // what each staging buffer's last copy was issued from (blob, or file and offset), so that a
+  // prefetch made from entries the caller has since changed is not used
+  struct Src {
+    const void* blob;
+    int tier, fd;
+    int64_t off;
+    bool operator==(const Src& o) const { return blob == o.blob && tier == o.tier && fd == o.fd && off == o.off; }
+  } src[2];
   int64_t c_run;    // next streamed-layer sequence number to run
   int64_t c_issue;  // next streamed-layer sequence number to copy
 };
@@ -669,6 +678,13 @@ static int check_plan(const nt_model_plan* plan, const nt_streamer* st) {
       if (!st->bounce[0]) return fail(NT_EINVAL, "layer %d is read from a file but the streamer has no bounce buffers", l);
       if ((size_t)plan->layout.blob_bytes > st->bounce_bytes)
         return fail(NT_EINVAL, "layer blob larger than the bounce buffers");
+      // the whole blob must lie inside the file now, so that a short read cannot stop the call
+      // after earlier layers were enqueued (only an I/O error or a file shrinking meanwhile can)
+      struct stat sb;
+      if (fstat(e.fd, &sb) != 0) return fail(NT_EHOSTMEM, "layer %d: fstat of its file failed (errno %d)", l, errno);
+      if (e.file_offset + plan->layout.blob_bytes > (int64_t)sb.st_size)
+        return fail(NT_EHOSTMEM, "layer %d: blob at offset %lld runs past the end of its file (%lld bytes)", l,
+                    (long long)e.file_offset, (long long)sb.st_size);
       continue;
     }
     if (!e.blob) return fail(NT_EINVAL, "layer %d has a null blob", l);
@@ -725,12 +741,22 @@ static bool read_blob(int fd, int64_t off, uint8_t* dst, size_t n, int t) {
   return true;
 }
 
+static nt_streamer::Src entry_src(const nt_layer_entry& e) {
+  nt_streamer::Src r;
+  r.tier = e.resident;
+  r.blob = e.resident == NT_TIER_FILE ? nullptr : e.blob;
+  r.fd = e.resident == NT_TIER_FILE ? e.fd : -1;
+  r.off = e.resident == NT_TIER_FILE ? e.file_offset : 0;
+  return r;
+}
+
 static int stream_issue(nt_streamer* st, const nt_model_plan* plan, const std::vector<int>& streamed, hipStream_t copy,
                         nt_stream_stats* stats) {
   const int64_t q = st->c_issue;
   const int b = (int)(q & 1);
   const int layer = streamed[(size_t)(q % (int64_t)streamed.size())];
   const nt_layer_entry& ent = plan->layers[layer];
+  st->src[b] = entry_src(ent);
   const size_t nbytes = (size_t)plan->layout.blob_bytes;
   hipError_t e;
   const void* src = ent.blob;
@@ -768,7 +794,14 @@ static int stream_layers_impl(nt_streamer* st, const nt_model_plan* plan, int po
   for (int l = 0; l < plan->n_layers; ++l)
     if (plan->layers[l].resident != NT_TIER_RESIDENT && !plan->layers[l].skip) streamed.push_back(l);
   if (st && !streamed.empty()) {
-    if (st->plan_layers != (const void*)plan->layers || st->streamed != streamed) {
+    // the copies in flight from the previous call (sequence numbers c_run .. c_issue - 1) must
+    // come from the entries as they are now
+    bool same = st->plan_layers == (const void*)plan->layers && st->streamed == streamed;
+    for (int64_t q = st->c_run; same && q < st->c_issue; ++q) {
+      const int layer = streamed[(size_t)(q % (int64_t)streamed.size())];
+      same = st->src[q & 1] == entry_src(plan->layers[layer]);
+    }
+    if (!same) {
       // a new plan: drain what the streamer had in flight, then restart its sequence
       for (int b = 0; b < 2; ++b) {
         (void)hipEventSynchronize(st->ready[b]);

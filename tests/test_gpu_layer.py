@@ -278,6 +278,121 @@ def test_token_step_matches_layer_calls():
         assert same_value(host(kd[l]), kcs[l]) and same_value(host(vd[l]), vcs[l])
 
 
+def decode_tokens_async(model, streamed, tok0, pos0, n_tokens, staging, sleep_compute=0, sleep_copy=0):
+    """n_tokens greedy tokens enqueued back to back with no host synchronisation between them;
+    each token's outputs are copied on the compute stream into per-token buffers.  Optional
+    bounded spin kernels (torch.cuda._sleep, in GPU clock cycles) at the start of each call on
+    the compute or the copy stream make that stream lag the other by about a millisecond."""
+    kcs, vcs = model.caches()
+    plan, keep = model.plan(kcs, vcs, streamed)
+    shp = tg.layer_shape(model.shape)
+    wsb = nt.nt_decode_token_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(model.shape.dim, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(model.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.tensor([tok0], dtype=torch.int32, device="cuda")
+    H = torch.zeros(n_tokens, model.shape.dim, dtype=torch.float32, device="cuda")
+    LG = torch.zeros(n_tokens, model.vocab, dtype=torch.float32, device="cuda")
+    T = torch.zeros(n_tokens, dtype=torch.int32, device="cuda")
+    compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), staging[0].numel()) if streamed else None
+    stats = nt.StreamStats()
+    torch.cuda.synchronize()
+    try:
+        for i in range(n_tokens):
+            if sleep_compute:
+                with torch.cuda.stream(compute):
+                    torch.cuda._sleep(sleep_compute)
+            if sleep_copy:
+                with torch.cuda.stream(copy):
+                    torch.cuda._sleep(sleep_copy)
+            nt.nt_decode_token(st, plan, model.head(), pos0 + i, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                               ws.data_ptr(), wsb, compute.cuda_stream, copy.cuda_stream, stats)
+            with torch.cuda.stream(compute):
+                H[i].copy_(h)
+                LG[i].copy_(logits)
+                T[i:i + 1].copy_(tok)
+        torch.cuda.synchronize()
+    finally:
+        if st is not None:
+            torch.cuda.synchronize()
+            nt.nt_stream_destroy(st)
+    return host(T).tolist(), host(H), host(LG), [host(k) for k in kcs], [host(v) for v in vcs]
+
+
+@pytest.mark.parametrize("sleep_compute,sleep_copy", [(0, 0), (4_000_000, 0), (0, 4_000_000)])
+def test_streaming_staging_reuse_under_delays(sleep_compute, sleep_copy):
+    """Five distinct streamed layers through two staging buffers (so each buffer holds a different
+    layer on every reuse), four tokens enqueued back to back without a host synchronisation, with
+    the compute stream held back (copies run ahead: only the buffers' free events keep them from
+    overwriting a layer before it ran) or the copy stream held back (only the ready events keep
+    compute from running a layer on the previous occupant's weights): bit for bit the resident run."""
+    say(f"staging reuse: 5 streamed layers, sleeps compute {sleep_compute} copy {sleep_copy} cycles")
+    m = Model(TINY, recipes.MIX_Q4_K_M, 6, vocab=1000, n_slots=24)
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    tok0 = synth.uniform_index(1000, 0, 83)
+    a = decode_tokens_async(m, set(), tok0, 24, 4, staging)
+    b = decode_tokens_async(m, {1, 2, 3, 4, 5}, tok0, 24, 4, staging, sleep_compute, sleep_copy)
+    assert a[0] == b[0]
+    assert same_value(a[1], b[1]) and same_value(a[2], b[2])
+    for x, y in zip(a[3] + a[4], b[3] + b[4]):
+        assert same_value(x, y)
+
+
+def test_stream_prefetch_from_changed_entries_is_not_used():
+    """The streamer prefetches the first streamed layers of the next token at the end of a call;
+    if the caller then points those entries at other blobs (same plan array, same streamed list),
+    the prefetched copies are dropped and the new blobs are used."""
+    say("streamer: changed plan entries after a prefetch")
+    m = Model(TINY, recipes.MIX_Q4_K_M, 4, vocab=1000, n_slots=24)
+    staging = [torch.empty(m.lay.nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    kcs, vcs = m.caches()
+    plan, keep = m.plan(kcs, vcs, {1, 3})
+    shp = tg.layer_shape(TINY)
+    wsb = nt.nt_decode_token_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(TINY.dim, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(1000, dtype=torch.float32, device="cuda")
+    tok = torch.tensor([7], dtype=torch.int32, device="cuda")
+    cs, cp = torch.cuda.Stream(), torch.cuda.Stream()
+    st = nt.nt_stream_create(staging[0].data_ptr(), staging[1].data_ptr(), m.lay.nbytes)
+    try:
+        nt.nt_decode_token(st, plan, m.head(), 24, tok.data_ptr(), logits.data_ptr(), h.data_ptr(), ws.data_ptr(),
+                           wsb, cs.cuda_stream, cp.cuda_stream)
+        torch.cuda.synchronize()
+        # swap the two streamed entries' blobs in place: layer 1 now runs layer 3's weights and back
+        b1, b3 = keep[1].blob, keep[3].blob
+        keep[1].blob, keep[3].blob = b3, b1
+        tok.fill_(11)
+        nt.nt_decode_token(st, plan, m.head(), 25, tok.data_ptr(), logits.data_ptr(), h.data_ptr(), ws.data_ptr(),
+                           wsb, cs.cuda_stream, cp.cuda_stream)
+        torch.cuda.synchronize()
+        got_h = host(h).copy()
+    finally:
+        torch.cuda.synchronize()
+        nt.nt_stream_destroy(st)
+    # the same two tokens with fresh caches, resident, the second with layers 1 and 3 swapped the same way
+    shp_layers = []
+    for l in range(4):
+        blob = m.blobs_dev[{1: 3, 3: 1}.get(l, l)]
+        mats = [blob[m.lay.offsets[n]:] for n in recipes.TENSORS]
+        shp_layers.append(tg.layer_weights(m.lay.fmt_list(), mats, blob[m.lay.offsets["attn_norm"]:].view(torch.float32),
+                                           blob[m.lay.offsets["ffn_norm"]:].view(torch.float32)))
+    kd2, vd2 = m.caches()
+    plan2, keep2 = m.plan(kd2, vd2, set())
+    t2 = torch.tensor([7], dtype=torch.int32, device="cuda")
+    h2 = torch.zeros(TINY.dim, dtype=torch.float32, device="cuda")
+    nt.nt_decode_token(None, plan2, m.head(), 24, t2.data_ptr(), logits.data_ptr(), h2.data_ptr(), ws.data_ptr(), wsb,
+                       stream(), stream())
+    t2.fill_(11)
+    nt.nt_embed_row(synth.Q4_K, 1000, TINY.dim, m.embd_d.data_ptr(), t2.data_ptr(), h2.data_ptr(), stream())
+    lws = torch.zeros(nt.nt_decode_layer_ws_bytes(shp), dtype=torch.uint8, device="cuda")
+    for l in range(4):
+        nt.nt_decode_layer(shp_layers[l], shp, 25, h2.data_ptr(), kd2[l].data_ptr(), vd2[l].data_ptr(), lws.data_ptr(),
+                           lws.numel(), stream())
+    assert same_value(host(h2), got_h)
+
+
 def test_layer_skip_equals_leaving_the_layers_out():
     """Skipped layers are not run: decoding with layers 1 and 2 of 4 skipped gives bit for bit
     what a plan listing only layers 0 and 3 gives, the skipped layers' caches are untouched,
