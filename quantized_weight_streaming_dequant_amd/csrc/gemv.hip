@@ -908,6 +908,17 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int s, const GemvSeg
   }
 }
 
+// Instruction-issue priority of this wave (0..3).  A SIMD's arbiter favours higher priority,
+// then older waves, so with equal static shares the waves that start later fall behind and
+// finish last; a wave that lowers its priority as its own remaining share shrinks lets the
+// waves that are behind take the issue slots, and the waves of a CU end closer together.
+__device__ __forceinline__ void set_wave_priority(int p) {
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // This wave's groups of R rows of one segment: group grp0 + k for k = wave_id, wave_id + W, ...
 // over the launch's W waves.  The loads of the next step (or of the next group's first
 // step) are in flight while the current step computes.  For the first segment the wave
@@ -977,8 +988,13 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
       ct = 0;
       ck += W;
     }
-    return ++item < n_items;
+    // priority from the remaining fraction of this segment's items: 3 for the first quarter,
+    // then 2, 1, 0
+    ++item;
+    set_wave_priority((4 * (n_items - item)) / (n_items + 1));
+    return item < n_items;
   };
+  set_wave_priority(3);
   if constexpr (DEPTH == 3) {
     for (;;) {
       if (!step(b0, b2)) break;
