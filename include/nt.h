@@ -100,6 +100,16 @@ int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w
  * (fp32 accumulation, scale factors applied per block). */
 int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream);
 
+/* Launch policy of the GEMVs (nt_gemv_q and every GEMV of the layer, token and head calls):
+ * a launch whose matrices hold at least min_weights weights in all (rows x cols summed over
+ * the matrices it covers) takes the streamed global->LDS path where the formats (Q8_0, Q4_0,
+ * Q6_K) and alignment allow it; a smaller one takes the register path.  Default 10^8, the
+ * measured crossover on MI355X (the streamed path costs more per launch and streams faster).
+ * Both paths compute the same products to the accuracy stated above.  Process-wide, read at
+ * every launch: set it while no other host thread enqueues GEMVs.  min_weights < 0 leaves the
+ * policy unchanged.  Returns the previous value. */
+int64_t nt_set_stream_min_weights(int64_t min_weights);
+
 /* Largest token count of nt_gemm_q. */
 #define NT_GEMM_MAX_TOK 8
 

@@ -72,6 +72,7 @@ _lib = None
 
 EXPORTS = [
     "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q", "nt_gemm_q", "nt_layer_cosine", "nt_read_probe",
+    "nt_set_stream_min_weights",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
     "nt_decode_layer_noalloc", "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
     "nt_stream_destroy", "nt_stream_set_bounce", "nt_stream_layers", "nt_decode_token", "nt_decode_token_ws_bytes", "nt_lm_head", "nt_decode_layer_k",
@@ -102,6 +103,7 @@ def load(path: str = LIB_PATH):
         "nt_gemm_q": ([i, i64, i64, i, vp, vp, vp, vp], i),
         "nt_layer_cosine": ([i64, vp, vp, vp, vp], i),
         "nt_read_probe": ([vp, i64, vp, vp], i),
+        "nt_set_stream_min_weights": ([i64], i64),
         "nt_rmsnorm": ([i64, vp, vp, f, vp, vp], i),
         "nt_rope": ([i, i, i, f, vp, vp], i),
         "nt_attn_decode": ([i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp], i),
@@ -180,6 +182,12 @@ def nt_layer_cosine(n, a, b, out, stream=None):
 
 def nt_read_probe(buf, nbytes, sink, stream=None):
     return _check(load().nt_read_probe(buf, nbytes, sink, stream))
+
+
+def nt_set_stream_min_weights(min_weights: int) -> int:
+    """Set the GEMV launch policy's streamed-path threshold (weights per launch; < 0 leaves it);
+    returns the previous value."""
+    return load().nt_set_stream_min_weights(min_weights)
 
 
 def nt_gemm_q(fmt, rows, cols, n_tok, blocks, x, y, stream=None):

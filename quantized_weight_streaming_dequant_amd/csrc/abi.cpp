@@ -571,6 +571,8 @@ int nt_layer_cosine(int64_t n, const float* a, const float* b, float* out, void*
   return e == hipSuccess ? NT_OK : hip_fail(e, "cosine launch");
 }
 
+int64_t nt_set_stream_min_weights(int64_t min_weights) { return gemv_set_stream_min_weights(min_weights); }
+
 int nt_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   if (bytes <= 0 || bytes % 16) return fail(NT_ESHAPE, "bytes must be a positive multiple of 16");
   if (!buf || !sink) return fail(NT_EINVAL, "null pointer");

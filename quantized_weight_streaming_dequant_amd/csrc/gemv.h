@@ -55,6 +55,10 @@ int gemv_groups(const GemvPlan& p, int rows);
 // launch's row groups over all segments.
 hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s);
 
+// The streamed path's launch threshold in weights per launch (w < 0: unchanged); returns the
+// previous value.
+int64_t gemv_set_stream_min_weights(int64_t w);
+
 // k-token GEMM: y[t][r] = sum_c W[r][c] x[t][c] for t < n_tok (1..GEMM_MAX_TOK), x [n_tok][cols],
 // y [n_tok][rows], all device fp32; one launch per column chunk (the weights are read once).
 constexpr int GEMM_MAX_TOK = 8;

@@ -2199,6 +2199,12 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
 
 // ---- streamed path
 static bool st_family(int fmt) { return fmt == FMT_Q4_K || fmt == FMT_Q6_K; }
+// launches with fewer weights take the register path (see gemv_stream_launch)
+static std::atomic<int64_t> g_st_min_weights{100000000};
+
+int64_t gemv_set_stream_min_weights(int64_t w) {
+  return w < 0 ? g_st_min_weights.load(std::memory_order_relaxed) : g_st_min_weights.exchange(w, std::memory_order_relaxed);
+}
 
 constexpr size_t ST_LDS_MAX = 160 * 1024 - 2048;  // dynamic LDS budget (static LDS on top)
 
@@ -2230,6 +2236,13 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) 
   // the kernel's segment layout: one matrix, gate + up, or q + k + v
   if (nseg != (epi == EPI_SWIGLU ? 2 : epi == EPI_QKV ? 3 : 1)) return hipErrorNotSupported;
   const bool kf = st_family(a.seg[0].fmt);
+  // The streamed path pays more per launch than the register path (its rings fill before the
+  // first product), which only its higher rate on large launches earns back: below 10^8
+  // weights per launch the register path is faster (measured: Q8_0 4096 x 4096 6.8 vs
+  // 10.9 us, Q6_K 8192 x 8192 20.2 vs 22.8 us; Q6_K 8192 x 28672 44.5 vs 57 us the other way).
+  int64_t weights = 0;
+  for (int i = 0; i < nseg; ++i) weights += (int64_t)a.seg[i].rows * a.cols;
+  if (weights < g_st_min_weights.load(std::memory_order_relaxed)) return hipErrorNotSupported;
   for (int i = 0; i < nseg; ++i) {
     const GemvSeg& g = a.seg[i];
     if (st_family(g.fmt) != kf) return hipErrorNotSupported;

@@ -222,3 +222,17 @@ def test_header_constants_match_binding():
         assert m and int(m.group(1)) == getattr(nt, name), name
     m = re.search(r"#define\s+NT_MAX_ROWS\s+\(1 << (\d+)\)", text)
     assert m and (1 << int(m.group(1))) == nt.NT_MAX_ROWS
+
+
+def test_stream_threshold_policy_round_trips():
+    """The GEMV launch policy's streamed-path threshold: default 10^8 weights, returned as the
+    previous value on every set, left alone by a negative argument (host state only)."""
+    prev = nt.nt_set_stream_min_weights(-1)
+    assert prev == 10 ** 8
+    try:
+        assert nt.nt_set_stream_min_weights(0) == 10 ** 8
+        assert nt.nt_set_stream_min_weights(-5) == 0
+        assert nt.nt_set_stream_min_weights(12345) == 0
+        assert nt.nt_set_stream_min_weights(-1) == 12345
+    finally:
+        nt.nt_set_stream_min_weights(prev)

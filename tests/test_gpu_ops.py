@@ -124,6 +124,31 @@ def test_gemv_matches_oracle(fmt, rows, cols):
     say(f"  worst rel err {worst:.2e}")
 
 
+# The streamed path at the shapes built for its edge cases (rows past a workgroup's task
+# range, a partial last column slice, single blocks): the launch policy sends launches under
+# 10^8 weights to the register path, so these force it with a threshold of 0.
+STREAMED_CASES = [(f, r, c) for f in (synth.Q8_0, synth.Q4_0, synth.Q6_K) for (r, c) in GEMV_SHAPES[f]
+                  if r * c < 10 ** 8] + [(f, 64, nt.NT_GEMV_MAX_COLS) for f in (synth.Q8_0, synth.Q4_0, synth.Q6_K)]
+
+
+@pytest.fixture
+def streamed_path():
+    prev = nt.nt_set_stream_min_weights(0)
+    yield
+    nt.nt_set_stream_min_weights(prev)
+
+
+@pytest.mark.parametrize("fmt,rows,cols", STREAMED_CASES)
+def test_gemv_streamed_path_matches_oracle(fmt, rows, cols, streamed_path):
+    say(f"gemv (streamed path) {NAMES[fmt]} {rows}x{cols}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=0, stream=200 + fmt)
+    x = synth.normal_f32(cols, seed=0, stream=300 + fmt)
+    y = gpu_gemv(fmt, rows, cols, blocks, x)
+    ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+    worst = check_rel(y, ref, nrm, what=f"{NAMES[fmt]} {rows}x{cols}")
+    say(f"  worst rel err {worst:.2e}")
+
+
 def gpu_gemm(fmt, rows, cols, n_tok, blocks, X):
     wb = dev(blocks)
     xd = dev(np.ascontiguousarray(X, dtype=np.float32).ravel())
