@@ -194,7 +194,7 @@ static int lm_head_enqueue(int fmt, int64_t n_vocab, int dim, const void* output
   hipError_t e;
   if (reset && (e = key_reset_launch(key, 1, st)) != hipSuccess) return hip_fail(e, "key reset launch");
   {
-    const GemvPlan p = gemv_plan(EPI_LOGITS, dim, 1 << fmt);
+    const GemvPlan p = gemv_plan(EPI_LOGITS, dim, 1 << fmt, (int)n_vocab);
     GemvArgs a = blank_args();
     a.x = h; a.gain = gain; a.eps = eps; a.cols = dim; a.nseg = 1;
     a.seg[0] = make_seg(output, fmt, (int)n_vocab, dim, 0);
@@ -242,7 +242,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
     if ((e = attn_launch(a, s.n_q_heads / s.n_kv_heads, st)) != hipSuccess) return hip_fail(e, "attention launch");
   }
   {  // a5: O GEMV + residual (h1 also kept in the workspace)
-    const GemvPlan p = gemv_plan(EPI_RESID, nq, 1 << w.fmt[NT_W_O]);
+    const GemvPlan p = gemv_plan(EPI_RESID, nq, 1 << w.fmt[NT_W_O], s.dim);
     GemvArgs a = blank_args();
     a.x = wo; a.cols = nq; a.nseg = 1;
     a.seg[0] = make_seg(w.w[NT_W_O], w.fmt[NT_W_O], s.dim, nq, 0);
@@ -254,7 +254,7 @@ int run_layer(const nt_layer_weights& w, const nt_layer_shape& s, int pos, float
   // a6-a8: RMSNorm prologue, paired gate/up GEMV, SwiGLU epilogue
   if ((e = ffn_up_launch(w, s, h, wa, st)) != hipSuccess) return hip_fail(e, "gate/up launch");
   {  // a9: down GEMV + residual
-    const GemvPlan p = gemv_plan(EPI_RESID, s.ffn_dim, 1 << w.fmt[NT_W_DOWN]);
+    const GemvPlan p = gemv_plan(EPI_RESID, s.ffn_dim, 1 << w.fmt[NT_W_DOWN], s.dim);
     GemvArgs a = blank_args();
     a.x = wa; a.cols = s.ffn_dim; a.nseg = 1;
     a.seg[0] = make_seg(w.w[NT_W_DOWN], w.fmt[NT_W_DOWN], s.dim, s.ffn_dim, 0);
@@ -428,7 +428,7 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
                 col_unit(fmt), NT_GEMV_MAX_COLS, (long long)rows, (long long)cols);
   if (!blocks || !x || !y) return fail(NT_EINVAL, "null pointer");
   if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return fail(NT_EALIGN, "blocks and x must be 16-byte aligned, y 4-byte");
-  const GemvPlan p = gemv_plan(EPI_STORE, (int)cols, 1 << fmt);
+  const GemvPlan p = gemv_plan(EPI_STORE, (int)cols, 1 << fmt, (int)rows);
   GemvArgs a = blank_args();
   a.x = x; a.cols = (int)cols; a.nseg = 1;
   a.seg[0] = make_seg(blocks, fmt, (int)rows, (int)cols, 0);

@@ -48,7 +48,8 @@ struct GemvPlan {
 };
 
 // Launch geometry for a format mix (bit f set for every format present) and shape.
-GemvPlan gemv_plan(int epi, int cols, int fmt_mask);
+// rows: the launch's matrix rows (0: unknown), for the choice of rows per work item.
+GemvPlan gemv_plan(int epi, int cols, int fmt_mask, int rows = 0);
 // Row groups (of rows_per_wave rows) a segment of `rows` rows makes under `plan`.
 int gemv_groups(const GemvPlan& p, int rows);
 // Enqueue.  fmt_mask: bit f set for every format present in the segments; n_groups: the
