@@ -132,6 +132,14 @@ struct XLimbs {
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
+// The same with c = 0, in the three-operand encoding with an inline-constant 0: the compiler
+// otherwise picks the accumulating two-operand form and zeroes the destination first, one
+// extra instruction per run of products.
+__device__ __forceinline__ int sdot4_0(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 // 256^(XL-1) (D1 + D2 / 256 (+ D3 / 65536)): the staged scale per 32 columns is stored as
 // s / 256^(XL-1), so that the product of the two is s (D1 + ...).  |Dk| < 2^20 here (at most
 // 32 codes of magnitude <= 128 times digits of magnitude <= 128), so 256 D1 + D2 fits an int.
@@ -155,10 +163,11 @@ __device__ __forceinline__ XRun x_run(const XLimbs& xs, int c) {
   }
   return r;
 }
-// d[l] += sum over the four bytes of q and of dword i of limb plane l
-__device__ __forceinline__ void dot_limbs(uint32_t q, const XRun& x, int i, int (&d)[XL]) {
+// d[l] += sum over the four bytes of q and of dword i of limb plane l (first: d[l] = that sum,
+// so that the first product of a run takes an immediate 0 instead of a zeroed register)
+__device__ __forceinline__ void dot_limbs(uint32_t q, const XRun& x, int i, int (&d)[XL], bool first = false) {
 #pragma unroll
-  for (int l = 0; l < XL; ++l) d[l] = sdot4(q, x.p[l][i], d[l]);
+  for (int l = 0; l < XL; ++l) d[l] = first ? sdot4_0(q, x.p[l][i]) : sdot4(q, x.p[l][i], d[l]);
 }
 template <int NR>
 __device__ __forceinline__ void zero_limbs(int (&d)[NR][XL]) {
@@ -262,7 +271,7 @@ struct Q8_0F {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int k = 0; k < NR; ++k) dot_limbs(q[k][4 * h + i], x, i, D[k]);
+        for (int k = 0; k < NR; ++k) dot_limbs(q[k][4 * h + i], x, i, D[k], h == 0 && i == 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     const float s = xs.sc[blk];
@@ -324,7 +333,8 @@ struct Q4_0F {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int k = 0; k < NR; ++k) dot_limbs(h == 0 ? (q[k][i] & m0f) : ((q[k][i] >> 4) & m0f), x, i, D[k]);
+        for (int k = 0; k < NR; ++k)
+          dot_limbs(h == 0 ? (q[k][i] & m0f) : ((q[k][i] >> 4) & m0f), x, i, D[k], h == 0 && i == 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     const float s = xs.sc[blk];
@@ -378,9 +388,9 @@ struct Q4_KF {
         for (int k = 0; k < NR; ++k) {
           const uint32_t v = (h & 1) ? raw[k].qb[i] : raw[k].qa[i];
           if (h < 2)
-            dot_limbs(v & m0f, x, i, da[k]);
+            dot_limbs(v & m0f, x, i, da[k], h == 0 && i == 0);
           else
-            dot_limbs((v >> 4) & m0f, x, i, db[k]);
+            dot_limbs((v >> 4) & m0f, x, i, db[k], h == 2 && i == 0);
         }
       // keep each run's LDS reads next to their use
       __builtin_amdgcn_sched_barrier(0);
@@ -459,9 +469,10 @@ struct Q5_KF {
           const uint32_t v = (h & 1) ? raw[k].qb[i] : raw[k].qa[i];
           const uint32_t hv = (h & 1) ? raw[k].hb[i] : raw[k].ha[i];
           if (h < 2)
-            dot_limbs(and_or(__builtin_amdgcn_alignbit(hv, hv, rot_a), m10, v & m0f), x, i, da[k]);
+            dot_limbs(and_or(__builtin_amdgcn_alignbit(hv, hv, rot_a), m10, v & m0f), x, i, da[k], h == 0 && i == 0);
           else
-            dot_limbs(and_or(__builtin_amdgcn_alignbit(hv, hv, rot_b), m10, (v >> 4) & m0f), x, i, db[k]);
+            dot_limbs(and_or(__builtin_amdgcn_alignbit(hv, hv, rot_b), m10, (v >> 4) & m0f), x, i, db[k],
+                      h == 2 && i == 0);
         }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1195,7 +1206,7 @@ __device__ __forceinline__ void kapply(const KDec<NR>& D, const XLimbs& xs, floa
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int k = 0; k < NR; ++k) dot_limbs(D.code[k][h][i], x, i, h < 2 ? da[k] : db[k]);
+      for (int k = 0; k < NR; ++k) dot_limbs(D.code[k][h][i], x, i, h < 2 ? da[k] : db[k], (h & 1) == 0 && i == 0);
   }
   const float sA = xs.sc[D.c0 >> 5], sB = xs.sc[(D.c0 >> 5) + 1];
   const float xa = xs.s16[D.c0 >> 4] + xs.s16[(D.c0 >> 4) + 1];
@@ -1727,7 +1738,7 @@ struct Q6K_S {
         const uint32_t code = and_or(__builtin_amdgcn_alignbit(Hw[k + 1], Hw[k], hsh), m30, lo);
         int(&d)[XL] = dg[2 * half + (k >> 2)];
 #pragma unroll
-        for (int l = 0; l < XL; ++l) d[l] = sdot4(code, xq[l][8 * half + k], d[l]);
+        for (int l = 0; l < XL; ++l) d[l] = (k & 3) == 0 ? sdot4_0(code, xq[l][8 * half + k]) : sdot4(code, xq[l][8 * half + k], d[l]);
       }
     }
     float r = 0.f;
