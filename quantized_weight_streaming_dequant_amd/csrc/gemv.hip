@@ -233,7 +233,7 @@ struct Q8_0F {
     bool ok;
     const int blk = block_of(cols, step, lane, ok);
     Raw r;
-    const uint8_t* A = rowp + (size_t)(ok ? blk : (blk & 1)) * 34;
+    const uint8_t* A = rowp + (uint32_t)(ok ? blk : (blk & 1)) * 34u;
     r.ph = uni((uint32_t)((uintptr_t)A & 3u));  // the same for every lane of the step
     const uint8_t* B = A - r.ph;
     const int o = r.ph ? 4 : 0;
@@ -295,7 +295,7 @@ struct Q4_0F {
     bool ok;
     const int blk = Q8_0F::block_of(cols, step, lane, ok);
     Raw r;
-    const uint8_t* A = rowp + (size_t)(ok ? blk : (blk & 1)) * 18;
+    const uint8_t* A = rowp + (uint32_t)(ok ? blk : (blk & 1)) * 18u;
     r.ph = uni((uint32_t)((uintptr_t)A & 3u));
     const uint8_t* B = A - r.ph;
     const u32x4 a = wld16(B + (r.ph ? 4 : 0));
@@ -358,11 +358,13 @@ struct Q4_KF {
     int sb = step * 16 + (lane >> 2);
     sb = sb < nsb ? sb : 0;
     const int g = lane & 3;
-    const uint8_t* p = rowp + (size_t)sb * 144;
+    // a 32-bit offset from the row's (wave-uniform) start: the loads take the scalar base and
+    // a vector offset, with no 64-bit address arithmetic per lane
+    const uint32_t off = (uint32_t)sb * 144u;
     Raw r;
-    r.hd = wld16(p);
-    r.qa = wld16(p + 16 + 32 * g);
-    r.qb = wld16(p + 32 + 32 * g);
+    r.hd = wld16(rowp + off);
+    r.qa = wld16(rowp + (off + 16u + 32u * (uint32_t)g));
+    r.qb = wld16(rowp + (off + 32u + 32u * (uint32_t)g));
     return r;
   }
   template <int NR>
@@ -436,7 +438,7 @@ struct Q5_KF {
     int sb = step * 16 + (lane >> 2);
     sb = sb < nsb ? sb : 0;
     const int g = lane & 3;
-    const uint8_t* p = rowp + (size_t)sb * 176;
+    const uint8_t* p = rowp + (uint32_t)sb * 176u;
     Raw r;
     r.hd = wld16(p);
     r.ha = wld16(p + 16);
@@ -528,7 +530,7 @@ struct Q6_KF {
     bool ok;
     const int sb = sb_of(cols, step, lane, ok);
     const int e = lane & 7, hh = e >> 2, tp = (e >> 1) & 1, half = e & 1;
-    const uint8_t* A = rowp + (size_t)(ok ? sb : (sb & 1)) * 210;
+    const uint8_t* A = rowp + (uint32_t)(ok ? sb : (sb & 1)) * 210u;
     Raw r;
     r.ph = uni((uint32_t)((uintptr_t)A & 3u));  // the same for every lane of the step
     const uint8_t* B = A - r.ph;                // 4-byte aligned
@@ -621,7 +623,7 @@ struct FloatF {
     for (int i = 0; i < 4; ++i) {
       int c = col(step, i, lane);
       c = c < cols ? c : 0;  // past the row end: reread its start (dropped)
-      r.v[i] = wld16(rowp + (size_t)c * (H ? 2 : 4));
+      r.v[i] = wld16(rowp + (uint32_t)c * (H ? 2u : 4u));
     }
     return r;
   }
