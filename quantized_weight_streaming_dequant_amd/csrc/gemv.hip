@@ -1667,6 +1667,10 @@ constexpr int ST_MAX_WAVES = 16;
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, NT_STREAM_CPOL);
 }
+// the same with a cached read (data that other workgroups read too)
+__device__ __forceinline__ void dma16c(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
 __device__ __forceinline__ uint32_t lds4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 __device__ __forceinline__ u32x4 lds16a(const uint8_t* p) {
   const u32x4a16 v = *reinterpret_cast<const u32x4a16*>(p);
@@ -1810,6 +1814,7 @@ struct StreamArgs {
   int tpw;         // tasks per workgroup (even)
   int ns;          // column slices
   int rsub;        // waves per slice
+  int xring;       // 1: the x slice is staged through the slice's rings (they hold a whole slice)
 };
 
 // Per-wave constants of the launch's segments (one for STORE / RESID / LOGITS, gate and
@@ -1921,10 +1926,45 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
   __syncthreads();
 
   // ---- x slice into registers, issued first so that it arrives first
-  const int c0 = KF ? sl * ST_SLICE_COLS_K + 64 * lane : sl * ST_SLICE_COLS_B + 32 * lane;
+  constexpr int SC = KF ? ST_SLICE_COLS_K : ST_SLICE_COLS_B;  // columns of a slice
+  constexpr int RB = D * SLOT;                                 // ring bytes of a wave
+  const int c0 = sl * SC + XN * lane;
   const bool xvalid = c0 < a.cols;
   float x[XN];
-  {
+  if (sa.xring) {
+    // A lane's columns are XN consecutive floats, so lane-contiguous loads of them touch 64
+    // lines per instruction and occupy the CU's load path ~16 times longer than loads of
+    // whole lines; the later waves of a workgroup then wait microseconds for x.  Instead
+    // the slice goes through the slice's rings first (before any weight transfer): each
+    // wave moves its share with the global->LDS path, 1 KiB of whole lines per instruction,
+    // in a swizzled order (float4 f of a block of 16 at position (f + block) mod 16), so
+    // that the lanes' 16-byte reads of their own columns below meet no bank conflicts.
+    constexpr int NF = SC / 4;                   // float4 of a slice (a multiple of 64)
+    const int lim = (a.cols - sl * SC) / 4;      // valid float4 of this slice
+    const float* xsl = a.x + (size_t)sl * SC;
+#pragma unroll
+    for (int k = 0; k < RB / 1024; ++k) {
+      if (sub * (RB / 16) + 64 * k < NF) {       // wave-uniform
+        const int sidx = sub * (RB / 16) + 64 * k + lane;  // slot of this lane's float4
+        const int blk = sidx >> 4;
+        int f = 16 * blk + (((sidx & 15) - blk) & 15);
+        f = f < lim ? f : 0;                     // past the last column: a valid address, unused
+        dma16c(xsl + 4 * f, ring + 1024 * k);
+      }
+    }
+    wait_vm<0>();
+    __syncthreads();
+    const uint8_t* lds0 = reinterpret_cast<const uint8_t*>(smem4);
+#pragma unroll
+    for (int q = 0; q < XN / 4; ++q) {
+      const int f = lane * (XN / 4) + q;
+      const int sidx = (f & ~15) | ((f + (f >> 4)) & 15);
+      const int so = sidx / (RB / 16);           // the slice's wave whose ring holds it
+      const float4 v = *reinterpret_cast<const float4*>(lds0 + (size_t)(so * sa.ns + sl) * RB + (sidx % (RB / 16)) * 16);
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+    __syncthreads();  // every ring read before the weight transfers below refill it
+  } else {
     const float4* xp = reinterpret_cast<const float4*>(a.x + (xvalid ? c0 : 0));
 #pragma unroll
     for (int i = 0; i < XN / 4; ++i) {
@@ -2343,6 +2383,8 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) 
     --rsub;
   }
   sa.rsub = rsub;
+  // x through the rings when a slice's rings hold the whole slice (fp32)
+  sa.xring = ((size_t)rsub * d * slot_bytes >= (size_t)4 * slice_cols) ? 1 : 0;
   const int nw = sa.ns * rsub;
   const size_t lds = (size_t)nw * d * slot_bytes + part;
   switch (epi) {
