@@ -1814,7 +1814,8 @@ struct StreamArgs {
   int tpw;         // tasks per workgroup (even)
   int ns;          // column slices
   int rsub;        // waves per slice
-  int xring;       // 1: the x slice is staged through the slice's rings (they hold a whole slice)
+  int xring;       // 1: the x slice is staged through the slice's rings (they hold a whole slice);
+                   // 2: the x slice and the gain slice (they hold both)
 };
 
 // Per-wave constants of the launch's segments (one for STORE / RESID / LOGITS, gate and
@@ -1897,6 +1898,23 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// A lane's XN floats (its own columns, XN / 4 float4 from float4 lane XN / 4 of the vector)
+// from the slice's rings, where float4 f of a vector sits in slot base + s(f), s(f) = f with
+// its position in its block of 16 rotated by the block index (so that the 16-byte reads of
+// 16 consecutive lanes fall on distinct banks); slot s is in the ring of the slice's wave
+// s / (RB / 16), at byte 16 (s mod (RB / 16)).
+template <int XN, int RB>
+__device__ __forceinline__ void x_from_rings(float (&x)[XN], const uint8_t* lds0, int base, int lane, int sl, int ns) {
+#pragma unroll
+  for (int q = 0; q < XN / 4; ++q) {
+    const int f = lane * (XN / 4) + q;
+    const int sidx = base + ((f & ~15) | ((f + (f >> 4)) & 15));
+    const int so = sidx / (RB / 16);
+    const float4 v = *reinterpret_cast<const float4*>(lds0 + (size_t)(so * ns + sl) * RB + (sidx % (RB / 16)) * 16);
+    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+  }
+}
+
 template <int KF, int EPI, int D, int NI>
 __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const StreamArgs sa) {
   constexpr int XN = KF ? 64 : 32;   // x values per lane
@@ -1939,29 +1957,41 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
     // wave moves its share with the global->LDS path, 1 KiB of whole lines per instruction,
     // in a swizzled order (float4 f of a block of 16 at position (f + block) mod 16), so
     // that the lanes' 16-byte reads of their own columns below meet no bank conflicts.
+    // With a gain (xring 2) its slice follows x's in the rings, and the norm is applied
+    // below before the rings are refilled.
     constexpr int NF = SC / 4;                   // float4 of a slice (a multiple of 64)
     const int lim = (a.cols - sl * SC) / 4;      // valid float4 of this slice
-    const float* xsl = a.x + (size_t)sl * SC;
+    const int nslots = sa.xring == 2 ? 2 * NF : NF;
 #pragma unroll
     for (int k = 0; k < RB / 1024; ++k) {
-      if (sub * (RB / 16) + 64 * k < NF) {       // wave-uniform
+      if (sub * (RB / 16) + 64 * k < nslots) {   // wave-uniform
         const int sidx = sub * (RB / 16) + 64 * k + lane;  // slot of this lane's float4
-        const int blk = sidx >> 4;
-        int f = 16 * blk + (((sidx & 15) - blk) & 15);
+        const int vec = sidx >= NF ? 1 : 0;      // 0: x, 1: gain (wave-uniform: NF % 64 == 0)
+        const int sv = sidx - vec * NF;
+        const int blk = sv >> 4;
+        int f = 16 * blk + (((sv & 15) - blk) & 15);
         f = f < lim ? f : 0;                     // past the last column: a valid address, unused
-        dma16c(xsl + 4 * f, ring + 1024 * k);
+        dma16c((vec ? a.gain : a.x) + (size_t)sl * SC + 4 * f, ring + 1024 * k);
       }
     }
     wait_vm<0>();
     __syncthreads();
-    const uint8_t* lds0 = reinterpret_cast<const uint8_t*>(smem4);
+    x_from_rings<XN, RB>(x, reinterpret_cast<const uint8_t*>(smem4), 0, lane, sl, sa.ns);
+    if (sa.xring == 2) {
+      // the norm's scale from the sum of squares over all slices, then the gain from the rings
+      float q = 0.f;
 #pragma unroll
-    for (int q = 0; q < XN / 4; ++q) {
-      const int f = lane * (XN / 4) + q;
-      const int sidx = (f & ~15) | ((f + (f >> 4)) & 15);
-      const int so = sidx / (RB / 16);           // the slice's wave whose ring holds it
-      const float4 v = *reinterpret_cast<const float4*>(lds0 + (size_t)(so * sa.ns + sl) * RB + (sidx % (RB / 16)) * 16);
-      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+      for (int i = 0; i < XN; ++i) q += x[i] * x[i];
+      q = wave_sum(xvalid ? q : 0.f);
+      if (sub == 0 && lane == 0) ssq[sl] = q;
+      __syncthreads();
+      float tot = 0.f;
+      for (int i = 0; i < sa.ns; ++i) tot += ssq[i];
+      const float scale = 1.0f / sqrtf(tot / (float)a.cols + a.eps);
+      float g[XN];
+      x_from_rings<XN, RB>(g, reinterpret_cast<const uint8_t*>(smem4), NF, lane, sl, sa.ns);
+#pragma unroll
+      for (int i = 0; i < XN; ++i) x[i] = x[i] * scale * g[i];
     }
     __syncthreads();  // every ring read before the weight transfers below refill it
   } else {
@@ -1981,8 +2011,8 @@ __global__ __launch_bounds__(ST_MAX_WAVES * 64) void gemv_stream_kernel(const St
     st_issue<EPI, NI>(sc, min(tslot[d], t1 - 1), lane, ring + d * SLOT);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // ---- RMSNorm prologue: scale from the sum of squares over all slices
-  if (a.gain) {
+  // ---- RMSNorm prologue: scale from the sum of squares over all slices (unless done above)
+  if (a.gain && sa.xring != 2) {
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < XN; ++i) q += x[i] * x[i];
@@ -2384,7 +2414,10 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) 
   }
   sa.rsub = rsub;
   // x through the rings when a slice's rings hold the whole slice (fp32)
-  sa.xring = ((size_t)rsub * d * slot_bytes >= (size_t)4 * slice_cols) ? 1 : 0;
+  {
+    const size_t cap = (size_t)rsub * d * slot_bytes, vec = (size_t)4 * slice_cols;
+    sa.xring = (a.gain && cap >= 2 * vec) ? 2 : (cap >= vec ? 1 : 0);
+  }
   const int nw = sa.ns * rsub;
   const size_t lds = (size_t)nw * d * slot_bytes + part;
   switch (epi) {
