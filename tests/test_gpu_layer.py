@@ -119,6 +119,21 @@ def test_layer_small_shapes(mix, pos):
     run_layer_and_check(SMALL, mix, pos=pos, n_slots=96)
 
 
+# Every launch that the streamed path can take, forced onto it (the launch policy otherwise keeps
+# launches under 10^8 weights on the register path): its q/k/v + RoPE, gate/up + SwiGLU and
+# residual epilogues, the x and gain slices staged through its rings, partial column slices
+# (dim 1024 against 4096- or 2048-column slices) and full ones (the 8B shape).
+@pytest.mark.parametrize("shape,mix,pos", [(SMALL, recipes.MIX_Q8_0, 50), (SMALL, recipes.MIX_Q6_K, 95),
+                                           (SMALL, {n: synth.Q4_0 for n in recipes.TENSORS}, 17),
+                                           (SMALL, recipes.MIX_Q4_K_M, 3), (recipes.LLAMA3_8B, recipes.MIX_Q8_0, 700)])
+def test_layer_streamed_path_forced(shape, mix, pos):
+    prev = nt.nt_set_stream_min_weights(0)
+    try:
+        run_layer_and_check(shape, mix, pos=pos, n_slots=min(shape.max_ctx, 1000))
+    finally:
+        nt.nt_set_stream_min_weights(prev)
+
+
 @pytest.mark.parametrize("shape,mix", [(SMALL, recipes.MIX_Q4_K_M), (recipes.LLAMA31_70B, recipes.MIX_Q4_K_M),
                                        (recipes.LLAMA3_8B, recipes.MIX_Q8_0)])
 def test_ffn_up_entry_matches_layer(shape, mix):
