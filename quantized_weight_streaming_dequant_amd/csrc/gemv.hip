@@ -375,12 +375,16 @@ struct Q4_KF {
     if (sb >= nsb) return;
     const int g = lane & 3;
     const int c0 = (sb << 8) + (g << 6);
-    const uint32_t m0f = vreg(0x0F0F0F0Fu);
+    const uint32_t m0f = vreg(0x0F0F0F0Fu), mf0 = 0xF0F0F0F0u, m80 = 0x80808080u;
     int da[NR][XL], db[NR][XL];
     zero_limbs(da);
     zero_limbs(db);
     // run h of 16 columns at c0 + 16 h: low nibbles of qa (h = 0) and qb (h = 1) belong to
-    // sub-block 2g, high nibbles of qa (h = 2) and qb (h = 3) to sub-block 2g + 1
+    // sub-block 2g, high nibbles of qa (h = 2) and qb (h = 3) to sub-block 2g + 1.  A high
+    // nibble n is used in place, as the signed byte (16 n) ^ 0x80 = 16 n - 128 (one
+    // three-input bit operation instead of a shift and a mask), so db holds 16 (sum n X) -
+    // 128 (sum X) over the sub-block; the 128 (sum X) part is restored from the fp32 sum of
+    // x below.
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const XRun x = x_run(xs, c0 + 16 * h);
@@ -392,7 +396,7 @@ struct Q4_KF {
           if (h < 2)
             dot_limbs(v & m0f, x, i, da[k], h == 0 && i == 0);
           else
-            dot_limbs((v >> 4) & m0f, x, i, db[k], h == 2 && i == 0);
+            dot_limbs((v & mf0) ^ m80, x, i, db[k], h == 2 && i == 0);
         }
       // keep each run's LDS reads next to their use
       __builtin_amdgcn_sched_barrier(0);
@@ -400,6 +404,7 @@ struct Q4_KF {
     const float sA = xs.sc[c0 >> 5], sB = xs.sc[(c0 >> 5) + 1];
     const float xa = xs.s16[c0 >> 4] + xs.s16[(c0 >> 4) + 1];
     const float xb = xs.s16[(c0 >> 4) + 2] + xs.s16[(c0 >> 4) + 3];
+    const float sB16 = sB * 0.0625f, xb8 = 8.f * xb;
     // 6-bit scales and mins of sub-blocks 2g, 2g+1 gathered as the bytes [sc_a, sc_b, m_a, m_b]
     // from the scale words Y (bytes 4..7), Z (8..11), W (12..15), p = 2 (g & 1):
     //  sub-blocks 0..3: scale = bits 0..5 of Y byte p (+1), min = bits 0..5 of Z byte p (+1);
@@ -416,8 +421,12 @@ struct Q4_KF {
       const uint32_t lo = upper ? __builtin_amdgcn_perm(W >> 4, W, sel) : yz;  // [W p, W p+1, W p>>4, W p+1>>4]
       const uint32_t sm = and_or(yz >> 2, mtop, lo & mlow);
       const float d = h2f(raw[k].hd.x), dmin = h2f(raw[k].hd.x >> 16);
+      // sub-block 2g + 1: sB (sum n X) = (sB / 16) db + 8 sB (sum X), and sB (sum X) is the
+      // sum of the staged x, within rounding of the fp32 sum xb
+      const float sb = d * ub1(sm);
       acc[k] += (d * sA * ub0(sm)) * limb_sum(da[k]);
-      acc[k] += (d * sB * ub1(sm)) * limb_sum(db[k]);
+      acc[k] += (sb * sB16) * limb_sum(db[k]);
+      acc[k] += sb * xb8;
       acc[k] -= dmin * (ub2(sm) * xa + ub3(sm) * xb);
     }
   }
