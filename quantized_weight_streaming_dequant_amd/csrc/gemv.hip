@@ -680,16 +680,6 @@ constexpr int GEMV_DEPTH = EPI == EPI_QKV ? NT_GEMV_DEPTH_QKV : EPI == EPI_SWIGL
 template <int EPI>
 constexpr int GEMV_ROWS = (EPI == EPI_SWIGLU) ? 1 : (EPI == EPI_QKV) ? 2 : NT_GEMV_ROWS;
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int i = 0; i < nw; ++i) t += red[i];
-  return t;
-}
-
 // Power-of-two staging scale of a 32-column block whose largest |x| has the bit pattern mb
 // (of a non-negative float, NaN included): the smallest s = 2^e with max |x| / s <= 127.
 // Returns su = s / 256^(XL-1) (the stored scale) and k = 1 / su, which maps x to its
@@ -782,16 +772,19 @@ __device__ __forceinline__ void stage_group(const XLimbs& xs, int gi, const floa
     *reinterpret_cast<u32x4a16*>(xs.q + l * xs.plane + xq_off(gi * 16)) = u32x4a16{w[l][0], w[l][1], w[l][2], w[l][3]};
 }
 
-// Stage x (optionally RMS-normalised) into LDS: XL limb planes, the scale of every 32
-// columns and the fp32 sum of every 16.  Every thread of the workgroup calls this exactly
-// once, with what stage_x_load returned.  A thread takes 16 columns per round, the first
-// round from the preloaded registers; threads 2t and 2t+1 (one DPP quad pair) share a scale.
-// cols / 16 is even and the block size a multiple of 64, so both threads of a pair run the
-// same rounds.
-__device__ __forceinline__ void stage_x(const GemvArgs& a, const XPre& pre, const XLimbs& xs, float* red) {
+// Stage x into LDS: XL limb planes, the scale of every 32 columns and the fp32 sum of
+// every 16.  Every thread of the workgroup calls this exactly once, with what stage_x_load
+// returned.  A thread takes 16 columns per round, the first round from the preloaded
+// registers; threads 2t and 2t+1 (one DPP quad pair) share a scale.  cols / 16 is even and
+// the block size a multiple of 64, so both threads of a pair run the same rounds.
+// With a gain the launch computes W (r x * g) for the RMSNorm factor r = 1 / sqrt(mean(x^2)
+// + eps): x * g is staged as it arrives and r, a scalar per token, multiplies each row's dot
+// product instead (W (r v) = r (W v); the limbs' power-of-two scale per 32 columns makes
+// their precision independent of r), so the limbs do not wait for the workgroup's sum of
+// squares.  Returns r (1 without a gain), valid after the staging's closing barrier.
+__device__ __forceinline__ float stage_x(const GemvArgs& a, const XPre& pre, const XLimbs& xs, float* red) {
   const int cols = a.cols, ng = cols >> 4;
   const int g0 = (int)threadIdx.x;
-  float scale = 1.f;
   if (a.gain) {
     float ss = 0.f;
     if (g0 < ng) {
@@ -807,8 +800,9 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, const XPre& pre, cons
         ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
       }
     }
-    ss = block_sum(ss, red);
-    scale = 1.0f / sqrtf(ss / (float)cols + a.eps);
+    // this wave's part of the sum of squares; the waves' parts are added after the barrier
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   }
   if (g0 < ng) {
     float v[16];
@@ -816,8 +810,7 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, const XPre& pre, cons
     for (int i = 0; i < 4; ++i) {
       float4 t = pre.v[i];
       if (a.gain) {
-        t.x = t.x * scale * pre.g[i].x; t.y = t.y * scale * pre.g[i].y;
-        t.z = t.z * scale * pre.g[i].z; t.w = t.w * scale * pre.g[i].w;
+        t.x *= pre.g[i].x; t.y *= pre.g[i].y; t.z *= pre.g[i].z; t.w *= pre.g[i].w;
       }
       v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
     }
@@ -831,13 +824,17 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, const XPre& pre, cons
       float4 t = src[i];
       if (a.gain) {
         const float4 g = reinterpret_cast<const float4*>(a.gain + gi * 16)[i];
-        t.x = t.x * scale * g.x; t.y = t.y * scale * g.y; t.z = t.z * scale * g.z; t.w = t.w * scale * g.w;
+        t.x *= g.x; t.y *= g.y; t.z *= g.z; t.w *= g.w;
       }
       v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
     }
     stage_group(xs, gi, v);
   }
   __syncthreads();
+  if (!a.gain) return 1.f;
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
+  return 1.0f / sqrtf(t / (float)cols + a.eps);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
@@ -950,7 +947,7 @@ __device__ __forceinline__ void set_wave_priority(int p) {
 // (unrolled over the ring, so that no buffer is copied).
 template <typename F, int R, int EPI, int DEPTH, bool STAGE>
 __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, int wid, int W, const XLimbs& xs,
-                                            float* red, unsigned long long& best, const float2* rope,
+                                            float* red, float& xscale, unsigned long long& best, const float2* rope,
                                             const XPre xpre) {
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * R : R;
   typedef typename F::Raw Raw;
@@ -986,7 +983,7 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
   // that the count in flight is static and the staging's waits leave these loads in flight
   issue(b0);
   if (DEPTH == 3) issue(b1);
-  if constexpr (STAGE) stage_x(a, xpre, xs, red);
+  if constexpr (STAGE) xscale = stage_x(a, xpre, xs, red);
   if (n_items == 0) return;
   float acc[NR];
 #pragma unroll
@@ -1001,7 +998,7 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
     F::template fma<NR>(cur, a.cols, ct, lane, xs, acc);
     if (ct == nsteps - 1) {
 #pragma unroll
-      for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
+      for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]) * xscale;
       epilogue<R, EPI>(a, s, sg, ck * R, lane, acc, best, rope);
 #pragma unroll
       for (int j = 0; j < NR; ++j) acc[j] = 0.f;
@@ -1039,29 +1036,29 @@ constexpr int FMTS_Q5K_Q5K_Q6K = 1 << 9;
 // Segment s with its format's work loop (STAGE: the first segment, which stages x).
 template <int FMTMASK, int R, int EPI, bool STAGE>
 __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int wid, int W, const XLimbs& xs,
-                                        float* red, unsigned long long& best, const float2* rope, const XPre xpre) {
+                                        float* red, float& xscale, unsigned long long& best, const float2* rope, const XPre xpre) {
   constexpr int D = GEMV_DEPTH<EPI>;
   switch (a.seg[s].fmt) {
     case FMT_Q8_0:
-      if constexpr ((FMTMASK >> FMT_Q8_0) & 1) run_segment<Q8_0F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      if constexpr ((FMTMASK >> FMT_Q8_0) & 1) run_segment<Q8_0F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     case FMT_Q4_0:
-      if constexpr ((FMTMASK >> FMT_Q4_0) & 1) run_segment<Q4_0F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      if constexpr ((FMTMASK >> FMT_Q4_0) & 1) run_segment<Q4_0F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     case FMT_Q4_K:
-      if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     case FMT_Q5_K:
-      if constexpr ((FMTMASK >> FMT_Q5_K) & 1) run_segment<Q5_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      if constexpr ((FMTMASK >> FMT_Q5_K) & 1) run_segment<Q5_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     case FMT_F16:
-      if constexpr ((FMTMASK >> FMT_F16) & 1) run_segment<F16F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      if constexpr ((FMTMASK >> FMT_F16) & 1) run_segment<F16F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     case FMT_F32:
-      if constexpr ((FMTMASK >> FMT_F32) & 1) run_segment<F32F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      if constexpr ((FMTMASK >> FMT_F32) & 1) run_segment<F32F, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     default:
-      if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, best, rope, xpre);
+      if constexpr ((FMTMASK >> FMT_Q6_K) & 1) run_segment<Q6_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
   }
 }
@@ -1090,6 +1087,7 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   const int wid = (int)blockIdx.x * NW + wave;
   const int W = (int)gridDim.x * NW;
   unsigned long long best = 0;
+  float xscale = 1.f;  // the RMSNorm factor, set by the staging of x (first segment)
   // RoPE table for this position (visible after the barrier inside the staging of x)
   __shared__ float2 rope[64];
   if constexpr (EPI == EPI_QKV) {
@@ -1103,13 +1101,13 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
     // are allocated per segment rather than for every format at every segment
     constexpr int D = GEMV_DEPTH<EPI>;
     using FK = std::conditional_t<FMTMASK == FMTS_Q4K_Q4K_Q6K, Q4_KF, Q5_KF>;
-    run_segment<FK, R, EPI, D, true>(a, 0, lane, wid, W, xs, red, best, rope, xpre);
-    run_segment<FK, R, EPI, D, false>(a, 1, lane, wid, W, xs, red, best, rope, XPre{});
-    run_segment<Q6_KF, R, EPI, D, false>(a, 2, lane, wid, W, xs, red, best, rope, XPre{});
+    run_segment<FK, R, EPI, D, true>(a, 0, lane, wid, W, xs, red, xscale, best, rope, xpre);
+    run_segment<FK, R, EPI, D, false>(a, 1, lane, wid, W, xs, red, xscale, best, rope, XPre{});
+    run_segment<Q6_KF, R, EPI, D, false>(a, 2, lane, wid, W, xs, red, xscale, best, rope, XPre{});
   } else {
-    run_any<FMTMASK, R, EPI, true>(a, 0, lane, wid, W, xs, red, best, rope, xpre);
+    run_any<FMTMASK, R, EPI, true>(a, 0, lane, wid, W, xs, red, xscale, best, rope, xpre);
     const int nseg = (EPI == EPI_SWIGLU) ? 1 : a.nseg;
-    for (int s = 1; s < nseg; ++s) run_any<FMTMASK, R, EPI, false>(a, s, lane, wid, W, xs, red, best, rope, XPre{});
+    for (int s = 1; s < nseg; ++s) run_any<FMTMASK, R, EPI, false>(a, s, lane, wid, W, xs, red, xscale, best, rope, XPre{});
   }
   if constexpr (EPI == EPI_LOGITS) {
     // one atomic per workgroup: lane 0 of each wave holds the wave's best key

@@ -250,6 +250,25 @@ def test_gemv_outlier_activations(fmt, kind):
     say(f"  worst rel err {worst:.2e}")
 
 
+@pytest.mark.parametrize("mean", [50.0, -3.0])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_offset_activations(fmt, mean):
+    """x = mean + N(0, 1): each block's sum of x is large next to the spread of x, which is
+    what the kernels scale and subtract where they restore a bias from that sum (the Q4_K
+    high nibbles taken as the bytes 16 n - 128, the Q4_0 codes' offset of 8, the K formats'
+    minimum terms).  Held to the same limb-precision bound as the outliers."""
+    rows, cols = 512, 8192
+    say(f"gemv offset x mean {mean} {NAMES[fmt]}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=5, stream=510 + fmt)
+    x = synth.normal_f32(cols, seed=5, stream=610 + fmt, mean=mean)
+    y = gpu_gemv(fmt, rows, cols, blocks, x)
+    ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+    worst = check_rel(y, ref, nrm, what=f"{NAMES[fmt]} mean {mean}")
+    if fmt not in (synth.F16, synth.F32):
+        worst = check_rel(y, ref, nrm, tol=1e-5, what=f"{NAMES[fmt]} mean {mean} (limb precision)")
+    say(f"  worst rel err {worst:.2e}")
+
+
 @pytest.mark.parametrize("fmt", [synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.Q8_0])
 @pytest.mark.parametrize("kind", list(OUTLIER_KINDS))
 def test_gemm_outlier_activations(kind, fmt):
