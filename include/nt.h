@@ -103,8 +103,12 @@ int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const flo
 /* Launch policy of the GEMVs (nt_gemv_q and every GEMV of the layer, token and head calls):
  * a launch whose matrices hold at least min_weights weights in all (rows x cols summed over
  * the matrices it covers) takes the streamed global->LDS path where the formats (Q8_0, Q4_0,
- * Q6_K) and alignment allow it; a smaller one takes the register path.  Default 10^8, the
- * measured crossover on MI355X (the streamed path costs more per launch and streams faster).
+ * Q6_K) and alignment allow it, and so does one of at least min_weights / 8 weights whose
+ * register-path waves would each run 7 or more work items in a row (long rows over few row
+ * groups, which the streamed path splits over several waves); the others take the register
+ * path.  Default 10^8, the measured crossover on MI355X (the streamed path costs more per
+ * launch and streams faster).  0 streams every launch the formats allow; a value no launch
+ * reaches (say 2^62) keeps every launch on the register path.
  * Both paths compute the same products to the accuracy stated above.  Process-wide, read at
  * every launch: set it while no other host thread enqueues GEMVs.  min_weights < 0 leaves the
  * policy unchanged.  Returns the previous value. */

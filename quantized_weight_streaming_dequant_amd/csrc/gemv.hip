@@ -216,7 +216,7 @@ struct Q8_0F {
     uint32_t e;
     uint32_t ph;
   };
-  static __device__ __forceinline__ int steps(int cols) {
+  static __host__ __device__ __forceinline__ int steps(int cols) {
     const int nb = cols >> 5;
     return ((nb + 1) / 2 + 63) / 64 + (nb / 2 + 63) / 64;
   }
@@ -522,7 +522,7 @@ struct Q6_KF {
     uint32_t d;
     uint32_t ph;
   };
-  static __device__ __forceinline__ int steps(int cols) {
+  static __host__ __device__ __forceinline__ int steps(int cols) {
     const int nsb = cols >> 8;
     return ((nsb + 1) / 2 + 7) / 8 + (nsb / 2 + 7) / 8;
   }
@@ -2346,20 +2346,43 @@ static hipError_t st_dispatch(bool kf, int ni, int d, const StreamArgs& sa, int 
   return d == 3 ? st_launch<0, EPI, 3, 3>(sa, grid, nw, lds, s) : st_launch<0, EPI, 2, 3>(sa, grid, nw, lds, s);
 }
 
+// Work items that each busy wave of the register path runs one after another for this launch
+// (row groups per wave, the chip holding 16 waves per CU, times steps per row; 0 for the
+// formats the streamed path does not take).
+static int reg_depth(int fmt, int cols, int n_groups) {
+  int steps;
+  switch (fmt) {
+    case FMT_Q8_0: case FMT_Q4_0: steps = Q8_0F::steps(cols); break;
+    case FMT_Q6_K: steps = Q6_KF::steps(cols); break;
+    default: return 0;
+  }
+  const int waves = 16 * num_cu();
+  return (n_groups + waves - 1) / waves * steps;
+}
+
 // Launch the streamed path if the shape allows it (rows and x 16-byte aligned, one format
 // family).  Returns hipErrorNotSupported, with nothing launched, if it does not.
-static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) {
+static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, int n_groups, hipStream_t s) {
   const int nseg = (epi == EPI_SWIGLU) ? 2 : a.nseg;
   // the kernel's segment layout: one matrix, gate + up, or q + k + v
   if (nseg != (epi == EPI_SWIGLU ? 2 : epi == EPI_QKV ? 3 : 1)) return hipErrorNotSupported;
   const bool kf = st_family(a.seg[0].fmt);
   // The streamed path pays more per launch than the register path (its rings fill before the
   // first product), which only its higher rate on large launches earns back: below 10^8
-  // weights per launch the register path is faster (measured: Q8_0 4096 x 4096 6.8 vs
-  // 10.9 us, Q6_K 8192 x 8192 20.2 vs 22.8 us; Q6_K 8192 x 28672 44.5 vs 57 us the other way).
+  // weights per launch the register path is as fast or faster (measured, register vs
+  // streamed: Q8_0 4096 x 4096 6.7 vs 9.4 us, Q4_0 4096 x 8192 7.5 vs 10.0 us; within a few
+  // percent near the threshold: Q6_K 8192 x 8192 19.2 vs 18.6 us; above it Q6_K 8192 x 28672
+  // 57 vs 44.5 us), except where the register path's waves would each run 7 or more items in a row (long
+  // rows over few row groups: the streamed path splits a row's columns over several waves).
+  // From an eighth of the threshold such deep launches stream too (measured, register vs
+  // streamed: Q8_0 4096 x 14336 (depth 8) 22.7 vs 16.4 us, 1024 x 28672 (14) 22.2 vs 13.0 us,
+  // 28672 x 1024 (8) 12.7 vs 11.9 us, 2048 x 14336 (8) 11.8 vs 11.6 us; Q6_K 4096 x 28672 (14)
+  // 44.2 vs 26.8 us; at depth 4: Q8_0 4096 x 8192 10.9 vs 12.4 us, Q4_0 8192 x 8192 13.0 vs
+  // 13.3 us).  A threshold of 0 streams every launch the formats allow.
   int64_t weights = 0;
   for (int i = 0; i < nseg; ++i) weights += (int64_t)a.seg[i].rows * a.cols;
-  if (weights < g_st_min_weights.load(std::memory_order_relaxed)) return hipErrorNotSupported;
+  const int64_t t = g_st_min_weights.load(std::memory_order_relaxed);
+  if (weights < t && !(weights >= t / 8 && reg_depth(a.seg[0].fmt, a.cols, n_groups) >= 7)) return hipErrorNotSupported;
   for (int i = 0; i < nseg; ++i) {
     const GemvSeg& g = a.seg[i];
     if (st_family(g.fmt) != kf) return hipErrorNotSupported;
@@ -2438,7 +2461,7 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, hipStream_t s) 
 
 hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s) {
   if (NT_GEMV_STREAM) {
-    const hipError_t e = gemv_stream_launch(epi, a, s);
+    const hipError_t e = gemv_stream_launch(epi, a, n_groups, s);
     if (e != hipErrorNotSupported) return e;
   }
   switch (epi) {

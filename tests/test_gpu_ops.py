@@ -149,6 +149,31 @@ def test_gemv_streamed_path_matches_oracle(fmt, rows, cols, streamed_path):
     say(f"  worst rel err {worst:.2e}")
 
 
+# The register path at the workload shapes the launch policy streams (10^8 weights and up,
+# or from 1.25 10^7 where each register-path wave would run 7 or more items in a row): a
+# threshold no launch reaches keeps them on the register path.
+REGISTER_CASES = [(synth.Q8_0, 4096, 14336), (synth.Q8_0, 14336, 4096), (synth.Q6_K, 28672, 8192),
+                  (synth.Q6_K, 8192, 28672)]
+
+
+@pytest.fixture
+def register_path():
+    prev = nt.nt_set_stream_min_weights(1 << 62)
+    yield
+    nt.nt_set_stream_min_weights(prev)
+
+
+@pytest.mark.parametrize("fmt,rows,cols", REGISTER_CASES)
+def test_gemv_register_path_matches_oracle(fmt, rows, cols, register_path):
+    say(f"gemv (register path) {NAMES[fmt]} {rows}x{cols}")
+    blocks = synth.quant_matrix(fmt, rows, cols, seed=0, stream=200 + fmt)
+    x = synth.normal_f32(cols, seed=0, stream=300 + fmt)
+    y = gpu_gemv(fmt, rows, cols, blocks, x)
+    ref, nrm = oracle.gemv(fmt, rows, cols, blocks, x.astype(np.float64))
+    worst = check_rel(y, ref, nrm, what=f"{NAMES[fmt]} {rows}x{cols}")
+    say(f"  worst rel err {worst:.2e}")
+
+
 def gpu_gemm(fmt, rows, cols, n_tok, blocks, X):
     wb = dev(blocks)
     xd = dev(np.ascontiguousarray(X, dtype=np.float32).ravel())
