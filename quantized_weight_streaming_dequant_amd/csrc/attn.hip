@@ -53,6 +53,27 @@ constexpr int CK = 16;             // splits per merge wave per round of loads
 
 __device__ __forceinline__ h8 as_h8(u32x4 v) { return __builtin_bit_cast(h8, v); }
 
+// The 32 slots of a wave starting at t0 (K rows, V groups of 8), loaded with the slots
+// clamped into [0, n_ctx): a branch here would make the compiler wait for every load before
+// the query staging.
+struct KVTile {
+  u32x4 k[2][4], v[8];
+};
+__device__ __forceinline__ void load_tile(KVTile& b, const uint16_t* kb, const uint16_t* vb, int t0, int n_ctx,
+                                          int r, int qd) {
+#pragma unroll
+  for (int ta = 0; ta < 2; ++ta) {
+    const int t = min(t0 + 8 * (r >> 2) + 4 * ta + (r & 3), n_ctx - 1);
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(kb + (size_t)t * HD + 8 * qd);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b.k[ta][j] = ld16(p + 64 * j);  // dims 32 j + 8 qd .. +7
+  }
+  const int grp = min((t0 >> 3) + qd, (n_ctx - 1) >> 3);
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(vb + ((size_t)grp * HD + r) * 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b.v[j] = ld16(vp + 256 * j);  // dimension 16 j + r, slots 8 grp .. +7
+}
+
 template <int G>
 __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a) {
   constexpr int NB = (G + 7) / 8;  // column blocks of 8 heads (hi and lo columns each)
@@ -70,7 +91,6 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
   if (split >= n_split) return;                  // the whole workgroup, before any barrier
   const float* qtok = a.q + (size_t)tok * a.q_stride;
   const int t0 = split * SWG + wave * SW;  // first slot of this wave
-  const bool active = t0 < n_ctx;          // wave-uniform
 
   // ---- 1. loads: this wave's query heads first (needed first), then its K and V tiles
   float2 qv[HPW];
@@ -80,24 +100,10 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
     qv[k] = *reinterpret_cast<const float2*>(qtok + (size_t)(g * G + hh) * HD + 2 * lane);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the cache loads
-  // Unconditional, with slots clamped into [0, n_ctx): a branch here would make the
-  // compiler wait for every load before the query staging below.
-  u32x4 kt[2][4], vt[8];
-  {
-    const uint16_t* kb = a.k_cache + (size_t)g * a.max_ctx * HD;
-#pragma unroll
-    for (int ta = 0; ta < 2; ++ta) {
-      const int t = min(t0 + 8 * (r >> 2) + 4 * ta + (r & 3), n_ctx - 1);
-      const uint8_t* p = reinterpret_cast<const uint8_t*>(kb + (size_t)t * HD + 8 * qd);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kt[ta][j] = ld16(p + 64 * j);  // dims 32 j + 8 qd .. +7
-    }
-    const int grp = min((t0 >> 3) + qd, (n_ctx - 1) >> 3);
-    const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v_cache + (size_t)g * a.max_ctx * HD +
-                                                         ((size_t)grp * HD + r) * 8);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) vt[j] = ld16(vp + 256 * j);  // dimension 16 j + r, slots 8 grp .. +7
-  }
+  const uint16_t* kb = a.k_cache + (size_t)g * a.max_ctx * HD;
+  const uint16_t* vb = a.v_cache + (size_t)g * a.max_ctx * HD;
+  KVTile cur;
+  load_tile(cur, kb, vb, t0, n_ctx, r, qd);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. stage hi/lo fp16 parts of the scaled queries (columns of absent heads are zero)
@@ -133,26 +139,34 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
   }
   __syncthreads();
 
-  if (active) {
-    // ---- 3. scores: B operand of lane (column r, quarter qd) for MFMA j = dims 32 j + 8 qd .. +7
-    float s[NB][8];  // s[cb][k]: slot t0 + 8 qd + k, head 8 cb + (r & 7)
+  // B operand of lane (column r, quarter qd) for MFMA j = dims 32 j + 8 qd .. +7; each head's scale
+  h8 bq[NB][4];
+  float sig[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bq[cb][j] = *reinterpret_cast<const h8*>(&qx[cb][r][32 * j + 8 * qd]);
+    sig[cb] = qsig[cb * 8 + (r & 7)];
+  }
+  float mw[NB], lw[NB];  // the wave's maximum and sum for the lane's head (r & 7)
+  f4 ow[NB][8];          // P V: rows 4 qd .. +3 (head rows, hi and lo), column r of dims 16 j ..
+  if (t0 < n_ctx) {  // wave-uniform
+    // ---- 3. scores: s[cb][k]: slot t0 + 8 qd + k, head 8 cb + (r & 7)
+    float s[NB][8];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-      h8 bq[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bq[j] = *reinterpret_cast<const h8*>(&qx[cb][r][32 * j + 8 * qd]);
-      const float sig = qsig[cb * 8 + (r & 7)];
 #pragma unroll
       for (int ta = 0; ta < 2; ++ta) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kt[ta][j]), bq[j], acc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(cur.k[ta][j]), bq[cb][j], acc, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = acc[i];
           v += dpp_mov<0x128>(v);  // row_ror:8 -> the head's other column (hi + lo)
           const int t = t0 + 8 * qd + 4 * ta + i;
-          s[cb][4 * ta + i] = (t < n_ctx) ? v * sig : -INFINITY;
+          s[cb][4 * ta + i] = (t < n_ctx) ? v * sig[cb] : -INFINITY;
         }
       }
     }
@@ -162,13 +176,13 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
       const int nl = n_ctx - (t0 + 8 * qd);  // live slots of this lane's group of 8
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint32_t w4[4] = {vt[j].x, vt[j].y, vt[j].z, vt[j].w};
+        uint32_t w4[4] = {cur.v[j].x, cur.v[j].y, cur.v[j].z, cur.v[j].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t keep = (2 * c + 1 < nl) ? 0xFFFFFFFFu : (2 * c < nl) ? 0x0000FFFFu : 0u;
           w4[c] &= keep;
         }
-        vt[j] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        cur.v[j] = u32x4{w4[0], w4[1], w4[2], w4[3]};
       }
     }
 
@@ -179,7 +193,7 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
 #pragma unroll
       for (int k = 1; k < 8; ++k) m = fmaxf(m, s[cb][k]);
       m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));  // slot 0 of the wave is live: m is finite
+      m = fmaxf(m, __shfl_xor(m, 32, 64));  // slot t0 is live: m is finite
       float l = 0.f;
       h8 pa;
 #pragma unroll
@@ -192,17 +206,26 @@ __global__ __launch_bounds__(AW * 64) void attn_partial_kernel(const AttnArgs a)
       }
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
+      mw[cb] = m;
+      lw[cb] = l;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        ow[cb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, as_h8(cur.v[j]), f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+  }
+  // the wave's part for the merge, written after all its products
+  __builtin_amdgcn_sched_barrier(0);
+  if (t0 < n_ctx) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
       if (qd == 0 && r < 8) {
-        wml[wave][cb * 8 + r][0] = m;
-        wml[wave][cb * 8 + r][1] = l;
+        wml[wave][cb * 8 + r][0] = mw[cb];
+        wml[wave][cb * 8 + r][1] = lw[cb];
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        f4 o = {0.f, 0.f, 0.f, 0.f};
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, as_h8(vt[j]), o, 0, 0, 0);
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ol[wave][cb][4 * qd + i][16 * j + r] = o[i];
-      }
+        for (int i = 0; i < 4; ++i) ol[wave][cb][4 * qd + i][16 * j + r] = ow[cb][j][i];
     }
   } else if (lane < NB * 8) {
     wml[wave][lane][0] = -INFINITY;

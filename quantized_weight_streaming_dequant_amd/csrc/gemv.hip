@@ -149,6 +149,14 @@ __device__ __forceinline__ float limb_sum(const int (&d)[XL]) {
   else
     return (float)((d[0] << 8) + d[1]);
 }
+// The fp32 sums of the four 16-column runs from c (a multiple of 64) in one 16-byte read.
+// A lane reading them as two pairs of dwords 16 bytes from its neighbour's made each dword
+// access a four-way LDS bank conflict; the 16-byte read is conflict-free.  The sums start on
+// a 16-byte boundary whenever the columns are whole 256-column superblocks (cols / 32
+// scales of 4 bytes before them, after 16-byte-aligned limb planes), as for Q4_K and Q5_K.
+__device__ __forceinline__ float4 s16x4(const XLimbs& xs, int c) {
+  return *reinterpret_cast<const float4*>(xs.s16 + (c >> 4));
+}
 // The limbs of 16 columns starting at c (a multiple of 16): 4 dwords per plane.
 struct XRun {
   u32x4 p[XL];
@@ -402,8 +410,8 @@ struct Q4_KF {
       __builtin_amdgcn_sched_barrier(0);
     }
     const float sA = xs.sc[c0 >> 5], sB = xs.sc[(c0 >> 5) + 1];
-    const float xa = xs.s16[c0 >> 4] + xs.s16[(c0 >> 4) + 1];
-    const float xb = xs.s16[(c0 >> 4) + 2] + xs.s16[(c0 >> 4) + 3];
+    const float4 x4 = s16x4(xs, c0);
+    const float xa = x4.x + x4.y, xb = x4.z + x4.w;
     const float sB16 = sB * 0.0625f, xb8 = 8.f * xb;
     // 6-bit scales and mins of sub-blocks 2g, 2g+1 gathered as the bytes [sc_a, sc_b, m_a, m_b]
     // from the scale words Y (bytes 4..7), Z (8..11), W (12..15), p = 2 (g & 1):
@@ -488,8 +496,8 @@ struct Q5_KF {
       __builtin_amdgcn_sched_barrier(0);
     }
     const float sA = xs.sc[c0 >> 5], sB = xs.sc[(c0 >> 5) + 1];
-    const float xa = xs.s16[c0 >> 4] + xs.s16[(c0 >> 4) + 1];
-    const float xb = xs.s16[(c0 >> 4) + 2] + xs.s16[(c0 >> 4) + 3];
+    const float4 x4 = s16x4(xs, c0);
+    const float xa = x4.x + x4.y, xb = x4.z + x4.w;
     // scales and mins exactly as Q4_K's (same 12-byte packing at bytes 4..15)
     const uint32_t p = 2u * (uint32_t)(g & 1);
     const uint32_t sel = p | ((p + 1) << 8) | ((p + 4) << 16) | ((p + 5) << 24);
@@ -1218,8 +1226,8 @@ __device__ __forceinline__ void kapply(const KDec<NR>& D, const XLimbs& xs, floa
       for (int k = 0; k < NR; ++k) dot_limbs(D.code[k][h][i], x, i, h < 2 ? da[k] : db[k], (h & 1) == 0 && i == 0);
   }
   const float sA = xs.sc[D.c0 >> 5], sB = xs.sc[(D.c0 >> 5) + 1];
-  const float xa = xs.s16[D.c0 >> 4] + xs.s16[(D.c0 >> 4) + 1];
-  const float xb = xs.s16[(D.c0 >> 4) + 2] + xs.s16[(D.c0 >> 4) + 3];
+  const float4 x4 = s16x4(xs, D.c0);
+  const float xa = x4.x + x4.y, xb = x4.z + x4.w;
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
     acc[k] += (D.dA[k] * sA) * limb_sum(da[k]);

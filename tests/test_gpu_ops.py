@@ -433,6 +433,8 @@ ATTN_CASES = [  # n_q, n_kv, n_ctx, max_ctx, q scale
     (8, 1, nt.NT_MAX_CTX, nt.NT_MAX_CTX, 1.0),  # the longest cache the header allows
     # the 256-slot split boundaries: one full split (one kernel), one slot into a second, two full
     (64, 8, 256, 256, 1.0), (64, 8, 257, 264, 1.0), (32, 8, 512, 512, 3.0), (16, 2, 255, 256, 1.0),
+    # a few splits with a ragged last one (the 8B shape's context length and either side of it)
+    (32, 8, 777, 1024, 1.0), (64, 8, 513, 520, 2.0), (8, 2, 1023, 1024, 1.0),
 ]
 
 
