@@ -430,6 +430,9 @@ def bench_decode_70b(args, torch, nt, tg):
         "kernels": kern,
         "last_token": last_tok,
     }
+    # the same step replayed from a HIP graph (one token at a fixed position, captured once)
+    # against the same launches enqueued directly: the decode does not need a graph
+    res["graph_replay"] = graph_replay(torch, nt, plan, head, m, wsb, ws, h, logits, tok)
     # the yardstick next to the published peak: what plain reads achieve on this part
     rp = read_probe(torch, nt)
     res["read_probe"] = rp
@@ -443,6 +446,53 @@ def bench_decode_70b(args, torch, nt, tg):
         log("cpu baseline (checker on a bounded sample)...")
         res["cpu_baseline"] = cpu_baseline_70b(mix, args.cpu_seconds)
     return res
+
+
+def graph_replay(torch, nt, plan, head, m, wsb, ws, h, logits, tok, pos=4100, n=32):
+    """Per-token time of one decode step (position pos) replayed from a HIP graph, next to the
+    same step enqueued directly, and whether the replay reproduces the direct step bit for bit."""
+    try:
+        s = torch.cuda.Stream()
+
+        def step():
+            r = nt.nt_decode_token(None, plan, head, pos, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                                   ws.data_ptr(), wsb, s.cuda_stream, s.cuda_stream, None)
+            if r != 0:
+                raise RuntimeError(nt.nt_last_error())
+
+        def timed(fn):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / n * 1e3
+
+        tok.fill_(m.first_token)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.synchronize()
+        ref = (tok.clone(), h.clone())
+        g = torch.cuda.CUDAGraph()
+        tok.fill_(m.first_token)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        torch.cuda.synchronize()
+        tok.fill_(m.first_token)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(tok, ref[0]) and torch.equal(h.view(torch.int32), ref[1].view(torch.int32)))
+        with torch.cuda.stream(s):
+            direct_ms = timed(step)
+        replay_ms = timed(g.replay)
+        del g
+        return {"pos": pos, "tokens": n, "replay_ms_per_token": replay_ms, "direct_ms_per_token": direct_ms,
+                "replay_bit_identical": same}
+    except Exception as e:  # reported, never fatal to the benchmark line
+        return {"error": str(e)}
 
 
 def rotating_gemv(torch, nt, fmt, rows, cols, copies, steps, warmup, seed=0):
