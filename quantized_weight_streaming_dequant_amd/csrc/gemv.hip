@@ -1545,12 +1545,12 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs
   const uint64_t half_a = q < 2 ? ~0ull : 0ull, half_b = ~half_a;
   (void)half_a;
   (void)half_b;
-  MmRaw<FMT> cur[S], nxt[S];
   int ct = blockIdx.x, buf = 0;
-  issue(cur, ct);
-  for (;;) {
+  // one tile: the next tile's loads go into the other buffer and stay in flight while this
+  // one is computed (the two buffers alternate, so no register copy waits for them)
+  auto tile = [&](const MmRaw<FMT> (&cur)[S], MmRaw<FMT> (&nxt)[S]) -> bool {
     const int tn = ct + (int)gridDim.x;
-    issue(nxt, min(tn, ntiles - 1));  // in flight while this tile is computed
+    issue(nxt, min(tn, ntiles - 1));
     float acc[NM], am[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[m] = am[m] = 0.f;
@@ -1643,11 +1643,13 @@ __global__ __launch_bounds__(MM_NW * 64, 1) void gemm_mfma_kernel(const GemmArgs
     }
     buf ^= 1;  // the other buffer: the next tile's writes cannot meet this tile's reads
     ct = tn;
-    if (ct >= ntiles) break;
-    cur[0] = nxt[0];
-    if constexpr (S >= 2) cur[1] = nxt[1];
-    if constexpr (S >= 3) cur[2] = nxt[2];
-    if constexpr (S >= 4) cur[3] = nxt[3];
+    return ct < ntiles;
+  };
+  MmRaw<FMT> b0[S], b1[S];
+  issue(b0, ct);
+  for (;;) {
+    if (!tile(b0, b1)) break;
+    if (!tile(b1, b0)) break;
   }
 }
 
