@@ -144,13 +144,14 @@ def timed_class(nt, torch, kclass, run, nbytes_per_launch):
 
 class Model70B:
     """80 layer blobs + embedding + LM head + caches, generated layer by layer on the host
-    (pinned staging) and copied into HBM."""
+    (pinned staging) and copied into HBM (another shape, such as the 8B one, by argument)."""
 
-    def __init__(self, torch, nt, tg, mix, n_layers, resident_layers, n_prefill=4096, seed=0):
+    def __init__(self, torch, nt, tg, mix, n_layers, resident_layers, n_prefill=4096, seed=0, shape=None,
+                 head_fmt=None):
         import synth
         from synth import recipes
         self.torch, self.nt, self.tg = torch, nt, tg
-        self.shape = recipes.LLAMA31_70B
+        self.shape = recipes.LLAMA31_70B if shape is None else shape
         self.mix = mix
         self.n_layers = n_layers
         self.vocab = recipes.VOCAB_70B
@@ -198,7 +199,7 @@ class Model70B:
                     d = v_to_device_layout(torch, d, shp.n_kv_heads, shp.max_ctx)
                 lst.append(d)
         # head
-        embd_fmt = out_fmt = synth.Q4_K if mix[ "q"] == synth.Q4_K else synth.Q6_K
+        embd_fmt = out_fmt = head_fmt if head_fmt is not None else (synth.Q4_K if mix["q"] == synth.Q4_K else synth.Q6_K)
         self.embd_fmt, self.out_fmt = embd_fmt, out_fmt
         eb = synth.matrix_bytes(embd_fmt, self.vocab, shp.dim)
         hb = torch.empty(eb, dtype=torch.uint8, pin_memory=True)
@@ -338,6 +339,7 @@ def metric_extras(torch, nt, tg):
     out["gemv_70b"] = lst
     out["layer_8b_q8_0"] = layer_8b_measure(torch, nt, tg, 100, 10)
     torch.cuda.empty_cache()
+    out["decode_8b_q8_0"] = decode_8b_measure(torch, nt, tg)
     return out
 
 
@@ -680,6 +682,48 @@ def bench_layer_skip_70b(args, torch, nt, tg):
         "tok_s_all_layers": res_t["all layers"],
         "layer_cosine": [float(v) for v in cv],
     }
+
+
+def decode_8b_measure(torch, nt, tg, steps=128, warmup=4):
+    """A whole Llama-3-8B-shaped Q8_0 model decoding greedily: 32 layers, Q8_0 embedding and LM
+    head (128256 x 4096), 1024-slot caches prefilled with N(0,1) in slots < 1024 - steps, then
+    `steps` tokens at positions 1024 - steps .. 1023, host-timed around the loop."""
+    from synth import recipes
+    import synth
+    n0 = recipes.LLAMA3_8B.max_ctx - steps
+    m = Model70B(torch, nt, tg, recipes.MIX_Q8_0, 32, range(32), n_prefill=n0, shape=recipes.LLAMA3_8B,
+                 head_fmt=synth.Q8_0)
+    plan, keep = m.plan()
+    head = m.head()
+    shp = tg.layer_shape(m.shape)
+    wsb = nt.nt_decode_token_ws_bytes(shp)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h = torch.zeros(m.shape.dim, dtype=torch.float32, device="cuda")
+    logits = torch.zeros(m.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cs = torch.cuda.current_stream().cuda_stream
+
+    def run(pos0, n):
+        tok.fill_(m.first_token)
+        for i in range(n):
+            nt.nt_decode_token(None, plan, head, pos0 + i, tok.data_ptr(), logits.data_ptr(), h.data_ptr(),
+                               ws.data_ptr(), wsb, cs, cs, None)
+
+    run(n0, warmup)  # rewrites slots n0.. that the timed run writes again
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(n0, steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    wbytes = m.lay.nbytes * 32 + synth.matrix_bytes(synth.Q8_0, m.vocab, m.shape.dim)
+    kv = 2 * 32 * m.shape.n_kv_heads * m.shape.head_dim * 2 * (n0 + steps / 2)  # average cache read per token
+    res = {"tok_s": steps / dt, "ms_per_token": dt / steps * 1e3, "layers": 32, "tokens": steps,
+           "positions": [n0, n0 + steps - 1], "weight_bytes_per_token": int(wbytes),
+           "GBps": (wbytes + kv) * steps / dt / 1e9, "frac_of_peak": (wbytes + kv) * steps / dt / 1e9 / HBM_PEAK_GBS,
+           "last_token": int(tok.item())}
+    del m, plan, keep, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def layer_8b_measure(torch, nt, tg, steps, warmup):
