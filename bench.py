@@ -297,6 +297,47 @@ def _oracle_token_sample(mix, target_s, max_layers=80, head_rows=8192):
     return s_per_tok, n, head_rows, t_layers + t_rows
 
 
+def cpu_baseline_extras():
+    """The checker on the metric's other halves, whole: the Q8_0 4096 x 4096 GEMV (config 1) and
+    one Llama-3-8B-shape Q8_0 layer at pos 1023 (config 2), with every host thread and with one."""
+    import oracle
+    import synth
+    from synth import recipes
+    cores = host_threads()
+    blocks = synth.quant_matrix(synth.Q8_0, 4096, 4096, 0, 5000)
+    x = synth.normal_f32(4096, 0, 999)
+    gbytes = synth.matrix_bytes(synth.Q8_0, 4096, 4096) + 4 * 2 * 4096
+    shp = recipes.LLAMA3_8B
+    w = recipes.layer_arrays(shp, recipes.MIX_Q8_0, 0)
+    kc = recipes.kv_cache_array(shp, 0, "k", 1024)
+    vc = recipes.kv_cache_array(shp, 0, "v", 1024)
+    h = recipes.hidden_input(shp.dim)
+    lbytes = sum(synth.matrix_bytes(synth.Q8_0, *shp.matrix_shape(n)) for n in recipes.TENSORS)
+
+    def timed(fn, min_s):
+        n, t = 0, time.time()
+        while n == 0 or time.time() - t < min_s:
+            fn()
+            n += 1
+        return (time.time() - t) / n
+
+    out = {}
+    for label, threads in (("all", None), ("one_thread", 1)):
+        old = oracle.set_threads(threads) if threads else None
+        try:
+            tg_ = timed(lambda: oracle.gemv(synth.Q8_0, 4096, 4096, blocks, x), 0.3)
+            tl = timed(lambda: oracle.decode_layer(w, recipes.MIX_Q8_0, shp, 1023, h, kc, vc), 0.5)
+        finally:
+            if threads:
+                oracle.set_threads(old)
+        out[label] = {"cores": cores if threads is None else 1,
+                      "gemv_q8_0_4096x4096": {"seconds": tg_, "GBps": gbytes / tg_ / 1e9},
+                      "layer_8b_q8_0": {"seconds": tl, "GBps": lbytes / tl / 1e9}}
+    out["kind"] = "oracle"
+    out["sample"] = "the Q8_0 4096x4096 GEMV and one 8B Q8_0 layer at pos 1023 (1024 keys), whole, fp64"
+    return out
+
+
 def cpu_baseline_70b(mix, target_s):
     """The checker (fp64, OpenMP) on a bounded sample of one decode token, scaled to one 80-layer
     token: with every host thread (whole layers until target_s of work, plus 8192 LM-head rows),
@@ -447,6 +488,8 @@ def bench_decode_70b(args, torch, nt, tg):
     if not args.no_cpu_baseline:
         log("cpu baseline (checker on a bounded sample)...")
         res["cpu_baseline"] = cpu_baseline_70b(mix, args.cpu_seconds)
+        if not args.no_extras:
+            res["cpu_baseline_extras"] = cpu_baseline_extras()
     return res
 
 

@@ -43,6 +43,9 @@ def test_bench_line_has_every_field():
         assert k in cb, k
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
     assert cb["one_thread"]["cores"] == 1 and cb["one_thread"]["value"] > 0
+    ce = d["cpu_baseline_extras"]
+    assert ce["kind"] == "oracle" and ce["one_thread"]["cores"] == 1
+    assert ce["all"]["gemv_q8_0_4096x4096"]["GBps"] > 0 and ce["all"]["layer_8b_q8_0"]["seconds"] > 0
     # the GEMV and 8B halves of the metric ride along in the default line
     assert d["gemv_q8_0_4096x4096"]["GBps"] > 0 and len(d["gemv_70b"]) == 8
     assert d["layer_8b_q8_0"]["derived_tok_s"] > 0
