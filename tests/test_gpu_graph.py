@@ -67,3 +67,48 @@ def test_token_step_graph_replay_bit_identical():
         for a, b in zip(got, ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
     say(f"  token {int(ref[0].item())}; three replays bit-identical to the direct call")
+
+
+def test_noalloc_layer_graph_replay_bit_identical():
+    """nt_decode_layer_noalloc is meant for callers under graph capture: captured once (after a
+    first direct call has looked up its static workspace) and replayed three times, it gives the
+    direct call's h, K and V bit for bit."""
+    from tests.gpu_util import dev, v_to_device
+    shape = recipes.LayerShape(dim=1024, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn_dim=2816, max_ctx=96)
+    mix, pos = recipes.MIX_Q4_K_M, 50
+    say(f"noalloc layer: HIP graph replay vs direct call (dim {shape.dim}, pos {pos})")
+    w = recipes.layer_arrays(shape, mix, 0)
+    d = {k: dev(v) for k, v in w.items()}
+    lw = tg.layer_weights([mix[n] for n in recipes.TENSORS], [d[n] for n in recipes.TENSORS], d["attn_norm"],
+                          d["ffn_norm"])
+    kc = dev(recipes.kv_cache_array(shape, 0, "k", pos))
+    vc = dev(v_to_device(recipes.kv_cache_array(shape, 0, "v", pos), shape.n_kv_heads, shape.max_ctx))
+    h0 = dev(recipes.hidden_input(shape.dim))
+    h = h0.clone()
+    shp = tg.layer_shape(shape)
+    s = torch.cuda.Stream()
+
+    def call():
+        nt.nt_decode_layer_noalloc(lw, shp, pos, h.data_ptr(), kc.data_ptr(), vc.data_ptr(), s.cuda_stream)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    ref = [h.clone(), kc.clone(), vc.clone()]
+    h.copy_(h0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        h.copy_(h0)
+        x = torch.randn(1 << 20, device="cuda")  # eager work between the replays
+        (x * x).sum().item()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((h, kc, vc), ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+    say("  three replays bit-identical to the direct call")
