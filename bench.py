@@ -147,12 +147,16 @@ class Model70B:
     (pinned staging) and copied into HBM (another shape, such as the 8B one, by argument)."""
 
     def __init__(self, torch, nt, tg, mix, n_layers, resident_layers, n_prefill=4096, seed=0, shape=None,
-                 head_fmt=None):
+                 head_fmt=None, tiles=False):
         import synth
         from synth import recipes
         self.torch, self.nt, self.tg = torch, nt, tg
         self.shape = recipes.LLAMA31_70B if shape is None else shape
         self.mix = mix
+        # tiles: the resident layers' Q4_K matrices and the Q4_K LM head rearranged on the device
+        # into the GEMV's tiled layout (nt_repack, Q4_KT); the same weights
+        self.tiles = tiles
+        self.fmts = {n: (synth.Q4_KT if tiles and mix[n] == synth.Q4_K else mix[n]) for n in recipes.TENSORS}
         self.n_layers = n_layers
         self.vocab = recipes.VOCAB_70B
         self.lay = recipes.blob_layout(self.shape, mix)
@@ -185,6 +189,19 @@ class Model70B:
                 log(f"  generated layer {l + 1}/{n_layers} ({time.time() - t0:.1f}s)")
         copy_stream.synchronize()
         del stage
+        tiled = [n for n in recipes.TENSORS if self.fmts[n] != mix[n]]
+        if tiled and self.resident:
+            nbytes = {n: synth.matrix_bytes(mix[n], *self.shape.matrix_shape(n)) for n in tiled}
+            scratch = torch.empty(max(nbytes.values()), dtype=torch.uint8, device="cuda")
+            cs = torch.cuda.current_stream().cuda_stream
+            for l in self.resident:
+                for n in tiled:
+                    rows, cols = self.shape.matrix_shape(n)
+                    o, nb = self.lay.offsets[n], nbytes[n]
+                    nt.nt_repack(synth.Q4_KT, rows, cols, self.dev_blobs[l][o:].data_ptr(), scratch.data_ptr(), cs)
+                    self.dev_blobs[l][o:o + nb].copy_(scratch[:nb])
+            torch.cuda.synchronize()
+            del scratch
         # KV caches per layer, slots < n_prefill ~ N(0,1): K as [n_kv][max_ctx][128] fp16,
         # V regrouped on the device into the library's [n_kv][max_ctx/8][128][8]
         cache_elems = shp.n_kv_heads * shp.max_ctx * shp.head_dim
@@ -210,6 +227,12 @@ class Model70B:
                           recipes.stream_id(recipes.GLOBAL_LAYER, recipes.GID_OUTPUT))
         self.out = hb.cuda()
         del hb
+        # the LM head the decode reads (self.out stays in Q4_K's block order for the checker)
+        self.head_fmt, self.head_out = out_fmt, self.out
+        if tiles and out_fmt == synth.Q4_K:
+            self.head_fmt, self.head_out = synth.Q4_KT, torch.empty_like(self.out)
+            nt.nt_repack(synth.Q4_KT, self.vocab, shp.dim, self.out.data_ptr(), self.head_out.data_ptr(),
+                         torch.cuda.current_stream().cuda_stream)
         self.onorm = torch.from_numpy(synth.uniform_f32(shp.dim, seed, recipes.stream_id(recipes.GLOBAL_LAYER,
                                                                                           recipes.GID_OUTPUT_NORM),
                                                         0.9, 1.1)).cuda()
@@ -218,9 +241,10 @@ class Model70B:
         log(f"  model ready in {time.time() - t0:.1f}s")
 
     def plan(self, skip=()):
+        from synth import recipes
         tg, nt = self.tg, self.nt
         shp = tg.layer_shape(self.shape)
-        lay = tg.layer_layout(self.lay.offset_list(), self.lay.fmt_list(), self.lay.nbytes)
+        lay = tg.layer_layout(self.lay.offset_list(), [self.fmts[n] for n in recipes.TENSORS], self.lay.nbytes)
         ents = []
         for l in range(self.n_layers):
             if l in self.resident:
@@ -235,13 +259,13 @@ class Model70B:
         blob = self.dev_blobs[l]
         off = self.lay.offsets
         mats = [blob[off[n]:] for n in recipes.TENSORS]
-        return self.tg.layer_weights([self.mix[n] for n in recipes.TENSORS], mats,
+        return self.tg.layer_weights([self.fmts[n] for n in recipes.TENSORS], mats,
                                      blob[off["attn_norm"]:].view(self.torch.float32),
                                      blob[off["ffn_norm"]:].view(self.torch.float32))
 
     def head(self):
-        return self.nt.ModelHead(self.embd_fmt, self.embd.data_ptr(), self.vocab, self.onorm.data_ptr(), self.out_fmt,
-                                 self.out.data_ptr())
+        return self.nt.ModelHead(self.embd_fmt, self.embd.data_ptr(), self.vocab, self.onorm.data_ptr(), self.head_fmt,
+                                 self.head_out.data_ptr())
 
 
 def token_bytes_70b(mix, n_layers, pos, vocab=128256):
@@ -394,7 +418,7 @@ def bench_decode_70b(args, torch, nt, tg):
     mix = recipes.MIX_Q4_K_M
     n_layers = args.layers
     log(f"config 4: 70B Q4_K_M, {n_layers} layers resident, {steps} tokens after a 4096-slot cache")
-    m = Model70B(torch, nt, tg, mix, n_layers, range(n_layers))
+    m = Model70B(torch, nt, tg, mix, n_layers, range(n_layers), tiles=True)
     plan, keep = m.plan()
     head = m.head()
     shp = tg.layer_shape(m.shape)
@@ -674,7 +698,7 @@ def bench_layer_skip_70b(args, torch, nt, tg):
     mix = recipes.MIX_Q4_K_M
     n_layers = args.layers
     log(f"config 7: 70B Q4_K_M, {n_layers} layers, the {args.skip} most input-like layers skipped")
-    m = Model70B(torch, nt, tg, mix, n_layers, range(n_layers))
+    m = Model70B(torch, nt, tg, mix, n_layers, range(n_layers), tiles=True)
     head = m.head()
     shp = tg.layer_shape(m.shape)
     wsb = nt.nt_decode_token_ws_bytes(shp)

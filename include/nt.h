@@ -57,10 +57,21 @@ extern "C" {
  *   NT_F16    2 B / 1 weight   : the weight as IEEE binary16 (GGUF's F16 tensors)
  *   NT_F32    4 B / 1 weight   : the weight as IEEE binary32 (GGUF's F32 tensors)
  * (the overview's format list, "Überblick über NTransformer", names both beside the quant types).
+ *   NT_Q4_KT  NT_Q4_K's bytes, each row's superblocks rearranged in tiles of 16 (made by
+ *            nt_repack; the same 144 B per 256 weights and the same weights).  Tile t of a row
+ *            (superblocks 16t .. 16t+m-1, m = min(16, nsb - 16t), nsb = cols/256) starts at byte
+ *            2304t of the row and holds: the m 16-byte headers (bytes 0..15 of each block), then
+ *            for j < m, g < 4 in that order the 16 code bytes 32g .. 32g+15 of block j's nibbles,
+ *            then the 16 code bytes 32g+16 .. 32g+31.  A wave whose lane 4j+g decodes quarter g
+ *            of block j then reads whole 128-byte lines with each of its three 16-byte loads,
+ *            which lets the GEMV stream them with the nontemporal policy.  Embedding rows,
+ *            nt_dequant, the GEMV and the k-token GEMM (on the vector units) read it;
+ *            nt_gemv_q and the layer calls never take the streamed path for it.
  * Every entry point that takes cols for NT_F16 / NT_F32 needs a multiple of 32 (so that rows
  * keep the 16-byte alignment the loads use).
  */
-typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4, NT_F16 = 5, NT_F32 = 6 } nt_format;
+typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4, NT_F16 = 5, NT_F32 = 6,
+               NT_Q4_KT = 7 } nt_format;
 
 typedef enum {
   NT_OK = 0,
@@ -90,6 +101,15 @@ int64_t nt_matrix_bytes(int fmt, int64_t rows, int64_t cols); /* bytes of a rows
  * A test hook for the bit-exactness of the decoders (format pages above).
  * blocks: 4-byte aligned.  Returns NT_ESHAPE if cols % block_elems != 0. */
 int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, void* stream);
+
+/* Rearrange a Q4_K matrix (rows x cols, GGUF's block order) into the NT_Q4_KT layout above:
+ * a layout of the same weights for the GEMV's loads ("Überblick über NTransformer" names
+ * Q4_K_M; the tiles are this library's own).  fmt: the target layout, NT_Q4_KT only (else
+ * NT_EFORMAT).  cols: a positive multiple of 256 up to 2^24; rows <= NT_MAX_ROWS (else
+ * NT_ESHAPE).  src, dst: device, 16-byte aligned (NT_EALIGN), rows*cols/256*144 bytes each,
+ * not overlapping (NT_EINVAL; the caller copies back if it wants the matrix in place).
+ * Enqueued on stream; src is only read. */
+int nt_repack(int fmt, int64_t rows, int64_t cols, const void* src, void* dst, void* stream);
 
 /* y = W x for a block-quantized W (rows x cols), x and y fp32.
  * The GEMV step of the decode path (ntransformer overview, "Architektur und

@@ -14,6 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnt.so")
 
 Q8_0, Q4_0, Q4_K, Q6_K, Q5_K, F16, F32 = 0, 1, 2, 3, 4, 5, 6
+Q4_KT = 7  # Q4_K in the library's tiles of 16 superblocks (nt_repack)
 NT_OK, NT_EINVAL, NT_EFORMAT, NT_ESHAPE, NT_EALIGN, NT_EHOSTMEM, NT_EHIP = 0, -1, -2, -3, -4, -5, -6
 W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN, W_COUNT = range(8)
 K_ATTN_IN, K_ATTN, K_O, K_FFN_UP, K_FFN_DOWN, K_LM_HEAD, K_GEMV, K_GEMM = range(8)
@@ -71,7 +72,7 @@ class ModelHead(ctypes.Structure):
 _lib = None
 
 EXPORTS = [
-    "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_gemv_q", "nt_gemm_q", "nt_layer_cosine", "nt_read_probe",
+    "nt_last_error", "nt_version", "nt_block_elems", "nt_block_bytes", "nt_matrix_bytes", "nt_dequant", "nt_repack", "nt_gemv_q", "nt_gemm_q", "nt_layer_cosine", "nt_read_probe",
     "nt_set_stream_min_weights",
     "nt_rmsnorm", "nt_rope", "nt_attn_decode", "nt_attn_decode_ws_bytes", "nt_swiglu", "nt_decode_layer",
     "nt_decode_layer_noalloc", "nt_decode_layer_ws_bytes", "nt_decode_layer_ws_offsets", "nt_ffn_up", "nt_embed_row", "nt_argmax", "nt_stream_create",
@@ -99,6 +100,7 @@ def load(path: str = LIB_PATH):
         "nt_block_bytes": ([i], i),
         "nt_matrix_bytes": ([i, i64, i64], i64),
         "nt_dequant": ([i, i64, i64, vp, vp, vp], i),
+        "nt_repack": ([i, i64, i64, vp, vp, vp], i),
         "nt_gemv_q": ([i, i64, i64, vp, vp, vp, vp], i),
         "nt_gemm_q": ([i, i64, i64, i, vp, vp, vp, vp], i),
         "nt_layer_cosine": ([i64, vp, vp, vp, vp], i),
@@ -170,6 +172,10 @@ def nt_matrix_bytes(fmt: int, rows: int, cols: int) -> int:
 
 def nt_dequant(fmt, rows, cols, blocks, w, stream=None):
     return _check(load().nt_dequant(fmt, rows, cols, blocks, w, stream))
+
+
+def nt_repack(fmt, rows, cols, src, dst, stream=None):
+    return _check(load().nt_repack(fmt, rows, cols, src, dst, stream))
 
 
 def nt_gemv_q(fmt, rows, cols, blocks, x, y, stream=None):

@@ -42,7 +42,7 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(NT_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_F32; }
+bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_Q4_KT; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -419,6 +419,20 @@ int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w
   if (!aligned(blocks, 4) || !aligned(w, 4)) return fail(NT_EALIGN, "blocks and w must be 4-byte aligned");
   hipError_t e = dequant_launch(fmt, rows, cols, blocks, w, (hipStream_t)stream);
   return e == hipSuccess ? NT_OK : hip_fail(e, "dequant launch");
+}
+
+int nt_repack(int fmt, int64_t rows, int64_t cols, const void* src, void* dst, void* stream) {
+  if (fmt != NT_Q4_KT) return fail(NT_EFORMAT, "repack: the only target layout is NT_Q4_KT (got %d)", fmt);
+  if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols % 256 || cols > (1 << 24))
+    return fail(NT_ESHAPE, "repack: need 0 < rows <= 2^30 and cols a positive multiple of 256 up to 2^24 (got %lld x %lld)",
+                (long long)rows, (long long)cols);
+  if (!src || !dst) return fail(NT_EINVAL, "null pointer");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(NT_EALIGN, "src and dst must be 16-byte aligned");
+  const uintptr_t bytes = (uintptr_t)(rows * (cols / 256) * 144);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return fail(NT_EINVAL, "repack: src and dst overlap");
+  hipError_t e = repack_q4kt_launch(rows, cols, src, dst, (hipStream_t)stream);
+  return e == hipSuccess ? NT_OK : hip_fail(e, "repack launch");
 }
 
 int nt_gemv_q(int fmt, int64_t rows, int64_t cols, const void* blocks, const float* x, float* y, void* stream) {

@@ -7,16 +7,33 @@
 
 namespace nt {
 
-// F16 and F32 are unquantized weight tensors: one weight per "block".
-enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4, FMT_F16 = 5, FMT_F32 = 6 };
-constexpr int FMT_COUNT = 7;
+// F16 and F32 are unquantized weight tensors: one weight per "block".  Q4_KT holds Q4_K's
+// bytes rearranged in tiles of 16 superblocks (q4kt_* below).
+enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4, FMT_F16 = 5, FMT_F32 = 6, FMT_Q4_KT = 7 };
+constexpr int FMT_COUNT = 8;
 
 __host__ __device__ constexpr bool is_float_fmt(int f) { return f == FMT_F16 || f == FMT_F32; }
 __host__ __device__ constexpr int block_elems(int f) { return f <= FMT_Q4_0 ? 32 : is_float_fmt(f) ? 1 : 256; }
 __host__ __device__ constexpr int block_bytes(int f) {
-  return f == FMT_Q8_0 ? 34 : f == FMT_Q4_0 ? 18 : f == FMT_Q4_K ? 144 : f == FMT_Q5_K ? 176 : f == FMT_F16 ? 2
+  return f == FMT_Q8_0 ? 34 : f == FMT_Q4_0 ? 18 : (f == FMT_Q4_K || f == FMT_Q4_KT) ? 144 : f == FMT_Q5_K ? 176 : f == FMT_F16 ? 2
          : f == FMT_F32 ? 4 : 210;
 }
+// Q4_KT: a row's Q4_K superblocks in tiles of 16 (the last tile of a row holds the m =
+// nsb - 16 t left over), tile t at byte 2304 t of the row, so that each 16-byte load of a wave
+// whose lanes take superblock j = lane / 4, quarter g = lane % 4 of a tile reads whole cache
+// lines: the tile's m 16-byte headers (d, dmin, packed scales: bytes 0..15 of the Q4_K
+// block) come first, then code bytes 32 g .. 32 g + 15 of each (j, g) in lane order, then
+// code bytes 32 g + 16 .. 32 g + 31 in lane order (block bytes 16 + 32 g .. and 32 + 32 g ..).
+// Byte offsets within the row of the three 16-byte parts of superblock b, quarter g:
+__host__ __device__ constexpr uint32_t q4kt_tile_m(int nsb, int b) { return (uint32_t)(nsb - (b & ~15) < 16 ? nsb - (b & ~15) : 16); }
+__host__ __device__ constexpr uint32_t q4kt_head(int nsb, int b) { return 144u * (uint32_t)(b & ~15) + 16u * (uint32_t)(b & 15); }
+__host__ __device__ constexpr uint32_t q4kt_qa(int nsb, int b, int g) {
+  return 144u * (uint32_t)(b & ~15) + 16u * q4kt_tile_m(nsb, b) + 16u * (4u * (uint32_t)(b & 15) + (uint32_t)g);
+}
+__host__ __device__ constexpr uint32_t q4kt_qb(int nsb, int b, int g) {
+  return 144u * (uint32_t)(b & ~15) + 80u * q4kt_tile_m(nsb, b) + 16u * (4u * (uint32_t)(b & 15) + (uint32_t)g);
+}
+
 // Column granularity of the kernels: a block, and at least 32 columns (one scale block of the
 // staged activations; F16 and F32 rows are then 64- and 128-byte multiples).
 __host__ __device__ constexpr int col_unit(int f) { return block_elems(f) < 32 ? 32 : block_elems(f); }

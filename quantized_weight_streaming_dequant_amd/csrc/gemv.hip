@@ -440,6 +440,35 @@ struct Q4_KF {
   }
 };
 
+// Q4_KT: Q4_K in tiles of 16 superblocks (common.h), the same lane work as Q4_KF; a step is
+// one tile, and each of the three 16-byte loads of a wave reads whole lines (the headers,
+// four lanes to an address, then 1 KiB of code bytes twice).  NTL: the nontemporal policy,
+// which the large launches take: with GGUF's layout a lane's line is split between two load
+// instructions and the policy costs 20-45%, while on whole lines it lifts the read rate
+// (measured, 70B decode, Q4_K -> Q4_KT: gate/up pair 50.0 -> 46.2 us, LM head 106 -> 96.3 us);
+// the small launches keep cached loads (q/k/v 19.4 against 20.3 us with the policy, O 13.4
+// against 13.7 us; 21.0 and 13.6 us in Q4_K's block order).
+__device__ __forceinline__ u32x4 wld16nt(const uint8_t* p) { return __builtin_nontemporal_load(NT_GPTR(u32x4, p)); }
+
+template <bool NTL>
+struct Q4_KTF : Q4_KF {
+  static __device__ __forceinline__ u32x4 ld(const uint8_t* p) {
+    if constexpr (NTL) return wld16nt(p);
+    else return *NT_GPTR(u32x4, p);
+  }
+  static __device__ __forceinline__ Raw load(const uint8_t* rowp, int cols, int step, int lane) {
+    const int nsb = cols >> 8;
+    int sb = step * 16 + (lane >> 2);
+    sb = sb < nsb ? sb : 0;
+    const int g = lane & 3;
+    Raw r;
+    r.hd = ld(rowp + q4kt_head(nsb, sb));
+    r.qa = ld(rowp + q4kt_qa(nsb, sb, g));
+    r.qb = ld(rowp + q4kt_qb(nsb, sb, g));
+    return r;
+  }
+};
+
 // Q5_K: the Q4_K lane layout over a 176-byte superblock (16-byte aligned: no phases), with
 // a fifth code bit worth 16: column l (0..31) of sub-block j has it in bit j of high-bit byte
 // l (bytes 16..47, which all four lanes of the superblock read).  Run h of the quarter takes
@@ -1037,9 +1066,15 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
 }
 
 // Format "masks" of the kernels instantiated for q/k/v launches whose segments are Q4_K,
-// Q4_K, Q6_K or Q5_K, Q5_K, Q6_K in that order (the Q4_K_M and Q5_K_M layers).
+// Q4_K, Q6_K or Q5_K, Q5_K, Q6_K or Q4_KT, Q4_KT, Q6_K in that order (the Q4_K_M and Q5_K_M
+// layers).
 constexpr int FMTS_Q4K_Q4K_Q6K = 1 << 8;
 constexpr int FMTS_Q5K_Q5K_Q6K = 1 << 9;
+constexpr int FMTS_Q4KT_Q4KT_Q6K = 1 << 10;
+// With a Q4_KT segment: its loads take the nontemporal policy (launches of at least 10^8
+// weights).
+constexpr int FMT_NTL = 1 << 11;
+constexpr bool is_fixed_qkv(int m) { return m == FMTS_Q4K_Q4K_Q6K || m == FMTS_Q5K_Q5K_Q6K || m == FMTS_Q4KT_Q4KT_Q6K; }
 
 // Segment s with its format's work loop (STAGE: the first segment, which stages x).
 template <int FMTMASK, int R, int EPI, bool STAGE>
@@ -1055,6 +1090,10 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
       break;
     case FMT_Q4_K:
       if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
+      break;
+    case FMT_Q4_KT:
+      if constexpr ((FMTMASK >> FMT_Q4_KT) & 1)
+        run_segment<Q4_KTF<(FMTMASK & FMT_NTL) != 0>, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     case FMT_Q5_K:
       if constexpr ((FMTMASK >> FMT_Q5_K) & 1) run_segment<Q5_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
@@ -1074,7 +1113,7 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
 // At least four waves per SIMD (at most 128 VGPRs): the stream needs many waves in flight.
 // Which staged forms of x a launch's formats read: the limbs (quantized formats) and/or the
 // fp32 copy (F16, F32).
-constexpr bool mask_has_q(int m) { return (m & (0x1F | FMTS_Q4K_Q4K_Q6K | FMTS_Q5K_Q5K_Q6K)) != 0; }
+constexpr bool mask_has_q(int m) { return (m & (0x1F | (1 << FMT_Q4_KT) | FMTS_Q4K_Q4K_Q6K | FMTS_Q5K_Q5K_Q6K | FMTS_Q4KT_Q4KT_Q6K)) != 0; }
 constexpr bool mask_has_f(int m) { return (m & ((1 << FMT_F16) | (1 << FMT_F32))) != 0; }
 
 template <int FMTMASK, int R, int NW, int EPI>
@@ -1104,11 +1143,12 @@ __global__ __launch_bounds__(NW * 64, 4) void gemv_kernel(const GemvArgs a) {
   // x is loaded first (its loads then complete before the weights'); the first segment
   // stages it after issuing its first weight loads
   const XPre xpre = stage_x_load(a);
-  if constexpr (FMTMASK == FMTS_Q4K_Q4K_Q6K || FMTMASK == FMTS_Q5K_Q5K_Q6K) {
+  if constexpr (is_fixed_qkv(FMTMASK)) {
     // the three segments' formats fixed at compile time: straight-line code, so registers
     // are allocated per segment rather than for every format at every segment
     constexpr int D = GEMV_DEPTH<EPI>;
-    using FK = std::conditional_t<FMTMASK == FMTS_Q4K_Q4K_Q6K, Q4_KF, Q5_KF>;
+    using FK = std::conditional_t<FMTMASK == FMTS_Q4K_Q4K_Q6K, Q4_KF,
+                                  std::conditional_t<FMTMASK == FMTS_Q4KT_Q4KT_Q6K, Q4_KTF<false>, Q5_KF>>;
     run_segment<FK, R, EPI, D, true>(a, 0, lane, wid, W, xs, red, xscale, best, rope, xpre);
     run_segment<FK, R, EPI, D, false>(a, 1, lane, wid, W, xs, red, xscale, best, rope, XPre{});
     run_segment<Q6_KF, R, EPI, D, false>(a, 2, lane, wid, W, xs, red, xscale, best, rope, XPre{});
@@ -1265,7 +1305,7 @@ __device__ __forceinline__ void gemm_rows(const GemmArgs& a, const XLimbs (&xs)[
   int ck = wid, ct = 0, item = 0;
   auto step = [&](const Raw (&cur)[R], Raw (&refill)[R]) -> bool {
     issue(refill);  // unconditional: the wait for this item leaves the next one in flight
-    if constexpr (std::is_same<F, Q4_KF>::value || std::is_same<F, Q5_KF>::value) {
+    if constexpr (std::is_base_of<Q4_KF, F>::value || std::is_same<F, Q5_KF>::value) {
       KDec<R> dec;
       kdecode<F, R>(cur, a.cols, ct, lane, dec);
 #pragma unroll
@@ -1329,7 +1369,7 @@ __device__ __forceinline__ void gemm_stage(const GemmArgs& a, int t, const XLimb
 // and NT tokens' accumulators would not fit the registers (Q5_K: five 128-bit loads per row;
 // Q4_K from two tokens on; Q6_K at 8 tokens).
 template <int FMT, int NT>
-constexpr int GEMM_ROWS = (FMT == FMT_Q5_K || (FMT == FMT_Q4_K && NT >= 2) || (FMT == FMT_Q6_K && NT == 8)) ? 1 : 2;
+constexpr int GEMM_ROWS = (FMT == FMT_Q5_K || ((FMT == FMT_Q4_K || FMT == FMT_Q4_KT) && NT >= 2) || (FMT == FMT_Q6_K && NT == 8)) ? 1 : 2;
 
 template <int FMT, int NT, int NW>
 __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
@@ -1356,6 +1396,7 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   if constexpr (FMT == FMT_Q8_0) gemm_rows<Q8_0F, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q4_0) gemm_rows<Q4_0F, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q4_K) gemm_rows<Q4_KF, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_Q4_KT) gemm_rows<Q4_KTF<false>, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q5_K) gemm_rows<Q5_KF, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_F16) gemm_rows<F16F, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_F32) gemm_rows<F32F, NT, R>(a, xs, lane, wid, W);
@@ -2215,8 +2256,8 @@ static size_t lds_for(int cols, int inst) {
 static int inst_mask(int m) {
   switch (m) {
     case 1 << FMT_Q8_0: case 1 << FMT_Q4_0: case 1 << FMT_Q4_K: case 1 << FMT_Q6_K: case 1 << FMT_Q5_K:
-    case 1 << FMT_F16: case 1 << FMT_F32:
-    case (1 << FMT_Q5_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_K) | (1 << FMT_Q6_K):
+    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT:
+    case (1 << FMT_Q5_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_KT) | (1 << FMT_Q6_K):
       return m;
     default:
       return (1 << FMT_COUNT) - 1;
@@ -2227,7 +2268,7 @@ static int inst_mask(int m) {
 static bool one_row_mask(int m) {
   switch (m) {
     case 1 << FMT_Q8_0: case 1 << FMT_Q4_0: case 1 << FMT_Q4_K: case 1 << FMT_Q6_K: case 1 << FMT_Q5_K:
-    case 1 << FMT_F16: case 1 << FMT_F32:
+    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT:
       return true;
     default:
       return false;
@@ -2291,7 +2332,8 @@ static hipError_t launch_nw_r(const GemvPlan& plan, int n_groups, const GemvArgs
 template <int FMTMASK, int EPI>
 static hipError_t launch_nw(const GemvPlan& plan, int n_groups, const GemvArgs& a, hipStream_t s) {
   constexpr int R = GEMV_ROWS<EPI>;
-  if constexpr (R == 2 && EPI != EPI_QKV && (FMTMASK & (FMTMASK - 1)) == 0 && FMTMASK < (1 << FMT_COUNT)) {
+  constexpr int FM = FMTMASK & ~FMT_NTL;
+  if constexpr (R == 2 && EPI != EPI_QKV && (FM & (FM - 1)) == 0 && FM < (1 << FMT_COUNT)) {
     if (plan.rows_per_wave == 1) return launch_nw_r<FMTMASK, EPI, 1>(plan, n_groups, a, s);
   }
   if (plan.rows_per_wave != R) return hipErrorInvalidConfiguration;
@@ -2320,6 +2362,14 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
           return launch_nw<FMTS_Q4K_Q4K_Q6K, EPI>(plan, n_groups, a, s);
       }
       return launch_nw<(1 << FMT_Q4_K) | (1 << FMT_Q6_K), EPI>(plan, n_groups, a, s);
+    case 1 << FMT_Q4_KT: return launch_nw<1 << FMT_Q4_KT, EPI>(plan, n_groups, a, s);
+    case (1 << FMT_Q4_KT) | FMT_NTL: return launch_nw<(1 << FMT_Q4_KT) | FMT_NTL, EPI>(plan, n_groups, a, s);
+    case (1 << FMT_Q4_KT) | (1 << FMT_Q6_K):
+      if constexpr (EPI == EPI_QKV) {
+        if (a.nseg == 3 && a.seg[0].fmt == FMT_Q4_KT && a.seg[1].fmt == FMT_Q4_KT && a.seg[2].fmt == FMT_Q6_K)
+          return launch_nw<FMTS_Q4KT_Q4KT_Q6K, EPI>(plan, n_groups, a, s);
+      }
+      return launch_nw<(1 << FMT_Q4_KT) | (1 << FMT_Q6_K), EPI>(plan, n_groups, a, s);
     default: return launch_nw<(1 << FMT_COUNT) - 1, EPI>(plan, n_groups, a, s);
   }
 }
@@ -2397,8 +2447,9 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, int n_groups, h
     const GemvSeg& g = a.seg[i];
     if (st_family(g.fmt) != kf) return hipErrorNotSupported;
     // Q4_K measured faster on the register path (also with integer dot products here:
-    // 64.7 vs 49.9 us for the 70B gate/up pair); Q5_K, its 5-bit sibling, has only that path
-    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q5_K || is_float_fmt(g.fmt)) return hipErrorNotSupported;
+    // 64.7 vs 49.9 us for the 70B gate/up pair); Q5_K, its 5-bit sibling, and Q4_KT, its
+    // tiled form, have only that path
+    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q4_KT || g.fmt == FMT_Q5_K || is_float_fmt(g.fmt)) return hipErrorNotSupported;
     if ((reinterpret_cast<uintptr_t>(g.w) & 15) || (g.row_bytes & 15) || g.rows <= 0) return hipErrorNotSupported;
   }
   if ((reinterpret_cast<uintptr_t>(a.x) & 15) || (a.gain && (reinterpret_cast<uintptr_t>(a.gain) & 15)))
@@ -2473,6 +2524,11 @@ hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups
   if (NT_GEMV_STREAM) {
     const hipError_t e = gemv_stream_launch(epi, a, n_groups, s);
     if (e != hipErrorNotSupported) return e;
+  }
+  if (fmt_mask == 1 << FMT_Q4_KT) {
+    int64_t weights = 0;
+    for (int i = 0; i < (epi == EPI_SWIGLU ? 2 : a.nseg); ++i) weights += (int64_t)a.seg[i].rows * a.cols;
+    if (weights >= 100000000) fmt_mask |= FMT_NTL;
   }
   switch (epi) {
     case EPI_STORE: return launch_mask<EPI_STORE>(fmt_mask, plan, n_groups, a, s);
@@ -2552,7 +2608,10 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
                        hipStream_t s, bool accum) {
   const int be = block_elems(fmt), bb = block_bytes(fmt);
   const bool mm = gemm_use_mfma(fmt, n_tok);
-  const int chunk = mm ? gemm_mfma_chunk_cols(fmt, n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, fmt);
+  int chunk = mm ? gemm_mfma_chunk_cols(fmt, n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, fmt);
+  // Q4_KT chunks start at tile boundaries (16 superblocks, 4096 columns), so that each chunk's
+  // tiles are laid out as those of a row of its own width
+  if (fmt == FMT_Q4_KT && chunk < cols) chunk -= chunk % 4096;
   if (chunk <= 0) return hipErrorInvalidValue;
   GemmArgs a;
   a.row_bytes = (int64_t)(cols / be) * bb;
@@ -2587,6 +2646,7 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
       case FMT_Q8_0: e = gemm_launch_fmt<FMT_Q8_0>(n_tok, a, s); break;
       case FMT_Q4_0: e = gemm_launch_fmt<FMT_Q4_0>(n_tok, a, s); break;
       case FMT_Q4_K: e = gemm_launch_fmt<FMT_Q4_K>(n_tok, a, s); break;
+      case FMT_Q4_KT: e = gemm_launch_fmt<FMT_Q4_KT>(n_tok, a, s); break;
       case FMT_Q5_K: e = gemm_launch_fmt<FMT_Q5_K>(n_tok, a, s); break;
       case FMT_F16: e = gemm_launch_fmt<FMT_F16>(n_tok, a, s); break;
       case FMT_F32: e = gemm_launch_fmt<FMT_F32>(n_tok, a, s); break;

@@ -67,6 +67,31 @@ __device__ void dequant_group(int fmt, const uint8_t* blk, int grp, float* out) 
   }
 }
 
+// Superblock b of a Q4_KT row (tiles of 16, common.h) gathered back into Q4_K's byte order.
+__device__ void q4kt_gather(const uint8_t* row, int nsb, int b, uint8_t* out) {
+  const uint8_t* hd = row + q4kt_head(nsb, b);
+  for (int i = 0; i < 16; ++i) out[i] = hd[i];
+  for (int g = 0; g < 4; ++g) {
+    const uint8_t* qa = row + q4kt_qa(nsb, b, g);
+    const uint8_t* qb = row + q4kt_qb(nsb, b, g);
+    for (int i = 0; i < 16; ++i) {
+      out[16 + 32 * g + i] = qa[i];
+      out[32 + 32 * g + i] = qb[i];
+    }
+  }
+}
+
+// 32 weights of group grp (of block b) of a row starting at row, any format.
+__device__ void dequant_row_group(int fmt, const uint8_t* row, int64_t cols, int64_t b, int grp, float* out) {
+  if (fmt == FMT_Q4_KT) {
+    uint8_t blk[144];
+    q4kt_gather(row, (int)(cols >> 8), (int)b, blk);
+    dequant_group(FMT_Q4_K, blk, grp, out);
+  } else {
+    dequant_group(fmt, row + b * block_bytes(fmt), grp, out);
+  }
+}
+
 __global__ void dequant_kernel(int fmt, int64_t rows, int64_t cols, const uint8_t* __restrict__ blocks,
                                float* __restrict__ w) {
   const int be = block_elems(fmt), bb = block_bytes(fmt);
@@ -77,12 +102,40 @@ __global__ void dequant_kernel(int fmt, int64_t rows, int64_t cols, const uint8_
     const int64_t c0 = cg * 32;
     const int64_t b = c0 / be;
     const int grp = (int)((c0 % be) / 32);
-    const uint8_t* blk = blocks + (r * (cols / be) + b) * bb;
     float tmp[32];
-    dequant_group(fmt, blk, grp, tmp);
+    dequant_row_group(fmt, blocks + r * (cols / be) * bb, cols, b, grp, tmp);
     float* o = w + r * cols + c0;
     for (int i = 0; i < 32; ++i) o[i] = tmp[i];
   }
+}
+
+// Q4_K -> Q4_KT: one thread per 16-byte part of the output.  Part k of tile t (m superblocks)
+// is, in the tile's Q4_K bytes (9 parts per superblock: header, then code bytes in 16-byte
+// runs), part 9k (k < m: headers), 9j + 1 + 2g (k = m + 4j + g: first halves of the quarters)
+// or 9j + 2 + 2g (k = 5m + 4j + g: second halves).
+__global__ void repack_q4kt_kernel(int64_t rows, int nsb, const uint8_t* __restrict__ src, uint8_t* __restrict__ dst) {
+  const int64_t per_row = 9 * (int64_t)nsb, total = rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / per_row;
+    const int c = (int)(i % per_row);
+    const int t = c / 144, k = c % 144;
+    const int m = nsb - 16 * t < 16 ? nsb - 16 * t : 16;
+    int from;
+    if (k < m) from = 9 * k;
+    else if (k < 5 * m) from = 9 * ((k - m) >> 2) + 1 + 2 * ((k - m) & 3);
+    else from = 9 * ((k - 5 * m) >> 2) + 2 + 2 * ((k - 5 * m) & 3);
+    const int64_t tile = r * 144 * (int64_t)nsb + 2304 * (int64_t)t;
+    *reinterpret_cast<uint4*>(dst + tile + 16 * k) = *reinterpret_cast<const uint4*>(src + tile + 16 * from);
+  }
+}
+
+hipError_t repack_q4kt_launch(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s) {
+  const int64_t total = rows * 9 * (cols >> 8);
+  const int64_t nb = (total + 255) / 256;
+  const int grid = (int)(nb < 65536 ? nb : 65536);
+  hipLaunchKernelGGL(repack_q4kt_kernel, dim3(grid), dim3(256), 0, s, rows, (int)(cols >> 8),
+                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint8_t*>(dst));
+  return hipGetLastError();
 }
 
 hipError_t dequant_launch(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, hipStream_t s) {
@@ -108,8 +161,7 @@ __global__ void embed_kernel(int fmt, int64_t n_vocab, int64_t dim, const uint8_
     float tmp[32];
     if (tok >= 0 && tok < n_vocab) {
       const int64_t c0 = gi * 32;
-      const uint8_t* blk = table + ((int64_t)tok * (dim / be) + c0 / be) * bb;
-      dequant_group(fmt, blk, (int)((c0 % be) / 32), tmp);
+      dequant_row_group(fmt, table + (int64_t)tok * (dim / be) * bb, dim, c0 / be, (int)((c0 % be) / 32), tmp);
     } else {
       for (int i = 0; i < 32; ++i) tmp[i] = 0.f;
     }

@@ -36,8 +36,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_block_geometry():
-    assert [nt.nt_block_elems(f) for f in range(7)] == [32, 32, 256, 256, 256, 1, 1]
-    assert [nt.nt_block_bytes(f) for f in range(7)] == [34, 18, 144, 210, 176, 2, 4]
+    assert [nt.nt_block_elems(f) for f in range(8)] == [32, 32, 256, 256, 256, 1, 1, 256]
+    assert [nt.nt_block_bytes(f) for f in range(8)] == [34, 18, 144, 210, 176, 2, 4, 144]
+    assert nt.nt_matrix_bytes(nt.Q4_KT, 28672, 8192) == nt.nt_matrix_bytes(nt.Q4_K, 28672, 8192)
     assert nt.nt_matrix_bytes(nt.F16, 28672, 8192) == 2 * 28672 * 8192
     assert nt.nt_matrix_bytes(nt.Q5_K, 28672, 8192) == 161_480_704
     assert nt.nt_matrix_bytes(nt.Q6_K, 8192, 28672) == 192_675_840
@@ -52,7 +53,13 @@ def test_block_geometry():
     (lambda: nt.nt_gemv_q(nt.Q8_0, 16, 256, None, 16, 16), nt.NT_EINVAL),
     (lambda: nt.nt_gemv_q(nt.Q8_0, 16, 256, 18, 16, 16), nt.NT_EALIGN),
     (lambda: nt.nt_dequant(nt.Q6_K, 4, 255, 16, 16), nt.NT_ESHAPE),
-    (lambda: nt.nt_gemv_q(7, 16, 256, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemv_q(8, 16, 256, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_repack(nt.Q4_K, 16, 256, 16, 4096, 16), nt.NT_EFORMAT),  # Q4_KT is the only target
+    (lambda: nt.nt_repack(nt.Q4_KT, 16, 200, 16, 4096, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_repack(nt.Q4_KT, 0, 256, 16, 4096, 16), nt.NT_ESHAPE),
+    (lambda: nt.nt_repack(nt.Q4_KT, 16, 256, None, 4096, 16), nt.NT_EINVAL),
+    (lambda: nt.nt_repack(nt.Q4_KT, 16, 256, 24, 4096, 16), nt.NT_EALIGN),
+    (lambda: nt.nt_repack(nt.Q4_KT, 16, 256, 4096, 4096 + 2304 - 16, 16), nt.NT_EINVAL),  # overlap
     (lambda: nt.nt_gemv_q(nt.F16, 16, 40, 16, 16, 16), nt.NT_ESHAPE),  # F16/F32 columns: multiples of 32
     (lambda: nt.nt_gemm_q(nt.F32, 16, 48, 2, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_dequant(nt.F16, 4, 16, 16, 16), nt.NT_ESHAPE),
@@ -64,7 +71,7 @@ def test_block_geometry():
     (lambda: nt.nt_read_probe(16, 24, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_read_probe(None, 16, 16), nt.NT_EINVAL),
     (lambda: nt.nt_read_probe(8, 16, 16), nt.NT_EALIGN),
-    (lambda: nt.nt_gemm_q(7, 16, 256, 2, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemm_q(8, 16, 256, 2, 16, 16, 16), nt.NT_EFORMAT),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, 0, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, nt.GEMM_MAX_TOK + 1, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 200, 2, 16, 16, 16), nt.NT_ESHAPE),

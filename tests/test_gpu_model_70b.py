@@ -1,6 +1,8 @@
 """Full-depth parity of the benchmarked workload (MI355X only): the 80-layer
 Llama-3.1-70B-shaped model in the Q4_K_M mix, resident, one greedy token at position 4096
-after a 4096-slot fp16 cache, with its 128256 x 8192 LM head.
+after a 4096-slot fp16 cache, with its 128256 x 8192 LM head; as in the benchmark, the Q4_K
+matrices and the LM head are held in the library's tiled layout (nt_repack, NT_Q4_KT), and the
+checker reads the same weights in Q4_K's block order.
 
 The token is decoded with nt_decode_token, the call the benchmark times, then replayed layer
 by layer with nt_decode_layer (the same kernels: the replay must reach the same final hidden
@@ -40,7 +42,7 @@ def decoded():
     import bench
     nt.load()
     say("70B Q4_K_M, 80 layers resident: generating the model")
-    m = bench.Model70B(torch, nt, tg, MIX, N_LAYERS, range(N_LAYERS))
+    m = bench.Model70B(torch, nt, tg, MIX, N_LAYERS, range(N_LAYERS), tiles=True)
     plan, keep = m.plan()
     head = m.head()
     shp = tg.layer_shape(SHAPE)
