@@ -485,11 +485,11 @@ def bench_decode_70b(args, torch, nt, tg):
         "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales, sums and activations, f16 kv (q4_k/q6_k weights)", "data": "synthetic (seeded, random weights of the named shape)",
         "config": {"workload": "llama3.1-70b-shape Q4_K_M resident decode, 128256 vocab, 4096-slot fp16 KV prefill, "
-                               "greedy, batch 1", "layers": n_layers, "global_batch": 1, "seq_len": 4096 + steps,
+                               "greedy, batch 1 (Q4_K matrices and LM head held in the library's tiled Q4_K layout)", "layers": n_layers, "global_batch": 1, "seq_len": 4096 + steps,
                    "parallelism": "none (1 GPU)"},
         "step_hbm": {"algorithmic_bytes_per_token": int(tb), "GBps": tb * tok_s / 1e9,
                      "frac_of_peak": tb * tok_s / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up_swiglu (fused RMSNorm + Q4_K gate/up GEMV + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up_swiglu (fused RMSNorm + Q4_K gate/up GEMV + SwiGLU, tiled Q4_K layout)",
                      "achieved": fb / (ffn_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": fb / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "bytes_per_launch": fb, "avg_launch_us": ffn_us, "launches": n_ffn,
