@@ -9,7 +9,7 @@ decode layers, final norm, LM head and argmax, every kernel in libnt.so.
 
 Prints one JSON line.  Other workloads (--config) print their own line for measurement
 runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B GEMV
-shapes in Q4_K, Q6_K, Q5_K, F16 and F32, 5 = the 70B Q6_K model with 54 layers streamed from pinned
+shapes in Q4_K, Q6_K, Q5_K, F16, F32 and tiled Q4_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
 host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes, 7 = the 70B model with
 cosine-based layer skip (--skip layers, default 20 of 80), 8 = 70B Q6_K layers read from a file
 (--file-layers, default 8) through page-locked bounce buffers, 9 = the self-speculative
@@ -384,7 +384,7 @@ def cpu_baseline_70b(mix, target_s):
 
 def metric_extras(torch, nt, tg):
     """The GEMV and 8B halves of the metric, measured in the default run: the Q8_0 4096x4096
-    GEMV, the 70B GEMV shapes in Q4_K and Q6_K (rotating weight copies past the 256 MB
+    GEMV, the 70B GEMV shapes in Q4_K, Q6_K and the tiled Q4_K layout (rotating weight copies past the 256 MB
     last-level cache, HIP events around back-to-back launches) and one Llama-3-8B-shaped
     Q8_0 layer with its derived tokens/s."""
     import synth
@@ -394,7 +394,7 @@ def metric_extras(torch, nt, tg):
     out["gemv_q8_0_4096x4096"] = {k: g[k] for k in keys}
     torch.cuda.empty_cache()
     lst = []
-    for fmt in (synth.Q4_K, synth.Q6_K):
+    for fmt in (synth.Q4_K, synth.Q6_K, synth.Q4_KT):
         for r, c in ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)):
             nbytes = synth.matrix_bytes(fmt, r, c)
             g = rotating_gemv(torch, nt, fmt, r, c, max(2, int(np.ceil(600e6 / nbytes))), 200, 10)
@@ -572,11 +572,17 @@ def rotating_gemv(torch, nt, fmt, rows, cols, copies, steps, warmup, seed=0):
     y = torch.empty(rows, dtype=torch.float32, device="cuda")
     nbytes = synth.matrix_bytes(fmt, rows, cols)
     hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    cs = torch.cuda.current_stream().cuda_stream
+    gen = synth.Q4_K if fmt == synth.Q4_KT else fmt  # Q4_KT: Q4_K blocks rearranged on the device
     ws = []
     for c in range(copies):
-        synth.fill_blocks(hb.data_ptr(), fmt, nbytes // synth.BLOCK_BYTES[fmt], seed, 5000 + c)
-        ws.append(hb.cuda())
-    cs = torch.cuda.current_stream().cuda_stream
+        synth.fill_blocks(hb.data_ptr(), gen, nbytes // synth.BLOCK_BYTES[gen], seed, 5000 + c)
+        d = hb.cuda()
+        if fmt == synth.Q4_KT:
+            t = torch.empty_like(d)
+            nt.nt_repack(synth.Q4_KT, rows, cols, d.data_ptr(), t.data_ptr(), cs)
+            d = t
+        ws.append(d)
 
     def run(n):
         for i in range(n):
@@ -611,7 +617,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
     if args.config == 1:
         shapes = [(synth.Q8_0, 4096, 4096)]
     else:
-        shapes = [(f, r, c) for f in (synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32)
+        shapes = [(f, r, c) for f in (synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32, synth.Q4_KT)
                   for (r, c) in ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672))]
     for fmt, r, c in shapes:
         nbytes = synth.matrix_bytes(fmt, r, c)
@@ -627,7 +633,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
         "value": best["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": best["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales and sums (quantized weights)", "data": "synthetic",
-        "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K, Q5_K, F16 and F32"},
+        "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K, Q5_K, F16, F32 and tiled Q4_K"},
         "roofline": {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": best["frac_of_peak"], "traffic": None},
         "gemv": out,
