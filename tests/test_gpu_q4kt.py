@@ -183,3 +183,44 @@ def test_decode_layer_tiled_equals_q4_k(shape, pos):
         outs.append([host(h).view(np.uint32).copy(), host(kc).copy(), host(vc).copy(), host(ws).copy()])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("n_tok", [2, 5])
+def test_decode_layer_k_tiled(n_tok):
+    """The k-token layer (the verification pass) over tiled Q4_K matrices: the k-token GEMM runs
+    on the vector units for Q4_KT at every k, so with two tokens (vector units for Q4_K too) the
+    outputs are bit for bit those of the Q4_K weights, and with five (matrix cores for Q4_K)
+    they agree to rounding."""
+    shape, pos = SMALL, 40
+    say(f"k-token layer Q4_K_M with tiled Q4_K, k={n_tok}, pos={pos}")
+    mix = recipes.MIX_Q4_K_M
+    arrays = recipes.layer_arrays(shape, mix, 0)
+    w_k = {k: dev(v) for k, v in arrays.items()}
+    w_t = dict(w_k)
+    fm_t = {n: mix[n] for n in recipes.TENSORS}
+    for n in recipes.TENSORS:
+        if mix[n] == Q4K:
+            w_t[n] = repack(*shape.matrix_shape(n), w_k[n])
+            fm_t[n] = Q4KT
+    shp = tg.layer_shape(shape)
+    wsb = nt.nt_decode_layer_k_ws_bytes(shp, n_tok)
+    kc0 = recipes.kv_cache_array(shape, 0, "k", pos)
+    vc0 = v_to_device(recipes.kv_cache_array(shape, 0, "v", pos), shape.n_kv_heads, shape.max_ctx)
+    h0 = np.stack([recipes.hidden_input(shape.dim, seed=t) for t in range(n_tok)]).astype(np.float32)
+    outs = []
+    for fm, w in (({n: mix[n] for n in recipes.TENSORS}, w_k), (fm_t, w_t)):
+        lw = tg.layer_weights([fm[n] for n in recipes.TENSORS], [w[n] for n in recipes.TENSORS], w["attn_norm"],
+                              w["ffn_norm"])
+        h, kc, vc = dev(h0), dev(kc0), dev(vc0)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        nt.nt_decode_layer_k(lw, shp, pos, n_tok, h.data_ptr(), kc.data_ptr(), vc.data_ptr(), ws.data_ptr(), wsb,
+                             stream())
+        torch.cuda.synchronize()
+        outs.append((host(h).copy(), host(kc).copy(), host(vc).copy()))
+    (h_k, kc_k, vc_k), (h_t, kc_t, vc_t) = outs
+    if n_tok == 2:
+        assert np.array_equal(h_k.view(np.uint32), h_t.view(np.uint32))
+        assert np.array_equal(kc_k, kc_t) and np.array_equal(vc_k, vc_t)
+    else:
+        scale = np.abs(h_k).max()
+        assert np.max(np.abs(h_k - h_t)) <= 1e-4 * scale
