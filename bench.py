@@ -153,10 +153,11 @@ class Model70B:
         self.torch, self.nt, self.tg = torch, nt, tg
         self.shape = recipes.LLAMA31_70B if shape is None else shape
         self.mix = mix
-        # tiles: the resident layers' Q4_K matrices and the Q4_K LM head rearranged on the device
-        # into the GEMV's tiled layout (nt_repack, Q4_KT); the same weights
+        # tiles: the resident layers' Q4_K and Q8_0 matrices and such an LM head rearranged on the
+        # device into the GEMV's tiled layouts (nt_repack: Q4_KT, Q8_0T); the same weights
         self.tiles = tiles
-        self.fmts = {n: (synth.Q4_KT if tiles and mix[n] == synth.Q4_K else mix[n]) for n in recipes.TENSORS}
+        tiled_fmt = {synth.Q4_K: synth.Q4_KT, synth.Q8_0: synth.Q8_0T}
+        self.fmts = {n: (tiled_fmt.get(mix[n], mix[n]) if tiles else mix[n]) for n in recipes.TENSORS}
         self.n_layers = n_layers
         self.vocab = recipes.VOCAB_70B
         self.lay = recipes.blob_layout(self.shape, mix)
@@ -198,7 +199,7 @@ class Model70B:
                 for n in tiled:
                     rows, cols = self.shape.matrix_shape(n)
                     o, nb = self.lay.offsets[n], nbytes[n]
-                    nt.nt_repack(synth.Q4_KT, rows, cols, self.dev_blobs[l][o:].data_ptr(), scratch.data_ptr(), cs)
+                    nt.nt_repack(self.fmts[n], rows, cols, self.dev_blobs[l][o:].data_ptr(), scratch.data_ptr(), cs)
                     self.dev_blobs[l][o:o + nb].copy_(scratch[:nb])
             torch.cuda.synchronize()
             del scratch
@@ -229,9 +230,9 @@ class Model70B:
         del hb
         # the LM head the decode reads (self.out stays in Q4_K's block order for the checker)
         self.head_fmt, self.head_out = out_fmt, self.out
-        if tiles and out_fmt == synth.Q4_K:
-            self.head_fmt, self.head_out = synth.Q4_KT, torch.empty_like(self.out)
-            nt.nt_repack(synth.Q4_KT, self.vocab, shp.dim, self.out.data_ptr(), self.head_out.data_ptr(),
+        if tiles and out_fmt in tiled_fmt:
+            self.head_fmt, self.head_out = tiled_fmt[out_fmt], torch.empty_like(self.out)
+            nt.nt_repack(self.head_fmt, self.vocab, shp.dim, self.out.data_ptr(), self.head_out.data_ptr(),
                          torch.cuda.current_stream().cuda_stream)
         self.onorm = torch.from_numpy(synth.uniform_f32(shp.dim, seed, recipes.stream_id(recipes.GLOBAL_LAYER,
                                                                                           recipes.GID_OUTPUT_NORM),
@@ -573,14 +574,14 @@ def rotating_gemv(torch, nt, fmt, rows, cols, copies, steps, warmup, seed=0):
     nbytes = synth.matrix_bytes(fmt, rows, cols)
     hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     cs = torch.cuda.current_stream().cuda_stream
-    gen = synth.Q4_K if fmt == synth.Q4_KT else fmt  # Q4_KT: Q4_K blocks rearranged on the device
+    gen = {synth.Q4_KT: synth.Q4_K, synth.Q8_0T: synth.Q8_0}.get(fmt, fmt)  # tiled: GGUF blocks rearranged on the device
     ws = []
     for c in range(copies):
         synth.fill_blocks(hb.data_ptr(), gen, nbytes // synth.BLOCK_BYTES[gen], seed, 5000 + c)
         d = hb.cuda()
-        if fmt == synth.Q4_KT:
+        if gen != fmt:
             t = torch.empty_like(d)
-            nt.nt_repack(synth.Q4_KT, rows, cols, d.data_ptr(), t.data_ptr(), cs)
+            nt.nt_repack(fmt, rows, cols, d.data_ptr(), t.data_ptr(), cs)
             d = t
         ws.append(d)
 
@@ -765,7 +766,7 @@ def decode_8b_measure(torch, nt, tg, steps=128, warmup=4):
     import synth
     n0 = recipes.LLAMA3_8B.max_ctx - steps
     m = Model70B(torch, nt, tg, recipes.MIX_Q8_0, 32, range(32), n_prefill=n0, shape=recipes.LLAMA3_8B,
-                 head_fmt=synth.Q8_0)
+                 head_fmt=synth.Q8_0, tiles=True)
     plan, keep = m.plan()
     head = m.head()
     shp = tg.layer_shape(m.shape)
@@ -802,14 +803,21 @@ def decode_8b_measure(torch, nt, tg, steps=128, warmup=4):
 def layer_8b_measure(torch, nt, tg, steps, warmup):
     """One Llama-3-8B-shaped Q8_0 decode layer at pos 1023 over a 1024-slot cache, over 4 distinct
     layers' weights in rotation (past the 256 MB last-level cache), host-timed around the batch;
-    derived tokens/s = 1 / (32 layers + the Q8_0 128256 x 4096 LM head)."""
+    derived tokens/s = 1 / (32 layers + the Q8_0 128256 x 4096 LM head); the matrices in the
+    tiled Q8_0 layout (Q8_0T), as the whole-model measurement holds them."""
     import synth
     from synth import recipes
     shape, mix = recipes.LLAMA3_8B, recipes.MIX_Q8_0
     copies = 4
     lays = [recipes.layer_arrays(shape, mix, l) for l in range(copies)]
     dl = [{k: torch.from_numpy(v).cuda() for k, v in L.items()} for L in lays]
-    ws_list = [tg.layer_weights([mix[n] for n in recipes.TENSORS], [d[n] for n in recipes.TENSORS], d["attn_norm"],
+    cs0 = torch.cuda.current_stream().cuda_stream
+    for d in dl:
+        for n in recipes.TENSORS:
+            t = torch.empty_like(d[n])
+            nt.nt_repack(synth.Q8_0T, *shape.matrix_shape(n), d[n].data_ptr(), t.data_ptr(), cs0)
+            d[n] = t
+    ws_list = [tg.layer_weights([synth.Q8_0T] * len(recipes.TENSORS), [d[n] for n in recipes.TENSORS], d["attn_norm"],
                                 d["ffn_norm"]) for d in dl]
     kc = torch.from_numpy(recipes.kv_cache_array(shape, 0, "k", 1024)).cuda()
     vc = v_to_device_layout(torch, torch.from_numpy(recipes.kv_cache_array(shape, 0, "v", 1024)).cuda(),
@@ -831,7 +839,7 @@ def layer_8b_measure(torch, nt, tg, steps, warmup):
     run(steps)
     torch.cuda.synchronize()
     t_layer = (time.perf_counter() - t0) / steps
-    lm = rotating_gemv(torch, nt, synth.Q8_0, 128256, 4096, 2, 50, 5)
+    lm = rotating_gemv(torch, nt, synth.Q8_0T, 128256, 4096, 2, 50, 5)
     tok_s = 1.0 / (32 * t_layer + lm["avg_us"] * 1e-6)
     lb = recipes.layer_weight_bytes(shape, mix) + 2 * 8 * 1024 * 128 * 2
     del dl, ws_list

@@ -67,11 +67,18 @@ extern "C" {
  *            which lets the GEMV stream them with the nontemporal policy.  Embedding rows,
  *            nt_dequant, the GEMV and the k-token GEMM (on the vector units) read it;
  *            nt_gemv_q and the layer calls never take the streamed path for it.
+ *   NT_Q8_0T  NT_Q8_0's bytes, each row's blocks rearranged in tiles of 64 (made by nt_repack;
+ *            34 B per 32 weights, the same weights; cols a multiple of 256 so that rows stay
+ *            16-byte multiples).  Tile t of a row (blocks 64t .. 64t+m-1, m = min(64, nb - 64t),
+ *            nb = cols/32) starts at byte 2176t and holds, in block order, the first 16 codes of
+ *            each block (block bytes 2..17), then the last 16 (bytes 18..33), then the m fp16
+ *            scales (bytes 0..1): lane l of a wave reads block l's parts, each load whole lines.
+ *            Read where NT_Q4_KT is (register path only, nontemporal loads from 10^8 weights).
  * Every entry point that takes cols for NT_F16 / NT_F32 needs a multiple of 32 (so that rows
  * keep the 16-byte alignment the loads use).
  */
 typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4, NT_F16 = 5, NT_F32 = 6,
-               NT_Q4_KT = 7 } nt_format;
+               NT_Q4_KT = 7, NT_Q8_0T = 8 } nt_format;
 
 typedef enum {
   NT_OK = 0,
@@ -102,13 +109,14 @@ int64_t nt_matrix_bytes(int fmt, int64_t rows, int64_t cols); /* bytes of a rows
  * blocks: 4-byte aligned.  Returns NT_ESHAPE if cols % block_elems != 0. */
 int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, void* stream);
 
-/* Rearrange a Q4_K matrix (rows x cols, GGUF's block order) into the NT_Q4_KT layout above:
- * a layout of the same weights for the GEMV's loads ("Überblick über NTransformer" names
- * Q4_K_M; the tiles are this library's own).  fmt: the target layout, NT_Q4_KT only (else
- * NT_EFORMAT).  cols: a positive multiple of 256 up to 2^24; rows <= NT_MAX_ROWS (else
- * NT_ESHAPE).  src, dst: device, 16-byte aligned (NT_EALIGN), rows*cols/256*144 bytes each,
- * not overlapping (NT_EINVAL; the caller copies back if it wants the matrix in place).
- * Enqueued on stream; src is only read. */
+/* Rearrange a Q4_K or Q8_0 matrix (rows x cols, GGUF's block order) into the NT_Q4_KT or
+ * NT_Q8_0T layout above: a layout of the same weights for the GEMV's loads ("Überblick über
+ * NTransformer" names the formats; the tiles are this library's own).  fmt: the target layout,
+ * NT_Q4_KT (src in NT_Q4_K) or NT_Q8_0T (src in NT_Q8_0), else NT_EFORMAT.  cols: a positive
+ * multiple of 256 up to 2^24; rows <= NT_MAX_ROWS (else NT_ESHAPE).  src, dst: device,
+ * 16-byte aligned (NT_EALIGN), nt_matrix_bytes(fmt, rows, cols) bytes each, not overlapping
+ * (NT_EINVAL; the caller copies back if it wants the matrix in place).  Enqueued on stream;
+ * src is only read. */
 int nt_repack(int fmt, int64_t rows, int64_t cols, const void* src, void* dst, void* stream);
 
 /* y = W x for a block-quantized W (rows x cols), x and y fp32.

@@ -7,15 +7,16 @@
 
 namespace nt {
 
-// F16 and F32 are unquantized weight tensors: one weight per "block".  Q4_KT holds Q4_K's
-// bytes rearranged in tiles of 16 superblocks (q4kt_* below).
-enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4, FMT_F16 = 5, FMT_F32 = 6, FMT_Q4_KT = 7 };
-constexpr int FMT_COUNT = 8;
+// F16 and F32 are unquantized weight tensors: one weight per "block".  Q4_KT and Q8_0T hold
+// Q4_K's and Q8_0's bytes rearranged in tiles (q4kt_*, q8t_* below).
+enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4, FMT_F16 = 5, FMT_F32 = 6, FMT_Q4_KT = 7,
+       FMT_Q8_0T = 8 };
+constexpr int FMT_COUNT = 9;
 
 __host__ __device__ constexpr bool is_float_fmt(int f) { return f == FMT_F16 || f == FMT_F32; }
-__host__ __device__ constexpr int block_elems(int f) { return f <= FMT_Q4_0 ? 32 : is_float_fmt(f) ? 1 : 256; }
+__host__ __device__ constexpr int block_elems(int f) { return (f <= FMT_Q4_0 || f == FMT_Q8_0T) ? 32 : is_float_fmt(f) ? 1 : 256; }
 __host__ __device__ constexpr int block_bytes(int f) {
-  return f == FMT_Q8_0 ? 34 : f == FMT_Q4_0 ? 18 : (f == FMT_Q4_K || f == FMT_Q4_KT) ? 144 : f == FMT_Q5_K ? 176 : f == FMT_F16 ? 2
+  return (f == FMT_Q8_0 || f == FMT_Q8_0T) ? 34 : f == FMT_Q4_0 ? 18 : (f == FMT_Q4_K || f == FMT_Q4_KT) ? 144 : f == FMT_Q5_K ? 176 : f == FMT_F16 ? 2
          : f == FMT_F32 ? 4 : 210;
 }
 // Q4_KT: a row's Q4_K superblocks in tiles of 16 (the last tile of a row holds the m =
@@ -34,9 +35,24 @@ __host__ __device__ constexpr uint32_t q4kt_qb(int nsb, int b, int g) {
   return 144u * (uint32_t)(b & ~15) + 80u * q4kt_tile_m(nsb, b) + 16u * (4u * (uint32_t)(b & 15) + (uint32_t)g);
 }
 
+// Q8_0T: a row's Q8_0 blocks in tiles of 64 (the last tile of a row holds the m = nb - 64 t
+// left over), tile t at byte 2176 t of the row, so that a wave whose lane l takes block l of a
+// tile reads whole lines: the first 16 code bytes of each block in lane order (block bytes
+// 2..17), then the second 16 (bytes 18..33), then the m fp16 scales (bytes 0..1).  Rows must
+// be 16-byte multiples (cols a multiple of 256).
+__host__ __device__ constexpr uint32_t q8t_tile_m(int nb, int b) { return (uint32_t)(nb - (b & ~63) < 64 ? nb - (b & ~63) : 64); }
+__host__ __device__ constexpr uint32_t q8t_qa(int nb, int b) { return 34u * (uint32_t)(b & ~63) + 16u * (uint32_t)(b & 63); }
+__host__ __device__ constexpr uint32_t q8t_qb(int nb, int b) {
+  return 34u * (uint32_t)(b & ~63) + 16u * q8t_tile_m(nb, b) + 16u * (uint32_t)(b & 63);
+}
+__host__ __device__ constexpr uint32_t q8t_d(int nb, int b) {
+  return 34u * (uint32_t)(b & ~63) + 32u * q8t_tile_m(nb, b) + 2u * (uint32_t)(b & 63);
+}
+
 // Column granularity of the kernels: a block, and at least 32 columns (one scale block of the
-// staged activations; F16 and F32 rows are then 64- and 128-byte multiples).
-__host__ __device__ constexpr int col_unit(int f) { return block_elems(f) < 32 ? 32 : block_elems(f); }
+// staged activations; F16 and F32 rows are then 64- and 128-byte multiples); Q8_0T 256 columns
+// (16-byte rows).
+__host__ __device__ constexpr int col_unit(int f) { return f == FMT_Q8_0T ? 256 : block_elems(f) < 32 ? 32 : block_elems(f); }
 
 // 4-byte-aligned 128/64-bit vector types: global_load_dwordx4/x2 only need dword alignment,
 // and telling the compiler the true alignment keeps it from splitting or assuming more.

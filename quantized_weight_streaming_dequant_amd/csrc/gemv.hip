@@ -271,6 +271,12 @@ struct Q8_0F {
         for (int i = 0; i < 8; ++i) q[k][i] = raw[k].w[i];
       }
     }
+    apply<NR>(q, d, blk, xs, acc);
+  }
+  // acc[k] += d[k] s sum_i q[k][i] x~_i over block blk (32 int8 codes in 8 dwords)
+  template <int NR>
+  static __device__ __forceinline__ void apply(const uint32_t (&q)[NR][8], const float (&d)[NR], int blk,
+                                               const XLimbs& xs, float (&acc)[NR]) {
     int D[NR][XL];
     zero_limbs(D);
 #pragma unroll
@@ -285,6 +291,50 @@ struct Q8_0F {
     const float s = xs.sc[blk];
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] += (d[k] * s) * limb_sum(D[k]);
+  }
+};
+
+// Q8_0T: Q8_0 in tiles of 64 blocks (common.h); lane l takes block l of a tile, a step is one
+// tile, and the two 16-byte code loads and the 2-byte scale load of a wave each read whole
+// lines (1 KiB, 1 KiB, 128 B), with the nontemporal policy for launches of at least 10^8
+// weights (NTL) as for Q4_KT; the products are Q8_0F's.
+template <bool NTL>
+struct Q8_0TF {
+  struct Raw {
+    uint32_t w[8];
+    uint32_t e;
+  };
+  static __host__ __device__ __forceinline__ int steps(int cols) { return ((cols >> 5) + 63) / 64; }
+  static __device__ __forceinline__ u32x4 ld(const uint8_t* p) {
+    if constexpr (NTL) return __builtin_nontemporal_load(NT_GPTR(u32x4, p));
+    else return *NT_GPTR(u32x4, p);
+  }
+  static __device__ __forceinline__ Raw load(const uint8_t* rowp, int cols, int step, int lane) {
+    const int nb = cols >> 5;
+    int b = step * 64 + lane;
+    b = b < nb ? b : 0;
+    const u32x4 a = ld(rowp + q8t_qa(nb, b)), c = ld(rowp + q8t_qb(nb, b));
+    Raw r;
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = c.x; r.w[5] = c.y; r.w[6] = c.z; r.w[7] = c.w;
+    if constexpr (NTL) r.e = __builtin_nontemporal_load(NT_GPTR(uint16_t, rowp + q8t_d(nb, b)));
+    else r.e = *NT_GPTR(uint16_t, rowp + q8t_d(nb, b));
+    return r;
+  }
+  template <int NR>
+  static __device__ __forceinline__ void fma(const Raw (&raw)[NR], int cols, int step, int lane, const XLimbs& xs,
+                                             float (&acc)[NR]) {
+    const int blk = step * 64 + lane;
+    if (blk >= (cols >> 5)) return;
+    uint32_t q[NR][8];
+    float d[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      d[k] = h2f(raw[k].e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[k][i] = raw[k].w[i];
+    }
+    Q8_0F::apply<NR>(q, d, blk, xs, acc);
   }
 };
 
@@ -1068,12 +1118,12 @@ __device__ __forceinline__ void run_segment(const GemvArgs& a, int s, int lane, 
 // Format "masks" of the kernels instantiated for q/k/v launches whose segments are Q4_K,
 // Q4_K, Q6_K or Q5_K, Q5_K, Q6_K or Q4_KT, Q4_KT, Q6_K in that order (the Q4_K_M and Q5_K_M
 // layers).
-constexpr int FMTS_Q4K_Q4K_Q6K = 1 << 8;
-constexpr int FMTS_Q5K_Q5K_Q6K = 1 << 9;
-constexpr int FMTS_Q4KT_Q4KT_Q6K = 1 << 10;
-// With a Q4_KT segment: its loads take the nontemporal policy (launches of at least 10^8
-// weights).
-constexpr int FMT_NTL = 1 << 11;
+constexpr int FMTS_Q4K_Q4K_Q6K = 1 << 12;
+constexpr int FMTS_Q5K_Q5K_Q6K = 1 << 13;
+constexpr int FMTS_Q4KT_Q4KT_Q6K = 1 << 14;
+// With a Q4_KT or Q8_0T segment: its loads take the nontemporal policy (launches of at least
+// 10^8 weights).
+constexpr int FMT_NTL = 1 << 15;
 constexpr bool is_fixed_qkv(int m) { return m == FMTS_Q4K_Q4K_Q6K || m == FMTS_Q5K_Q5K_Q6K || m == FMTS_Q4KT_Q4KT_Q6K; }
 
 // Segment s with its format's work loop (STAGE: the first segment, which stages x).
@@ -1090,6 +1140,10 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
       break;
     case FMT_Q4_K:
       if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
+      break;
+    case FMT_Q8_0T:
+      if constexpr ((FMTMASK >> FMT_Q8_0T) & 1)
+        run_segment<Q8_0TF<(FMTMASK & FMT_NTL) != 0>, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
     case FMT_Q4_KT:
       if constexpr ((FMTMASK >> FMT_Q4_KT) & 1)
@@ -1113,7 +1167,7 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
 // At least four waves per SIMD (at most 128 VGPRs): the stream needs many waves in flight.
 // Which staged forms of x a launch's formats read: the limbs (quantized formats) and/or the
 // fp32 copy (F16, F32).
-constexpr bool mask_has_q(int m) { return (m & (0x1F | (1 << FMT_Q4_KT) | FMTS_Q4K_Q4K_Q6K | FMTS_Q5K_Q5K_Q6K | FMTS_Q4KT_Q4KT_Q6K)) != 0; }
+constexpr bool mask_has_q(int m) { return (m & (0x1F | (1 << FMT_Q4_KT) | (1 << FMT_Q8_0T) | FMTS_Q4K_Q4K_Q6K | FMTS_Q5K_Q5K_Q6K | FMTS_Q4KT_Q4KT_Q6K)) != 0; }
 constexpr bool mask_has_f(int m) { return (m & ((1 << FMT_F16) | (1 << FMT_F32))) != 0; }
 
 template <int FMTMASK, int R, int NW, int EPI>
@@ -1397,6 +1451,7 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   else if constexpr (FMT == FMT_Q4_0) gemm_rows<Q4_0F, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q4_K) gemm_rows<Q4_KF, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q4_KT) gemm_rows<Q4_KTF<false>, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_Q8_0T) gemm_rows<Q8_0TF<false>, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q5_K) gemm_rows<Q5_KF, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_F16) gemm_rows<F16F, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_F32) gemm_rows<F32F, NT, R>(a, xs, lane, wid, W);
@@ -2256,7 +2311,7 @@ static size_t lds_for(int cols, int inst) {
 static int inst_mask(int m) {
   switch (m) {
     case 1 << FMT_Q8_0: case 1 << FMT_Q4_0: case 1 << FMT_Q4_K: case 1 << FMT_Q6_K: case 1 << FMT_Q5_K:
-    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT:
+    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT: case 1 << FMT_Q8_0T:
     case (1 << FMT_Q5_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_KT) | (1 << FMT_Q6_K):
       return m;
     default:
@@ -2268,7 +2323,7 @@ static int inst_mask(int m) {
 static bool one_row_mask(int m) {
   switch (m) {
     case 1 << FMT_Q8_0: case 1 << FMT_Q4_0: case 1 << FMT_Q4_K: case 1 << FMT_Q6_K: case 1 << FMT_Q5_K:
-    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT:
+    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT: case 1 << FMT_Q8_0T:
       return true;
     default:
       return false;
@@ -2364,6 +2419,8 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
       return launch_nw<(1 << FMT_Q4_K) | (1 << FMT_Q6_K), EPI>(plan, n_groups, a, s);
     case 1 << FMT_Q4_KT: return launch_nw<1 << FMT_Q4_KT, EPI>(plan, n_groups, a, s);
     case (1 << FMT_Q4_KT) | FMT_NTL: return launch_nw<(1 << FMT_Q4_KT) | FMT_NTL, EPI>(plan, n_groups, a, s);
+    case 1 << FMT_Q8_0T: return launch_nw<1 << FMT_Q8_0T, EPI>(plan, n_groups, a, s);
+    case (1 << FMT_Q8_0T) | FMT_NTL: return launch_nw<(1 << FMT_Q8_0T) | FMT_NTL, EPI>(plan, n_groups, a, s);
     case (1 << FMT_Q4_KT) | (1 << FMT_Q6_K):
       if constexpr (EPI == EPI_QKV) {
         if (a.nseg == 3 && a.seg[0].fmt == FMT_Q4_KT && a.seg[1].fmt == FMT_Q4_KT && a.seg[2].fmt == FMT_Q6_K)
@@ -2447,9 +2504,10 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, int n_groups, h
     const GemvSeg& g = a.seg[i];
     if (st_family(g.fmt) != kf) return hipErrorNotSupported;
     // Q4_K measured faster on the register path (also with integer dot products here:
-    // 64.7 vs 49.9 us for the 70B gate/up pair); Q5_K, its 5-bit sibling, and Q4_KT, its
-    // tiled form, have only that path
-    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q4_KT || g.fmt == FMT_Q5_K || is_float_fmt(g.fmt)) return hipErrorNotSupported;
+    // 64.7 vs 49.9 us for the 70B gate/up pair); Q5_K, its 5-bit sibling, and the tiled
+    // layouts Q4_KT and Q8_0T have only that path
+    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q4_KT || g.fmt == FMT_Q8_0T || g.fmt == FMT_Q5_K || is_float_fmt(g.fmt))
+      return hipErrorNotSupported;
     if ((reinterpret_cast<uintptr_t>(g.w) & 15) || (g.row_bytes & 15) || g.rows <= 0) return hipErrorNotSupported;
   }
   if ((reinterpret_cast<uintptr_t>(a.x) & 15) || (a.gain && (reinterpret_cast<uintptr_t>(a.gain) & 15)))
@@ -2525,7 +2583,7 @@ hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups
     const hipError_t e = gemv_stream_launch(epi, a, n_groups, s);
     if (e != hipErrorNotSupported) return e;
   }
-  if (fmt_mask == 1 << FMT_Q4_KT) {
+  if (fmt_mask == 1 << FMT_Q4_KT || fmt_mask == 1 << FMT_Q8_0T) {
     int64_t weights = 0;
     for (int i = 0; i < (epi == EPI_SWIGLU ? 2 : a.nseg); ++i) weights += (int64_t)a.seg[i].rows * a.cols;
     if (weights >= 100000000) fmt_mask |= FMT_NTL;
@@ -2612,6 +2670,7 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
   // Q4_KT chunks start at tile boundaries (16 superblocks, 4096 columns), so that each chunk's
   // tiles are laid out as those of a row of its own width
   if (fmt == FMT_Q4_KT && chunk < cols) chunk -= chunk % 4096;
+  if (fmt == FMT_Q8_0T && chunk < cols) chunk -= chunk % 2048;  // tiles of 64 blocks
   if (chunk <= 0) return hipErrorInvalidValue;
   GemmArgs a;
   a.row_bytes = (int64_t)(cols / be) * bb;
@@ -2647,6 +2706,7 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
       case FMT_Q4_0: e = gemm_launch_fmt<FMT_Q4_0>(n_tok, a, s); break;
       case FMT_Q4_K: e = gemm_launch_fmt<FMT_Q4_K>(n_tok, a, s); break;
       case FMT_Q4_KT: e = gemm_launch_fmt<FMT_Q4_KT>(n_tok, a, s); break;
+      case FMT_Q8_0T: e = gemm_launch_fmt<FMT_Q8_0T>(n_tok, a, s); break;
       case FMT_Q5_K: e = gemm_launch_fmt<FMT_Q5_K>(n_tok, a, s); break;
       case FMT_F16: e = gemm_launch_fmt<FMT_F16>(n_tok, a, s); break;
       case FMT_F32: e = gemm_launch_fmt<FMT_F32>(n_tok, a, s); break;

@@ -87,6 +87,15 @@ __device__ void dequant_row_group(int fmt, const uint8_t* row, int64_t cols, int
     uint8_t blk[144];
     q4kt_gather(row, (int)(cols >> 8), (int)b, blk);
     dequant_group(FMT_Q4_K, blk, grp, out);
+  } else if (fmt == FMT_Q8_0T) {  // block b of a Q8_0T row gathered back into Q8_0's byte order
+    const int nb = (int)(cols >> 5);
+    uint8_t blk[34];
+    for (int i = 0; i < 2; ++i) blk[i] = row[q8t_d(nb, (int)b) + i];
+    for (int i = 0; i < 16; ++i) {
+      blk[2 + i] = row[q8t_qa(nb, (int)b) + i];
+      blk[18 + i] = row[q8t_qb(nb, (int)b) + i];
+    }
+    dequant_group(FMT_Q8_0, blk, grp, out);
   } else {
     dequant_group(fmt, row + b * block_bytes(fmt), grp, out);
   }
@@ -134,6 +143,31 @@ hipError_t repack_q4kt_launch(int64_t rows, int64_t cols, const void* src, void*
   const int64_t nb = (total + 255) / 256;
   const int grid = (int)(nb < 65536 ? nb : 65536);
   hipLaunchKernelGGL(repack_q4kt_kernel, dim3(grid), dim3(256), 0, s, rows, (int)(cols >> 8),
+                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint8_t*>(dst));
+  return hipGetLastError();
+}
+
+// Q8_0 -> Q8_0T: one thread per block, its 34 bytes (at a 2-byte phase) moved as bytes.
+__global__ void repack_q8t_kernel(int64_t rows, int nb, const uint8_t* __restrict__ src, uint8_t* __restrict__ dst) {
+  const int64_t total = rows * nb;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nb;
+    const int b = (int)(i % nb);
+    const uint8_t* in = src + r * 34 * (int64_t)nb + 34 * (int64_t)b;
+    uint8_t* row = dst + r * 34 * (int64_t)nb;
+    for (int k = 0; k < 2; ++k) row[q8t_d(nb, b) + k] = in[k];
+    for (int k = 0; k < 16; ++k) {
+      row[q8t_qa(nb, b) + k] = in[2 + k];
+      row[q8t_qb(nb, b) + k] = in[18 + k];
+    }
+  }
+}
+
+hipError_t repack_q8t_launch(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s) {
+  const int64_t total = rows * (cols >> 5);
+  const int64_t nb = (total + 255) / 256;
+  const int grid = (int)(nb < 65536 ? nb : 65536);
+  hipLaunchKernelGGL(repack_q8t_kernel, dim3(grid), dim3(256), 0, s, rows, (int)(cols >> 5),
                      reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint8_t*>(dst));
   return hipGetLastError();
 }

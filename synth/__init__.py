@@ -26,14 +26,14 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 # format ids, block geometry (weights per block, bytes per block)
 Q8_0, Q4_0, Q4_K, Q6_K, Q5_K, F16, F32 = 0, 1, 2, 3, 4, 5, 6
-# Q4_KT: the library's tiled arrangement of Q4_K bytes (made on the device from Q4_K blocks;
-# the generators here write Q4_K only)
-Q4_KT = 7
+# Q4_KT, Q8_0T: the library's tiled arrangements of Q4_K and Q8_0 bytes (made on the device from
+# GGUF blocks; the generators here write GGUF blocks only)
+Q4_KT, Q8_0T = 7, 8
 FORMAT_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_K: "Q5_K", F16: "F16", F32: "F32",
-                Q4_KT: "Q4_KT"}
+                Q4_KT: "Q4_KT", Q8_0T: "Q8_0T"}
 # F16 and F32 tensors hold one weight per "block" (GGUF's unquantized types)
-BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256, Q5_K: 256, F16: 1, F32: 1, Q4_KT: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210, Q5_K: 176, F16: 2, F32: 4, Q4_KT: 144}
+BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256, Q5_K: 256, F16: 1, F32: 1, Q4_KT: 256, Q8_0T: 32}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210, Q5_K: 176, F16: 2, F32: 4, Q4_KT: 144, Q8_0T: 34}
 # unquantized weights ~ N(0, F_STD): about the spread of trained Llama weight matrices (a reading:
 # the pages give no distribution for them)
 F_STD = 0.02

@@ -36,8 +36,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_block_geometry():
-    assert [nt.nt_block_elems(f) for f in range(8)] == [32, 32, 256, 256, 256, 1, 1, 256]
-    assert [nt.nt_block_bytes(f) for f in range(8)] == [34, 18, 144, 210, 176, 2, 4, 144]
+    assert [nt.nt_block_elems(f) for f in range(9)] == [32, 32, 256, 256, 256, 1, 1, 256, 32]
+    assert [nt.nt_block_bytes(f) for f in range(9)] == [34, 18, 144, 210, 176, 2, 4, 144, 34]
+    assert nt.nt_matrix_bytes(nt.Q8_0T, 14336, 4096) == nt.nt_matrix_bytes(nt.Q8_0, 14336, 4096)
     assert nt.nt_matrix_bytes(nt.Q4_KT, 28672, 8192) == nt.nt_matrix_bytes(nt.Q4_K, 28672, 8192)
     assert nt.nt_matrix_bytes(nt.F16, 28672, 8192) == 2 * 28672 * 8192
     assert nt.nt_matrix_bytes(nt.Q5_K, 28672, 8192) == 161_480_704
@@ -53,7 +54,9 @@ def test_block_geometry():
     (lambda: nt.nt_gemv_q(nt.Q8_0, 16, 256, None, 16, 16), nt.NT_EINVAL),
     (lambda: nt.nt_gemv_q(nt.Q8_0, 16, 256, 18, 16, 16), nt.NT_EALIGN),
     (lambda: nt.nt_dequant(nt.Q6_K, 4, 255, 16, 16), nt.NT_ESHAPE),
-    (lambda: nt.nt_gemv_q(8, 16, 256, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemv_q(11, 16, 256, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemv_q(nt.Q8_0T, 16, 224, 16, 16, 16), nt.NT_ESHAPE),  # Q8_0T rows: multiples of 256 columns
+    (lambda: nt.nt_repack(nt.Q8_0T, 16, 96, 16, 4096, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_repack(nt.Q4_K, 16, 256, 16, 4096, 16), nt.NT_EFORMAT),  # Q4_KT is the only target
     (lambda: nt.nt_repack(nt.Q4_KT, 16, 200, 16, 4096, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_repack(nt.Q4_KT, 0, 256, 16, 4096, 16), nt.NT_ESHAPE),
@@ -71,7 +74,7 @@ def test_block_geometry():
     (lambda: nt.nt_read_probe(16, 24, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_read_probe(None, 16, 16), nt.NT_EINVAL),
     (lambda: nt.nt_read_probe(8, 16, 16), nt.NT_EALIGN),
-    (lambda: nt.nt_gemm_q(8, 16, 256, 2, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemm_q(10, 16, 256, 2, 16, 16, 16), nt.NT_EFORMAT),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, 0, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, nt.GEMM_MAX_TOK + 1, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 200, 2, 16, 16, 16), nt.NT_ESHAPE),

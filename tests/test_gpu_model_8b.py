@@ -37,7 +37,8 @@ def decoded():
     import bench
     nt.load()
     say("8B Q8_0, 32 layers resident: generating the model")
-    m = bench.Model70B(torch, nt, tg, MIX, N_LAYERS, range(N_LAYERS), n_prefill=POS, shape=SHAPE, head_fmt=synth.Q8_0)
+    m = bench.Model70B(torch, nt, tg, MIX, N_LAYERS, range(N_LAYERS), n_prefill=POS, shape=SHAPE, head_fmt=synth.Q8_0,
+                       tiles=True)
     plan, keep = m.plan()
     head = m.head()
     shp = tg.layer_shape(SHAPE)

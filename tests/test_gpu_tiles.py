@@ -1,4 +1,4 @@
-"""GPU parity of the tiled Q4_K layout, NT_Q4_KT (MI355X only), through the C ABI.
+"""GPU parity of the tiled layouts NT_Q4_KT and NT_Q8_0T (MI355X only), through the C ABI.
 
 nt_repack rearranges Q4_K matrices (GGUF's block order; the overview, de.news.hada.io,
 "Überblick über NTransformer", names Q4_K_M) into tiles of 16 superblocks whose 16-byte
@@ -224,3 +224,154 @@ def test_decode_layer_k_tiled(n_tok):
     else:
         scale = np.abs(h_k).max()
         assert np.max(np.abs(h_k - h_t)) <= 1e-4 * scale
+
+
+# ------------------------------------------------------------------ Q8_0T
+
+Q80, Q80T = synth.Q8_0, synth.Q8_0T
+
+
+def q8t_layout(blocks: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """The NT_Q8_0T bytes of a Q8_0 matrix as include/nt.h describes them: per row, tiles of
+    64 blocks (m in the last), the first 16 codes of each block, then the last 16, then the
+    scales."""
+    nb = cols // 32
+    b = blocks.reshape(rows, nb, 34)
+    out = np.empty((rows, nb * 34), np.uint8)
+    for t0 in range(0, nb, 64):
+        m = min(64, nb - t0)
+        tile = b[:, t0:t0 + m]
+        base = 34 * t0
+        out[:, base:base + 16 * m] = tile[:, :, 2:18].reshape(rows, -1)
+        out[:, base + 16 * m:base + 32 * m] = tile[:, :, 18:34].reshape(rows, -1)
+        out[:, base + 32 * m:base + 34 * m] = tile[:, :, 0:2].reshape(rows, -1)
+    return out.ravel()
+
+
+def repack_to(fmt, rows, cols, src):
+    dst = torch.empty_like(src)
+    nt.nt_repack(fmt, rows, cols, src.data_ptr(), dst.data_ptr(), stream())
+    return dst
+
+
+@pytest.fixture
+def register_path():
+    """Q8_0 in GGUF order on the register path at every size (the launch policy streams large
+    Q8_0 launches), so that it runs the same products as Q8_0T."""
+    old = nt.nt_set_stream_min_weights(10 ** 15)
+    yield
+    nt.nt_set_stream_min_weights(old)
+
+
+Q8_SHAPES = [(1, 256), (7, 768), (3, 4096), (5, 14336), (2, 2304), (3, 1792), (33, 4096 + 256 * 3)]
+
+
+@pytest.mark.parametrize("rows,cols", Q8_SHAPES)
+def test_repack_q8_0t_layout_and_dequant_bit_exact(rows, cols):
+    say(f"repack Q8_0 -> Q8_0T {rows}x{cols}")
+    blocks = synth.quant_matrix(Q80, rows, cols, seed=3, stream=2200)
+    t = repack_to(Q80T, rows, cols, dev(blocks))
+    assert np.array_equal(host(t), q8t_layout(blocks, rows, cols))
+    w = torch.empty(rows * cols, dtype=torch.float32, device="cuda")
+    nt.nt_dequant(Q80T, rows, cols, t.data_ptr(), w.data_ptr(), stream())
+    assert same_value(host(w).reshape(rows, cols), oracle.dequant_f32(Q80, rows, cols, blocks))
+
+
+# one block, partial tiles, the 8B shapes (14336 x 4096 and 28672 x 4096 from 10^8 weights:
+# nontemporal loads), the widest x
+Q8_GEMV_SHAPES = [(1, 256), (23, 1280), (130, 4352), (4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336),
+                  (28672, 4096), (64, nt.NT_GEMV_MAX_COLS)]
+
+
+@pytest.mark.parametrize("rows,cols", Q8_GEMV_SHAPES)
+def test_gemv_q8_0t_matches_oracle(rows, cols):
+    """Q8_0T's lanes take a tile's blocks in order where Q8_0's take even then odd blocks, so the
+    sums are ordered differently and the two agree within the tolerance, not bit for bit."""
+    say(f"gemv Q8_0T {rows}x{cols}")
+    blocks = synth.quant_matrix(Q80, rows, cols, seed=0, stream=2300)
+    x = synth.normal_f32(cols, seed=0, stream=2301)
+    w, xd = dev(blocks), dev(x)
+    y_t = gemv(Q80T, rows, cols, repack_to(Q80T, rows, cols, w), xd)
+    ref, nrm = oracle.gemv(Q80, rows, cols, blocks, x.astype(np.float64))
+    worst = check_rel(y_t, ref, nrm, what=f"Q8_0T {rows}x{cols}")
+    say(f"  worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("rows,cols,n_tok", [(1, 256, 1), (17, 512, 4), (300, 4352, 6), (40, 32768, 8),
+                                             (14336, 4096, 7), (512, 6144, 2)])
+def test_gemm_q8_0t_matches_oracle(rows, cols, n_tok):
+    say(f"gemm Q8_0T {rows}x{cols} x {n_tok}")
+    blocks = synth.quant_matrix(Q80, rows, cols, seed=8, stream=2400)
+    X = np.stack([synth.normal_f32(cols, seed=8, stream=2401 + t) for t in range(n_tok)])
+    w = repack_to(Q80T, rows, cols, dev(blocks))
+    xd = dev(X.astype(np.float32))
+    Y = torch.empty(n_tok * rows, dtype=torch.float32, device="cuda")
+    nt.nt_gemm_q(Q80T, rows, cols, n_tok, w.data_ptr(), xd.data_ptr(), Y.data_ptr(), stream())
+    Y = host(Y).reshape(n_tok, rows)
+    ref, nrm = oracle.gemm(Q80, rows, cols, blocks, X.astype(np.float64))
+    for t in range(n_tok):
+        check_rel(Y[t], ref[t], nrm[t], what=f"Q8_0T {rows}x{cols} token {t}")
+
+
+def test_embed_row_q8_0t_equals_q8_0():
+    vocab, dim = 1000, 4352
+    table = dev(synth.quant_matrix(Q80, vocab, dim, seed=4, stream=2500))
+    tiled = repack_to(Q80T, vocab, dim, table)
+    for tok in (0, 63, 64, vocab - 1):
+        t = torch.tensor([tok], dtype=torch.int32, device="cuda")
+        a = torch.empty(dim, dtype=torch.float32, device="cuda")
+        b = torch.empty(dim, dtype=torch.float32, device="cuda")
+        nt.nt_embed_row(Q80, vocab, dim, table.data_ptr(), t.data_ptr(), a.data_ptr(), stream())
+        nt.nt_embed_row(Q80T, vocab, dim, tiled.data_ptr(), t.data_ptr(), b.data_ptr(), stream())
+        assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32)), tok
+
+
+@pytest.mark.parametrize("vocab,dim", [(1000, 1024), (128256, 4096)])
+def test_lm_head_q8_0t_matches_oracle(vocab, dim):
+    say(f"LM head Q8_0T {vocab}x{dim}")
+    blocks = synth.quant_matrix(Q80, vocab, dim, seed=5, stream=2600)
+    tiled = repack_to(Q80T, vocab, dim, dev(blocks))
+    onorm_h = synth.uniform_f32(dim, 5, 2601, 0.9, 1.1)
+    h_h = synth.normal_f32(dim, seed=5, stream=2602)
+    onorm, h = dev(onorm_h), dev(h_h)
+    res = []
+    for fmt, w in ((Q80T, tiled),):
+        logits = torch.empty(vocab, dtype=torch.float32, device="cuda")
+        tok = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(nt.NT_LM_HEAD_WS_BYTES, dtype=torch.uint8, device="cuda")
+        nt.nt_lm_head(fmt, vocab, dim, w.data_ptr(), onorm.data_ptr(), 1e-5, h.data_ptr(), logits.data_ptr(),
+                      tok.data_ptr(), ws.data_ptr(), ws.numel(), stream())
+        torch.cuda.synchronize()
+        res.append((int(tok.item()), host(logits).copy()))
+    tok, logits = res[0]
+    ref, nrm = oracle.gemv(Q80, vocab, dim, blocks, oracle.rmsnorm(h_h, onorm_h, 1e-5))
+    check_rel(logits, ref, nrm, what=f"Q8_0T head {vocab}x{dim}")
+    assert tok == int(np.argmax(logits)) and ref[tok] >= ref.max() - 1e-3 * nrm[tok]
+
+
+@pytest.mark.parametrize("shape,pos", [(SMALL, 5), (recipes.LLAMA3_8B, 1023)])
+def test_decode_layer_q8_0t_close_to_q8_0(shape, pos, register_path):
+    """The fused Q8_0 layer with every matrix tiled gives h within rounding of the Q8_0 matrices
+    on the register path (the products are ordered differently; the stage-wise check against
+    the checker is tests/test_gpu_model_8b.py, whose model holds its matrices tiled)."""
+    say(f"decode layer Q8_0 tiled, dim={shape.dim} pos={pos}")
+    mix = recipes.MIX_Q8_0
+    arrays = recipes.layer_arrays(shape, mix, 0)
+    w_k = {k: dev(v) for k, v in arrays.items()}
+    w_t = dict(w_k)
+    for n in recipes.TENSORS:
+        w_t[n] = repack_to(Q80T, *shape.matrix_shape(n), w_k[n])
+    shp = tg.layer_shape(shape)
+    wsb = nt.nt_decode_layer_ws_bytes(shp)
+    kc0 = recipes.kv_cache_array(shape, 0, "k", pos)
+    vc0 = v_to_device(recipes.kv_cache_array(shape, 0, "v", pos), shape.n_kv_heads, shape.max_ctx)
+    outs = []
+    for f, w in ((Q80, w_k), (Q80T, w_t)):
+        lw = tg.layer_weights([f] * len(recipes.TENSORS), [w[n] for n in recipes.TENSORS], w["attn_norm"],
+                              w["ffn_norm"])
+        h, kc, vc = dev(recipes.hidden_input(shape.dim)), dev(kc0), dev(vc0)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        nt.nt_decode_layer(lw, shp, pos, h.data_ptr(), kc.data_ptr(), vc.data_ptr(), ws.data_ptr(), wsb, stream())
+        torch.cuda.synchronize()
+        outs.append(host(h).copy())
+    assert np.max(np.abs(outs[0] - outs[1])) <= 1e-4 * np.abs(outs[0]).max()
