@@ -9,7 +9,7 @@ decode layers, final norm, LM head and argmax, every kernel in libnt.so.
 
 Prints one JSON line.  Other workloads (--config) print their own line for measurement
 runs: 1 = Q8_0 GEMV 4096x4096, 2 = one Llama-3-8B-shaped Q8_0 layer, 3 = the 70B GEMV
-shapes in Q4_K, Q6_K, Q5_K, F16, F32 and tiled Q4_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
+shapes in Q4_K, Q6_K, Q5_K, F16, F32 and tiled Q4_K and Q5_K, 5 = the 70B Q6_K model with 54 layers streamed from pinned
 host memory, 6 = the k-token GEMM (k = 1, 2, 4, 8) at the 70B shapes, 7 = the 70B model with
 cosine-based layer skip (--skip layers, default 20 of 80), 8 = 70B Q6_K layers read from a file
 (--file-layers, default 8) through page-locked bounce buffers, 9 = the self-speculative
@@ -156,7 +156,7 @@ class Model70B:
         # tiles: the resident layers' Q4_K and Q8_0 matrices and such an LM head rearranged on the
         # device into the GEMV's tiled layouts (nt_repack: Q4_KT, Q8_0T); the same weights
         self.tiles = tiles
-        tiled_fmt = {synth.Q4_K: synth.Q4_KT, synth.Q8_0: synth.Q8_0T}
+        tiled_fmt = {synth.Q4_K: synth.Q4_KT, synth.Q8_0: synth.Q8_0T, synth.Q5_K: synth.Q5_KT}
         self.fmts = {n: (tiled_fmt.get(mix[n], mix[n]) if tiles else mix[n]) for n in recipes.TENSORS}
         self.n_layers = n_layers
         self.vocab = recipes.VOCAB_70B
@@ -574,7 +574,7 @@ def rotating_gemv(torch, nt, fmt, rows, cols, copies, steps, warmup, seed=0):
     nbytes = synth.matrix_bytes(fmt, rows, cols)
     hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     cs = torch.cuda.current_stream().cuda_stream
-    gen = {synth.Q4_KT: synth.Q4_K, synth.Q8_0T: synth.Q8_0}.get(fmt, fmt)  # tiled: GGUF blocks rearranged on the device
+    gen = {synth.Q4_KT: synth.Q4_K, synth.Q8_0T: synth.Q8_0, synth.Q5_KT: synth.Q5_K}.get(fmt, fmt)  # tiled: GGUF blocks rearranged on the device
     ws = []
     for c in range(copies):
         synth.fill_blocks(hb.data_ptr(), gen, nbytes // synth.BLOCK_BYTES[gen], seed, 5000 + c)
@@ -618,7 +618,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
     if args.config == 1:
         shapes = [(synth.Q8_0, 4096, 4096)]
     else:
-        shapes = [(f, r, c) for f in (synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32, synth.Q4_KT)
+        shapes = [(f, r, c) for f in (synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32, synth.Q4_KT, synth.Q5_KT)
                   for (r, c) in ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672))]
     for fmt, r, c in shapes:
         nbytes = synth.matrix_bytes(fmt, r, c)
@@ -634,7 +634,7 @@ def bench_gemv_shapes(args, torch, nt, tg):
         "value": best["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": best["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 x i8 -> i32 dots (x as three int8 limbs per column with a power-of-two scale per 32 columns), f32 scales and sums (quantized weights)", "data": "synthetic",
-        "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K, Q5_K, F16, F32 and tiled Q4_K"},
+        "config": {"workload": "Q8_0 GEMV 4096x4096" if args.config == 1 else "70B-shape GEMVs, Q4_K, Q6_K, Q5_K, F16, F32 and tiled Q4_K and Q5_K"},
         "roofline": {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": best["frac_of_peak"], "traffic": None},
         "gemv": out,

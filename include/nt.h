@@ -74,11 +74,16 @@ extern "C" {
  *            each block (block bytes 2..17), then the last 16 (bytes 18..33), then the m fp16
  *            scales (bytes 0..1): lane l of a wave reads block l's parts, each load whole lines.
  *            Read where NT_Q4_KT is (register path only, nontemporal loads from 10^8 weights).
+ *   NT_Q5_KT  NT_Q5_K's bytes in tiles of 16 superblocks (made by nt_repack; 176 B per 256 weights).
+ *            Tile t of a row (m superblocks) starts at byte 2816t and holds the m 16-byte headers
+ *            (block bytes 0..15), the m first halves of the high bits (16..31), the m second halves
+ *            (32..47), then code bytes 48+32g .. +15 of each (j, g) in lane order, then 64+32g ..
+ *            +15 in lane order; read where NT_Q4_KT is.
  * Every entry point that takes cols for NT_F16 / NT_F32 needs a multiple of 32 (so that rows
  * keep the 16-byte alignment the loads use).
  */
 typedef enum { NT_Q8_0 = 0, NT_Q4_0 = 1, NT_Q4_K = 2, NT_Q6_K = 3, NT_Q5_K = 4, NT_F16 = 5, NT_F32 = 6,
-               NT_Q4_KT = 7, NT_Q8_0T = 8 } nt_format;
+               NT_Q4_KT = 7, NT_Q8_0T = 8, NT_Q5_KT = 9 } nt_format;
 
 typedef enum {
   NT_OK = 0,
@@ -109,10 +114,10 @@ int64_t nt_matrix_bytes(int fmt, int64_t rows, int64_t cols); /* bytes of a rows
  * blocks: 4-byte aligned.  Returns NT_ESHAPE if cols % block_elems != 0. */
 int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, void* stream);
 
-/* Rearrange a Q4_K or Q8_0 matrix (rows x cols, GGUF's block order) into the NT_Q4_KT or
- * NT_Q8_0T layout above: a layout of the same weights for the GEMV's loads ("Überblick über
+/* Rearrange a Q4_K, Q8_0 or Q5_K matrix (rows x cols, GGUF's block order) into the NT_Q4_KT,
+ * NT_Q8_0T or NT_Q5_KT layout above: a layout of the same weights for the GEMV's loads ("Überblick über
  * NTransformer" names the formats; the tiles are this library's own).  fmt: the target layout,
- * NT_Q4_KT (src in NT_Q4_K) or NT_Q8_0T (src in NT_Q8_0), else NT_EFORMAT.  cols: a positive
+ * NT_Q4_KT (src in NT_Q4_K), NT_Q8_0T (src in NT_Q8_0) or NT_Q5_KT (src in NT_Q5_K), else NT_EFORMAT.  cols: a positive
  * multiple of 256 up to 2^24; rows <= NT_MAX_ROWS (else NT_ESHAPE).  src, dst: device,
  * 16-byte aligned (NT_EALIGN), nt_matrix_bytes(fmt, rows, cols) bytes each, not overlapping
  * (NT_EINVAL; the caller copies back if it wants the matrix in place).  Enqueued on stream;

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libnt.so")
 Q8_0, Q4_0, Q4_K, Q6_K, Q5_K, F16, F32 = 0, 1, 2, 3, 4, 5, 6
 Q4_KT = 7  # Q4_K in the library's tiles of 16 superblocks (nt_repack)
 Q8_0T = 8  # Q8_0 in the library's tiles of 64 blocks (nt_repack)
+Q5_KT = 9  # Q5_K in the library's tiles of 16 superblocks (nt_repack)
 NT_OK, NT_EINVAL, NT_EFORMAT, NT_ESHAPE, NT_EALIGN, NT_EHOSTMEM, NT_EHIP = 0, -1, -2, -3, -4, -5, -6
 W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN, W_COUNT = range(8)
 K_ATTN_IN, K_ATTN, K_O, K_FFN_UP, K_FFN_DOWN, K_LM_HEAD, K_GEMV, K_GEMM = range(8)

@@ -42,7 +42,7 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(NT_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_Q8_0T; }
+bool fmt_ok(int f) { return f >= NT_Q8_0 && f <= NT_Q5_KT; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -422,18 +422,20 @@ int nt_dequant(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w
 }
 
 int nt_repack(int fmt, int64_t rows, int64_t cols, const void* src, void* dst, void* stream) {
-  if (fmt != NT_Q4_KT && fmt != NT_Q8_0T)
-    return fail(NT_EFORMAT, "repack: the target layout must be NT_Q4_KT or NT_Q8_0T (got %d)", fmt);
+  if (fmt != NT_Q4_KT && fmt != NT_Q8_0T && fmt != NT_Q5_KT)
+    return fail(NT_EFORMAT, "repack: the target layout must be NT_Q4_KT, NT_Q8_0T or NT_Q5_KT (got %d)", fmt);
   if (rows <= 0 || rows > NT_MAX_ROWS || cols <= 0 || cols % 256 || cols > (1 << 24))
     return fail(NT_ESHAPE, "repack: need 0 < rows <= 2^30 and cols a positive multiple of 256 up to 2^24 (got %lld x %lld)",
                 (long long)rows, (long long)cols);
   if (!src || !dst) return fail(NT_EINVAL, "null pointer");
   if (!aligned(src, 16) || !aligned(dst, 16)) return fail(NT_EALIGN, "src and dst must be 16-byte aligned");
-  const uintptr_t bytes = (uintptr_t)(fmt == NT_Q4_KT ? rows * (cols / 256) * 144 : rows * (cols / 32) * 34);
+  const uintptr_t bytes = (uintptr_t)(fmt == NT_Q4_KT ? rows * (cols / 256) * 144
+                                      : fmt == NT_Q5_KT ? rows * (cols / 256) * 176 : rows * (cols / 32) * 34);
   const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
   if (a < b + bytes && b < a + bytes) return fail(NT_EINVAL, "repack: src and dst overlap");
-  hipError_t e = fmt == NT_Q4_KT ? repack_q4kt_launch(rows, cols, src, dst, (hipStream_t)stream)
-                                  : repack_q8t_launch(rows, cols, src, dst, (hipStream_t)stream);
+  hipError_t e = fmt == NT_Q4_KT   ? repack_q4kt_launch(rows, cols, src, dst, (hipStream_t)stream)
+                 : fmt == NT_Q5_KT ? repack_q5kt_launch(rows, cols, src, dst, (hipStream_t)stream)
+                                   : repack_q8t_launch(rows, cols, src, dst, (hipStream_t)stream);
   return e == hipSuccess ? NT_OK : hip_fail(e, "repack launch");
 }
 

@@ -7,16 +7,16 @@
 
 namespace nt {
 
-// F16 and F32 are unquantized weight tensors: one weight per "block".  Q4_KT and Q8_0T hold
-// Q4_K's and Q8_0's bytes rearranged in tiles (q4kt_*, q8t_* below).
+// F16 and F32 are unquantized weight tensors: one weight per "block".  Q4_KT, Q8_0T and Q5_KT
+// hold Q4_K's, Q8_0's and Q5_K's bytes rearranged in tiles (q4kt_*, q8t_*, q5kt_* below).
 enum { FMT_Q8_0 = 0, FMT_Q4_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_Q5_K = 4, FMT_F16 = 5, FMT_F32 = 6, FMT_Q4_KT = 7,
-       FMT_Q8_0T = 8 };
-constexpr int FMT_COUNT = 9;
+       FMT_Q8_0T = 8, FMT_Q5_KT = 9 };
+constexpr int FMT_COUNT = 10;
 
 __host__ __device__ constexpr bool is_float_fmt(int f) { return f == FMT_F16 || f == FMT_F32; }
 __host__ __device__ constexpr int block_elems(int f) { return (f <= FMT_Q4_0 || f == FMT_Q8_0T) ? 32 : is_float_fmt(f) ? 1 : 256; }
 __host__ __device__ constexpr int block_bytes(int f) {
-  return (f == FMT_Q8_0 || f == FMT_Q8_0T) ? 34 : f == FMT_Q4_0 ? 18 : (f == FMT_Q4_K || f == FMT_Q4_KT) ? 144 : f == FMT_Q5_K ? 176 : f == FMT_F16 ? 2
+  return (f == FMT_Q8_0 || f == FMT_Q8_0T) ? 34 : f == FMT_Q4_0 ? 18 : (f == FMT_Q4_K || f == FMT_Q4_KT) ? 144 : (f == FMT_Q5_K || f == FMT_Q5_KT) ? 176 : f == FMT_F16 ? 2
          : f == FMT_F32 ? 4 : 210;
 }
 // Q4_KT: a row's Q4_K superblocks in tiles of 16 (the last tile of a row holds the m =
@@ -33,6 +33,22 @@ __host__ __device__ constexpr uint32_t q4kt_qa(int nsb, int b, int g) {
 }
 __host__ __device__ constexpr uint32_t q4kt_qb(int nsb, int b, int g) {
   return 144u * (uint32_t)(b & ~15) + 80u * q4kt_tile_m(nsb, b) + 16u * (4u * (uint32_t)(b & 15) + (uint32_t)g);
+}
+
+// Q5_KT: a row's Q5_K superblocks in tiles of 16 (m in the last), tile t at byte 2816 t: the m
+// headers (bytes 0..15 of each block), the m first halves of the high bits (bytes 16..31), the
+// m second halves (32..47), then code bytes 48 + 32 g .. of each (j, g) in lane order, then
+// 64 + 32 g .. in lane order; the same lane work as Q5_K, each load reading whole lines.
+__host__ __device__ constexpr uint32_t q5kt_base(int b) { return 176u * (uint32_t)(b & ~15); }
+__host__ __device__ constexpr uint32_t q5kt_m(int nsb, int b) { return q4kt_tile_m(nsb, b); }
+__host__ __device__ constexpr uint32_t q5kt_hd(int nsb, int b) { return q5kt_base(b) + 16u * (uint32_t)(b & 15); }
+__host__ __device__ constexpr uint32_t q5kt_ha(int nsb, int b) { return q5kt_base(b) + 16u * q5kt_m(nsb, b) + 16u * (uint32_t)(b & 15); }
+__host__ __device__ constexpr uint32_t q5kt_hb(int nsb, int b) { return q5kt_base(b) + 32u * q5kt_m(nsb, b) + 16u * (uint32_t)(b & 15); }
+__host__ __device__ constexpr uint32_t q5kt_qa(int nsb, int b, int g) {
+  return q5kt_base(b) + 48u * q5kt_m(nsb, b) + 16u * (4u * (uint32_t)(b & 15) + (uint32_t)g);
+}
+__host__ __device__ constexpr uint32_t q5kt_qb(int nsb, int b, int g) {
+  return q5kt_base(b) + 112u * q5kt_m(nsb, b) + 16u * (4u * (uint32_t)(b & 15) + (uint32_t)g);
 }
 
 // Q8_0T: a row's Q8_0 blocks in tiles of 64 (the last tile of a row holds the m = nb - 64 t

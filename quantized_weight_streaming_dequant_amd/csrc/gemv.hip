@@ -596,6 +596,30 @@ struct Q5_KF {
   }
 };
 
+// Q5_KT: Q5_K in tiles of 16 superblocks (common.h), the same lane work as Q5_KF, each of its
+// five loads reading whole lines (the headers and high bits four lanes to an address); the
+// nontemporal policy from 10^8 weights as for Q4_KT.
+template <bool NTL>
+struct Q5_KTF : Q5_KF {
+  static __device__ __forceinline__ u32x4 ld(const uint8_t* p) {
+    if constexpr (NTL) return __builtin_nontemporal_load(NT_GPTR(u32x4, p));
+    else return *NT_GPTR(u32x4, p);
+  }
+  static __device__ __forceinline__ Raw load(const uint8_t* rowp, int cols, int step, int lane) {
+    const int nsb = cols >> 8;
+    int sb = step * 16 + (lane >> 2);
+    sb = sb < nsb ? sb : 0;
+    const int g = lane & 3;
+    Raw r;
+    r.hd = ld(rowp + q5kt_hd(nsb, sb));
+    r.ha = ld(rowp + q5kt_ha(nsb, sb));
+    r.hb = ld(rowp + q5kt_hb(nsb, sb));
+    r.qa = ld(rowp + q5kt_qa(nsb, sb, g));
+    r.qb = ld(rowp + q5kt_qb(nsb, sb, g));
+    return r;
+  }
+};
+
 // Q6_K: lane = one eighth of a 210-byte superblock, (h, tp, half) with h, tp, half in {0,1}:
 // the 16 low-nibble bytes at 64h + 32tp + 16half (the next eight lanes read the next 128
 // bytes), the 16 high-bit bytes at 128 + 32h + 16half, and the scale group at 192 + 8h.
@@ -1141,6 +1165,10 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
     case FMT_Q4_K:
       if constexpr ((FMTMASK >> FMT_Q4_K) & 1) run_segment<Q4_KF, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
       break;
+    case FMT_Q5_KT:
+      if constexpr ((FMTMASK >> FMT_Q5_KT) & 1)
+        run_segment<Q5_KTF<(FMTMASK & FMT_NTL) != 0>, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
+      break;
     case FMT_Q8_0T:
       if constexpr ((FMTMASK >> FMT_Q8_0T) & 1)
         run_segment<Q8_0TF<(FMTMASK & FMT_NTL) != 0>, R, EPI, D, STAGE>(a, s, lane, wid, W, xs, red, xscale, best, rope, xpre);
@@ -1167,7 +1195,7 @@ __device__ __forceinline__ void run_any(const GemvArgs& a, int s, int lane, int 
 // At least four waves per SIMD (at most 128 VGPRs): the stream needs many waves in flight.
 // Which staged forms of x a launch's formats read: the limbs (quantized formats) and/or the
 // fp32 copy (F16, F32).
-constexpr bool mask_has_q(int m) { return (m & (0x1F | (1 << FMT_Q4_KT) | (1 << FMT_Q8_0T) | FMTS_Q4K_Q4K_Q6K | FMTS_Q5K_Q5K_Q6K | FMTS_Q4KT_Q4KT_Q6K)) != 0; }
+constexpr bool mask_has_q(int m) { return (m & (0x1F | (1 << FMT_Q4_KT) | (1 << FMT_Q8_0T) | (1 << FMT_Q5_KT) | FMTS_Q4K_Q4K_Q6K | FMTS_Q5K_Q5K_Q6K | FMTS_Q4KT_Q4KT_Q6K)) != 0; }
 constexpr bool mask_has_f(int m) { return (m & ((1 << FMT_F16) | (1 << FMT_F32))) != 0; }
 
 template <int FMTMASK, int R, int NW, int EPI>
@@ -1265,7 +1293,7 @@ struct KDec {
 
 template <typename F, int NR>
 __device__ __forceinline__ void kdecode(const typename F::Raw (&raw)[NR], int cols, int step, int lane, KDec<NR>& D) {
-  constexpr bool K5 = std::is_same<F, Q5_KF>::value;
+  constexpr bool K5 = std::is_base_of<Q5_KF, F>::value;
   const int sb = step * 16 + (lane >> 2);
   D.ok = sb < (cols >> 8);
   const int g = lane & 3;
@@ -1359,7 +1387,7 @@ __device__ __forceinline__ void gemm_rows(const GemmArgs& a, const XLimbs (&xs)[
   int ck = wid, ct = 0, item = 0;
   auto step = [&](const Raw (&cur)[R], Raw (&refill)[R]) -> bool {
     issue(refill);  // unconditional: the wait for this item leaves the next one in flight
-    if constexpr (std::is_base_of<Q4_KF, F>::value || std::is_same<F, Q5_KF>::value) {
+    if constexpr (std::is_base_of<Q4_KF, F>::value || std::is_base_of<Q5_KF, F>::value) {
       KDec<R> dec;
       kdecode<F, R>(cur, a.cols, ct, lane, dec);
 #pragma unroll
@@ -1423,7 +1451,7 @@ __device__ __forceinline__ void gemm_stage(const GemmArgs& a, int t, const XLimb
 // and NT tokens' accumulators would not fit the registers (Q5_K: five 128-bit loads per row;
 // Q4_K from two tokens on; Q6_K at 8 tokens).
 template <int FMT, int NT>
-constexpr int GEMM_ROWS = (FMT == FMT_Q5_K || ((FMT == FMT_Q4_K || FMT == FMT_Q4_KT) && NT >= 2) || (FMT == FMT_Q6_K && NT == 8)) ? 1 : 2;
+constexpr int GEMM_ROWS = (FMT == FMT_Q5_K || FMT == FMT_Q5_KT || ((FMT == FMT_Q4_K || FMT == FMT_Q4_KT) && NT >= 2) || (FMT == FMT_Q6_K && NT == 8)) ? 1 : 2;
 
 template <int FMT, int NT, int NW>
 __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
@@ -1452,6 +1480,7 @@ __global__ __launch_bounds__(NW * 64, 4) void gemm_kernel(const GemmArgs a) {
   else if constexpr (FMT == FMT_Q4_K) gemm_rows<Q4_KF, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q4_KT) gemm_rows<Q4_KTF<false>, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q8_0T) gemm_rows<Q8_0TF<false>, NT, R>(a, xs, lane, wid, W);
+  else if constexpr (FMT == FMT_Q5_KT) gemm_rows<Q5_KTF<false>, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_Q5_K) gemm_rows<Q5_KF, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_F16) gemm_rows<F16F, NT, R>(a, xs, lane, wid, W);
   else if constexpr (FMT == FMT_F32) gemm_rows<F32F, NT, R>(a, xs, lane, wid, W);
@@ -2311,7 +2340,8 @@ static size_t lds_for(int cols, int inst) {
 static int inst_mask(int m) {
   switch (m) {
     case 1 << FMT_Q8_0: case 1 << FMT_Q4_0: case 1 << FMT_Q4_K: case 1 << FMT_Q6_K: case 1 << FMT_Q5_K:
-    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT: case 1 << FMT_Q8_0T:
+    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT: case 1 << FMT_Q8_0T: case 1 << FMT_Q5_KT:
+    case (1 << FMT_Q5_KT) | (1 << FMT_Q6_K):
     case (1 << FMT_Q5_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_K) | (1 << FMT_Q6_K): case (1 << FMT_Q4_KT) | (1 << FMT_Q6_K):
       return m;
     default:
@@ -2323,7 +2353,7 @@ static int inst_mask(int m) {
 static bool one_row_mask(int m) {
   switch (m) {
     case 1 << FMT_Q8_0: case 1 << FMT_Q4_0: case 1 << FMT_Q4_K: case 1 << FMT_Q6_K: case 1 << FMT_Q5_K:
-    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT: case 1 << FMT_Q8_0T:
+    case 1 << FMT_F16: case 1 << FMT_F32: case 1 << FMT_Q4_KT: case 1 << FMT_Q8_0T: case 1 << FMT_Q5_KT:
       return true;
     default:
       return false;
@@ -2421,6 +2451,9 @@ static hipError_t launch_mask(int fmt_mask, const GemvPlan& plan, int n_groups, 
     case (1 << FMT_Q4_KT) | FMT_NTL: return launch_nw<(1 << FMT_Q4_KT) | FMT_NTL, EPI>(plan, n_groups, a, s);
     case 1 << FMT_Q8_0T: return launch_nw<1 << FMT_Q8_0T, EPI>(plan, n_groups, a, s);
     case (1 << FMT_Q8_0T) | FMT_NTL: return launch_nw<(1 << FMT_Q8_0T) | FMT_NTL, EPI>(plan, n_groups, a, s);
+    case 1 << FMT_Q5_KT: return launch_nw<1 << FMT_Q5_KT, EPI>(plan, n_groups, a, s);
+    case (1 << FMT_Q5_KT) | FMT_NTL: return launch_nw<(1 << FMT_Q5_KT) | FMT_NTL, EPI>(plan, n_groups, a, s);
+    case (1 << FMT_Q5_KT) | (1 << FMT_Q6_K): return launch_nw<(1 << FMT_Q5_KT) | (1 << FMT_Q6_K), EPI>(plan, n_groups, a, s);
     case (1 << FMT_Q4_KT) | (1 << FMT_Q6_K):
       if constexpr (EPI == EPI_QKV) {
         if (a.nseg == 3 && a.seg[0].fmt == FMT_Q4_KT && a.seg[1].fmt == FMT_Q4_KT && a.seg[2].fmt == FMT_Q6_K)
@@ -2506,7 +2539,8 @@ static hipError_t gemv_stream_launch(int epi, const GemvArgs& a, int n_groups, h
     // Q4_K measured faster on the register path (also with integer dot products here:
     // 64.7 vs 49.9 us for the 70B gate/up pair); Q5_K, its 5-bit sibling, and the tiled
     // layouts Q4_KT and Q8_0T have only that path
-    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q4_KT || g.fmt == FMT_Q8_0T || g.fmt == FMT_Q5_K || is_float_fmt(g.fmt))
+    if (g.fmt == FMT_Q4_K || g.fmt == FMT_Q4_KT || g.fmt == FMT_Q8_0T || g.fmt == FMT_Q5_K || g.fmt == FMT_Q5_KT ||
+        is_float_fmt(g.fmt))
       return hipErrorNotSupported;
     if ((reinterpret_cast<uintptr_t>(g.w) & 15) || (g.row_bytes & 15) || g.rows <= 0) return hipErrorNotSupported;
   }
@@ -2583,7 +2617,7 @@ hipError_t gemv_launch(int fmt_mask, int epi, const GemvPlan& plan, int n_groups
     const hipError_t e = gemv_stream_launch(epi, a, n_groups, s);
     if (e != hipErrorNotSupported) return e;
   }
-  if (fmt_mask == 1 << FMT_Q4_KT || fmt_mask == 1 << FMT_Q8_0T) {
+  if (fmt_mask == 1 << FMT_Q4_KT || fmt_mask == 1 << FMT_Q8_0T || fmt_mask == 1 << FMT_Q5_KT) {
     int64_t weights = 0;
     for (int i = 0; i < (epi == EPI_SWIGLU ? 2 : a.nseg); ++i) weights += (int64_t)a.seg[i].rows * a.cols;
     if (weights >= 100000000) fmt_mask |= FMT_NTL;
@@ -2669,7 +2703,7 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
   int chunk = mm ? gemm_mfma_chunk_cols(fmt, n_tok, (int)cols) : gemm_chunk_cols(n_tok, (int)cols, fmt);
   // Q4_KT chunks start at tile boundaries (16 superblocks, 4096 columns), so that each chunk's
   // tiles are laid out as those of a row of its own width
-  if (fmt == FMT_Q4_KT && chunk < cols) chunk -= chunk % 4096;
+  if ((fmt == FMT_Q4_KT || fmt == FMT_Q5_KT) && chunk < cols) chunk -= chunk % 4096;
   if (fmt == FMT_Q8_0T && chunk < cols) chunk -= chunk % 2048;  // tiles of 64 blocks
   if (chunk <= 0) return hipErrorInvalidValue;
   GemmArgs a;
@@ -2707,6 +2741,7 @@ hipError_t gemm_launch(int fmt, const uint8_t* w, int64_t rows, int64_t cols, in
       case FMT_Q4_K: e = gemm_launch_fmt<FMT_Q4_K>(n_tok, a, s); break;
       case FMT_Q4_KT: e = gemm_launch_fmt<FMT_Q4_KT>(n_tok, a, s); break;
       case FMT_Q8_0T: e = gemm_launch_fmt<FMT_Q8_0T>(n_tok, a, s); break;
+      case FMT_Q5_KT: e = gemm_launch_fmt<FMT_Q5_KT>(n_tok, a, s); break;
       case FMT_Q5_K: e = gemm_launch_fmt<FMT_Q5_K>(n_tok, a, s); break;
       case FMT_F16: e = gemm_launch_fmt<FMT_F16>(n_tok, a, s); break;
       case FMT_F32: e = gemm_launch_fmt<FMT_F32>(n_tok, a, s); break;

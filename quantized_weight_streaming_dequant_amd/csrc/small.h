@@ -9,6 +9,7 @@ namespace nt {
 hipError_t dequant_launch(int fmt, int64_t rows, int64_t cols, const void* blocks, float* w, hipStream_t s);
 hipError_t repack_q4kt_launch(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s);
 hipError_t repack_q8t_launch(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s);
+hipError_t repack_q5kt_launch(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s);
 // h[t] = dequantized row token[t] of the table, for t < n_tok (rows of dim floats)
 hipError_t embed_launch(int fmt, int64_t n_vocab, int64_t dim, const void* table, const int32_t* token, float* h,
                         unsigned long long* amax_reset, hipStream_t s, int n_tok = 1);

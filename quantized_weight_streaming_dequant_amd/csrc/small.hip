@@ -87,6 +87,20 @@ __device__ void dequant_row_group(int fmt, const uint8_t* row, int64_t cols, int
     uint8_t blk[144];
     q4kt_gather(row, (int)(cols >> 8), (int)b, blk);
     dequant_group(FMT_Q4_K, blk, grp, out);
+  } else if (fmt == FMT_Q5_KT) {  // superblock b of a Q5_KT row gathered back into Q5_K's byte order
+    const int nsb = (int)(cols >> 8);
+    uint8_t blk[176];
+    for (int i = 0; i < 16; ++i) {
+      blk[i] = row[q5kt_hd(nsb, (int)b) + i];
+      blk[16 + i] = row[q5kt_ha(nsb, (int)b) + i];
+      blk[32 + i] = row[q5kt_hb(nsb, (int)b) + i];
+    }
+    for (int g = 0; g < 4; ++g)
+      for (int i = 0; i < 16; ++i) {
+        blk[48 + 32 * g + i] = row[q5kt_qa(nsb, (int)b, g) + i];
+        blk[64 + 32 * g + i] = row[q5kt_qb(nsb, (int)b, g) + i];
+      }
+    dequant_group(FMT_Q5_K, blk, grp, out);
   } else if (fmt == FMT_Q8_0T) {  // block b of a Q8_0T row gathered back into Q8_0's byte order
     const int nb = (int)(cols >> 5);
     uint8_t blk[34];
@@ -161,6 +175,33 @@ __global__ void repack_q8t_kernel(int64_t rows, int nb, const uint8_t* __restric
       row[q8t_qb(nb, b) + k] = in[18 + k];
     }
   }
+}
+
+// Q5_K -> Q5_KT: one thread per 16-byte part of the output; 11 parts per superblock in Q5_K's
+// order (header, two high-bit halves, eight code runs).
+__global__ void repack_q5kt_kernel(int64_t rows, int nsb, const uint8_t* __restrict__ src, uint8_t* __restrict__ dst) {
+  const int64_t per_row = 11 * (int64_t)nsb, total = rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / per_row;
+    const int c = (int)(i % per_row);
+    const int t = c / 176, k = c % 176;
+    const int m = nsb - 16 * t < 16 ? nsb - 16 * t : 16;
+    int from;
+    if (k < 3 * m) from = 11 * (k % m) + k / m;  // headers, then the two high-bit halves
+    else if (k < 7 * m) from = 11 * ((k - 3 * m) >> 2) + 3 + 2 * ((k - 3 * m) & 3);
+    else from = 11 * ((k - 7 * m) >> 2) + 4 + 2 * ((k - 7 * m) & 3);
+    const int64_t tile = r * 176 * (int64_t)nsb + 2816 * (int64_t)t;
+    *reinterpret_cast<uint4*>(dst + tile + 16 * k) = *reinterpret_cast<const uint4*>(src + tile + 16 * from);
+  }
+}
+
+hipError_t repack_q5kt_launch(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s) {
+  const int64_t total = rows * 11 * (cols >> 8);
+  const int64_t nb = (total + 255) / 256;
+  const int grid = (int)(nb < 65536 ? nb : 65536);
+  hipLaunchKernelGGL(repack_q5kt_kernel, dim3(grid), dim3(256), 0, s, rows, (int)(cols >> 8),
+                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint8_t*>(dst));
+  return hipGetLastError();
 }
 
 hipError_t repack_q8t_launch(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s) {

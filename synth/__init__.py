@@ -26,14 +26,14 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 # format ids, block geometry (weights per block, bytes per block)
 Q8_0, Q4_0, Q4_K, Q6_K, Q5_K, F16, F32 = 0, 1, 2, 3, 4, 5, 6
-# Q4_KT, Q8_0T: the library's tiled arrangements of Q4_K and Q8_0 bytes (made on the device from
+# Q4_KT, Q8_0T, Q5_KT: the library's tiled arrangements of Q4_K, Q8_0 and Q5_K bytes (made on the device from
 # GGUF blocks; the generators here write GGUF blocks only)
-Q4_KT, Q8_0T = 7, 8
+Q4_KT, Q8_0T, Q5_KT = 7, 8, 9
 FORMAT_NAMES = {Q8_0: "Q8_0", Q4_0: "Q4_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_K: "Q5_K", F16: "F16", F32: "F32",
-                Q4_KT: "Q4_KT", Q8_0T: "Q8_0T"}
+                Q4_KT: "Q4_KT", Q8_0T: "Q8_0T", Q5_KT: "Q5_KT"}
 # F16 and F32 tensors hold one weight per "block" (GGUF's unquantized types)
-BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256, Q5_K: 256, F16: 1, F32: 1, Q4_KT: 256, Q8_0T: 32}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210, Q5_K: 176, F16: 2, F32: 4, Q4_KT: 144, Q8_0T: 34}
+BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256, Q5_K: 256, F16: 1, F32: 1, Q4_KT: 256, Q8_0T: 32, Q5_KT: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210, Q5_K: 176, F16: 2, F32: 4, Q4_KT: 144, Q8_0T: 34, Q5_KT: 176}
 # unquantized weights ~ N(0, F_STD): about the spread of trained Llama weight matrices (a reading:
 # the pages give no distribution for them)
 F_STD = 0.02

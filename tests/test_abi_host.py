@@ -36,8 +36,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_block_geometry():
-    assert [nt.nt_block_elems(f) for f in range(9)] == [32, 32, 256, 256, 256, 1, 1, 256, 32]
-    assert [nt.nt_block_bytes(f) for f in range(9)] == [34, 18, 144, 210, 176, 2, 4, 144, 34]
+    assert [nt.nt_block_elems(f) for f in range(10)] == [32, 32, 256, 256, 256, 1, 1, 256, 32, 256]
+    assert [nt.nt_block_bytes(f) for f in range(10)] == [34, 18, 144, 210, 176, 2, 4, 144, 34, 176]
     assert nt.nt_matrix_bytes(nt.Q8_0T, 14336, 4096) == nt.nt_matrix_bytes(nt.Q8_0, 14336, 4096)
     assert nt.nt_matrix_bytes(nt.Q4_KT, 28672, 8192) == nt.nt_matrix_bytes(nt.Q4_K, 28672, 8192)
     assert nt.nt_matrix_bytes(nt.F16, 28672, 8192) == 2 * 28672 * 8192
@@ -47,7 +47,7 @@ def test_block_geometry():
 
 
 @pytest.mark.parametrize("call,code", [
-    (lambda: nt.nt_gemv_q(9, 16, 256, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemv_q(12, 16, 256, 16, 16, 16), nt.NT_EFORMAT),
     (lambda: nt.nt_gemv_q(nt.Q4_K, 16, 100, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemv_q(nt.Q4_K, 0, 256, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemv_q(nt.Q4_K, 16, 65536, 16, 16, 16), nt.NT_ESHAPE),
@@ -74,7 +74,7 @@ def test_block_geometry():
     (lambda: nt.nt_read_probe(16, 24, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_read_probe(None, 16, 16), nt.NT_EINVAL),
     (lambda: nt.nt_read_probe(8, 16, 16), nt.NT_EALIGN),
-    (lambda: nt.nt_gemm_q(10, 16, 256, 2, 16, 16, 16), nt.NT_EFORMAT),
+    (lambda: nt.nt_gemm_q(13, 16, 256, 2, 16, 16, 16), nt.NT_EFORMAT),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, 0, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 256, nt.GEMM_MAX_TOK + 1, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_K, 16, 200, 2, 16, 16, 16), nt.NT_ESHAPE),
@@ -101,7 +101,7 @@ def test_block_geometry():
     (lambda: nt.nt_gemv_q(nt.Q4_0, nt.NT_MAX_ROWS + 1, 32, 16, 16, 16), nt.NT_ESHAPE),
     (lambda: nt.nt_gemm_q(nt.Q4_0, nt.NT_MAX_ROWS + 1, 32, 2, 16, 16, 16), nt.NT_ESHAPE),
     # the greedy head
-    (lambda: nt.nt_lm_head(9, 1000, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_EFORMAT),
+    (lambda: nt.nt_lm_head(14, 1000, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_EFORMAT),
     (lambda: nt.nt_lm_head(nt.Q4_K, 1000, 1000, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_ESHAPE),
     (lambda: nt.nt_lm_head(nt.Q4_K, 0, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_ESHAPE),
     (lambda: nt.nt_lm_head(nt.Q4_K, nt.NT_MAX_ROWS + 1, 1024, 256, 256, 1e-5, 256, 256, 256, 256, 256), nt.NT_ESHAPE),

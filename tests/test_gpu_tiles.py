@@ -375,3 +375,95 @@ def test_decode_layer_q8_0t_close_to_q8_0(shape, pos, register_path):
         torch.cuda.synchronize()
         outs.append(host(h).copy())
     assert np.max(np.abs(outs[0] - outs[1])) <= 1e-4 * np.abs(outs[0]).max()
+
+
+# ------------------------------------------------------------------ Q5_KT
+
+Q5K, Q5KT = synth.Q5_K, synth.Q5_KT
+
+
+def q5kt_layout(blocks: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """The NT_Q5_KT bytes of a Q5_K matrix as include/nt.h describes them."""
+    nsb = cols // 256
+    b = blocks.reshape(rows, nsb, 176)
+    out = np.empty((rows, nsb * 176), np.uint8)
+    for t0 in range(0, nsb, 16):
+        m = min(16, nsb - t0)
+        tile = b[:, t0:t0 + m]
+        base = 176 * t0
+        for part, (lo, hi) in enumerate(((0, 16), (16, 32), (32, 48))):
+            out[:, base + 16 * m * part:base + 16 * m * (part + 1)] = tile[:, :, lo:hi].reshape(rows, -1)
+        qs = tile[:, :, 48:].reshape(rows, m, 4, 2, 16)
+        out[:, base + 48 * m:base + 112 * m] = qs[:, :, :, 0, :].reshape(rows, -1)
+        out[:, base + 112 * m:base + 176 * m] = qs[:, :, :, 1, :].reshape(rows, -1)
+    return out.ravel()
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_repack_q5_kt_layout_and_dequant_bit_exact(rows, cols):
+    say(f"repack Q5_K -> Q5_KT {rows}x{cols}")
+    blocks = synth.quant_matrix(Q5K, rows, cols, seed=3, stream=3200)
+    t = repack_to(Q5KT, rows, cols, dev(blocks))
+    assert np.array_equal(host(t), q5kt_layout(blocks, rows, cols))
+    w = torch.empty(rows * cols, dtype=torch.float32, device="cuda")
+    nt.nt_dequant(Q5KT, rows, cols, t.data_ptr(), w.data_ptr(), stream())
+    assert same_value(host(w).reshape(rows, cols), oracle.dequant_f32(Q5K, rows, cols, blocks))
+
+
+@pytest.mark.parametrize("rows,cols", GEMV_SHAPES)
+def test_gemv_q5_kt_equals_q5_k_and_matches_oracle(rows, cols):
+    say(f"gemv Q5_KT {rows}x{cols}")
+    blocks = synth.quant_matrix(Q5K, rows, cols, seed=0, stream=3300)
+    x = synth.normal_f32(cols, seed=0, stream=3301)
+    w, xd = dev(blocks), dev(x)
+    y_k = gemv(Q5K, rows, cols, w, xd)
+    y_t = gemv(Q5KT, rows, cols, repack_to(Q5KT, rows, cols, w), xd)
+    assert np.array_equal(y_t.view(np.uint32), y_k.view(np.uint32))
+    ref, nrm = oracle.gemv(Q5K, rows, cols, blocks, x.astype(np.float64))
+    check_rel(y_t, ref, nrm, what=f"Q5_KT {rows}x{cols}")
+
+
+@pytest.mark.parametrize("rows,cols,n_tok", [(1, 256, 1), (37, 2304, 3), (300, 16640, 6), (40, 32768, 5), (512, 8192, 2)])
+def test_gemm_q5_kt_matches_oracle(rows, cols, n_tok):
+    say(f"gemm Q5_KT {rows}x{cols} x {n_tok}")
+    blocks = synth.quant_matrix(Q5K, rows, cols, seed=8, stream=3400)
+    X = np.stack([synth.normal_f32(cols, seed=8, stream=3401 + t) for t in range(n_tok)])
+    w = repack_to(Q5KT, rows, cols, dev(blocks))
+    xd = dev(X.astype(np.float32))
+    Y = torch.empty(n_tok * rows, dtype=torch.float32, device="cuda")
+    nt.nt_gemm_q(Q5KT, rows, cols, n_tok, w.data_ptr(), xd.data_ptr(), Y.data_ptr(), stream())
+    Y = host(Y).reshape(n_tok, rows)
+    ref, nrm = oracle.gemm(Q5K, rows, cols, blocks, X.astype(np.float64))
+    for t in range(n_tok):
+        check_rel(Y[t], ref[t], nrm[t], what=f"Q5_KT {rows}x{cols} token {t}")
+
+
+@pytest.mark.parametrize("shape,pos", [(SMALL, 33), (recipes.LLAMA31_70B, 4096)])
+def test_decode_layer_q5_kt_equals_q5_k(shape, pos):
+    """The Q5_K_M layer with its Q5_K matrices tiled gives h, the new K and V and every stage in
+    the workspace bit for bit as with the Q5_K ones."""
+    say(f"decode layer Q5_K_M with tiled Q5_K, dim={shape.dim} pos={pos}")
+    mix = recipes.MIX_Q5_K_M
+    arrays = recipes.layer_arrays(shape, mix, 0)
+    w_k = {k: dev(v) for k, v in arrays.items()}
+    w_t = dict(w_k)
+    fm_t = {n: mix[n] for n in recipes.TENSORS}
+    for n in recipes.TENSORS:
+        if mix[n] == Q5K:
+            w_t[n] = repack_to(Q5KT, *shape.matrix_shape(n), w_k[n])
+            fm_t[n] = Q5KT
+    shp = tg.layer_shape(shape)
+    wsb = nt.nt_decode_layer_ws_bytes(shp)
+    kc0 = recipes.kv_cache_array(shape, 0, "k", pos)
+    vc0 = v_to_device(recipes.kv_cache_array(shape, 0, "v", pos), shape.n_kv_heads, shape.max_ctx)
+    outs = []
+    for fm, w in (({n: mix[n] for n in recipes.TENSORS}, w_k), (fm_t, w_t)):
+        lw = tg.layer_weights([fm[n] for n in recipes.TENSORS], [w[n] for n in recipes.TENSORS], w["attn_norm"],
+                              w["ffn_norm"])
+        h, kc, vc = dev(recipes.hidden_input(shape.dim)), dev(kc0), dev(vc0)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        nt.nt_decode_layer(lw, shp, pos, h.data_ptr(), kc.data_ptr(), vc.data_ptr(), ws.data_ptr(), wsb, stream())
+        torch.cuda.synchronize()
+        outs.append([host(h).view(np.uint32).copy(), host(kc).copy(), host(vc).copy(), host(ws).copy()])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)

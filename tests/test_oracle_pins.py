@@ -257,7 +257,7 @@ def test_format_sizes_match_page_figures():
 def test_bits_per_weight():
     bpw = {f: 8 * synth.BLOCK_BYTES[f] / synth.BLOCK_ELEMS[f] for f in synth.BLOCK_BYTES}
     assert bpw == {synth.Q8_0: 8.5, synth.Q4_0: 4.5, synth.Q4_K: 4.5, synth.Q6_K: 6.5625, synth.Q5_K: 5.5,
-                   synth.F16: 16.0, synth.F32: 32.0, synth.Q4_KT: 4.5, synth.Q8_0T: 8.5}
+                   synth.F16: 16.0, synth.F32: 32.0, synth.Q4_KT: 4.5, synth.Q8_0T: 8.5, synth.Q5_KT: 5.5}
     # the checker knows the pages' formats; Q4_KT is the library's arrangement of Q4_K bytes
     for f in (synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K, synth.Q5_K, synth.F16, synth.F32):
         assert oracle.block_bytes(f) == synth.BLOCK_BYTES[f]
